@@ -1,0 +1,260 @@
+"""Benchmark of the MX quantized linear hot path on one MI355X.
+
+A step is one forward pass of every quantized linear of the workload (the
+policy lookup, activation quantization and scaled GEMM of each linear, the
+FFN's GELU epilogue and the re-quantization of its hidden state), with all
+inputs and packed weights already resident in HBM. Weight packing is offline
+and is timed separately (reported, not part of the step).
+
+    python bench.py [--steps K] [--warmup W] [--workload a14b_stack|a14b_ffn|qkv|ti2v|tiny]
+
+Prints one JSON line. Per-launch kernel durations come from HIP events
+recorded on the launch stream around every kernel inside the timed steps.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+METRIC = "W4A4/W4A8 qlinear TFLOP/s + % MFMA peak at Wan2.2-A14B 720p shapes"
+PEAK_TFLOPS = {0: 10100.0, 1: 5000.0}  # dense MFMA: fp4 (W4A4), fp8 (W4A8 issues at the fp8 rate)
+PEAK_HBM_GBS = 8000.0
+WORKLOADS = {"tiny": 1, "qkv": 2, "a14b_ffn": 3, "ti2v": 4, "a14b_stack": 5}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="a14b_stack", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rows", type=int, default=512)
+    return ap.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+class Stack:
+    """Packed weights, inputs and buffers of one workload on the device."""
+
+    def __init__(self, wl, torch, mxq):
+        self.wl, self.torch, self.mxq = wl, torch, mxq
+        dev = "cuda:0"
+        t0 = time.time()
+        self.policy_table = wl.policy()
+        self.policy = mxq.Policy(self.policy_table)
+        to_dev = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
+        self.x_video = to_dev(synth.activation_bf16(wl.config_id, wl.m_video, wl.dim, wl.outliers,
+                                                    tensor_id=synth.T_X_VIDEO))
+        self.x_text = None
+        if wl.m_text:
+            self.x_text = to_dev(synth.activation_bf16(wl.config_id, wl.m_text, wl.dim, wl.outliers,
+                                                       tensor_id=synth.T_X_TEXT))
+        log(f"activations ready in {time.time() - t0:.1f}s")
+        # packed weights: drawn on the device per linear, packed, bf16 copy freed
+        self.weights = {}
+        pack_bytes, pack_ms = 0, 0.0
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for e in range(wl.n_experts):
+            for b in range(wl.n_blocks):
+                for li, lin in enumerate(wl.linears):
+                    w = synth.weight_bf16_device(wl.config_id, lin.n, lin.k, e, b, li)
+                    codes = torch.empty((lin.n, lin.k // 2), dtype=torch.uint8, device=dev)
+                    scales = torch.empty((lin.n, lin.k // 32), dtype=torch.uint8, device=dev)
+                    ev0.record()
+                    mxq.quantize_weight_mxfp4(w, codes, scales)
+                    ev1.record()
+                    torch.cuda.synchronize()
+                    pack_ms += ev0.elapsed_time(ev1)
+                    pack_bytes += lin.n * lin.k * 2 + lin.n * lin.k // 2 + lin.n * lin.k // 32
+                    self.weights[(e, b, li)] = (codes, scales)
+                    del w
+        self.pack_gbs = pack_bytes / (pack_ms * 1e-3) / 1e9
+        log(f"weights packed in {time.time() - t0:.1f}s ({pack_bytes / 1e9:.1f} GB traffic, {self.pack_gbs:.0f} GB/s)")
+        m_max = wl.m_video
+        n_max = max(l.n for l in wl.linears)
+        self.y = torch.empty((m_max * n_max,), dtype=torch.bfloat16, device=dev)
+        self.h = torch.empty((wl.m_video * max(wl.ffn, 1),), dtype=torch.bfloat16, device=dev)
+        ws = max(mxq.qlinear_workspace_bytes(md, m_max, l.k) for md in (0, 1) for l in wl.linears)
+        self.codes_buf = torch.empty((ws,), dtype=torch.uint8, device=dev)
+        self.records = []  # (kind, mode, flops, bytes, ev_start, ev_end)
+
+    def _act_views(self, mode, m, k):
+        torch = self.torch
+        if mode == 0:
+            cb = m * k // 2
+            codes = self.codes_buf[:cb].view(m, k // 2)
+            off = (cb + 255) // 256 * 256
+            scales = self.codes_buf[off:off + m * k // 32].view(m, k // 32)
+        else:
+            cb = m * k
+            codes = self.codes_buf[:cb].view(m, k)
+            off = (cb + 255) // 256 * 256
+            scales = self.codes_buf[off:off + 4 * m].view(torch.float32)
+        return codes, scales
+
+    def step(self, timed):
+        torch, mxq, wl = self.torch, self.mxq, self.wl
+        for e in range(wl.n_experts):
+            for b in range(wl.n_blocks):
+                mode = self.policy.mode(e, b)
+                for li, lin in enumerate(wl.linears):
+                    m = wl.m_of(lin)
+                    if lin.m_role == "video":
+                        x = self.x_video
+                    elif lin.m_role == "text":
+                        x = self.x_text
+                    else:
+                        x = self.h[: m * lin.k].view(m, lin.k)
+                    out = (self.h if lin.epilogue == 1 else self.y)[: m * lin.n].view(m, lin.n)
+                    codes, scales = self._act_views(mode, m, lin.k)
+                    wc, wsc = self.weights[(e, b, li)]
+                    if timed:
+                        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+                        e0.record()
+                    mxq.quantize_act(mode, x, codes, scales)
+                    if timed:
+                        e1.record()
+                    mxq.gemm(mode, codes, scales, wc, wsc, None, lin.epilogue, out)
+                    if timed:
+                        e2.record()
+                        qbytes = m * lin.k * 2 + (m * lin.k // 2 + m * lin.k // 32 if mode == 0 else m * lin.k + 4 * m)
+                        gbytes = ((m * lin.k // 2 + m * lin.k // 32) if mode == 0 else (m * lin.k + 4 * m)) \
+                            + lin.n * lin.k // 2 + lin.n * lin.k // 32 + m * lin.n * 2
+                        self.records.append(("quant", mode, 0, qbytes, e0, e1))
+                        self.records.append(("gemm", mode, 2 * m * lin.n * lin.k, gbytes, e1, e2))
+
+
+def cpu_baseline(wl, sample_rows):
+    """Oracle throughput on a bounded sample: `sample_rows` token rows through one block's linears."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    table = wl.policy()
+    mode_block = {0: None, 1: None}
+    for b in range(wl.n_blocks):
+        md = int(table[0, b])
+        if mode_block[md] is None:
+            mode_block[md] = b
+    flops, secs = 0, 0.0
+    rows = min(sample_rows, wl.m_video)
+    x = synth.activation_bf16(wl.config_id, rows, wl.dim, wl.outliers, tensor_id=synth.T_X_VIDEO)
+    for md, b in mode_block.items():
+        if b is None:
+            continue
+        for li, lin in enumerate(wl.linears):
+            if lin.m_role == "ffn_hidden":
+                continue
+            w = synth.weight_bf16(wl.config_id, lin.n, lin.k, 0, b, li)
+            wq, wsc = oracle.mxfp4_quantize(w)  # offline on both sides; not timed
+            t0 = time.perf_counter()
+            y, _, _ = oracle.qlinear(md, x[:, : lin.k], wq, wsc, epilogue=lin.epilogue)
+            secs += time.perf_counter() - t0
+            flops += 2 * rows * lin.n * lin.k
+            if secs > 10:
+                break
+        if secs > 10:
+            break
+    return {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{rows} token rows through the first W4A4 and first W4A8 block's video-token linears "
+                      f"(quantize + float64 QDQ matmul), {flops / 1e9:.1f} GFLOP in {secs:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import mx_bit_quantized_amd as mxq
+
+    assert torch.cuda.is_available(), "bench.py needs a HIP device"
+    torch.cuda.set_device(0)
+    mxq.lib()
+    wl = synth.workload(WORKLOADS[args.workload])
+    stack = Stack(wl, torch, mxq)
+    for _ in range(args.warmup):
+        stack.step(timed=False)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        stack.step(timed=True)
+    end.record()
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+    tflops = wl.total_flops() / (ms_per_step * 1e-3) / 1e12
+
+    # per-kernel aggregates from the per-launch events
+    agg = {}
+    for kind, mode, fl, by, e0, e1 in stack.records:
+        ms = e0.elapsed_time(e1)
+        a = agg.setdefault((kind, mode), {"ms": 0.0, "flops": 0, "bytes": 0, "launches": 0})
+        a["ms"] += ms
+        a["flops"] += fl
+        a["bytes"] += by
+        a["launches"] += 1
+    kernels = {}
+    for (kind, mode), a in agg.items():
+        name = f"{kind}_{'w4a4' if mode == 0 else 'w4a8'}"
+        d = {"launches_per_step": a["launches"] // args.steps, "avg_us": round(1e3 * a["ms"] / a["launches"], 2),
+             "share_of_step": round(a["ms"] / total_ms, 4)}
+        if kind == "gemm":
+            d["tflops"] = round(a["flops"] / (a["ms"] * 1e-3) / 1e12, 1)
+            d["frac_of_peak"] = round(d["tflops"] / PEAK_TFLOPS[mode], 4)
+        else:
+            d["gbs"] = round(a["bytes"] / (a["ms"] * 1e-3) / 1e9, 1)
+            d["frac_of_hbm"] = round(d["gbs"] / PEAK_HBM_GBS, 4)
+        kernels[name] = d
+    dom = max((k for k in agg if k[0] == "gemm"), key=lambda k: agg[k]["ms"])
+    a = agg[dom]
+    achieved = a["flops"] / (a["ms"] * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_TFLOPS[dom[1]], "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_TFLOPS[dom[1]], 4), "traffic": None,
+                "kernel": f"gemm_{'w4a4' if dom[1] == 0 else 'w4a8'}"}
+    modes = set(int(v) for v in stack.policy_table.flat)
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "+".join(x for x, md in (("mxfp4xmxfp4", 0), ("fp8e4m3xmxfp4", 1)) if md in modes) + "->fp32acc->bf16",
+        "data": "synthetic (seeded activations with Student-t outlier channels; N(0,0.02) weights, RTN MXFP4)",
+        "config": {"workload": wl.name, "m_video": wl.m_video, "m_text": wl.m_text, "dim": wl.dim, "ffn": wl.ffn,
+                   "experts": wl.n_experts, "blocks": wl.n_blocks,
+                   "w4a8_blocks": int((stack.policy_table == 1).sum()),
+                   "linears_per_block": len(wl.linears), "tflop_per_step": round(wl.total_flops() / 1e12, 2)},
+        "roofline": roofline,
+        "kernels": kernels,
+        "weight_pack_gbs": round(stack.pack_gbs, 1),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

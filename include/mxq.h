@@ -1,0 +1,169 @@
+/*
+ * mxq.h - C ABI of libmxq, the MI355X (gfx950) MX quantized linear.
+ *
+ * The operations follow the page "Quark Mixed-Precision Quantization for
+ * Wan2.2 Video Generation on AMD Instinct GPUs":
+ *   - section "Quantization formats": W4A4 = OCP MXFP4 weights with dynamic
+ *     MXFP4 activations (the default, natively executed path); W4A8 = OCP
+ *     MXFP4 weights with FP8 E4M3 activations (the promotion path);
+ *   - section "Results" (rows marked RTN): weights are quantized by plain
+ *     round-to-nearest;
+ *   - section "Practical workflow" (step 6 and the paragraph after it): a
+ *     per-expert, per-block policy artifact lets the runtime keep most blocks
+ *     on W4A4 and spend W4A8 only on the blocks calibration flagged.
+ *
+ * Data formats (all row-major, K contiguous):
+ *   bf16 tensor      uint16 bit patterns, [rows][ld] with ld >= K.
+ *   MXFP4 codes      uint8 [rows][K/2]; element 2t of a row in the low
+ *                    nibble of byte t, element 2t+1 in the high nibble.
+ *                    Each nibble is E2M1 (sign bit 3; magnitudes 0, .5, 1,
+ *                    1.5, 2, 3, 4, 6).
+ *   MXFP4 scales     uint8 [rows][K/32], E8M0 (value 2^(u-127)), one per 32
+ *                    consecutive elements along K.
+ *   FP8 codes        uint8 [M][K], E4M3FN (max 448, 0x7F/0xFF NaN).
+ *   FP8 scales       float32 [M], one per row (token).
+ *
+ * Quantization rules:
+ *   MXFP4 block: E = floor(log2 amax) - 2, clamped to [-127, 127]; an
+ *     all-zero block has E = -127. code = E2M1 round-half-to-even of
+ *     v / 2^E, saturating at +-6; the sign of v is kept (also for zeros).
+ *   FP8 per token: s = fp32(amax) / 448 (IEEE fp32 division);
+ *     code = E4M3FN round-half-to-even of the IEEE fp32 quotient x / s,
+ *     saturating at +-448; a row of zeros has s = 0 and signed-zero codes.
+ *   GEMM: y[m][n] = sum_k deqA[m][k] * deqW[n][k] accumulated in fp32, plus
+ *     bias[n] (if given), optional tanh-GELU, rounded to bf16
+ *     (round-half-to-even). For W4A8 the per-token scale multiplies the fp32
+ *     sum of row m.
+ *
+ * Conventions of every entry point:
+ *   - Device pointers are plain addresses in the current HIP device's memory;
+ *     host pointers are marked as such. The caller owns every buffer and
+ *     keeps it alive until the work on the stream has completed. The library
+ *     allocates no device memory.
+ *   - Work is only enqueued on `stream` (0 = the null stream); nothing
+ *     synchronizes. Results are valid once the stream has reached that point.
+ *   - Arguments are validated on the host before anything is enqueued; on an
+ *     error nothing is written. An empty problem (M == 0 or N == 0) enqueues
+ *     nothing, returns MXQ_OK and accepts null pointers.
+ *   - Device pointers must be 16-byte aligned and leading dimensions multiples
+ *     of 8 elements (MXQ_ERR_ALIGN otherwise).
+ *   - K must be a positive multiple of 32 (MXQ_ERR_SHAPE otherwise); sizes
+ *     must stay below 2^31 elements per dimension and 2^31 rows.
+ *   - Functions are thread-safe; calls that share output buffers must be
+ *     ordered by the caller.
+ */
+#ifndef MXQ_H
+#define MXQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes returned by every entry point. */
+enum {
+  MXQ_OK = 0,
+  MXQ_ERR_NULL = 1,      /* a required pointer is null                      */
+  MXQ_ERR_SHAPE = 2,     /* negative size, K not a positive multiple of 32,
+                            ld < K, or a size beyond the supported range    */
+  MXQ_ERR_ALIGN = 3,     /* device pointer not 16-byte aligned, or ld not a
+                            multiple of 8                                   */
+  MXQ_ERR_MODE = 4,      /* mode/epilogue not supported: only W4A4 and W4A8
+                            are quantized-linear modes (no silent fallback) */
+  MXQ_ERR_WORKSPACE = 5, /* workspace missing or too small                  */
+  MXQ_ERR_HIP = 6,       /* a HIP launch or runtime call failed             */
+  MXQ_ERR_RANGE = 7      /* policy index (expert, block) out of range       */
+};
+
+/* Precision modes: values of the policy table. The page's policy artifact
+ * also has "bf16" and "transform_on" entries; they are not modes of this
+ * layer and are rejected with MXQ_ERR_MODE. */
+enum { MXQ_W4A4 = 0, MXQ_W4A8 = 1, MXQ_POLICY_BF16 = 2, MXQ_POLICY_TRANSFORM_ON = 3 };
+
+/* GEMM epilogues. The FFN's first projection is followed by tanh-GELU:
+ * 0.5 y (1 + tanh(sqrt(2/pi) (y + 0.044715 y^3))). */
+enum { MXQ_EPI_NONE = 0, MXQ_EPI_GELU_TANH = 1 };
+
+/* Human-readable name of a status code (static string, never null). */
+const char* mxq_status_string(int status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int mxq_version(void);
+
+/*
+ * Offline round-to-nearest MXFP4 weight packing (weights W [N][K] bf16,
+ * nn.Linear layout) - the RTN weight quantization of the page's "Results"
+ * table, in the MXFP4 format of "Quantization formats".
+ *   w       device, bf16 [N][ldw]
+ *   codes   device, uint8 [N][K/2]   (output)
+ *   scales  device, uint8 [N][K/32]  (output, E8M0)
+ */
+int mxq_quantize_weight_mxfp4(const void* w, int64_t N, int64_t K, int64_t ldw,
+                              void* codes, void* scales, hipStream_t stream);
+
+/*
+ * Dynamic activation quantization ("Quantization formats"): MXQ_W4A4 gives
+ * MXFP4 codes [M][K/2] + E8M0 scales [M][K/32]; MXQ_W4A8 gives E4M3FN codes
+ * [M][K] + float32 per-token scales [M].
+ *   x       device, bf16 [M][ldx]
+ *   codes   device (output), scales device (output)
+ */
+int mxq_quantize_act(int mode, const void* x, int64_t M, int64_t K, int64_t ldx,
+                     void* codes, void* scales, hipStream_t stream);
+
+/*
+ * Scaled GEMM on quantized operands (the native MXFP4 / W4A8 execution of
+ * "Quantization formats", kernel note): y [M][N] bf16 =
+ *   epilogue( sum_k deqA[m][k] deqW[n][k] + bias[n] ).
+ *   a_codes/a_scales  device, from mxq_quantize_act(mode, ...)
+ *   w_codes/w_scales  device, from mxq_quantize_weight_mxfp4
+ *   bias              device bf16 [N], or null for none
+ *   y                 device bf16 [M][N] (output, dense)
+ */
+int mxq_gemm(int mode, const void* a_codes, const void* a_scales,
+             const void* w_codes, const void* w_scales, const void* bias,
+             int epilogue, void* y, int64_t M, int64_t N, int64_t K,
+             hipStream_t stream);
+
+/*
+ * Per-expert, per-block policy table ("Practical workflow", step 6).
+ *   modes   host, uint8 [n_experts][n_blocks]; each entry MXQ_W4A4 or
+ *           MXQ_W4A8 (anything else: MXQ_ERR_MODE). Copied; the caller may
+ *           free it after the call.
+ *   policy  host, receives an opaque handle owned by the caller, released
+ *           with mxq_policy_destroy.
+ */
+int mxq_policy_create(const uint8_t* modes, int32_t n_experts, int32_t n_blocks, void** policy);
+int mxq_policy_destroy(void* policy);
+/* Mode of (expert, block): MXQ_ERR_RANGE when out of range. mode: host out. */
+int mxq_policy_mode(const void* policy, int32_t expert, int32_t block, int* mode);
+
+/* Workspace bytes mxq_qlinear needs for the activation codes and scales of
+ * an [M][K] input in `mode` (bytes: host out). */
+int mxq_qlinear_workspace_bytes(int mode, int64_t M, int64_t K, size_t* bytes);
+
+/*
+ * One quantized linear layer: looks up the mode of (expert, block) in the
+ * policy, quantizes x into the workspace with that mode's activation format,
+ * then runs the scaled GEMM into y. Exactly mxq_quantize_act followed by
+ * mxq_gemm.
+ *   x          device bf16 [M][K] (dense)
+ *   w_codes    device uint8 [N][K/2], w_scales device uint8 [N][K/32]
+ *   bias       device bf16 [N] or null
+ *   y          device bf16 [M][N] (output)
+ *   workspace  device, at least mxq_qlinear_workspace_bytes(mode, M, K)
+ */
+int mxq_qlinear(const void* policy, int32_t expert, int32_t block,
+                const void* x, int64_t M, int64_t K,
+                const void* w_codes, const void* w_scales, int64_t N,
+                const void* bias, int epilogue, void* y,
+                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXQ_H */

@@ -1,0 +1,245 @@
+"""mx_bit_quantized_amd - MI355X-native W4A4 / W4A8 MX quantized linear.
+
+Thin Python binding over libmxq.so (include/mxq.h): argument marshalling
+only. Every step of the computation runs in the library's gfx950 kernels;
+torch supplies device memory and the current HIP stream. There is no CPU or
+PyTorch fallback: if the library is missing, every call raises.
+
+Names mirror the C ABI without its ``mxq_`` prefix:
+
+    quantize_weight_mxfp4(w)                      -> (codes, scales)
+    quantize_act(mode, x)                         -> (codes, scales)
+    gemm(mode, a_codes, a_scales, w_codes, w_scales, bias=None, epilogue=EPI_NONE)
+    Policy(table) / policy_create / policy_destroy / policy_mode
+    qlinear_workspace_bytes(mode, M, K)
+    qlinear(policy, expert, block, x, w_codes, w_scales, bias=None, epilogue=EPI_NONE)
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmxq.so")
+
+# status codes, modes and epilogues (include/mxq.h)
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_MODE, ERR_WORKSPACE, ERR_HIP, ERR_RANGE = range(8)
+W4A4, W4A8, POLICY_BF16, POLICY_TRANSFORM_ON = 0, 1, 2, 3
+EPI_NONE, EPI_GELU_TANH = 0, 1
+
+# every function the header declares, with its ctypes signature
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_SIGS = {
+    "mxq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "mxq_version": (ctypes.c_int, []),
+    "mxq_quantize_weight_mxfp4": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P]),
+    "mxq_quantize_act": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, _I64, _P, _P, _P]),
+    "mxq_gemm": (ctypes.c_int, [ctypes.c_int, _P, _P, _P, _P, _P, ctypes.c_int, _P, _I64, _I64, _I64, _P]),
+    "mxq_policy_create": (ctypes.c_int, [_P, _I32, _I32, ctypes.POINTER(_P)]),
+    "mxq_policy_destroy": (ctypes.c_int, [_P]),
+    "mxq_policy_mode": (ctypes.c_int, [_P, _I32, _I32, ctypes.POINTER(ctypes.c_int)]),
+    "mxq_qlinear_workspace_bytes": (ctypes.c_int, [ctypes.c_int, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)]),
+    "mxq_qlinear": (ctypes.c_int, [_P, _I32, _I32, _P, _I64, _I64, _P, _P, _I64, _P, ctypes.c_int, _P,
+                                   _P, ctypes.c_size_t, _P]),
+}
+
+
+class MxqError(RuntimeError):
+    def __init__(self, status, what):
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libmxq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m mx_bit_quantized_amd._build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def status_string(status):
+    return lib().mxq_status_string(int(status)).decode()
+
+
+def version():
+    return lib().mxq_version()
+
+
+def _check(status, what):
+    if status != OK:
+        raise MxqError(status, what)
+
+
+# ------------------------------------------------------------- tensors ----
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _stream_handle(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev_ptr(t, name, dtype=None):
+    if t is None:
+        return None
+    torch = _torch()
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must have dtype {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (no implicit copies)")
+    return ctypes.c_void_p(t.data_ptr()) if t.numel() else None
+
+
+def _rows_k(t, name):
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D [rows, K]")
+    return int(t.shape[0]), int(t.shape[1])
+
+
+def act_buffers(mode, M, K, device):
+    """Empty (codes, scales) tensors for quantize_act in ``mode``."""
+    torch = _torch()
+    if mode == W4A4:
+        return (torch.empty((M, K // 2), dtype=torch.uint8, device=device),
+                torch.empty((M, K // 32), dtype=torch.uint8, device=device))
+    if mode == W4A8:
+        return (torch.empty((M, K), dtype=torch.uint8, device=device),
+                torch.empty((M,), dtype=torch.float32, device=device))
+    raise MxqError(ERR_MODE, "act_buffers")
+
+
+def quantize_weight_mxfp4(w, codes=None, scales=None, stream=None):
+    """RTN MXFP4 packing of bf16 weights [N, K] -> (codes uint8 [N, K/2], scales uint8 [N, K/32])."""
+    torch = _torch()
+    n, k = _rows_k(w, "w")
+    if codes is None:
+        codes = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
+    if scales is None:
+        scales = torch.empty((n, k // 32), dtype=torch.uint8, device=w.device)
+    st = lib().mxq_quantize_weight_mxfp4(_dev_ptr(w, "w", torch.bfloat16), n, k, k,
+                                          _dev_ptr(codes, "codes", torch.uint8),
+                                          _dev_ptr(scales, "scales", torch.uint8), _stream_handle(stream))
+    _check(st, "quantize_weight_mxfp4")
+    return codes, scales
+
+
+def quantize_act(mode, x, codes=None, scales=None, stream=None):
+    """Dynamic activation quantization of bf16 x [M, K] in ``mode`` -> (codes, scales)."""
+    torch = _torch()
+    m, k = _rows_k(x, "x")
+    if codes is None or scales is None:
+        codes, scales = act_buffers(mode, m, k, x.device) if mode in (W4A4, W4A8) else (None, None)
+    st = lib().mxq_quantize_act(int(mode), _dev_ptr(x, "x", torch.bfloat16), m, k, k,
+                                 _dev_ptr(codes, "codes"), _dev_ptr(scales, "scales"), _stream_handle(stream))
+    _check(st, "quantize_act")
+    return codes, scales
+
+
+def gemm(mode, a_codes, a_scales, w_codes, w_scales, bias=None, epilogue=EPI_NONE, y=None, stream=None):
+    """Scaled GEMM on quantized operands -> y bf16 [M, N]."""
+    torch = _torch()
+    m = int(a_codes.shape[0])
+    n = int(w_codes.shape[0])
+    k = int(w_codes.shape[1]) * 2
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=w_codes.device)
+    st = lib().mxq_gemm(int(mode), _dev_ptr(a_codes, "a_codes"), _dev_ptr(a_scales, "a_scales"),
+                         _dev_ptr(w_codes, "w_codes", torch.uint8), _dev_ptr(w_scales, "w_scales", torch.uint8),
+                         _dev_ptr(bias, "bias", torch.bfloat16), int(epilogue),
+                         _dev_ptr(y, "y", torch.bfloat16), m, n, k, _stream_handle(stream))
+    _check(st, "gemm")
+    return y
+
+
+# -------------------------------------------------------------- policy ----
+
+def policy_create(table):
+    t = np.ascontiguousarray(np.asarray(table, dtype=np.uint8))
+    if t.ndim != 2:
+        raise ValueError("policy table must be 2-D [n_experts, n_blocks]")
+    h = ctypes.c_void_p()
+    st = lib().mxq_policy_create(t.ctypes.data_as(ctypes.c_void_p), t.shape[0], t.shape[1], ctypes.byref(h))
+    _check(st, "policy_create")
+    return h
+
+
+def policy_destroy(handle):
+    _check(lib().mxq_policy_destroy(handle), "policy_destroy")
+
+
+def policy_mode(handle, expert, block):
+    mode = ctypes.c_int()
+    _check(lib().mxq_policy_mode(handle, int(expert), int(block), ctypes.byref(mode)), "policy_mode")
+    return mode.value
+
+
+class Policy:
+    """Per-expert, per-block W4A4 / W4A8 table owned by the library."""
+
+    def __init__(self, table):
+        self.table = np.array(table, dtype=np.uint8)
+        self.handle = policy_create(self.table)
+
+    def mode(self, expert, block):
+        return policy_mode(self.handle, expert, block)
+
+    def close(self):
+        if self.handle is not None and _lib is not None:
+            policy_destroy(self.handle)
+        self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def qlinear_workspace_bytes(mode, M, K):
+    out = ctypes.c_size_t()
+    _check(lib().mxq_qlinear_workspace_bytes(int(mode), int(M), int(K), ctypes.byref(out)),
+           "qlinear_workspace_bytes")
+    return out.value
+
+
+def qlinear(policy, expert, block, x, w_codes, w_scales, bias=None, epilogue=EPI_NONE,
+            y=None, workspace=None, stream=None):
+    """One quantized linear under the policy: quantize x with (expert, block)'s mode, then GEMM."""
+    torch = _torch()
+    handle = policy.handle if isinstance(policy, Policy) else policy
+    m, k = _rows_k(x, "x")
+    n = int(w_codes.shape[0])
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        mode = policy_mode(handle, expert, block)
+        workspace = torch.empty((max(qlinear_workspace_bytes(mode, m, k), 1),), dtype=torch.uint8,
+                                device=x.device)
+    st = lib().mxq_qlinear(handle, int(expert), int(block), _dev_ptr(x, "x", torch.bfloat16), m, k,
+                            _dev_ptr(w_codes, "w_codes", torch.uint8), _dev_ptr(w_scales, "w_scales", torch.uint8),
+                            n, _dev_ptr(bias, "bias", torch.bfloat16), int(epilogue),
+                            _dev_ptr(y, "y", torch.bfloat16), _dev_ptr(workspace, "workspace", torch.uint8),
+                            int(workspace.numel()), _stream_handle(stream))
+    _check(st, "qlinear")
+    return y

@@ -1,0 +1,194 @@
+// mxq_api.cpp - the extern "C" boundary of libmxq (declared in include/mxq.h).
+//
+// Host-side validation, the per-expert / per-block policy table of section
+// "Practical workflow" (step 6) of the page "Quark Mixed-Precision
+// Quantization for Wan2.2 Video Generation on AMD Instinct GPUs", and dispatch
+// to the gfx950 kernels. Every check runs before anything is enqueued, so a
+// failing call writes nothing; modes other than W4A4 / W4A8 are errors, never
+// a silent fallback.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <new>
+#include <vector>
+
+#include "mxq.h"
+#include "mxq_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t)1 << 31;
+
+struct Policy {
+  int32_t n_experts;
+  int32_t n_blocks;
+  std::vector<uint8_t> modes;
+};
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool log_enabled() {
+  static const int on = [] {
+    const char* v = getenv("MXQ_LOG");
+    return (v != nullptr && v[0] != '\0' && v[0] != '0') ? 1 : 0;
+  }();
+  return on != 0;
+}
+
+int check_mk(int64_t rows, int64_t K, int64_t ld) {
+  if (rows < 0 || K <= 0 || ld < 0) return MXQ_ERR_SHAPE;
+  if (K % 32 != 0 || ld < K) return MXQ_ERR_SHAPE;
+  if (rows >= kMaxDim || K >= kMaxDim || ld >= kMaxDim) return MXQ_ERR_SHAPE;
+  return MXQ_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MXQ_OK : MXQ_ERR_HIP; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Workspace layout of mxq_qlinear: codes first, scales at a 256-byte boundary.
+void workspace_layout(int mode, int64_t M, int64_t K, size_t* codes_bytes, size_t* total) {
+  size_t cb = mode == MXQ_W4A4 ? (size_t)M * (size_t)(K / 2) : (size_t)M * (size_t)K;
+  size_t sb = mode == MXQ_W4A4 ? (size_t)M * (size_t)(K / 32) : (size_t)M * sizeof(float);
+  *codes_bytes = round_up(cb, 256);
+  *total = *codes_bytes + round_up(sb, 256);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mxq_status_string(int status) {
+  switch (status) {
+    case MXQ_OK: return "ok";
+    case MXQ_ERR_NULL: return "null pointer";
+    case MXQ_ERR_SHAPE: return "bad shape (sizes must be >= 0, K a positive multiple of 32, ld >= K, dims < 2^31)";
+    case MXQ_ERR_ALIGN: return "misaligned (device pointers need 16-byte alignment, ld a multiple of 8)";
+    case MXQ_ERR_MODE: return "unsupported mode or epilogue (quantized linear modes are W4A4 and W4A8)";
+    case MXQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case MXQ_ERR_HIP: return "HIP launch or runtime error";
+    case MXQ_ERR_RANGE: return "policy index out of range";
+    default: return "unknown status";
+  }
+}
+
+int mxq_version(void) { return 10000; }
+
+int mxq_quantize_weight_mxfp4(const void* w, int64_t N, int64_t K, int64_t ldw,
+                              void* codes, void* scales, hipStream_t stream) {
+  int st = check_mk(N, K, ldw);
+  if (st != MXQ_OK) return st;
+  if (N == 0) return MXQ_OK;
+  if (w == nullptr || codes == nullptr || scales == nullptr) return MXQ_ERR_NULL;
+  if (!aligned16(w) || !aligned16(codes) || !aligned16(scales) || ldw % 8 != 0) return MXQ_ERR_ALIGN;
+  if (log_enabled()) fprintf(stderr, "[mxq] quantize_weight_mxfp4 N=%lld K=%lld\n", (long long)N, (long long)K);
+  return hip_status(mxq::launch_mxfp4_quant(w, N, K, ldw, codes, scales, stream));
+}
+
+int mxq_quantize_act(int mode, const void* x, int64_t M, int64_t K, int64_t ldx,
+                     void* codes, void* scales, hipStream_t stream) {
+  if (mode != MXQ_W4A4 && mode != MXQ_W4A8) return MXQ_ERR_MODE;
+  int st = check_mk(M, K, ldx);
+  if (st != MXQ_OK) return st;
+  if (M == 0) return MXQ_OK;
+  if (x == nullptr || codes == nullptr || scales == nullptr) return MXQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || ldx % 8 != 0) return MXQ_ERR_ALIGN;
+  if (log_enabled())
+    fprintf(stderr, "[mxq] quantize_act %s M=%lld K=%lld\n", mode == MXQ_W4A4 ? "mxfp4" : "fp8_per_token",
+            (long long)M, (long long)K);
+  if (mode == MXQ_W4A4) return hip_status(mxq::launch_mxfp4_quant(x, M, K, ldx, codes, scales, stream));
+  return hip_status(mxq::launch_fp8_quant(x, M, K, ldx, codes, scales, stream));
+}
+
+int mxq_gemm(int mode, const void* a_codes, const void* a_scales,
+             const void* w_codes, const void* w_scales, const void* bias,
+             int epilogue, void* y, int64_t M, int64_t N, int64_t K,
+             hipStream_t stream) {
+  if (mode != MXQ_W4A4 && mode != MXQ_W4A8) return MXQ_ERR_MODE;
+  if (epilogue != MXQ_EPI_NONE && epilogue != MXQ_EPI_GELU_TANH) return MXQ_ERR_MODE;
+  int st = check_mk(M, K, K);
+  if (st != MXQ_OK) return st;
+  if (N < 0 || N >= kMaxDim) return MXQ_ERR_SHAPE;
+  if (M == 0 || N == 0) return MXQ_OK;
+  if (a_codes == nullptr || a_scales == nullptr || w_codes == nullptr || w_scales == nullptr || y == nullptr)
+    return MXQ_ERR_NULL;
+  if (!aligned16(a_codes) || !aligned16(a_scales) || !aligned16(w_codes) || !aligned16(w_scales) ||
+      !aligned16(y) || (bias != nullptr && !aligned16(bias)))
+    return MXQ_ERR_ALIGN;
+  if (log_enabled())
+    fprintf(stderr, "[mxq] gemm %s M=%lld N=%lld K=%lld epi=%d kernel=%s\n", mode == MXQ_W4A4 ? "w4a4" : "w4a8",
+            (long long)M, (long long)N, (long long)K, epilogue, mxq::gemm_variant_name(mode, M, N, K));
+  return hip_status(mxq::launch_gemm(mode, a_codes, a_scales, w_codes, w_scales, bias, epilogue, y, M, N, K, stream));
+}
+
+int mxq_policy_create(const uint8_t* modes, int32_t n_experts, int32_t n_blocks, void** policy) {
+  if (policy == nullptr) return MXQ_ERR_NULL;
+  *policy = nullptr;
+  if (n_experts <= 0 || n_blocks <= 0) return MXQ_ERR_SHAPE;
+  if (modes == nullptr) return MXQ_ERR_NULL;
+  const size_t n = (size_t)n_experts * (size_t)n_blocks;
+  for (size_t i = 0; i < n; ++i)
+    if (modes[i] != MXQ_W4A4 && modes[i] != MXQ_W4A8) return MXQ_ERR_MODE;
+  Policy* p = new (std::nothrow) Policy;
+  if (p == nullptr) return MXQ_ERR_HIP;
+  p->n_experts = n_experts;
+  p->n_blocks = n_blocks;
+  p->modes.assign(modes, modes + n);
+  *policy = p;
+  return MXQ_OK;
+}
+
+int mxq_policy_destroy(void* policy) {
+  delete static_cast<Policy*>(policy);
+  return MXQ_OK;
+}
+
+int mxq_policy_mode(const void* policy, int32_t expert, int32_t block, int* mode) {
+  if (policy == nullptr || mode == nullptr) return MXQ_ERR_NULL;
+  const Policy* p = static_cast<const Policy*>(policy);
+  if (expert < 0 || expert >= p->n_experts || block < 0 || block >= p->n_blocks) return MXQ_ERR_RANGE;
+  *mode = p->modes[(size_t)expert * (size_t)p->n_blocks + (size_t)block];
+  return MXQ_OK;
+}
+
+int mxq_qlinear_workspace_bytes(int mode, int64_t M, int64_t K, size_t* bytes) {
+  if (bytes == nullptr) return MXQ_ERR_NULL;
+  if (mode != MXQ_W4A4 && mode != MXQ_W4A8) return MXQ_ERR_MODE;
+  int st = check_mk(M, K, K);
+  if (st != MXQ_OK) return st;
+  size_t cb = 0;
+  workspace_layout(mode, M, K, &cb, bytes);
+  return MXQ_OK;
+}
+
+int mxq_qlinear(const void* policy, int32_t expert, int32_t block,
+                const void* x, int64_t M, int64_t K,
+                const void* w_codes, const void* w_scales, int64_t N,
+                const void* bias, int epilogue, void* y,
+                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int mode = 0;
+  int st = mxq_policy_mode(policy, expert, block, &mode);
+  if (st != MXQ_OK) return st;
+  if (epilogue != MXQ_EPI_NONE && epilogue != MXQ_EPI_GELU_TANH) return MXQ_ERR_MODE;
+  st = check_mk(M, K, K);
+  if (st != MXQ_OK) return st;
+  if (N < 0 || N >= kMaxDim) return MXQ_ERR_SHAPE;
+  if (M == 0 || N == 0) return MXQ_OK;
+  if (x == nullptr || w_codes == nullptr || w_scales == nullptr || y == nullptr) return MXQ_ERR_NULL;
+  if (workspace == nullptr) return MXQ_ERR_WORKSPACE;
+  size_t codes_bytes = 0, need = 0;
+  workspace_layout(mode, M, K, &codes_bytes, &need);
+  if (workspace_bytes < need) return MXQ_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(w_codes) || !aligned16(w_scales) || !aligned16(y) ||
+      !aligned16(workspace) || (bias != nullptr && !aligned16(bias)))
+    return MXQ_ERR_ALIGN;
+  void* a_codes = workspace;
+  void* a_scales = static_cast<uint8_t*>(workspace) + codes_bytes;
+  st = mxq_quantize_act(mode, x, M, K, K, a_codes, a_scales, stream);
+  if (st != MXQ_OK) return st;
+  return mxq_gemm(mode, a_codes, a_scales, w_codes, w_scales, bias, epilogue, y, M, N, K, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,25 @@
+// mxq_internal.h - launchers shared between the C ABI layer and the kernels.
+// Callers have validated every argument; launchers only enqueue work.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxq {
+
+hipError_t launch_mxfp4_quant(const void* x, int64_t rows, int64_t K, int64_t ld,
+                              void* codes, void* scales, hipStream_t s);
+
+hipError_t launch_fp8_quant(const void* x, int64_t rows, int64_t K, int64_t ld,
+                            void* codes, void* scales, hipStream_t s);
+
+// y[M][N] = epilogue(A * W^T + bias); mode 0 = W4A4, 1 = W4A8.
+hipError_t launch_gemm(int mode, const void* a_codes, const void* a_scales,
+                       const void* w_codes, const void* w_scales, const void* bias,
+                       int epilogue, void* y, int64_t M, int64_t N, int64_t K,
+                       hipStream_t s);
+
+// Name of the GEMM kernel variant launch_gemm picks for a shape (for logs).
+const char* gemm_variant_name(int mode, int64_t M, int64_t N, int64_t K);
+
+}  // namespace mxq

@@ -1,0 +1,52 @@
+"""Helpers for the GPU parity tests: host<->device transfer of bf16 bit
+arrays, and oracle comparisons on full or sampled rows."""
+
+import numpy as np
+import torch
+
+import oracle
+
+
+def dev_bf16(bits):
+    """uint16 bf16 bits (host) -> bf16 tensor on cuda:0."""
+    t = torch.from_numpy(np.ascontiguousarray(bits, np.uint16).view(np.int16))
+    return t.view(torch.bfloat16).to("cuda:0")
+
+
+def host_bits(t):
+    """bf16 tensor -> uint16 bits on the host."""
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def host_u8(t):
+    return t.detach().cpu().numpy().view(np.uint8)
+
+
+def host_f32(t):
+    return t.detach().cpu().numpy().astype(np.float32)
+
+
+def sample_rows(m, n_sample, seed, tile=256):
+    """Seeded row sample that always holds row 0, row m-1 and rows of the last tile."""
+    g = np.random.default_rng(seed)
+    last = np.arange(max(0, (m - 1) // tile * tile), m)
+    pick = g.choice(m, size=min(n_sample, m), replace=False)
+    rows = np.unique(np.concatenate([[0, m - 1], last[-8:], pick]))
+    return rows.astype(np.int64)
+
+
+def assert_codes_equal(got, want, what):
+    got = np.asarray(got)
+    want = np.asarray(want)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, f"{what}: {len(bad)} mismatches, first at {bad[:5].tolist()}: " \
+                          f"got {got[tuple(bad[0])]!r} want {want[tuple(bad[0])]!r}"
+
+
+def assert_output_close(y_bits, y_ref, what):
+    y = oracle.bf16_bits_to_f64(y_bits)
+    rep = oracle.output_error_report(y, y_ref)
+    assert rep["finite"], f"{what}: non-finite output"
+    assert rep["worst_ratio"] <= 1.0, f"{what}: tolerance exceeded {rep}"
+    return rep

@@ -1,0 +1,139 @@
+"""The C ABI on the host: library loads, exports what include/mxq.h declares,
+and rejects bad arguments before any HIP call (no GPU needed)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import mx_bit_quantized_amd as mxq
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "mxq.h")
+FAKE = ctypes.c_void_p(0x10000)        # 16-byte aligned, never dereferenced
+FAKE_ODD = ctypes.c_void_p(0x10008)    # 8-byte aligned only
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mxq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = mxq.lib()
+    names = declared_functions()
+    assert len(names) == 10, names
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(mxq._SIGS)
+
+
+def test_status_strings_and_version():
+    assert mxq.version() == 10000
+    for st in range(8):
+        assert mxq.status_string(st)
+    assert mxq.status_string(99) == "unknown status"
+
+
+def test_quantize_act_rejects_modes_shapes_nulls_alignment():
+    L = mxq.lib()
+    S = None
+    # bf16 and transform_on policy values are not quantized-linear modes
+    for mode in (mxq.POLICY_BF16, mxq.POLICY_TRANSFORM_ON, -1, 7):
+        assert L.mxq_quantize_act(mode, FAKE, 4, 64, 64, FAKE, FAKE, S) == mxq.ERR_MODE
+    for k in (0, 16, 48, -32):
+        assert L.mxq_quantize_act(mxq.W4A4, FAKE, 4, k, 64, FAKE, FAKE, S) == mxq.ERR_SHAPE
+    assert L.mxq_quantize_act(mxq.W4A4, FAKE, -1, 64, 64, FAKE, FAKE, S) == mxq.ERR_SHAPE
+    assert L.mxq_quantize_act(mxq.W4A4, FAKE, 4, 64, 32, FAKE, FAKE, S) == mxq.ERR_SHAPE  # ld < K
+    assert L.mxq_quantize_act(mxq.W4A4, FAKE, 1 << 31, 64, 64, FAKE, FAKE, S) == mxq.ERR_SHAPE
+    assert L.mxq_quantize_act(mxq.W4A8, None, 4, 64, 64, FAKE, FAKE, S) == mxq.ERR_NULL
+    assert L.mxq_quantize_act(mxq.W4A8, FAKE, 4, 64, 64, None, FAKE, S) == mxq.ERR_NULL
+    assert L.mxq_quantize_act(mxq.W4A8, FAKE_ODD, 4, 64, 64, FAKE, FAKE, S) == mxq.ERR_ALIGN
+    assert L.mxq_quantize_act(mxq.W4A8, FAKE, 4, 64, 68, FAKE, FAKE, S) == mxq.ERR_ALIGN  # ld % 8
+    # empty problems enqueue nothing and accept null pointers
+    assert L.mxq_quantize_act(mxq.W4A4, None, 0, 64, 64, None, None, S) == mxq.OK
+
+
+def test_weight_pack_and_gemm_validation():
+    L = mxq.lib()
+    S = None
+    assert L.mxq_quantize_weight_mxfp4(FAKE, 8, 40, 40, FAKE, FAKE, S) == mxq.ERR_SHAPE
+    assert L.mxq_quantize_weight_mxfp4(None, 8, 64, 64, FAKE, FAKE, S) == mxq.ERR_NULL
+    assert L.mxq_quantize_weight_mxfp4(FAKE, 8, 64, 64, FAKE_ODD, FAKE, S) == mxq.ERR_ALIGN
+    assert L.mxq_quantize_weight_mxfp4(None, 0, 64, 64, None, None, S) == mxq.OK
+    args = [FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, 4, 8, 64, S]
+    assert L.mxq_gemm(2, *args) == mxq.ERR_MODE
+    bad_epi = list(args)
+    bad_epi[5] = 2
+    assert L.mxq_gemm(mxq.W4A4, *bad_epi) == mxq.ERR_MODE
+    bad_k = list(args)
+    bad_k[9] = 100
+    assert L.mxq_gemm(mxq.W4A4, *bad_k) == mxq.ERR_SHAPE
+    bad_n = list(args)
+    bad_n[8] = -3
+    assert L.mxq_gemm(mxq.W4A4, *bad_n) == mxq.ERR_SHAPE
+    null_y = list(args)
+    null_y[6] = None
+    assert L.mxq_gemm(mxq.W4A8, *null_y) == mxq.ERR_NULL
+    odd_bias = list(args)
+    odd_bias[4] = FAKE_ODD
+    assert L.mxq_gemm(mxq.W4A8, *odd_bias) == mxq.ERR_ALIGN
+    empty = list(args)
+    empty[7] = 0
+    empty[0] = None
+    assert L.mxq_gemm(mxq.W4A8, *empty) == mxq.OK
+
+
+def test_policy_table_roundtrip_and_errors():
+    table = np.array([[0, 1, 0], [1, 1, 0]], np.uint8)
+    p = mxq.Policy(table)
+    for e in range(2):
+        for b in range(3):
+            assert p.mode(e, b) == table[e, b]
+    for e, b in ((2, 0), (0, 3), (-1, 0), (0, -1)):
+        with pytest.raises(mxq.MxqError) as ei:
+            p.mode(e, b)
+        assert ei.value.status == mxq.ERR_RANGE
+    p.close()
+    for bad in ([[0, 2]], [[3, 0]], [[9]]):
+        with pytest.raises(mxq.MxqError) as ei:
+            mxq.Policy(bad)
+        assert ei.value.status == mxq.ERR_MODE
+    h = ctypes.c_void_p()
+    assert mxq.lib().mxq_policy_create(None, 1, 1, ctypes.byref(h)) == mxq.ERR_NULL
+    assert mxq.lib().mxq_policy_create(table.ctypes.data_as(ctypes.c_void_p), 0, 3, ctypes.byref(h)) == mxq.ERR_SHAPE
+    assert mxq.lib().mxq_policy_destroy(None) == mxq.OK
+
+
+def test_workspace_bytes_and_qlinear_validation():
+    assert mxq.qlinear_workspace_bytes(mxq.W4A4, 256, 512) == 256 * 256 + 256 * 16
+    assert mxq.qlinear_workspace_bytes(mxq.W4A8, 256, 512) == 256 * 512 + 1024
+    assert mxq.qlinear_workspace_bytes(mxq.W4A8, 3, 32) == 256 + 256
+    with pytest.raises(mxq.MxqError):
+        mxq.qlinear_workspace_bytes(mxq.POLICY_BF16, 4, 64)
+    L = mxq.lib()
+    p = mxq.Policy([[0, 1]])
+    S = None
+    ws_small = mxq.qlinear_workspace_bytes(mxq.W4A8, 4, 64) - 1
+    # W4A8 block with a workspace one byte short
+    assert L.mxq_qlinear(p.handle, 0, 1, FAKE, 4, 64, FAKE, FAKE, 8, None, 0, FAKE, FAKE, ws_small, S) \
+        == mxq.ERR_WORKSPACE
+    assert L.mxq_qlinear(p.handle, 0, 0, FAKE, 4, 64, FAKE, FAKE, 8, None, 0, FAKE, None, 1 << 20, S) \
+        == mxq.ERR_WORKSPACE
+    assert L.mxq_qlinear(p.handle, 1, 0, FAKE, 4, 64, FAKE, FAKE, 8, None, 0, FAKE, FAKE, 1 << 20, S) \
+        == mxq.ERR_RANGE
+    assert L.mxq_qlinear(None, 0, 0, FAKE, 4, 64, FAKE, FAKE, 8, None, 0, FAKE, FAKE, 1 << 20, S) \
+        == mxq.ERR_NULL
+    assert L.mxq_qlinear(p.handle, 0, 0, FAKE, 4, 64, FAKE, FAKE, 8, None, 5, FAKE, FAKE, 1 << 20, S) \
+        == mxq.ERR_MODE
+    assert L.mxq_qlinear(p.handle, 0, 0, FAKE, 0, 64, None, None, 8, None, 0, None, None, 0, S) == mxq.OK
+    p.close()
+
+
+def test_python_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    with pytest.raises(TypeError):
+        mxq.quantize_weight_mxfp4(torch.zeros((4, 64), dtype=torch.bfloat16))
