@@ -40,7 +40,7 @@ struct FragFp4 {  // one lane, one K tile: 4 blocks of 16 bytes + 4 scale bytes
   uint4 d[4];
   uint32_t sc;
 };
-struct FragFp8 {  // one lane, one K tile: 4 blocks of 32 bytes
+struct FragFp8 {  // one lane, one K tile: 4 steps x two 16-byte halves
   uint4 d[8];
 };
 
@@ -62,14 +62,21 @@ __device__ __forceinline__ void load_fp4(FragFp4& f, const uint8_t* q, const uin
   f.sc = load_scales4(sc, b0, KB, TAIL);
 }
 
+// FP8 operand of the mixed FP8 x FP4 instruction. The FP4 operand's lane slot
+// h (lanes 32h .. 32h+31) covers K 32h .. 32h+31 of a step in natural nibble
+// order, but the FP8 operand is split by halves: its bytes 0..15 in slot h
+// pair with K 16h .. 16h+15 and bytes 16..31 with K 32+16h .. 32+16h+15.
+// With block kk on FP4 slot 0 and block 4+kk on FP4 slot 1 (see above), FP8
+// slot h therefore carries half h of block kk, then half h of block 4+kk.
 template <bool TAIL>
-__device__ __forceinline__ void load_fp8(FragFp8& f, const uint8_t* q, int b0, int KB) {
-  const uint4* p = reinterpret_cast<const uint4*>(q) + 2 * b0;
+__device__ __forceinline__ void load_fp8(FragFp8& f, const uint8_t* q, int kt, int h, int KB) {
+  const uint4* p = reinterpret_cast<const uint4*>(q);
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const bool ok = !TAIL || b0 + t < KB;
-    f.d[2 * t] = ok ? p[2 * t] : make_uint4(0, 0, 0, 0);
-    f.d[2 * t + 1] = ok ? p[2 * t + 1] : make_uint4(0, 0, 0, 0);
+    const int b0 = kt * 8 + t;
+    const int b1 = kt * 8 + 4 + t;
+    f.d[2 * t] = (!TAIL || b0 < KB) ? p[2 * b0 + h] : make_uint4(0, 0, 0, 0);
+    f.d[2 * t + 1] = (!TAIL || b1 < KB) ? p[2 * b1 + h] : make_uint4(0, 0, 0, 0);
   }
 }
 
@@ -164,7 +171,7 @@ __global__ __launch_bounds__(256) void gemm_direct_kernel(
         load_fp4<TAIL>(reinterpret_cast<FragFp4&>(xf[j]), xrow[j], xsrow[j], b0, KB);
         xs[j] = reinterpret_cast<FragFp4&>(xf[j]).sc;
       } else {
-        load_fp8<TAIL>(reinterpret_cast<FragFp8&>(xf[j]), xrow[j], b0, KB);
+        load_fp8<TAIL>(reinterpret_cast<FragFp8&>(xf[j]), xrow[j], kt, g, KB);
         xs[j] = kUnitScales;
       }
     }
@@ -213,6 +220,338 @@ __global__ __launch_bounds__(256) void gemm_direct_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// LDS-pipelined kernel for the large shapes.
+//
+// Workgroup tile 256 (n) x 256 (m), 4 waves in a 2 x 2 grid, each wave owns a
+// 128 x 128 output block = 4 x 4 MFMA tiles (256 fp32 accumulators per lane,
+// held in AGPRs). K advances in stages of 128 elements (4 MX blocks): FP4
+// lane slot g owns blocks 2g and 2g+1, MFMA step kk (0, 1) uses block 2g+kk.
+//
+// Global -> LDS moves use buffer loads that write LDS directly (no staging
+// registers): each wave instruction fills 1 KiB of LDS, lane i writing bytes
+// [16 i, 16 i + 16) of it, so the layout is set by choosing each lane's global
+// address. A ring of NB stage buffers (separate LDS arrays, so the compiler
+// can tell the DMA target from the buffer being read) keeps NB-1 stages in
+// flight: W4A4 (34 KiB stages) runs 4 buffers, W4A8 (49 KiB) 3. Per stage:
+// wait for this wave's own copies of the stage, barrier (every wave's copies
+// landed and every wave finished the stage that last used the buffer about
+// to be refilled), issue the copies of stage s+NB-1, then the MFMAs.
+// Buffer resources carry the operand sizes: rows past M or N read as zero.
+//
+// LDS rows hold one stage of one operand row (64 bytes FP4, 128 bytes FP8).
+// The 16-byte chunks of each 128-byte line are XOR-permuted by the line
+// index, so the 8 lanes of a ds_read_b128 phase (8 consecutive rows, same
+// chunk) hit 8 distinct bank groups.
+//
+// Tile order: workgroups are dealt round-robin to the 8 XCDs; the kernel maps
+// the dispatch index so that each XCD receives a contiguous range of tiles,
+// and walks that range in groups of 8 tile-rows (m) per tile-column (n), so
+// the workgroups resident on one XCD share W and X panels in its L2.
+
+template <int MODE>
+struct PipeCfg {
+  static constexpr int KT = 128;                      // K elements per stage
+  static constexpr int W_RB = 64;                     // FP4 row bytes per stage
+  static constexpr int X_RB = MODE == 0 ? 64 : 128;   // FP4 / FP8 row bytes per stage
+  static constexpr int SB = 4;                        // E8M0 bytes per row per stage
+  static constexpr int W_OFF = 0;
+  static constexpr int X_OFF = 256 * W_RB;
+  static constexpr int WS_OFF = X_OFF + 256 * X_RB;
+  static constexpr int XS_OFF = WS_OFF + 256 * SB;
+  static constexpr int STAGE = XS_OFF + (MODE == 0 ? 256 * SB : 0);
+  static constexpr int NB = MODE == 0 ? 4 : 3;        // ring depth
+  static constexpr int W_INSTR = 256 * W_RB / 1024 / 4;   // 1 KiB copies per wave per stage
+  static constexpr int X_INSTR = 256 * X_RB / 1024 / 4;
+  static constexpr int S_INSTR = MODE == 0 ? 2 : 1;       // 256 B scale copies per wave
+  static constexpr int PER_WAVE = W_INSTR + X_INSTR + S_INSTR;
+};
+
+// LDS byte offset of 16-byte chunk c of `row` in a tile with rows of RB bytes.
+template <int RB>
+__device__ __forceinline__ int swz(int row, int c) {
+  if constexpr (RB == 128) {
+    return row * 128 + ((c ^ (row & 7)) << 4);
+  } else {  // RB == 64: two rows per 128-byte line
+    const int line = row >> 1;
+    return line * 128 + (((((row & 1) << 2) | c) ^ (line & 7)) << 4);
+  }
+}
+
+// Inverse of swz: the (row, chunk) whose data belongs in 16-byte LDS slot `slot`.
+template <int RB>
+__device__ __forceinline__ void unswz(int slot, int& row, int& c) {
+  const int line = slot >> 3;
+  const int p = (slot & 7) ^ (line & 7);
+  if constexpr (RB == 128) {
+    row = line;
+    c = p;
+  } else {
+    row = 2 * line + (p >> 2);
+    c = p & 3;
+  }
+}
+
+__device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int total = tiles_m * tiles_n;
+  const int per = total / 8;
+  int t = bid;
+  if (bid < per * 8) t = (bid & 7) * per + (bid >> 3);  // contiguous range per XCD
+  constexpr int G = 8;
+  const int group = t / (G * tiles_n);
+  const int first_m = group * G;
+  const int gm = min(G, tiles_m - first_m);
+  const int in = t - group * G * tiles_n;
+  tm = first_m + in % gm;
+  tn = in / gm;
+}
+
+__device__ __forceinline__ float gelu_tanh_dev(float y) {
+  // 0.5 y (1 + tanh(u)) = y / (1 + exp(-2u)), u = sqrt(2/pi) (y + 0.044715 y^3)
+  const float u = 0.7978845608028654f * y * (1.0f + 0.044715f * y * y);
+  const float e = __builtin_amdgcn_exp2f(-2.0f * 1.4426950408889634f * u);
+  return y * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+#define MXQ_LDS __attribute__((address_space(3)))
+
+constexpr int waitcnt_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+
+// Buffer resource (V#) of a byte range: base, stride 0, size in bytes, and the
+// gfx9 raw-buffer format word. Loads past `bytes` return zeros.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  i32x4 r;
+  r.x = (int)(uint32_t)a;
+  r.y = (int)(uint32_t)(a >> 32);
+  r.z = (int)bytes;
+  r.w = 0x00020000;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)((const MXQ_LDS uint8_t*)p));
+}
+
+// One wave-wide copy from a buffer into LDS: lane i's 16 (or 4) bytes at byte
+// offset `voff` of the resource land at LDS address lds + 16 i (4 i). The copy
+// is written in asm so that the compiler's wait-count pass does not track it;
+// the kernel orders it explicitly with s_waitcnt vmcnt + s_barrier. It has no
+// register result, so nothing the compiler allocates can be overwritten while
+// it is in flight; M0 needs one wait state before the copy reads it.
+__device__ __forceinline__ void lds_dma16(const i32x4& rs, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rs) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_dma4(const i32x4& rs, uint32_t lds, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rs) : "memory", "m0");
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_pipe_kernel(
+    const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws,
+    const uint8_t* __restrict__ aq, const void* __restrict__ asc,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
+    int M, int N, int K, int epi, int tiles_m, int tiles_n) {
+  using C = PipeCfg<MODE>;
+  __shared__ __attribute__((aligned(1024))) uint8_t sb0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t sb1[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t sb2[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t sb3[C::NB == 4 ? C::STAGE : 16];
+
+  int tm, tn;
+  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int n_base = tn * 256;
+  const int m_base = tm * 256;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int r = lane & 31;
+  const int g = lane >> 5;
+  const int wn = wave & 1;
+  const int wm = wave >> 1;
+  const int KB = K >> 5;
+  const uint32_t w_row = (uint32_t)K >> 1;
+  const uint32_t x_row = MODE == 0 ? ((uint32_t)K >> 1) : (uint32_t)K;
+  const int n_stages = K / C::KT;
+
+  const i32x4 rw = make_rsrc(wq, w_row * (uint32_t)N);
+  const i32x4 rx = make_rsrc(aq, x_row * (uint32_t)M);
+  const i32x4 rws = make_rsrc(ws, (uint32_t)KB * (uint32_t)N);
+  const i32x4 rxs = make_rsrc(asc, MODE == 0 ? (uint32_t)KB * (uint32_t)M : 0u);
+
+  // Per-lane source offsets of this wave's copies (stage 0); stage s adds s * RB.
+  uint32_t vw[C::W_INSTR], vx[C::X_INSTR];
+#pragma unroll
+  for (int q = 0; q < C::W_INSTR; ++q) {
+    int row, c;
+    unswz<C::W_RB>((wave * C::W_INSTR + q) * 64 + lane, row, c);
+    vw[q] = (uint32_t)(n_base + row) * w_row + (uint32_t)c * 16;
+  }
+#pragma unroll
+  for (int q = 0; q < C::X_INSTR; ++q) {
+    int row, c;
+    unswz<C::X_RB>((wave * C::X_INSTR + q) * 64 + lane, row, c);
+    vx[q] = (uint32_t)(m_base + row) * x_row + (uint32_t)c * 16;
+  }
+  // scales: wave w copies rows 64 w .. 64 w + 63 (4 bytes each) of W, and of X for W4A4
+  const uint32_t vws = (uint32_t)(n_base + wave * 64 + lane) * (uint32_t)KB;
+  const uint32_t vxs = (uint32_t)(m_base + wave * 64 + lane) * (uint32_t)KB;
+
+  // Copies of stage s into `buf`. Stages past the end are still issued (so
+  // the wait counts stay constant and the issue has no branch) but with an
+  // offset beyond every buffer's size: the hardware then writes zeros to LDS
+  // without reading memory. Offsets stay in the per-lane operand, which is
+  // the part the range check covers.
+  auto issue = [&](int s, uint8_t* buf) {
+    const bool live = s < n_stages;
+    const uint32_t oob = 0x80000000u;
+#pragma unroll
+    for (int q = 0; q < C::W_INSTR; ++q)
+      lds_dma16(rw, lds_addr(buf + C::W_OFF + (wave * C::W_INSTR + q) * 1024), live ? vw[q] + (uint32_t)s * C::W_RB : oob);
+#pragma unroll
+    for (int q = 0; q < C::X_INSTR; ++q)
+      lds_dma16(rx, lds_addr(buf + C::X_OFF + (wave * C::X_INSTR + q) * 1024), live ? vx[q] + (uint32_t)s * C::X_RB : oob);
+    lds_dma4(rws, lds_addr(buf + C::WS_OFF + wave * 256), live ? vws + (uint32_t)s * C::SB : oob);
+    if constexpr (MODE == 0) lds_dma4(rxs, lds_addr(buf + C::XS_OFF + wave * 256), live ? vxs + (uint32_t)s * C::SB : oob);
+  };
+
+  v16f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+  const int wrow0 = wn * 128 + r;  // + 32 i
+  const int xrow0 = wm * 128 + r;  // + 32 j
+
+  auto compute = [&](const uint8_t* base) {
+    uint32_t wsc[4], xsc[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      wsc[i] = *reinterpret_cast<const uint16_t*>(base + C::WS_OFF + (wrow0 + 32 * i) * 4 + 2 * g);
+    if constexpr (MODE == 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        xsc[j] = *reinterpret_cast<const uint16_t*>(base + C::XS_OFF + (xrow0 + 32 * j) * 4 + 2 * g);
+    }
+    auto step = [&](auto kk_tag) {
+      constexpr int KK = decltype(kk_tag)::value;
+      v8i a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        a[i] = op_fp4(*reinterpret_cast<const uint4*>(base + C::W_OFF + swz<C::W_RB>(wrow0 + 32 * i, 2 * g + KK)));
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = xrow0 + 32 * j;
+        if constexpr (MODE == 0) {
+          b[j] = op_fp4(*reinterpret_cast<const uint4*>(base + C::X_OFF + swz<C::X_RB>(row, 2 * g + KK)));
+        } else {
+          // FP8 slot h = g: half g of block KK (FP4 slot 0), then half g of block 2+KK (slot 1)
+          const uint4 lo = *reinterpret_cast<const uint4*>(base + C::X_OFF + swz<C::X_RB>(row, 2 * KK + g));
+          const uint4 hi = *reinterpret_cast<const uint4*>(base + C::X_OFF + swz<C::X_RB>(row, 2 * (2 + KK) + g));
+          b[j] = op_fp8(lo, hi);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if constexpr (MODE == 0)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], kFmtFp4, kFmtFp4,
+                                                                        KK, (int)wsc[i], KK, (int)xsc[j]);
+          else
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], kFmtFp4, kFmtFp8,
+                                                                        KK, (int)wsc[i], KK, (int)kUnitScales);
+        }
+    };
+    step(std::integral_constant<int, 0>{});
+    step(std::integral_constant<int, 1>{});
+  };
+
+  auto buf_of = [&](auto u_tag) -> uint8_t* {
+    constexpr int U = decltype(u_tag)::value;
+    if constexpr (U == 0) return sb0;
+    else if constexpr (U == 1) return sb1;
+    else if constexpr (U == 2) return sb2;
+    else return sb3;
+  };
+
+  constexpr int D = C::NB - 1;  // stages in flight ahead of the one computed
+  // prologue: stages 0 .. D-1 into buffers 0 .. D-1
+  issue(0, buf_of(std::integral_constant<int, 0>{}));
+  issue(1, buf_of(std::integral_constant<int, 1>{}));
+  if constexpr (D >= 3) issue(2, buf_of(std::integral_constant<int, 2>{}));
+
+  auto stage = [&](int s, auto u_tag) {
+    constexpr int U = decltype(u_tag)::value;
+    // this wave's copies of stage s have landed once at most the copies of
+    // the D-1 later stages are still outstanding
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((D - 1) * C::PER_WAVE));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    issue(s + D, buf_of(std::integral_constant<int, (U + D) % C::NB>{}));
+    compute(buf_of(u_tag));
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  };
+
+  for (int s0 = 0; s0 < n_stages; s0 += C::NB) {
+    stage(s0, std::integral_constant<int, 0>{});
+    if (s0 + 1 < n_stages) stage(s0 + 1, std::integral_constant<int, 1>{});
+    if (s0 + 2 < n_stages) stage(s0 + 2, std::integral_constant<int, 2>{});
+    if constexpr (C::NB == 4) {
+      if (s0 + 3 < n_stages) stage(s0 + 3, std::integral_constant<int, 3>{});
+    }
+  }
+  // no copy may still be writing LDS when the workgroup retires
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+
+  // ---- epilogue: accumulator q of lane (r, g) in a 32x32 tile holds
+  // n = 8 (q / 4) + 4 g + (q % 4), m = r
+  const float* tok_scale = static_cast<const float*>(asc);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = m_base + wm * 128 + 32 * j + r;
+    if (m >= M) continue;
+    const float sm = MODE == 1 ? tok_scale[m] : 1.0f;
+    uint16_t* yrow = y + (int64_t)m * N;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int qq = 0; qq < 4; ++qq) {
+        const int nb = n_base + wn * 128 + 32 * i + 8 * qq + 4 * g;
+        if (nb >= N) continue;  // N is a multiple of 4 on this path
+        float v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          v[u] = acc[i][j][4 * qq + u] * sm;
+          if (bias != nullptr) v[u] += as_float((uint32_t)bias[nb + u] << 16);
+          if (epi == 1) v[u] = gelu_tanh_dev(v[u]);
+        }
+        *reinterpret_cast<uint2*>(yrow + nb) =
+            make_uint2(bf16_rne(v[0]) | (bf16_rne(v[1]) << 16), bf16_rne(v[2]) | (bf16_rne(v[3]) << 16));
+      }
+    }
+  }
+}
+
+template <int MODE>
+static hipError_t launch_pipe(const void* aq, const void* as, const void* wq, const void* ws, const void* bias,
+                              int epi, void* y, int64_t M, int64_t N, int64_t K, hipStream_t s) {
+  const int tiles_m = (int)((M + 255) / 256);
+  const int tiles_n = (int)((N + 255) / 256);
+  hipLaunchKernelGGL((gemm_pipe_kernel<MODE>), dim3(tiles_m * tiles_n), dim3(256), 0, s,
+                     static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws),
+                     static_cast<const uint8_t*>(aq), as, static_cast<const uint16_t*>(bias),
+                     static_cast<uint16_t*>(y), (int)M, (int)N, (int)K, epi, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
 template <int MODE, int TN, int TM>
 static hipError_t launch_direct(const void* aq, const void* as, const void* wq, const void* ws,
                                 const void* bias, int epi, void* y, int64_t M, int64_t N,
@@ -225,18 +564,33 @@ static hipError_t launch_direct(const void* aq, const void* as, const void* wq, 
   return hipGetLastError();
 }
 
+// The LDS kernel needs whole stages along K and N in multiples of 4 (8-byte
+// stores); every Wan2.2 linear qualifies. Everything else takes the direct
+// kernel.
+static bool use_lds(int mode, int64_t M, int64_t N, int64_t K) {
+  const int64_t a_bytes = mode == 0 ? M * (K / 2) : M * K;
+  // 32-bit buffer offsets: every operand must stay below 2^31 bytes
+  return K % 128 == 0 && N % 4 == 0 && M >= 256 && N >= 256 && a_bytes < (int64_t(1) << 31) &&
+         N * (K / 2) < (int64_t(1) << 31);
+}
+
 hipError_t launch_gemm(int mode, const void* a_codes, const void* a_scales,
                        const void* w_codes, const void* w_scales, const void* bias,
                        int epilogue, void* y, int64_t M, int64_t N, int64_t K,
                        hipStream_t s) {
+  if (use_lds(mode, M, N, K)) {
+    if (mode == 0) return launch_pipe<0>(a_codes, a_scales, w_codes, w_scales, bias, epilogue, y, M, N, K, s);
+    return launch_pipe<1>(a_codes, a_scales, w_codes, w_scales, bias, epilogue, y, M, N, K, s);
+  }
   if (mode == 0)
     return launch_direct<0, 2, 2>(a_codes, a_scales, w_codes, w_scales, bias, epilogue, y, M, N, K, s);
   return launch_direct<1, 2, 2>(a_codes, a_scales, w_codes, w_scales, bias, epilogue, y, M, N, K, s);
 }
 
-const char* gemm_variant_name(int mode, int64_t, int64_t, int64_t) {
-  return mode == 0 ? "direct_w4a4_32x32x64_wave64x64_wg128x128"
-                   : "direct_w4a8_32x32x64_wave64x64_wg128x128";
+const char* gemm_variant_name(int mode, int64_t M, int64_t N, int64_t K) {
+  if (use_lds(mode, M, N, K))
+    return mode == 0 ? "pipe_w4a4_wg256x256_wave128x128_kt128_ring4" : "pipe_w4a8_wg256x256_wave128x128_kt128_ring3";
+  return mode == 0 ? "direct_w4a4_wg128x128_wave64x64" : "direct_w4a8_wg128x128_wave64x64";
 }
 
 }  // namespace mxq
