@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--workload", default="a14b_stack", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=512)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (calibrates HBM byte counters) and exit")
     return ap.parse_args()
 
 
@@ -186,6 +188,15 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a HIP device"
     torch.cuda.set_device(0)
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n}), flush=True)
+        return
     mxq.lib()
     wl = synth.workload(WORKLOADS[args.workload])
     stack = Stack(wl, torch, mxq)
