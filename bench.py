@@ -74,7 +74,7 @@ class Stack:
                 for li, lin in enumerate(wl.linears):
                     w = synth.weight_bf16_device(wl.config_id, lin.n, lin.k, e, b, li)
                     codes = torch.empty((lin.n, lin.k // 2), dtype=torch.uint8, device=dev)
-                    scales = torch.empty((lin.n, lin.k // 32), dtype=torch.uint8, device=dev)
+                    scales = torch.empty(mxq.mx_scale_shape(lin.n, lin.k), dtype=torch.uint8, device=dev)
                     ev0.record()
                     mxq.quantize_weight_mxfp4(w, codes, scales)
                     ev1.record()
@@ -99,7 +99,8 @@ class Stack:
             cb = m * k // 2
             codes = self.codes_buf[:cb].view(m, k // 2)
             off = (cb + 255) // 256 * 256
-            scales = self.codes_buf[off:off + m * k // 32].view(m, k // 32)
+            shape = self.mxq.mx_scale_shape(m, k)
+            scales = self.codes_buf[off:off + shape[0] * m * 4].view(shape)
         else:
             cb = m * k
             codes = self.codes_buf[:cb].view(m, k)

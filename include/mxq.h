@@ -18,8 +18,13 @@
  *                    nibble of byte t, element 2t+1 in the high nibble.
  *                    Each nibble is E2M1 (sign bit 3; magnitudes 0, .5, 1,
  *                    1.5, 2, 3, 4, 6).
- *   MXFP4 scales     uint8 [rows][K/32], E8M0 (value 2^(u-127)), one per 32
- *                    consecutive elements along K.
+ *   MXFP4 scales     E8M0 bytes (value 2^(u-127)), one per 32 consecutive
+ *                    elements along K, stored group-major as
+ *                    uint8 [ceil(K/128)][rows][4]: the byte of row r, block j
+ *                    (elements 32j .. 32j+31) is at ((j/4) * rows + r) * 4 +
+ *                    j%4; bytes of blocks past K/32 are zero. One K stage of
+ *                    a row tile is then one contiguous run (the GEMM copies
+ *                    it with a few wide loads).
  *   FP8 codes        uint8 [M][K], E4M3FN (max 448, 0x7F/0xFF NaN).
  *   FP8 scales       float32 [M], one per row (token).
  *
@@ -99,15 +104,15 @@ int mxq_version(void);
  * table, in the MXFP4 format of "Quantization formats".
  *   w       device, bf16 [N][ldw]
  *   codes   device, uint8 [N][K/2]   (output)
- *   scales  device, uint8 [N][K/32]  (output, E8M0)
+ *   scales  device, uint8 [ceil(K/128)][N][4]  (output, E8M0, group-major)
  */
 int mxq_quantize_weight_mxfp4(const void* w, int64_t N, int64_t K, int64_t ldw,
                               void* codes, void* scales, hipStream_t stream);
 
 /*
  * Dynamic activation quantization ("Quantization formats"): MXQ_W4A4 gives
- * MXFP4 codes [M][K/2] + E8M0 scales [M][K/32]; MXQ_W4A8 gives E4M3FN codes
- * [M][K] + float32 per-token scales [M].
+ * MXFP4 codes [M][K/2] + E8M0 scales [ceil(K/128)][M][4] (group-major);
+ * MXQ_W4A8 gives E4M3FN codes [M][K] + float32 per-token scales [M].
  *   x       device, bf16 [M][ldx]
  *   codes   device (output), scales device (output)
  */
@@ -151,7 +156,7 @@ int mxq_qlinear_workspace_bytes(int mode, int64_t M, int64_t K, size_t* bytes);
  * then runs the scaled GEMM into y. Exactly mxq_quantize_act followed by
  * mxq_gemm.
  *   x          device bf16 [M][K] (dense)
- *   w_codes    device uint8 [N][K/2], w_scales device uint8 [N][K/32]
+ *   w_codes    device uint8 [N][K/2], w_scales device uint8 [ceil(K/128)][N][4]
  *   bias       device bf16 [N] or null
  *   y          device bf16 [M][N] (output)
  *   workspace  device, at least mxq_qlinear_workspace_bytes(mode, M, K)

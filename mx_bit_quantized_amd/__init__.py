@@ -117,12 +117,17 @@ def _rows_k(t, name):
     return int(t.shape[0]), int(t.shape[1])
 
 
+def mx_scale_shape(rows, K):
+    """Shape of group-major MXFP4 scales: [ceil(K/128), rows, 4] bytes."""
+    return ((K + 127) // 128, rows, 4)
+
+
 def act_buffers(mode, M, K, device):
     """Empty (codes, scales) tensors for quantize_act in ``mode``."""
     torch = _torch()
     if mode == W4A4:
         return (torch.empty((M, K // 2), dtype=torch.uint8, device=device),
-                torch.empty((M, K // 32), dtype=torch.uint8, device=device))
+                torch.empty(mx_scale_shape(M, K), dtype=torch.uint8, device=device))
     if mode == W4A8:
         return (torch.empty((M, K), dtype=torch.uint8, device=device),
                 torch.empty((M,), dtype=torch.float32, device=device))
@@ -130,13 +135,13 @@ def act_buffers(mode, M, K, device):
 
 
 def quantize_weight_mxfp4(w, codes=None, scales=None, stream=None):
-    """RTN MXFP4 packing of bf16 weights [N, K] -> (codes uint8 [N, K/2], scales uint8 [N, K/32])."""
+    """RTN MXFP4 packing of bf16 weights [N, K] -> (codes uint8 [N, K/2], scales uint8 [ceil(K/128), N, 4])."""
     torch = _torch()
     n, k = _rows_k(w, "w")
     if codes is None:
         codes = torch.empty((n, k // 2), dtype=torch.uint8, device=w.device)
     if scales is None:
-        scales = torch.empty((n, k // 32), dtype=torch.uint8, device=w.device)
+        scales = torch.empty(mx_scale_shape(n, k), dtype=torch.uint8, device=w.device)
     st = lib().mxq_quantize_weight_mxfp4(_dev_ptr(w, "w", torch.bfloat16), n, k, k,
                                           _dev_ptr(codes, "codes", torch.uint8),
                                           _dev_ptr(scales, "scales", torch.uint8), _stream_handle(stream))

@@ -51,7 +51,7 @@ size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // Workspace layout of mxq_qlinear: codes first, scales at a 256-byte boundary.
 void workspace_layout(int mode, int64_t M, int64_t K, size_t* codes_bytes, size_t* total) {
   size_t cb = mode == MXQ_W4A4 ? (size_t)M * (size_t)(K / 2) : (size_t)M * (size_t)K;
-  size_t sb = mode == MXQ_W4A4 ? (size_t)M * (size_t)(K / 32) : (size_t)M * sizeof(float);
+  size_t sb = mode == MXQ_W4A4 ? (size_t)M * 4 * (size_t)((K + 127) / 128) : (size_t)M * sizeof(float);
   *codes_bytes = round_up(cb, 256);
   *total = *codes_bytes + round_up(sb, 256);
 }

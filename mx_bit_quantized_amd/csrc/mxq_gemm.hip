@@ -44,22 +44,16 @@ struct FragFp8 {  // one lane, one K tile: 4 steps x two 16-byte halves
   uint4 d[8];
 };
 
-__device__ __forceinline__ uint32_t load_scales4(const uint8_t* p, int b0, int KB, bool tail) {
-  uint32_t s = 0;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    uint32_t v = (!tail || b0 + t < KB) ? (uint32_t)p[b0 + t] : 0u;
-    s |= v << (8 * t);
-  }
-  return s;
-}
-
+// Scales are group-major: the dword of group gi (blocks 4gi .. 4gi+3) of row
+// `row` sits at sc[gi * rows + row]. A lane slot's four blocks of a 256-wide
+// tile are exactly one group, so one dword load serves 4 MFMA steps.
 template <bool TAIL>
-__device__ __forceinline__ void load_fp4(FragFp4& f, const uint8_t* q, const uint8_t* sc, int b0, int KB) {
+__device__ __forceinline__ void load_fp4(FragFp4& f, const uint8_t* q, const uint32_t* sc, int64_t rows, int row,
+                                         int gi, int n_groups, int b0, int KB) {
   const uint4* p = reinterpret_cast<const uint4*>(q) + b0;
 #pragma unroll
   for (int t = 0; t < 4; ++t) f.d[t] = (!TAIL || b0 + t < KB) ? p[t] : make_uint4(0, 0, 0, 0);
-  f.sc = load_scales4(sc, b0, KB, TAIL);
+  f.sc = (!TAIL || gi < n_groups) ? sc[(int64_t)gi * rows + row] : 0u;
 }
 
 // FP8 operand of the mixed FP8 x FP4 instruction. The FP4 operand's lane slot
@@ -132,21 +126,22 @@ __global__ __launch_bounds__(256) void gemm_direct_kernel(
   const int KB = K >> 5;
   const int64_t a_row_bytes = MODE == 0 ? (K >> 1) : K;
 
+  const int n_groups = (KB + 3) >> 2;
+  const uint32_t* wsc = reinterpret_cast<const uint32_t*>(ws);
+  const uint32_t* xsc = static_cast<const uint32_t*>(asc);
   const uint8_t* wrow[TN];
-  const uint8_t* wsrow[TN];
+  int wn_row[TN];
 #pragma unroll
   for (int i = 0; i < TN; ++i) {
-    int n = min(n0 + 32 * i + r, N - 1);  // rows past the edge re-read the last row
-    wrow[i] = wq + (int64_t)n * (K >> 1);
-    wsrow[i] = ws + (int64_t)n * KB;
+    wn_row[i] = min(n0 + 32 * i + r, N - 1);  // rows past the edge re-read the last row
+    wrow[i] = wq + (int64_t)wn_row[i] * (K >> 1);
   }
   const uint8_t* xrow[TM];
-  const uint8_t* xsrow[TM];
+  int xm_row[TM];
 #pragma unroll
   for (int j = 0; j < TM; ++j) {
-    int m = min(m0 + 32 * j + r, M - 1);
-    xrow[j] = aq + (int64_t)m * a_row_bytes;
-    xsrow[j] = MODE == 0 ? static_cast<const uint8_t*>(asc) + (int64_t)m * KB : nullptr;
+    xm_row[j] = min(m0 + 32 * j + r, M - 1);
+    xrow[j] = aq + (int64_t)xm_row[j] * a_row_bytes;
   }
 
   v16f acc[TN][TM];
@@ -160,15 +155,16 @@ __global__ __launch_bounds__(256) void gemm_direct_kernel(
   auto tile = [&](int kt, auto tail_tag) {
     constexpr bool TAIL = decltype(tail_tag)::value;
     const int b0 = kt * 8 + 4 * g;
+    const int gi = kt * 2 + g;
     FragFp4 wf[TN];
     XFrag xf[TM];
     uint32_t xs[TM];
 #pragma unroll
-    for (int i = 0; i < TN; ++i) load_fp4<TAIL>(wf[i], wrow[i], wsrow[i], b0, KB);
+    for (int i = 0; i < TN; ++i) load_fp4<TAIL>(wf[i], wrow[i], wsc, N, wn_row[i], gi, n_groups, b0, KB);
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
       if constexpr (MODE == 0) {
-        load_fp4<TAIL>(reinterpret_cast<FragFp4&>(xf[j]), xrow[j], xsrow[j], b0, KB);
+        load_fp4<TAIL>(reinterpret_cast<FragFp4&>(xf[j]), xrow[j], xsc, M, xm_row[j], gi, n_groups, b0, KB);
         xs[j] = reinterpret_cast<FragFp4&>(xf[j]).sc;
       } else {
         load_fp8<TAIL>(reinterpret_cast<FragFp8&>(xf[j]), xrow[j], kt, g, KB);
@@ -267,29 +263,31 @@ struct PipeCfg {
   static constexpr int PER_WAVE = W_INSTR + X_INSTR + S_INSTR;
 };
 
-// LDS byte offset of 16-byte chunk c of `row` in a tile with rows of RB bytes.
+// LDS placement of 16-byte chunk c of `row` in a tile with rows of RB bytes:
+// row-major, chunks XOR-permuted within the row by f(row). A ds_read_b128 of
+// a fragment has 16 consecutive lanes reading the same chunk of 16 consecutive
+// rows; f makes those 16 reads land in 16 different 16-byte bank groups of a
+// 256-byte window (64 banks) and any 8 consecutive ones in 8 different groups
+// of a 128-byte window (32 banks).
+//   RB = 64  (4 chunks): bank group (4 row + c') mod 16 -> f = ((row>>1)&3) ^ ((row>>3)&1)
+//   RB = 128 (8 chunks): bank group (8 row + c') mod 16 -> f = ((row>>1)&7) ^ ((row&1)<<2)
+template <int RB>
+__device__ __forceinline__ int swz_f(int row) {
+  if constexpr (RB == 128) return ((row >> 1) & 7) ^ ((row & 1) << 2);
+  else return ((row >> 1) & 3) ^ ((row >> 3) & 1);
+}
+
 template <int RB>
 __device__ __forceinline__ int swz(int row, int c) {
-  if constexpr (RB == 128) {
-    return row * 128 + ((c ^ (row & 7)) << 4);
-  } else {  // RB == 64: two rows per 128-byte line
-    const int line = row >> 1;
-    return line * 128 + (((((row & 1) << 2) | c) ^ (line & 7)) << 4);
-  }
+  return row * RB + ((c ^ swz_f<RB>(row)) << 4);
 }
 
 // Inverse of swz: the (row, chunk) whose data belongs in 16-byte LDS slot `slot`.
 template <int RB>
 __device__ __forceinline__ void unswz(int slot, int& row, int& c) {
-  const int line = slot >> 3;
-  const int p = (slot & 7) ^ (line & 7);
-  if constexpr (RB == 128) {
-    row = line;
-    c = p;
-  } else {
-    row = 2 * line + (p >> 2);
-    c = p & 3;
-  }
+  constexpr int CPR = RB / 16;
+  row = slot / CPR;
+  c = (slot % CPR) ^ swz_f<RB>(row);
 }
 
 __device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
@@ -397,9 +395,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     unswz<C::X_RB>((wave * C::X_INSTR + q) * 64 + lane, row, c);
     vx[q] = (uint32_t)(m_base + row) * x_row + (uint32_t)c * 16;
   }
-  // scales: wave w copies rows 64 w .. 64 w + 63 (4 bytes each) of W, and of X for W4A4
-  const uint32_t vws = (uint32_t)(n_base + wave * 64 + lane) * (uint32_t)KB;
-  const uint32_t vxs = (uint32_t)(m_base + wave * 64 + lane) * (uint32_t)KB;
+  // scales (group-major, one 128-element group per stage): the tile's 256
+  // dwords of stage s are contiguous at byte (s * rows + base) * 4; wave w
+  // copies dwords 64 w .. 64 w + 63. Past the last row they belong to other
+  // rows (or read as zero at the end of the buffer) and only feed outputs
+  // that are never stored.
+  const uint32_t vws = (uint32_t)(n_base + wave * 64 + lane) * 4u;
+  const uint32_t vxs = (uint32_t)(m_base + wave * 64 + lane) * 4u;
+  const uint32_t ws_stage = (uint32_t)N * 4u;
+  const uint32_t xs_stage = (uint32_t)M * 4u;
 
   // Copies of stage s into `buf`. Stages past the end are still issued (so
   // the wait counts stay constant and the issue has no branch) but with an
@@ -415,8 +419,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int q = 0; q < C::X_INSTR; ++q)
       lds_dma16(rx, lds_addr(buf + C::X_OFF + (wave * C::X_INSTR + q) * 1024), live ? vx[q] + (uint32_t)s * C::X_RB : oob);
-    lds_dma4(rws, lds_addr(buf + C::WS_OFF + wave * 256), live ? vws + (uint32_t)s * C::SB : oob);
-    if constexpr (MODE == 0) lds_dma4(rxs, lds_addr(buf + C::XS_OFF + wave * 256), live ? vxs + (uint32_t)s * C::SB : oob);
+    lds_dma4(rws, lds_addr(buf + C::WS_OFF + wave * 256), live ? vws + (uint32_t)s * ws_stage : oob);
+    if constexpr (MODE == 0) lds_dma4(rxs, lds_addr(buf + C::XS_OFF + wave * 256), live ? vxs + (uint32_t)s * xs_stage : oob);
   };
 
   v16f acc[4][4];

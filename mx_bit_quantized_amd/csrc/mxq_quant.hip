@@ -16,11 +16,19 @@ namespace mxq {
 // ------------------------------------------------------------ MXFP4 -------
 //
 // Mapping: a wave walks one row at a time; each lane owns one 16-byte chunk
-// (8 bf16) per step, so four neighbouring lanes hold one 32-element block.
-// A step reads 1 KiB contiguous per wave and writes 256 contiguous bytes of
-// codes (4 per lane) and 16 scale bytes. The block amax is a max over the
-// magnitude bit patterns (sign cleared) across the 4 lanes - exact for finite
-// bf16, no float compare, no denormal flush.
+// (8 bf16) per step, so four neighbouring lanes hold one 32-element block and
+// sixteen lanes one 128-element group. A step reads 1 KiB contiguous per wave
+// and writes 256 contiguous bytes of codes (4 per lane). The block amax is a
+// max over the magnitude bit patterns (sign cleared) across the 4 lanes -
+// exact for finite bf16, no float compare, no denormal flush.
+//
+// Scales are stored group-major, [ceil(K/128)][rows][4]: the four E8M0 bytes
+// of the blocks of one 128-element group of one row form one dword, and the
+// dwords of all rows for one group are contiguous. The GEMM then fetches the
+// scales of a 256-row tile for one K stage as 1 KiB of consecutive memory.
+// The first lane of each group assembles the dword from the four block
+// leaders and writes it; bytes of blocks past K/32 in a ragged last group are
+// written as zero.
 
 __device__ __forceinline__ uint32_t quad_max(uint32_t v) {
   v = umax(v, (uint32_t)__shfl_xor((int)v, 1));
@@ -52,7 +60,7 @@ constexpr int kQuantWaves = 4;  // waves per workgroup
 
 __global__ __launch_bounds__(64 * kQuantWaves) void mxfp4_quant_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t K, int64_t ld,
-    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+    uint8_t* __restrict__ codes, uint32_t* __restrict__ scales) {
   const int lane = threadIdx.x & 63;
   const int64_t wave_id = (int64_t)blockIdx.x * kQuantWaves + (threadIdx.x >> 6);
   const int64_t n_waves = (int64_t)gridDim.x * kQuantWaves;
@@ -60,21 +68,25 @@ __global__ __launch_bounds__(64 * kQuantWaves) void mxfp4_quant_kernel(
   for (int64_t row = wave_id; row < rows; row += n_waves) {
     const uint4* src = reinterpret_cast<const uint4*>(x + row * ld);
     uint32_t* dst = reinterpret_cast<uint32_t*>(codes + row * (K >> 1));
-    uint8_t* sdst = scales + row * (K >> 5);
-
     for (int64_t c0 = 0; c0 < chunks; c0 += 64) {
       const int64_t c = c0 + lane;
       // chunks is a multiple of 4 and c0 of 64, so a whole 4-lane block is
-      // either in range or out of range: the shuffles below stay uniform
-      // within each block.
+      // either in range or out of range: the shuffles stay uniform per block.
       const bool ok = c < chunks;
       uint4 v = ok ? src[c] : make_uint4(0, 0, 0, 0);
       uint32_t amax = quad_max(chunk_amax(v));
       uint32_t sb = mx_scale_byte(amax);
       uint32_t packed = pack8_fp4(v, mx_inv_scale(sb));
+      // gather the 4 block scales of this lane's 128-element group into its
+      // first lane (block leaders sit at lanes +0, +4, +8, +12); out-of-range
+      // blocks contribute zero bytes
+      const uint32_t mine = ok ? sb : 0u;
+      const uint32_t s1 = (uint32_t)__shfl_down((int)mine, 4);
+      const uint32_t s2 = (uint32_t)__shfl_down((int)mine, 8);
+      const uint32_t s3 = (uint32_t)__shfl_down((int)mine, 12);
       if (ok) {
         dst[c] = packed;
-        if ((lane & 3) == 0) sdst[c >> 2] = (uint8_t)sb;
+        if ((lane & 15) == 0) scales[(c >> 4) * rows + row] = mine | (s1 << 8) | (s2 << 16) | (s3 << 24);
       }
     }
   }
@@ -135,7 +147,7 @@ hipError_t launch_mxfp4_quant(const void* x, int64_t rows, int64_t K, int64_t ld
                               void* codes, void* scales, hipStream_t s) {
   hipLaunchKernelGGL(mxfp4_quant_kernel, dim3(grid_for_rows(rows)), dim3(64 * kQuantWaves), 0, s,
                      static_cast<const uint16_t*>(x), rows, K, ld,
-                     static_cast<uint8_t*>(codes), static_cast<uint8_t*>(scales));
+                     static_cast<uint8_t*>(codes), static_cast<uint32_t*>(scales));
   return hipGetLastError();
 }
 

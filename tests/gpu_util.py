@@ -26,6 +26,16 @@ def host_f32(t):
     return t.detach().cpu().numpy().astype(np.float32)
 
 
+def group_major_scales(scales_rows):
+    """[rows, K/32] E8M0 bytes (oracle order) -> [ceil(K/128), rows, 4] (library order), zero padded."""
+    s = np.asarray(scales_rows, np.uint8)
+    rows, kb = s.shape
+    g = (kb + 3) // 4
+    pad = np.zeros((rows, 4 * g), np.uint8)
+    pad[:, :kb] = s
+    return np.ascontiguousarray(pad.reshape(rows, g, 4).transpose(1, 0, 2))
+
+
 def sample_rows(m, n_sample, seed, tile=256):
     """Seeded row sample that always holds row 0, row m-1 and rows of the last tile."""
     g = np.random.default_rng(seed)

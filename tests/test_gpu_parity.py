@@ -14,8 +14,8 @@ import torch
 import mx_bit_quantized_amd as mxq
 import oracle
 import synth
-from gpu_util import (assert_codes_equal, assert_output_close, dev_bf16, host_bits, host_f32,
-                      host_u8, sample_rows)
+from gpu_util import (assert_codes_equal, assert_output_close, dev_bf16, group_major_scales, host_bits,
+                      host_f32, host_u8, sample_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -60,7 +60,7 @@ def test_weight_pack_bit_exact(n, k):
     codes, scales = mxq.quantize_weight_mxfp4(dev_bf16(w))
     torch.cuda.synchronize()
     want_c, want_s = oracle.mxfp4_quantize(w)
-    assert_codes_equal(host_u8(scales), want_s, "weight scales")
+    assert_codes_equal(host_u8(scales), group_major_scales(want_s), "weight scales")
     assert_codes_equal(host_u8(codes), want_c, "weight codes")
 
 
@@ -73,7 +73,7 @@ def test_quantize_act_bit_exact(mode, m, k):
     torch.cuda.synchronize()
     want_c, want_s = oracle.quantize_act(mode, x)
     if mode == mxq.W4A4:
-        assert_codes_equal(host_u8(scales), want_s, "mxfp4 scales")
+        assert_codes_equal(host_u8(scales), group_major_scales(want_s), "mxfp4 scales")
     else:
         assert_codes_equal(host_f32(scales).view(np.uint32), want_s.view(np.uint32), "fp8 scales")
     assert_codes_equal(host_u8(codes), want_c, "act codes")
@@ -151,9 +151,9 @@ def test_gemm_identity_weight_reproduces_dequantized_activations():
 def test_gemm_empty_is_noop():
     say("gemm empty")
     wc = torch.zeros((64, 128), dtype=torch.uint8, device="cuda")
-    ws = torch.full((64, 8), 127, dtype=torch.uint8, device="cuda")
+    ws = torch.full((2, 64, 4), 127, dtype=torch.uint8, device="cuda")
     ac = torch.zeros((0, 128), dtype=torch.uint8, device="cuda")
-    asc = torch.zeros((0, 8), dtype=torch.uint8, device="cuda")
+    asc = torch.zeros((2, 0, 4), dtype=torch.uint8, device="cuda")
     y = mxq.gemm(mxq.W4A4, ac, asc, wc, ws)
     assert y.shape == (0, 64)
 
@@ -171,7 +171,7 @@ def test_config1_qlinear_both_modes_through_policy():
     xd = dev_bf16(x)
     owc, ows = oracle.mxfp4_quantize(w)
     assert_codes_equal(host_u8(wc), owc, "config1 weight codes")
-    assert_codes_equal(host_u8(ws), ows, "config1 weight scales")
+    assert_codes_equal(host_u8(ws), group_major_scales(ows), "config1 weight scales")
     for block in range(2):
         mode = policy.mode(0, block)
         assert mode == oracle.policy_mode(wl.policy(), 0, block)
@@ -196,7 +196,7 @@ def test_qlinear_rejects_policy_modes_without_writing():
     with pytest.raises(mxq.MxqError):
         mxq.qlinear(p, 0, 1, torch.zeros((4, 64), dtype=torch.bfloat16, device="cuda"),
                     torch.zeros((64, 32), dtype=torch.uint8, device="cuda"),
-                    torch.zeros((64, 2), dtype=torch.uint8, device="cuda"), y=y)
+                    torch.zeros((1, 64, 4), dtype=torch.uint8, device="cuda"), y=y)
     torch.cuda.synchronize()
     assert torch.all(y == 7.0)
 
