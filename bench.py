@@ -140,6 +140,33 @@ class Stack:
                         self.records.append(("gemm", mode, 2 * m * lin.n * lin.k, gbytes, e1, e2))
 
 
+KERNEL_SYMBOL = {0: "gemm_pipe_kernel<0>", 1: "gemm_pipe_kernel<1>"}
+
+
+def profiled_traffic(workload_tag, mode):
+    """HBM bytes per launch of the mode's GEMM kernel from the committed counter summary.
+
+    profiles/hbm_traffic_<workload>.txt holds calibrated FETCH_SIZE + WRITE_SIZE
+    bytes per dispatch and the sha1 of the GEMM source they were taken on; a
+    different source means the numbers describe another kernel: None.
+    """
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload_tag}.txt")
+    src = os.path.join(ROOT, "mx_bit_quantized_amd", "csrc", "mxq_gemm.hip")
+    if not os.path.exists(path):
+        return None
+    sha = hashlib.sha1(open(src, "rb").read()).hexdigest()
+    recorded, traffic = None, None
+    for line in open(path):
+        parts = line.split()
+        if parts[:1] == ["source_sha1_gemm"]:
+            recorded = parts[1]
+        elif parts[:1] == ["kernel"] and parts[1] == KERNEL_SYMBOL[mode]:
+            traffic = int(parts[5])
+    return traffic if recorded == sha else None
+
+
 def cpu_baseline(wl, sample_rows):
     """Oracle throughput on a bounded sample: `sample_rows` token rows through one block's linears."""
     import oracle
@@ -238,9 +265,13 @@ def main():
     dom = max((k for k in agg if k[0] == "gemm"), key=lambda k: agg[k]["ms"])
     a = agg[dom]
     achieved = a["flops"] / (a["ms"] * 1e-3) / 1e12
+    tag = [k for k, v in WORKLOADS.items() if v == wl.config_id][0]
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_TFLOPS[dom[1]], "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_TFLOPS[dom[1]], 4), "traffic": None,
-                "kernel": f"gemm_{'w4a4' if dom[1] == 0 else 'w4a8'}"}
+                "frac": round(achieved / PEAK_TFLOPS[dom[1]], 4),
+                "traffic": profiled_traffic(tag, dom[1]),
+                "kernel": KERNEL_SYMBOL[dom[1]],
+                "avg_launch_us": round(1e3 * a["ms"] / a["launches"], 1),
+                "flop_per_launch": a["flops"] // a["launches"]}
     modes = set(int(v) for v in stack.policy_table.flat)
     out = {
         "metric": METRIC,
