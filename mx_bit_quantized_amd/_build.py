@@ -23,7 +23,8 @@ DEVICE_SOURCES = ["mxq_api.cpp", "mxq_quant.hip", "mxq_gemm.hip"]
 
 COMMON_FLAGS = [
     "-O3",
-    "-std=c++17",
+    "-std=c++20",
+    "-Wno-inline-asm",
     "-fPIC",
     "-shared",
     "-Wall",

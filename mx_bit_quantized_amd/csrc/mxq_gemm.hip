@@ -221,46 +221,55 @@ __global__ __launch_bounds__(256) void gemm_direct_kernel(
 //
 // Workgroup tile 256 (n) x 256 (m), 4 waves in a 2 x 2 grid, each wave owns a
 // 128 x 128 output block = 4 x 4 MFMA tiles (256 fp32 accumulators per lane,
-// held in AGPRs). K advances in stages of 128 elements (4 MX blocks): FP4
-// lane slot g owns blocks 2g and 2g+1, MFMA step kk (0, 1) uses block 2g+kk.
+// held in AGPRs). K advances in stages of KT = 64 BPL elements (2 BPL MX
+// blocks): FP4 lane slot g owns blocks g BPL .. g BPL + BPL - 1, and MFMA step
+// kk (0 .. BPL-1) uses block g BPL + kk.
 //
 // Global -> LDS moves use buffer loads that write LDS directly (no staging
 // registers): each wave instruction fills 1 KiB of LDS, lane i writing bytes
 // [16 i, 16 i + 16) of it, so the layout is set by choosing each lane's global
-// address. A ring of NB stage buffers (separate LDS arrays, so the compiler
-// can tell the DMA target from the buffer being read) keeps NB-1 stages in
-// flight: W4A4 (34 KiB stages) runs 4 buffers, W4A8 (49 KiB) 3. Per stage:
-// wait for this wave's own copies of the stage, barrier (every wave's copies
-// landed and every wave finished the stage that last used the buffer about
-// to be refilled), issue the copies of stage s+NB-1, then the MFMAs.
-// Buffer resources carry the operand sizes: rows past M or N read as zero.
+// address. Buffer resources carry the operand sizes: rows past M or N read as
+// zero. A ring of NB stage buffers (separate LDS arrays) holds the stages.
 //
-// LDS rows hold one stage of one operand row (64 bytes FP4, 128 bytes FP8).
-// The 16-byte chunks of each 128-byte line are XOR-permuted by the line
-// index, so the 8 lanes of a ds_read_b128 phase (8 consecutive rows, same
-// chunk) hit 8 distinct bank groups.
+// Synchronisation, one barrier per stage: the barrier that opens stage s
+// certifies that every wave's copies of stage s+1 have landed (each wave first
+// waits for its own with s_waitcnt vmcnt) and that every wave has finished
+// reading the buffer about to be refilled (the one of stage s-1). Stage s then
+// issues the copies of stage s+NB-1 between its first MFMAs, and while its
+// MFMAs run it already reads the first fragments of stage s+1 from LDS, so the
+// matrix pipe keeps working across the barrier. NB-3 stages stay in flight
+// while a wave waits at a barrier, NB-2 while it computes.
+//
+// LDS rows hold one stage of one operand row (32, 64 or 128 bytes); their
+// 16-byte chunks are XOR-permuted per row (swz) so that the 16 lanes of a
+// ds_read_b128 phase reading one chunk of 16 consecutive rows hit 16 distinct
+// bank groups.
 //
 // Tile order: workgroups are dealt round-robin to the 8 XCDs; the kernel maps
 // the dispatch index so that each XCD receives a contiguous range of tiles,
 // and walks that range in groups of 8 tile-rows (m) per tile-column (n), so
 // the workgroups resident on one XCD share W and X panels in its L2.
 
-template <int MODE>
+template <int MODE, int KT_, int NB_>
 struct PipeCfg {
-  static constexpr int KT = 128;                      // K elements per stage
-  static constexpr int W_RB = 64;                     // FP4 row bytes per stage
-  static constexpr int X_RB = MODE == 0 ? 64 : 128;   // FP4 / FP8 row bytes per stage
-  static constexpr int SB = 4;                        // E8M0 bytes per row per stage
+  static constexpr int KT = KT_;                      // K elements per stage
+  static constexpr int NB = NB_;                      // ring depth
+  static constexpr int BPL = KT / 64;                 // blocks per lane slot per stage
+  static constexpr int W_RB = KT / 2;                 // FP4 row bytes per stage
+  static constexpr int X_RB = MODE == 0 ? KT / 2 : KT;  // FP4 / FP8 row bytes per stage
   static constexpr int W_OFF = 0;
   static constexpr int X_OFF = 256 * W_RB;
-  static constexpr int WS_OFF = X_OFF + 256 * X_RB;
-  static constexpr int XS_OFF = WS_OFF + 256 * SB;
-  static constexpr int STAGE = XS_OFF + (MODE == 0 ? 256 * SB : 0);
-  static constexpr int NB = MODE == 0 ? 4 : 3;        // ring depth
+  static constexpr int WS_OFF = X_OFF + 256 * X_RB;   // 256 scale dwords (one group)
+  static constexpr int XS_OFF = WS_OFF + 1024;
+  static constexpr int STAGE = XS_OFF + (MODE == 0 ? 1024 : 0);
   static constexpr int W_INSTR = 256 * W_RB / 1024 / 4;   // 1 KiB copies per wave per stage
   static constexpr int X_INSTR = 256 * X_RB / 1024 / 4;
   static constexpr int S_INSTR = MODE == 0 ? 2 : 1;       // 256 B scale copies per wave
   static constexpr int PER_WAVE = W_INSTR + X_INSTR + S_INSTR;
+  static_assert(KT == 64 || KT == 128, "stage of one or two blocks per lane slot");
+  static_assert(NB >= 3 && NB <= 8, "ring depth");
+  static_assert(NB * STAGE <= 160 * 1024, "LDS");
+  static_assert(KT == 128 || NB % 2 == 0, "half-group stages alternate scale bytes");
 };
 
 // LDS placement of 16-byte chunk c of `row` in a tile with rows of RB bytes:
@@ -269,12 +278,14 @@ struct PipeCfg {
 // rows; f makes those 16 reads land in 16 different 16-byte bank groups of a
 // 256-byte window (64 banks) and any 8 consecutive ones in 8 different groups
 // of a 128-byte window (32 banks).
+//   RB = 32  (2 chunks): bank group (2 row + c') mod 16 -> f = ((row>>2)^(row>>3)) & 1
 //   RB = 64  (4 chunks): bank group (4 row + c') mod 16 -> f = ((row>>1)&3) ^ ((row>>3)&1)
 //   RB = 128 (8 chunks): bank group (8 row + c') mod 16 -> f = ((row>>1)&7) ^ ((row&1)<<2)
 template <int RB>
 __device__ __forceinline__ int swz_f(int row) {
   if constexpr (RB == 128) return ((row >> 1) & 7) ^ ((row & 1) << 2);
-  else return ((row >> 1) & 3) ^ ((row >> 3) & 1);
+  else if constexpr (RB == 64) return ((row >> 1) & 3) ^ ((row >> 3) & 1);
+  else return ((row >> 2) ^ (row >> 3)) & 1;
 }
 
 template <int RB>
@@ -329,8 +340,7 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
-  return __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)((const MXQ_LDS uint8_t*)p));
+  return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)((const MXQ_LDS uint8_t*)p));
 }
 
 // One wave-wide copy from a buffer into LDS: lane i's 16 (or 4) bytes at byte
@@ -348,17 +358,31 @@ __device__ __forceinline__ void lds_dma4(const i32x4& rs, uint32_t lds, uint32_t
                :: "s"(lds), "v"(voff), "s"(rs) : "memory", "m0");
 }
 
+// Operand fragments of one MFMA step: 4 W row groups, 4 X row groups, and
+// their scale registers (byte kk for KT = 128, byte 0 for KT = 64).
 template <int MODE>
+struct StepFrags {
+  uint4 a[4];
+  uint4 b[MODE == 0 ? 4 : 8];
+  uint32_t ws[4];
+  uint32_t xs[4];
+};
+
+template <int MODE, int KT, int NB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_pipe_kernel(
     const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws,
     const uint8_t* __restrict__ aq, const void* __restrict__ asc,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
     int M, int N, int K, int epi, int tiles_m, int tiles_n) {
-  using C = PipeCfg<MODE>;
+  using C = PipeCfg<MODE, KT, NB>;
   __shared__ __attribute__((aligned(1024))) uint8_t sb0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t sb1[C::STAGE];
   __shared__ __attribute__((aligned(1024))) uint8_t sb2[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t sb3[C::NB == 4 ? C::STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t sb3[NB > 3 ? C::STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t sb4[NB > 4 ? C::STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t sb5[NB > 5 ? C::STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t sb6[NB > 6 ? C::STAGE : 16];
+  __shared__ __attribute__((aligned(1024))) uint8_t sb7[NB > 7 ? C::STAGE : 16];
 
   int tm, tn;
   tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
@@ -366,7 +390,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int m_base = tm * 256;
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int wave = t >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int r = lane & 31;
   const int g = lane >> 5;
   const int wn = wave & 1;
@@ -374,7 +398,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int KB = K >> 5;
   const uint32_t w_row = (uint32_t)K >> 1;
   const uint32_t x_row = MODE == 0 ? ((uint32_t)K >> 1) : (uint32_t)K;
-  const int n_stages = K / C::KT;
+  const int n_stages = K / KT;
 
   const i32x4 rw = make_rsrc(wq, w_row * (uint32_t)N);
   const i32x4 rx = make_rsrc(aq, x_row * (uint32_t)M);
@@ -395,32 +419,48 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     unswz<C::X_RB>((wave * C::X_INSTR + q) * 64 + lane, row, c);
     vx[q] = (uint32_t)(m_base + row) * x_row + (uint32_t)c * 16;
   }
-  // scales (group-major, one 128-element group per stage): the tile's 256
-  // dwords of stage s are contiguous at byte (s * rows + base) * 4; wave w
-  // copies dwords 64 w .. 64 w + 63. Past the last row they belong to other
-  // rows (or read as zero at the end of the buffer) and only feed outputs
-  // that are never stored.
+  // Scales (group-major, 128-element groups): the tile's 256 dwords of group
+  // gi are contiguous at byte (gi * rows + base) * 4; wave w copies dwords
+  // 64 w .. 64 w + 63. A 64-element stage uses half of its group's bytes.
+  // Past the last row the dwords belong to other rows (or read as zero at the
+  // end of the buffer) and only feed outputs that are never stored.
   const uint32_t vws = (uint32_t)(n_base + wave * 64 + lane) * 4u;
   const uint32_t vxs = (uint32_t)(m_base + wave * 64 + lane) * 4u;
-  const uint32_t ws_stage = (uint32_t)N * 4u;
-  const uint32_t xs_stage = (uint32_t)M * 4u;
+  const uint32_t ws_group = (uint32_t)N * 4u;
+  const uint32_t xs_group = (uint32_t)M * 4u;
 
-  // Copies of stage s into `buf`. Stages past the end are still issued (so
-  // the wait counts stay constant and the issue has no branch) but with an
-  // offset beyond every buffer's size: the hardware then writes zeros to LDS
-  // without reading memory. Offsets stay in the per-lane operand, which is
-  // the part the range check covers.
-  auto issue = [&](int s, uint8_t* buf) {
+  auto buf_of = [&](auto u_tag) -> uint8_t* {
+    constexpr int U = decltype(u_tag)::value;
+    if constexpr (U == 0) return sb0;
+    else if constexpr (U == 1) return sb1;
+    else if constexpr (U == 2) return sb2;
+    else if constexpr (U == 3) return sb3;
+    else if constexpr (U == 4) return sb4;
+    else if constexpr (U == 5) return sb5;
+    else if constexpr (U == 6) return sb6;
+    else return sb7;
+  };
+
+  // Copy q (0 .. PER_WAVE-1) of stage s into `buf`. Stages past the end are
+  // still issued (so the wait counts stay constant and the issue has no
+  // branch) but with an offset beyond every buffer's size: the hardware then
+  // writes zeros to LDS without reading memory. Offsets stay in the per-lane
+  // operand, the part the range check covers.
+  auto issue_one = [&](int q, int s, uint8_t* buf) {
     const bool live = s < n_stages;
     const uint32_t oob = 0x80000000u;
-#pragma unroll
-    for (int q = 0; q < C::W_INSTR; ++q)
-      lds_dma16(rw, lds_addr(buf + C::W_OFF + (wave * C::W_INSTR + q) * 1024), live ? vw[q] + (uint32_t)s * C::W_RB : oob);
-#pragma unroll
-    for (int q = 0; q < C::X_INSTR; ++q)
-      lds_dma16(rx, lds_addr(buf + C::X_OFF + (wave * C::X_INSTR + q) * 1024), live ? vx[q] + (uint32_t)s * C::X_RB : oob);
-    lds_dma4(rws, lds_addr(buf + C::WS_OFF + wave * 256), live ? vws + (uint32_t)s * ws_stage : oob);
-    if constexpr (MODE == 0) lds_dma4(rxs, lds_addr(buf + C::XS_OFF + wave * 256), live ? vxs + (uint32_t)s * xs_stage : oob);
+    if (q < C::W_INSTR) {
+      lds_dma16(rw, lds_addr(buf + C::W_OFF + (wave * C::W_INSTR + q) * 1024),
+                live ? vw[q] + (uint32_t)s * C::W_RB : oob);
+    } else if (q < C::W_INSTR + C::X_INSTR) {
+      const int qx = q - C::W_INSTR;
+      lds_dma16(rx, lds_addr(buf + C::X_OFF + (wave * C::X_INSTR + qx) * 1024),
+                live ? vx[qx] + (uint32_t)s * C::X_RB : oob);
+    } else if (q == C::W_INSTR + C::X_INSTR) {
+      lds_dma4(rws, lds_addr(buf + C::WS_OFF + wave * 256), live ? vws + (uint32_t)(s * KT / 128) * ws_group : oob);
+    } else {
+      lds_dma4(rxs, lds_addr(buf + C::XS_OFF + wave * 256), live ? vxs + (uint32_t)(s * KT / 128) * xs_group : oob);
+    }
   };
 
   v16f acc[4][4];
@@ -434,83 +474,105 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int wrow0 = wn * 128 + r;  // + 32 i
   const int xrow0 = wm * 128 + r;  // + 32 j
 
-  auto compute = [&](const uint8_t* base) {
-    uint32_t wsc[4], xsc[4];
+  // Fragments of step kk of the stage held in `base`; `half` is the stage's
+  // position in its 128-element scale group (KT = 64 only).
+  auto load_step = [&](const uint8_t* base, int kk, int half, StepFrags<MODE>& f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = wrow0 + 32 * i;
+      f.a[i] = *reinterpret_cast<const uint4*>(base + C::W_OFF + swz<C::W_RB>(row, g * C::BPL + kk));
+      if constexpr (KT == 128) f.ws[i] = *reinterpret_cast<const uint16_t*>(base + C::WS_OFF + row * 4 + 2 * g);
+      else f.ws[i] = base[C::WS_OFF + row * 4 + 2 * half + g];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = xrow0 + 32 * j;
+      if constexpr (MODE == 0) {
+        f.b[j] = *reinterpret_cast<const uint4*>(base + C::X_OFF + swz<C::X_RB>(row, g * C::BPL + kk));
+        if constexpr (KT == 128) f.xs[j] = *reinterpret_cast<const uint16_t*>(base + C::XS_OFF + row * 4 + 2 * g);
+        else f.xs[j] = base[C::XS_OFF + row * 4 + 2 * half + g];
+      } else {
+        // FP8 slot h = g: half g of block kk (FP4 slot 0), then half g of block BPL+kk (slot 1)
+        f.b[2 * j] = *reinterpret_cast<const uint4*>(base + C::X_OFF + swz<C::X_RB>(row, 2 * kk + g));
+        f.b[2 * j + 1] = *reinterpret_cast<const uint4*>(base + C::X_OFF + swz<C::X_RB>(row, 2 * (C::BPL + kk) + g));
+      }
+    }
+  };
+
+  // MFMAs of one step; after MFMA number k (0..15) the callback may issue work.
+  auto mfma_step = [&](const StepFrags<MODE>& f, auto kk_tag, auto&& between) {
+    constexpr int KK = decltype(kk_tag)::value;
+    constexpr int SEL = KT == 128 ? KK : 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      wsc[i] = *reinterpret_cast<const uint16_t*>(base + C::WS_OFF + (wrow0 + 32 * i) * 4 + 2 * g);
-    if constexpr (MODE == 0) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        xsc[j] = *reinterpret_cast<const uint16_t*>(base + C::XS_OFF + (xrow0 + 32 * j) * 4 + 2 * g);
-    }
-    auto step = [&](auto kk_tag) {
-      constexpr int KK = decltype(kk_tag)::value;
-      v8i a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[i] = op_fp4(*reinterpret_cast<const uint4*>(base + C::W_OFF + swz<C::W_RB>(wrow0 + 32 * i, 2 * g + KK)));
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int row = xrow0 + 32 * j;
-        if constexpr (MODE == 0) {
-          b[j] = op_fp4(*reinterpret_cast<const uint4*>(base + C::X_OFF + swz<C::X_RB>(row, 2 * g + KK)));
-        } else {
-          // FP8 slot h = g: half g of block KK (FP4 slot 0), then half g of block 2+KK (slot 1)
-          const uint4 lo = *reinterpret_cast<const uint4*>(base + C::X_OFF + swz<C::X_RB>(row, 2 * KK + g));
-          const uint4 hi = *reinterpret_cast<const uint4*>(base + C::X_OFF + swz<C::X_RB>(row, 2 * (2 + KK) + g));
-          b[j] = op_fp8(lo, hi);
-        }
+        const v8i a = op_fp4(f.a[i]);
+        if constexpr (MODE == 0)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, op_fp4(f.b[j]), acc[i][j], kFmtFp4, kFmtFp4,
+                                                                      SEL, (int)f.ws[i], SEL, (int)f.xs[j]);
+        else
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, op_fp8(f.b[2 * j], f.b[2 * j + 1]), acc[i][j],
+                                                                      kFmtFp4, kFmtFp8, SEL, (int)f.ws[i], SEL,
+                                                                      (int)kUnitScales);
+        between(i * 4 + j);
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if constexpr (MODE == 0)
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], kFmtFp4, kFmtFp4,
-                                                                        KK, (int)wsc[i], KK, (int)xsc[j]);
-          else
-            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[i], b[j], acc[i][j], kFmtFp4, kFmtFp8,
-                                                                        KK, (int)wsc[i], KK, (int)kUnitScales);
-        }
-    };
-    step(std::integral_constant<int, 0>{});
-    step(std::integral_constant<int, 1>{});
   };
 
-  auto buf_of = [&](auto u_tag) -> uint8_t* {
-    constexpr int U = decltype(u_tag)::value;
-    if constexpr (U == 0) return sb0;
-    else if constexpr (U == 1) return sb1;
-    else if constexpr (U == 2) return sb2;
-    else return sb3;
-  };
-
-  constexpr int D = C::NB - 1;  // stages in flight ahead of the one computed
-  // prologue: stages 0 .. D-1 into buffers 0 .. D-1
-  issue(0, buf_of(std::integral_constant<int, 0>{}));
-  issue(1, buf_of(std::integral_constant<int, 1>{}));
-  if constexpr (D >= 3) issue(2, buf_of(std::integral_constant<int, 2>{}));
+  constexpr int D = NB - 1;  // copies run D stages ahead of the stage computed
+  // prologue: copies of stages 0 .. D-1; stages 0 and 1 must have landed
+  // before the first fragments are read
+  [&]<int... Q>(std::integer_sequence<int, Q...>) {
+    (([&] {
+       constexpr int U = Q;
+#pragma unroll
+       for (int q = 0; q < C::PER_WAVE; ++q) issue_one(q, U, buf_of(std::integral_constant<int, U>{}));
+     }()),
+     ...);
+  }(std::make_integer_sequence<int, D>{});
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm((D - 2) * C::PER_WAVE));
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  StepFrags<MODE> cur;
+  load_step(sb0, 0, 0, cur);
 
   auto stage = [&](int s, auto u_tag) {
     constexpr int U = decltype(u_tag)::value;
-    // this wave's copies of stage s have landed once at most the copies of
-    // the D-1 later stages are still outstanding
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm((D - 1) * C::PER_WAVE));
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    issue(s + D, buf_of(std::integral_constant<int, (U + D) % C::NB>{}));
-    compute(buf_of(u_tag));
+    constexpr int UN = (U + 1) % NB;  // buffer of stage s+1
+    if (s > 0) {
+      // own copies of stage s+1 landed: at most those of stages s+2 .. s+D-1 remain
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm((D - 2) * C::PER_WAVE));
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    }
+    uint8_t* refill = buf_of(std::integral_constant<int, (U + D) % NB>{});
+    // copies of stage s+D interleaved with the MFMAs of the first step
+    auto issue_between = [&](int k) {
+      if (k < C::PER_WAVE) {
+        issue_one(k, s + D, refill);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    auto nothing = [](int) {};
+    if constexpr (C::BPL == 2) {
+      StepFrags<MODE> nxt;
+      load_step(buf_of(u_tag), 1, 0, nxt);
+      mfma_step(cur, std::integral_constant<int, 0>{}, issue_between);
+      load_step(buf_of(std::integral_constant<int, UN>{}), 0, 0, cur);
+      mfma_step(nxt, std::integral_constant<int, 1>{}, nothing);
+    } else {
+      StepFrags<MODE> nxt;
+      load_step(buf_of(std::integral_constant<int, UN>{}), 0, (U + 1) & 1, nxt);
+      mfma_step(cur, std::integral_constant<int, 0>{}, issue_between);
+      cur = nxt;
+    }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   };
 
-  for (int s0 = 0; s0 < n_stages; s0 += C::NB) {
-    stage(s0, std::integral_constant<int, 0>{});
-    if (s0 + 1 < n_stages) stage(s0 + 1, std::integral_constant<int, 1>{});
-    if (s0 + 2 < n_stages) stage(s0 + 2, std::integral_constant<int, 2>{});
-    if constexpr (C::NB == 4) {
-      if (s0 + 3 < n_stages) stage(s0 + 3, std::integral_constant<int, 3>{});
-    }
+  for (int s0 = 0; s0 < n_stages; s0 += NB) {
+    [&]<int... Q>(std::integer_sequence<int, Q...>) {
+      ((s0 + Q < n_stages ? stage(s0 + Q, std::integral_constant<int, Q>{}) : void()), ...);
+    }(std::make_integer_sequence<int, NB>{});
   }
   // no copy may still be writing LDS when the workgroup retires
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
@@ -544,12 +606,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 }
 
-template <int MODE>
+template <int MODE, int KT, int NB>
 static hipError_t launch_pipe(const void* aq, const void* as, const void* wq, const void* ws, const void* bias,
                               int epi, void* y, int64_t M, int64_t N, int64_t K, hipStream_t s) {
   const int tiles_m = (int)((M + 255) / 256);
   const int tiles_n = (int)((N + 255) / 256);
-  hipLaunchKernelGGL((gemm_pipe_kernel<MODE>), dim3(tiles_m * tiles_n), dim3(256), 0, s,
+  hipLaunchKernelGGL((gemm_pipe_kernel<MODE, KT, NB>), dim3(tiles_m * tiles_n), dim3(256), 0, s,
                      static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws),
                      static_cast<const uint8_t*>(aq), as, static_cast<const uint16_t*>(bias),
                      static_cast<uint16_t*>(y), (int)M, (int)N, (int)K, epi, tiles_m, tiles_n);
@@ -568,13 +630,17 @@ static hipError_t launch_direct(const void* aq, const void* as, const void* wq, 
   return hipGetLastError();
 }
 
-// The LDS kernel needs whole stages along K and N in multiples of 4 (8-byte
-// stores); every Wan2.2 linear qualifies. Everything else takes the direct
-// kernel.
+// Stage shape of the pipelined kernel per mode: K elements per stage and LDS
+// ring depth (both chosen from measurements on MI355X).
+constexpr int kPipeKT[2] = {128, 128};
+constexpr int kPipeNB[2] = {4, 3};
+
+// The pipelined kernel needs whole stages along K and N in multiples of 4
+// (8-byte stores); every Wan2.2 linear qualifies. Everything else takes the
+// direct kernel. 32-bit buffer offsets bound every operand below 2^31 bytes.
 static bool use_lds(int mode, int64_t M, int64_t N, int64_t K) {
   const int64_t a_bytes = mode == 0 ? M * (K / 2) : M * K;
-  // 32-bit buffer offsets: every operand must stay below 2^31 bytes
-  return K % 128 == 0 && N % 4 == 0 && M >= 256 && N >= 256 && a_bytes < (int64_t(1) << 31) &&
+  return K % kPipeKT[mode] == 0 && N % 4 == 0 && M >= 256 && N >= 256 && a_bytes < (int64_t(1) << 31) &&
          N * (K / 2) < (int64_t(1) << 31);
 }
 
@@ -583,8 +649,10 @@ hipError_t launch_gemm(int mode, const void* a_codes, const void* a_scales,
                        int epilogue, void* y, int64_t M, int64_t N, int64_t K,
                        hipStream_t s) {
   if (use_lds(mode, M, N, K)) {
-    if (mode == 0) return launch_pipe<0>(a_codes, a_scales, w_codes, w_scales, bias, epilogue, y, M, N, K, s);
-    return launch_pipe<1>(a_codes, a_scales, w_codes, w_scales, bias, epilogue, y, M, N, K, s);
+    if (mode == 0)
+      return launch_pipe<0, kPipeKT[0], kPipeNB[0]>(a_codes, a_scales, w_codes, w_scales, bias, epilogue, y, M, N,
+                                                    K, s);
+    return launch_pipe<1, kPipeKT[1], kPipeNB[1]>(a_codes, a_scales, w_codes, w_scales, bias, epilogue, y, M, N, K, s);
   }
   if (mode == 0)
     return launch_direct<0, 2, 2>(a_codes, a_scales, w_codes, w_scales, bias, epilogue, y, M, N, K, s);
@@ -593,7 +661,7 @@ hipError_t launch_gemm(int mode, const void* a_codes, const void* a_scales,
 
 const char* gemm_variant_name(int mode, int64_t M, int64_t N, int64_t K) {
   if (use_lds(mode, M, N, K))
-    return mode == 0 ? "pipe_w4a4_wg256x256_wave128x128_kt128_ring4" : "pipe_w4a8_wg256x256_wave128x128_kt128_ring3";
+    return mode == 0 ? "pipe_w4a4_wg256x256_wave128x128" : "pipe_w4a8_wg256x256_wave128x128";
   return mode == 0 ? "direct_w4a4_wg128x128_wave64x64" : "direct_w4a8_wg128x128_wave64x64";
 }
 
