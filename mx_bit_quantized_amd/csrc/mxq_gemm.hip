@@ -358,12 +358,15 @@ __device__ __forceinline__ void lds_dma4(const i32x4& rs, uint32_t lds, uint32_t
                :: "s"(lds), "v"(voff), "s"(rs) : "memory", "m0");
 }
 
-// Operand fragments of one MFMA step: 4 W row groups, 4 X row groups, and
-// their scale registers (byte kk for KT = 128, byte 0 for KT = 64).
+// Operand fragments of one MFMA step (4 W row groups, 4 X row groups) and the
+// scale registers of a stage (one 16-bit pair per row group for KT = 128,
+// one byte for KT = 64).
 template <int MODE>
-struct StepFrags {
+struct StepData {
   uint4 a[4];
   uint4 b[MODE == 0 ? 4 : 8];
+};
+struct StageScales {
   uint32_t ws[4];
   uint32_t xs[4];
 };
@@ -474,33 +477,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int wrow0 = wn * 128 + r;  // + 32 i
   const int xrow0 = wm * 128 + r;  // + 32 j
 
-  // Fragments of step kk of the stage held in `base`; `half` is the stage's
-  // position in its 128-element scale group (KT = 64 only).
-  auto load_step = [&](const uint8_t* base, int kk, int half, StepFrags<MODE>& f) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = wrow0 + 32 * i;
-      f.a[i] = *reinterpret_cast<const uint4*>(base + C::W_OFF + swz<C::W_RB>(row, g * C::BPL + kk));
-      if constexpr (KT == 128) f.ws[i] = *reinterpret_cast<const uint16_t*>(base + C::WS_OFF + row * 4 + 2 * g);
-      else f.ws[i] = base[C::WS_OFF + row * 4 + 2 * half + g];
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = xrow0 + 32 * j;
+  // LDS reads are issued one item at a time between MFMAs, in the order the
+  // MFMAs consume them: an item is kind * 16 + index with kinds W fragment
+  // (a[i]), X fragment (b[j]; for FP8 b[2j] / b[2j+1] are the two halves of
+  // row group j), W scale (ws[i]) and X scale (xs[j]).
+  constexpr int KA = 0, KBX = 16, KWS = 32, KXS = 48;
+  constexpr int DATA_ITEMS = MODE == 0 ? 8 : 12;   // fragments of one step
+  constexpr int STAGE_ITEMS = 16;                   // step-0 fragments + scales of a stage
+  constexpr int kStepOrder[2][12] = {
+      {KA + 0, KBX + 0, KBX + 1, KBX + 2, KBX + 3, KA + 1, KA + 2, KA + 3, -1, -1, -1, -1},
+      {KA + 0, KBX + 0, KBX + 1, KBX + 2, KBX + 3, KBX + 4, KBX + 5, KBX + 6, KBX + 7, KA + 1, KA + 2, KA + 3}};
+  constexpr int kStageOrder[2][16] = {
+      {KA + 0, KBX + 0, KWS + 0, KXS + 0, KBX + 1, KXS + 1, KBX + 2, KXS + 2, KBX + 3, KXS + 3, KA + 1, KWS + 1,
+       KA + 2, KWS + 2, KA + 3, KWS + 3},
+      {KA + 0, KBX + 0, KBX + 1, KWS + 0, KBX + 2, KBX + 3, KBX + 4, KBX + 5, KBX + 6, KBX + 7, KA + 1, KWS + 1,
+       KA + 2, KWS + 2, KA + 3, KWS + 3}};
+  auto read_item = [&](const uint8_t* base, int kk, int half, int code, StepData<MODE>& f, StageScales& sc) {
+    const int kind = code & ~15, idx = code & 15;
+    if (kind == KA) {
+      f.a[idx] = *reinterpret_cast<const uint4*>(base + C::W_OFF + swz<C::W_RB>(wrow0 + 32 * idx, g * C::BPL + kk));
+    } else if (kind == KBX) {
       if constexpr (MODE == 0) {
-        f.b[j] = *reinterpret_cast<const uint4*>(base + C::X_OFF + swz<C::X_RB>(row, g * C::BPL + kk));
-        if constexpr (KT == 128) f.xs[j] = *reinterpret_cast<const uint16_t*>(base + C::XS_OFF + row * 4 + 2 * g);
-        else f.xs[j] = base[C::XS_OFF + row * 4 + 2 * half + g];
+        f.b[idx] = *reinterpret_cast<const uint4*>(base + C::X_OFF + swz<C::X_RB>(xrow0 + 32 * idx, g * C::BPL + kk));
       } else {
         // FP8 slot h = g: half g of block kk (FP4 slot 0), then half g of block BPL+kk (slot 1)
-        f.b[2 * j] = *reinterpret_cast<const uint4*>(base + C::X_OFF + swz<C::X_RB>(row, 2 * kk + g));
-        f.b[2 * j + 1] = *reinterpret_cast<const uint4*>(base + C::X_OFF + swz<C::X_RB>(row, 2 * (C::BPL + kk) + g));
+        const int j = idx >> 1;
+        const int chunk = (idx & 1) ? 2 * (C::BPL + kk) + g : 2 * kk + g;
+        f.b[idx] = *reinterpret_cast<const uint4*>(base + C::X_OFF + swz<C::X_RB>(xrow0 + 32 * j, chunk));
       }
+    } else {
+      const bool is_w = kind == KWS;
+      const int off = (is_w ? C::WS_OFF : C::XS_OFF) + ((is_w ? wrow0 : xrow0) + 32 * idx) * 4;
+      uint32_t v;
+      if constexpr (KT == 128) v = *reinterpret_cast<const uint16_t*>(base + off + 2 * g);
+      else v = base[off + 2 * half + g];
+      if (is_w) sc.ws[idx] = v;
+      else sc.xs[idx] = v;
     }
   };
 
-  // MFMAs of one step; after MFMA number k (0..15) the callback may issue work.
-  auto mfma_step = [&](const StepFrags<MODE>& f, auto kk_tag, auto&& between) {
+  // The 16 MFMAs of one step; after MFMA number k (0..15) `between(k)` may
+  // issue one deferred operation, and the order is pinned by a scheduling
+  // barrier so that the reads stay spread between the MFMAs.
+  auto mfma_step = [&](const StepData<MODE>& f, const StageScales& sc, auto kk_tag, auto&& between) {
     constexpr int KK = decltype(kk_tag)::value;
     constexpr int SEL = KT == 128 ? KK : 0;
 #pragma unroll
@@ -510,12 +529,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const v8i a = op_fp4(f.a[i]);
         if constexpr (MODE == 0)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, op_fp4(f.b[j]), acc[i][j], kFmtFp4, kFmtFp4,
-                                                                      SEL, (int)f.ws[i], SEL, (int)f.xs[j]);
+                                                                      SEL, (int)sc.ws[i], SEL, (int)sc.xs[j]);
         else
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, op_fp8(f.b[2 * j], f.b[2 * j + 1]), acc[i][j],
-                                                                      kFmtFp4, kFmtFp8, SEL, (int)f.ws[i], SEL,
+                                                                      kFmtFp4, kFmtFp8, SEL, (int)sc.ws[i], SEL,
                                                                       (int)kUnitScales);
         between(i * 4 + j);
+        __builtin_amdgcn_sched_barrier(0);
       }
   };
 
@@ -533,8 +553,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   __builtin_amdgcn_s_waitcnt(waitcnt_vm((D - 2) * C::PER_WAVE));
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  StepFrags<MODE> cur;
-  load_step(sb0, 0, 0, cur);
+  StepData<MODE> cur;
+  StageScales cur_sc;
+#pragma unroll
+  for (int k = 0; k < STAGE_ITEMS; ++k) read_item(sb0, 0, 0, kStageOrder[MODE][k], cur, cur_sc);
 
   auto stage = [&](int s, auto u_tag) {
     constexpr int U = decltype(u_tag)::value;
@@ -545,26 +567,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     }
+    uint8_t* here = buf_of(u_tag);
+    uint8_t* next = buf_of(std::integral_constant<int, UN>{});
     uint8_t* refill = buf_of(std::integral_constant<int, (U + D) % NB>{});
-    // copies of stage s+D interleaved with the MFMAs of the first step
-    auto issue_between = [&](int k) {
-      if (k < C::PER_WAVE) {
-        issue_one(k, s + D, refill);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
-    auto nothing = [](int) {};
+    const int next_half = (U + 1) & 1;
+    StepData<MODE> nxt;
+    StageScales nxt_sc;
     if constexpr (C::BPL == 2) {
-      StepFrags<MODE> nxt;
-      load_step(buf_of(u_tag), 1, 0, nxt);
-      mfma_step(cur, std::integral_constant<int, 0>{}, issue_between);
-      load_step(buf_of(std::integral_constant<int, UN>{}), 0, 0, cur);
-      mfma_step(nxt, std::integral_constant<int, 1>{}, nothing);
+      // step 0: MFMAs on `cur`; between them the reads of step 1's fragments
+      // (early, they are needed next) and the copies of stage s+D
+      mfma_step(cur, cur_sc, std::integral_constant<int, 0>{}, [&](int k) {
+        if (k < DATA_ITEMS) read_item(here, 1, 0, kStepOrder[MODE][k], nxt, nxt_sc);
+        if (k < C::PER_WAVE) issue_one(k, s + D, refill);
+      });
+      // step 1: MFMAs on `nxt`; between them the reads of stage s+1's step-0
+      // fragments and scales, in the order the next stage consumes them
+      const StageScales sc1 = cur_sc;
+      mfma_step(nxt, sc1, std::integral_constant<int, 1>{}, [&](int k) {
+        read_item(next, 0, next_half, kStageOrder[MODE][k], cur, cur_sc);
+      });
     } else {
-      StepFrags<MODE> nxt;
-      load_step(buf_of(std::integral_constant<int, UN>{}), 0, (U + 1) & 1, nxt);
-      mfma_step(cur, std::integral_constant<int, 0>{}, issue_between);
+      mfma_step(cur, cur_sc, std::integral_constant<int, 0>{}, [&](int k) {
+        read_item(next, 0, next_half, kStageOrder[MODE][k], nxt, nxt_sc);
+        if (k < C::PER_WAVE) issue_one(k, s + D, refill);
+      });
       cur = nxt;
+      cur_sc = nxt_sc;
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   };
