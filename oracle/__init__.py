@@ -11,7 +11,8 @@ W4A4 = OCP MXFP4 weights with dynamic MXFP4 activations, W4A8 = OCP MXFP4
 weights with FP8 E4M3 activations; its W4A8 rows were produced by
 quantize-dequantize emulation):
 
-* ``formats``  - bf16 bit handling, the E2M1 / E4M3FN / E8M0 code tables and a
+* ``formats``  - bf16 bit handling (decode, and the layer's bf16 output
+                 rounding), the E2M1 / E4M3FN / E8M0 code tables and a
                  generic round-to-nearest-even into a small binary float format.
 * ``quant``    - MXFP4 block quantizer (one E8M0 scale per 32 elements along K)
                  and FP8 E4M3FN per-token quantizer (scale = row amax / 448).
@@ -33,6 +34,8 @@ from .formats import (
     round_to_binary_format,
     e2m1_encode,
     e4m3fn_encode,
+    f64_to_bf16_bits,
+    BF16_MAX,
 )
 from .quant import (
     mxfp4_quantize,

@@ -111,3 +111,21 @@ def e4m3fn_encode(r):
     """float64 values -> E4M3FN codes (RNE, saturating at 448, never NaN)."""
     q = round_to_binary_format(r, mbits=3, emin=-6, maxval=448.0)
     return _encode_from_table(q, _E4M3_MAGNITUDES, 7)
+
+
+BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
+
+
+def f64_to_bf16_bits(r):
+    """float64 values -> bf16 bit patterns, IEEE round to nearest even.
+
+    The layer's output is stored in bf16 (8 exponent bits, 7 mantissa bits,
+    subnormals from 2^-133). Magnitudes that round above the largest finite
+    value become infinities, as in IEEE rounding; NaN stays NaN.
+    """
+    r = np.asarray(r, dtype=np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        q = round_to_binary_format(r, mbits=7, emin=-126, maxval=np.inf)
+        q = np.where(np.abs(q) > BF16_MAX, np.copysign(np.inf, r), q)
+        bits = (q.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    return bits

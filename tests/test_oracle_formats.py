@@ -159,3 +159,34 @@ def test_bf16_bits_roundtrip_through_torch():
     want = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
     got = oracle.bf16_bits_to_f64(bits)
     assert np.array_equal(got, want)
+
+
+def test_f64_to_bf16_matches_torch_rne_on_fp32_inputs():
+    """bf16 output rounding against torch's fp32 -> bf16 conversion (IEEE RNE).
+
+    Inputs are fp32-representable so that torch rounds once: every exact
+    midpoint between neighbouring bf16 values (ties, low half 0x8000), the
+    values one fp32 ulp either side of it, subnormals, and the overflow edge.
+    """
+    g = np.random.default_rng(7)
+    hi = g.integers(0, 1 << 16, size=200_000, dtype=np.uint32)
+    hi = hi[(hi & 0x7F80) != 0x7F80]  # finite bf16 prefixes
+    low = np.array([0x0000, 0x7FFF, 0x8000, 0x8001, 0xFFFF, 0x1234], np.uint32)
+    u = ((hi[:, None] << np.uint32(16)) | low[None, :]).ravel()
+    x32 = u.view(np.float32)
+    want = torch.from_numpy(x32.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle.f64_to_bf16_bits(x32.astype(np.float64))
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, (u[bad[:4]], got[bad[:4]], want[bad[:4]])
+
+
+def test_f64_to_bf16_closed_forms():
+    f = lambda v: int(oracle.f64_to_bf16_bits(np.array([v]))[0])
+    assert f(1.0) == 0x3F80 and f(-2.0) == 0xC000 and f(-0.0) == 0x8000
+    assert f(1.0 + 2.0 ** -8) == 0x3F80          # tie -> even (1.0)
+    assert f(1.0 + 3 * 2.0 ** -8) == 0x3F82      # tie -> even (1 + 2^-6)
+    assert f(1.0 + 2.0 ** -8 + 2.0 ** -40) == 0x3F81  # just above the tie (not fp32-representable)
+    assert f(2.0 ** -133) == 0x0001 and f(2.0 ** -134) == 0x0000  # smallest subnormal; tie to zero
+    assert f(oracle.BF16_MAX) == 0x7F7F
+    assert f(oracle.BF16_MAX + 2.0 ** 119) == 0x7F80  # halfway to 2^128 -> even -> inf
+    assert f(-1e300) == 0xFF80
