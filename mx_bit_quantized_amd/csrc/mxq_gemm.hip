@@ -602,35 +602,76 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       ((s0 + Q < n_stages ? stage(s0 + Q, std::integral_constant<int, Q>{}) : void()), ...);
     }(std::make_integer_sequence<int, NB>{});
   }
-  // no copy may still be writing LDS when the workgroup retires
+  // ---- epilogue. The ring is free once every copy has landed (own copies:
+  // vmcnt(0); the others': the barrier) and every wave is past its last read.
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
 
-  // ---- epilogue: accumulator q of lane (r, g) in a 32x32 tile holds
-  // n = 8 (q / 4) + 4 g + (q % 4), m = r
+  // Accumulator q of lane (r, g) in a 32x32 tile holds n = 8 (q / 4) + 4 g +
+  // (q % 4), m = r. Per group of 32 token rows (j) the wave writes its fp32
+  // accumulators to LDS (rows of 128 values, 528-byte pitch: conflict-free
+  // 16-byte writes and reads), then reads them back with 16 lanes per row,
+  // 8 consecutive columns per lane, applies scale, bias and GELU and stores
+  // 16 bytes of bf16. The per-element work sits in one short loop: the
+  // epilogue stays small enough to remain in the instruction cache next to
+  // the main loop. Region: half of ring buffer sb0 (waves 0, 1) or sb1 (2, 3).
+  constexpr int EP = 528;
+  static_assert(2 * 32 * EP <= C::STAGE, "epilogue staging fits in one ring buffer per wave pair");
+  uint8_t* region = (wm == 0 ? sb0 : sb1) + wn * (32 * EP);
   const float* tok_scale = static_cast<const float*>(asc);
+  const int lrow = lane >> 4;         // row within a group of 4 (read phase)
+  const int lcol = (lane & 15) * 8;   // first of the lane's 8 columns (read phase)
+  const int n0 = n_base + wn * 128 + lcol;
+  const bool vec16 = (N & 7) == 0;    // 16-byte aligned output rows
+  const bool has_bias = bias != nullptr;
+  float bv[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) bv[u] = has_bias && n0 + u < N ? as_float((uint32_t)bias[n0 + u] << 16) : 0.0f;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int m = m_base + wm * 128 + 32 * j + r;
-    if (m >= M) continue;
-    const float sm = MODE == 1 ? tok_scale[m] : 1.0f;
-    uint16_t* yrow = y + (int64_t)m * N;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
-        const int nb = n_base + wn * 128 + 32 * i + 8 * qq + 4 * g;
-        if (nb >= N) continue;  // N is a multiple of 4 on this path
-        float v[4];
+      for (int qq = 0; qq < 4; ++qq)
+        *reinterpret_cast<float4*>(region + r * EP + (32 * i + 8 * qq + 4 * g) * 4) =
+            make_float4(acc[i][j][4 * qq], acc[i][j][4 * qq + 1], acc[i][j][4 * qq + 2], acc[i][j][4 * qq + 3]);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    const int m_grp = m_base + wm * 128 + 32 * j;
+#pragma unroll 1
+    for (int k = 0; k < 8; ++k) {
+      const int row = 4 * k + lrow;
+      const int m = m_grp + row;
+      const float4 lo = *reinterpret_cast<const float4*>(region + row * EP + lcol * 4);
+      const float4 hi = *reinterpret_cast<const float4*>(region + row * EP + lcol * 4 + 16);
+      if (m < M) {
+        float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        if constexpr (MODE == 1) {
+          const float sm = tok_scale[m];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          v[u] = acc[i][j][4 * qq + u] * sm;
-          if (bias != nullptr) v[u] += as_float((uint32_t)bias[nb + u] << 16);
-          if (epi == 1) v[u] = gelu_tanh_dev(v[u]);
+          for (int u = 0; u < 8; ++u) v[u] *= sm;
         }
-        *reinterpret_cast<uint2*>(yrow + nb) =
-            make_uint2(bf16_rne(v[0]) | (bf16_rne(v[1]) << 16), bf16_rne(v[2]) | (bf16_rne(v[3]) << 16));
+        if (has_bias) {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) v[u] += bv[u];
+        }
+        if (epi == 1) {
+#pragma unroll
+          for (int u = 0; u < 8; ++u) v[u] = gelu_tanh_dev(v[u]);
+        }
+        uint32_t h[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) h[u] = bf16_rne(v[2 * u]) | (bf16_rne(v[2 * u + 1]) << 16);
+        uint16_t* dst = y + (int64_t)m * N + n0;
+        if (vec16 && n0 + 8 <= N) {
+          *reinterpret_cast<uint4*>(dst) = make_uint4(h[0], h[1], h[2], h[3]);
+        } else {
+          if (n0 + 4 <= N) *reinterpret_cast<uint2*>(dst) = make_uint2(h[0], h[1]);
+          if (n0 + 8 <= N) *reinterpret_cast<uint2*>(dst + 4) = make_uint2(h[2], h[3]);
+        }
       }
     }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
   }
 }
 
