@@ -134,6 +134,15 @@ int mxq_gemm(int mode, const void* a_codes, const void* a_scales,
              hipStream_t stream);
 
 /*
+ * Name of the kernel that mxq_gemm runs for (mode, M, N, K), as a static
+ * string: "pipe_..." for the LDS-pipelined persistent kernel (M, N >= 256,
+ * N a multiple of 8, K a multiple of 128 with at least one ring of stages),
+ * "direct_..." for the register-tiled kernel, "invalid" for a mode that is
+ * not W4A4 or W4A8. Host only: enqueues nothing, never fails.
+ */
+const char* mxq_gemm_kernel_name(int mode, int64_t M, int64_t N, int64_t K);
+
+/*
  * Per-expert, per-block policy table ("Practical workflow", step 6).
  *   modes   host, uint8 [n_experts][n_blocks]; each entry MXQ_W4A4 or
  *           MXQ_W4A8 (anything else: MXQ_ERR_MODE). Copied; the caller may

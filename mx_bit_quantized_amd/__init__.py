@@ -10,6 +10,7 @@ Names mirror the C ABI without its ``mxq_`` prefix:
     quantize_weight_mxfp4(w)                      -> (codes, scales)
     quantize_act(mode, x)                         -> (codes, scales)
     gemm(mode, a_codes, a_scales, w_codes, w_scales, bias=None, epilogue=EPI_NONE)
+    gemm_kernel_name(mode, M, N, K)
     Policy(table) / policy_create / policy_destroy / policy_mode
     qlinear_workspace_bytes(mode, M, K)
     qlinear(policy, expert, block, x, w_codes, w_scales, bias=None, epilogue=EPI_NONE)
@@ -38,6 +39,7 @@ _SIGS = {
     "mxq_quantize_weight_mxfp4": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "mxq_quantize_act": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, _I64, _P, _P, _P]),
     "mxq_gemm": (ctypes.c_int, [ctypes.c_int, _P, _P, _P, _P, _P, ctypes.c_int, _P, _I64, _I64, _I64, _P]),
+    "mxq_gemm_kernel_name": (ctypes.c_char_p, [ctypes.c_int, _I64, _I64, _I64]),
     "mxq_policy_create": (ctypes.c_int, [_P, _I32, _I32, ctypes.POINTER(_P)]),
     "mxq_policy_destroy": (ctypes.c_int, [_P]),
     "mxq_policy_mode": (ctypes.c_int, [_P, _I32, _I32, ctypes.POINTER(ctypes.c_int)]),
@@ -175,6 +177,11 @@ def gemm(mode, a_codes, a_scales, w_codes, w_scales, bias=None, epilogue=EPI_NON
                          _dev_ptr(y, "y", torch.bfloat16), m, n, k, _stream_handle(stream))
     _check(st, "gemm")
     return y
+
+
+def gemm_kernel_name(mode, M, N, K):
+    """Name of the kernel gemm() runs for this mode and shape (host query)."""
+    return lib().mxq_gemm_kernel_name(int(mode), int(M), int(N), int(K)).decode()
 
 
 # -------------------------------------------------------------- policy ----

@@ -123,6 +123,11 @@ int mxq_gemm(int mode, const void* a_codes, const void* a_scales,
   return hip_status(mxq::launch_gemm(mode, a_codes, a_scales, w_codes, w_scales, bias, epilogue, y, M, N, K, stream));
 }
 
+const char* mxq_gemm_kernel_name(int mode, int64_t M, int64_t N, int64_t K) {
+  if (mode != MXQ_W4A4 && mode != MXQ_W4A8) return "invalid";
+  return mxq::gemm_variant_name(mode, M, N, K);
+}
+
 int mxq_policy_create(const uint8_t* modes, int32_t n_experts, int32_t n_blocks, void** policy) {
   if (policy == nullptr) return MXQ_ERR_NULL;
   *policy = nullptr;

@@ -217,7 +217,7 @@ __global__ __launch_bounds__(256) void gemm_direct_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// LDS-pipelined kernel for the large shapes.
+// LDS-pipelined persistent kernel for the large shapes.
 //
 // Workgroup tile 256 (n) x 256 (m), 4 waves in a 2 x 2 grid, each wave owns a
 // 128 x 128 output block = 4 x 4 MFMA tiles (256 fp32 accumulators per lane,
@@ -225,30 +225,43 @@ __global__ __launch_bounds__(256) void gemm_direct_kernel(
 // blocks): FP4 lane slot g owns blocks g BPL .. g BPL + BPL - 1, and MFMA step
 // kk (0 .. BPL-1) uses block g BPL + kk.
 //
+// One workgroup per CU walks a list of tiles. The stages of all its tiles form
+// one stream: stage G of the stream lives in ring slot G mod NB, and the
+// copies of stage G + NB - 1 (possibly of the next tile) are issued while
+// stage G computes, so a tile starts with its first stages already in LDS.
+//
 // Global -> LDS moves use buffer loads that write LDS directly (no staging
 // registers): each wave instruction fills 1 KiB of LDS, lane i writing bytes
 // [16 i, 16 i + 16) of it, so the layout is set by choosing each lane's global
 // address. Buffer resources carry the operand sizes: rows past M or N read as
-// zero. A ring of NB stage buffers (separate LDS arrays) holds the stages.
+// zero.
 //
-// Synchronisation, one barrier per stage: the barrier that opens stage s
-// certifies that every wave's copies of stage s+1 have landed (each wave first
+// Synchronisation, one barrier per stage: the barrier that opens stage G
+// certifies that every wave's copies of stage G+1 have landed (each wave first
 // waits for its own with s_waitcnt vmcnt) and that every wave has finished
-// reading the buffer about to be refilled (the one of stage s-1). Stage s then
-// issues the copies of stage s+NB-1 between its first MFMAs, and while its
-// MFMAs run it already reads the first fragments of stage s+1 from LDS, so the
-// matrix pipe keeps working across the barrier. NB-3 stages stay in flight
-// while a wave waits at a barrier, NB-2 while it computes.
+// reading the slot about to be refilled (the one of stage G-1). Stage G then
+// issues the copies of stage G+NB-1 between its first MFMAs, and while its
+// MFMAs run it already reads the first fragments of stage G+1 from LDS, so the
+// matrix pipe keeps working across the barrier.
+//
+// Epilogue: after a tile's last stage its slot is free until the next stage's
+// copies; the waves stage their fp32 results there (16 rows at a time) and
+// send them out with range-checked buffer stores. The stores stay in flight
+// while the next tile computes: vmcnt counts loads and stores in issue order,
+// so for the NB-2 stages after an epilogue each wait allows that epilogue's
+// memory operations to remain outstanding. Bias and per-token scales reach LDS
+// by the same copy mechanism (issued one tile ahead), so the kernel issues no
+// load whose wait the compiler would place.
 //
 // LDS rows hold one stage of one operand row (32, 64 or 128 bytes); their
 // 16-byte chunks are XOR-permuted per row (swz) so that the 16 lanes of a
 // ds_read_b128 phase reading one chunk of 16 consecutive rows hit 16 distinct
 // bank groups.
 //
-// Tile order: workgroups are dealt round-robin to the 8 XCDs; the kernel maps
-// the dispatch index so that each XCD receives a contiguous range of tiles,
-// and walks that range in groups of 8 tile-rows (m) per tile-column (n), so
-// the workgroups resident on one XCD share W and X panels in its L2.
+// Tile order: workgroups are dealt round-robin to the 8 XCDs; XCD x owns a
+// contiguous range of tiles in an order that walks groups of 8 tile-rows (m)
+// per tile-column (n), and its workgroups take consecutive tiles of that
+// range, so the tiles in flight on one XCD share W and X panels in its L2.
 
 template <int MODE, int KT_, int NB_>
 struct PipeCfg {
@@ -301,11 +314,8 @@ __device__ __forceinline__ void unswz(int slot, int& row, int& c) {
   c = (slot % CPR) ^ swz_f<RB>(row);
 }
 
-__device__ __forceinline__ void tile_coords(int bid, int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int total = tiles_m * tiles_n;
-  const int per = total / 8;
-  int t = bid;
-  if (bid < per * 8) t = (bid & 7) * per + (bid >> 3);  // contiguous range per XCD
+// Tile t of the grouped order: groups of 8 tile-rows, m fastest inside a group.
+__device__ __forceinline__ void tile_of(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
   constexpr int G = 8;
   const int group = t / (G * tiles_n);
   const int first_m = group * G;
@@ -371,6 +381,23 @@ struct StageScales {
   uint32_t xs[4];
 };
 
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to packed bf16 (low half = a), round to nearest even: one
+// v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const v2f f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2));
+}
+
+// Range-checked 16-byte store: offsets at or past the resource size are dropped.
+__device__ __forceinline__ void buf_store16(const i32x4& rs, uint32_t voff, const uint4& v) {
+  const i32x4 d = {(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+  asm volatile("buffer_store_dwordx4 %0, %1, %2, 0 offen" :: "v"(d), "v"(voff), "s"(rs) : "memory");
+}
+
 template <int MODE, int KT, int NB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_pipe_kernel(
     const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws,
@@ -378,19 +405,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
     int M, int N, int K, int epi, int tiles_m, int tiles_n) {
   using C = PipeCfg<MODE, KT, NB>;
-  __shared__ __attribute__((aligned(1024))) uint8_t sb0[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t sb1[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t sb2[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) uint8_t sb3[NB > 3 ? C::STAGE : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t sb4[NB > 4 ? C::STAGE : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t sb5[NB > 5 ? C::STAGE : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t sb6[NB > 6 ? C::STAGE : 16];
-  __shared__ __attribute__((aligned(1024))) uint8_t sb7[NB > 7 ? C::STAGE : 16];
+  // ring of NB stage slots, then two tile-parameter blocks: bias slice (512
+  // bytes), a sink for the unused waves' copies (512), token scales (1024, FP8)
+  constexpr int P_BIAS = 0, P_SINK = 512, P_TOK = 1024;
+  constexpr int PARAM_BYTES = MODE == 1 ? 2048 : 1024;
+  constexpr int PARAM_OFF = NB * C::STAGE;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NB * C::STAGE + 2 * PARAM_BYTES];
 
-  int tm, tn;
-  tile_coords(blockIdx.x, tiles_m, tiles_n, tm, tn);
-  const int n_base = tn * 256;
-  const int m_base = tm * 256;
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -403,76 +424,128 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const uint32_t x_row = MODE == 0 ? ((uint32_t)K >> 1) : (uint32_t)K;
   const int n_stages = K / KT;
 
-  const i32x4 rw = make_rsrc(wq, w_row * (uint32_t)N);
-  const i32x4 rx = make_rsrc(aq, x_row * (uint32_t)M);
-  const i32x4 rws = make_rsrc(ws, (uint32_t)KB * (uint32_t)N);
-  const i32x4 rxs = make_rsrc(asc, MODE == 0 ? (uint32_t)KB * (uint32_t)M : 0u);
+  // This workgroup's tiles: first, first + stride, ... (count of them).
+  const int total = tiles_m * tiles_n;
+  const int P = gridDim.x;
+  int first, stride, count;
+  if ((P & 7) == 0 && total >= P) {
+    const int x = blockIdx.x & 7, c = blockIdx.x >> 3, S = P >> 3;
+    const int per = total >> 3, rem = total & 7;
+    const int lo = x * per + min(x, rem), hi = (x + 1) * per + min(x + 1, rem);
+    first = lo + c;
+    stride = S;
+    count = first < hi ? (hi - first + S - 1) / S : 0;
+  } else {
+    first = blockIdx.x;
+    stride = P;
+    count = (total - first + P - 1) / P;
+  }
+  first = __builtin_amdgcn_readfirstlane(first);
+  count = __builtin_amdgcn_readfirstlane(count);
+  const int total_stages = count * n_stages;
 
-  // Per-lane source offsets of this wave's copies (stage 0); stage s adds s * RB.
+  // Per-lane source offsets inside a tile (stage 0); stage s adds s * RB.
   uint32_t vw[C::W_INSTR], vx[C::X_INSTR];
 #pragma unroll
   for (int q = 0; q < C::W_INSTR; ++q) {
     int row, c;
     unswz<C::W_RB>((wave * C::W_INSTR + q) * 64 + lane, row, c);
-    vw[q] = (uint32_t)(n_base + row) * w_row + (uint32_t)c * 16;
+    vw[q] = (uint32_t)row * w_row + (uint32_t)c * 16;
   }
 #pragma unroll
   for (int q = 0; q < C::X_INSTR; ++q) {
     int row, c;
     unswz<C::X_RB>((wave * C::X_INSTR + q) * 64 + lane, row, c);
-    vx[q] = (uint32_t)(m_base + row) * x_row + (uint32_t)c * 16;
+    vx[q] = (uint32_t)row * x_row + (uint32_t)c * 16;
   }
   // Scales (group-major, 128-element groups): the tile's 256 dwords of group
   // gi are contiguous at byte (gi * rows + base) * 4; wave w copies dwords
   // 64 w .. 64 w + 63. A 64-element stage uses half of its group's bytes.
   // Past the last row the dwords belong to other rows (or read as zero at the
   // end of the buffer) and only feed outputs that are never stored.
-  const uint32_t vws = (uint32_t)(n_base + wave * 64 + lane) * 4u;
-  const uint32_t vxs = (uint32_t)(m_base + wave * 64 + lane) * 4u;
+  const uint32_t vs = (uint32_t)(wave * 64 + lane) * 4u;
   const uint32_t ws_group = (uint32_t)N * 4u;
   const uint32_t xs_group = (uint32_t)M * 4u;
 
-  auto buf_of = [&](auto u_tag) -> uint8_t* {
-    constexpr int U = decltype(u_tag)::value;
-    if constexpr (U == 0) return sb0;
-    else if constexpr (U == 1) return sb1;
-    else if constexpr (U == 2) return sb2;
-    else if constexpr (U == 3) return sb3;
-    else if constexpr (U == 4) return sb4;
-    else if constexpr (U == 5) return sb5;
-    else if constexpr (U == 6) return sb6;
-    else return sb7;
-  };
+  // Whole-operand buffer resources: rows past M or N fall outside them.
+  const i32x4 rw = make_rsrc(wq, w_row * (uint32_t)N);
+  const i32x4 rx = make_rsrc(aq, x_row * (uint32_t)M);
+  const i32x4 rws = make_rsrc(ws, (uint32_t)KB * (uint32_t)N);
+  const i32x4 rxs = make_rsrc(asc, MODE == 0 ? (uint32_t)KB * (uint32_t)M : 0u);
 
-  // Copy q (0 .. PER_WAVE-1) of stage s into `buf`. Stages past the end are
-  // still issued (so the wait counts stay constant and the issue has no
-  // branch) but with an offset beyond every buffer's size: the hardware then
-  // writes zeros to LDS without reading memory. Offsets stay in the per-lane
-  // operand, the part the range check covers.
-  auto issue_one = [&](int q, int s, uint8_t* buf) {
-    const bool live = s < n_stages;
+  // ---- copy cursor: the stage (tile cp_k, stage cp_s) whose copies come
+  // next, with the byte offsets of its tile in the W, X and scale operands.
+  // The offsets of the tile after it are prepared off the MFMA path (in the
+  // prologue and in each epilogue), so that moving on to the next tile takes
+  // a few scalar selects and no branch: a branch between the MFMA steps
+  // would split the block the reads and copies are interleaved in.
+  const uint32_t lds_ring = lds_addr(ring);
+  struct TileOff {
+    uint32_t w, x, ws, xs;
+  };
+  auto tile_off = [&](int k) {
+    int tm = 0, tn = 0;
+    if (k < count) tile_of(first + k * stride, tiles_m, tiles_n, tm, tn);
+    const uint32_t nb = (uint32_t)tn * 256u, mb = (uint32_t)tm * 256u;
+    return TileOff{nb * w_row, mb * x_row, nb * 4u, mb * 4u};
+  };
+  int cp_k = 0, cp_s = 0;
+  TileOff cp_off = tile_off(0), cp_next = tile_off(1);
+  // Copy q (0 .. PER_WAVE-1) of the cursor's stage into ring slot `slot`.
+  // Past the last tile the copies are still issued (so the wait counts stay
+  // constant and the issue has no branch) but with an offset beyond every
+  // resource's size: the hardware then writes zeros to LDS without reading
+  // memory. Offsets stay in the per-lane operand, the part the range check
+  // covers.
+  auto issue_one = [&](int q, int slot) {
+    const bool live = cp_k < count;
     const uint32_t oob = 0x80000000u;
+    const uint32_t base = lds_ring + (uint32_t)slot * C::STAGE;
     if (q < C::W_INSTR) {
-      lds_dma16(rw, lds_addr(buf + C::W_OFF + (wave * C::W_INSTR + q) * 1024),
-                live ? vw[q] + (uint32_t)s * C::W_RB : oob);
+      lds_dma16(rw, base + C::W_OFF + (wave * C::W_INSTR + q) * 1024,
+                live ? vw[q] + cp_off.w + (uint32_t)cp_s * C::W_RB : oob);
     } else if (q < C::W_INSTR + C::X_INSTR) {
       const int qx = q - C::W_INSTR;
-      lds_dma16(rx, lds_addr(buf + C::X_OFF + (wave * C::X_INSTR + qx) * 1024),
-                live ? vx[qx] + (uint32_t)s * C::X_RB : oob);
+      lds_dma16(rx, base + C::X_OFF + (wave * C::X_INSTR + qx) * 1024,
+                live ? vx[qx] + cp_off.x + (uint32_t)cp_s * C::X_RB : oob);
     } else if (q == C::W_INSTR + C::X_INSTR) {
-      lds_dma4(rws, lds_addr(buf + C::WS_OFF + wave * 256), live ? vws + (uint32_t)(s * KT / 128) * ws_group : oob);
+      lds_dma4(rws, base + C::WS_OFF + wave * 256,
+               live ? vs + cp_off.ws + (uint32_t)(cp_s * KT / 128) * ws_group : oob);
     } else {
-      lds_dma4(rxs, lds_addr(buf + C::XS_OFF + wave * 256), live ? vxs + (uint32_t)(s * KT / 128) * xs_group : oob);
+      lds_dma4(rxs, base + C::XS_OFF + wave * 256,
+               live ? vs + cp_off.xs + (uint32_t)(cp_s * KT / 128) * xs_group : oob);
+    }
+  };
+  auto advance_cursor = [&] {
+    const bool wrap = ++cp_s == n_stages;
+    cp_s = wrap ? 0 : cp_s;
+    cp_k += wrap ? 1 : 0;
+    cp_off.w = wrap ? cp_next.w : cp_off.w;
+    cp_off.x = wrap ? cp_next.x : cp_off.x;
+    cp_off.ws = wrap ? cp_next.ws : cp_off.ws;
+    cp_off.xs = wrap ? cp_next.xs : cp_off.xs;
+  };
+  // Tile parameters of tile k into parameter block k & 1: the bias slice
+  // (waves 0, 1: 256 bytes each; waves 2, 3 copy nothing into the sink) and,
+  // for FP8 activations, the 256 token scales (256 bytes per wave). Always
+  // EPI_PARAM_OPS copies per wave; no bias reads as zeros.
+  constexpr int EPI_PARAM_OPS = MODE == 1 ? 2 : 1;
+  auto issue_params = [&](int k) {
+    const bool live = k < count;
+    int tm = 0, tn = 0;
+    if (live) tile_of(first + k * stride, tiles_m, tiles_n, tm, tn);
+    const uint32_t pb = lds_ring + PARAM_OFF + (uint32_t)(k & 1) * PARAM_BYTES;
+    const uint32_t nb = (uint32_t)tn * 256u, mb = (uint32_t)tm * 256u;
+    const i32x4 rb = make_rsrc(bias + nb, bias != nullptr ? ((uint32_t)N - nb) * 2u : 0u);
+    lds_dma4(rb, pb + (wave < 2 ? P_BIAS + wave * 256 : P_SINK + (wave - 2) * 256),
+             live && wave < 2 ? (uint32_t)(wave * 256 + lane * 4) : 0x80000000u);
+    if constexpr (MODE == 1) {
+      const i32x4 rt = make_rsrc(static_cast<const uint8_t*>(asc) + mb * 4u, ((uint32_t)M - mb) * 4u);
+      lds_dma4(rt, pb + P_TOK + wave * 256, live ? (uint32_t)(wave * 256 + lane * 4) : 0x80000000u);
     }
   };
 
   v16f acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
   const int wrow0 = wn * 128 + r;  // + 32 i
   const int xrow0 = wm * 128 + r;  // + 32 j
@@ -539,148 +612,196 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       }
   };
 
-  constexpr int D = NB - 1;  // copies run D stages ahead of the stage computed
-  // prologue: copies of stages 0 .. D-1; stages 0 and 1 must have landed
-  // before the first fragments are read
-  [&]<int... Q>(std::integer_sequence<int, Q...>) {
-    (([&] {
-       constexpr int U = Q;
-#pragma unroll
-       for (int q = 0; q < C::PER_WAVE; ++q) issue_one(q, U, buf_of(std::integral_constant<int, U>{}));
-     }()),
-     ...);
-  }(std::make_integer_sequence<int, D>{});
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm((D - 2) * C::PER_WAVE));
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  StepData<MODE> cur;
-  StageScales cur_sc;
-#pragma unroll
-  for (int k = 0; k < STAGE_ITEMS; ++k) read_item(sb0, 0, 0, kStageOrder[MODE][k], cur, cur_sc);
-
-  auto stage = [&](int s, auto u_tag) {
-    constexpr int U = decltype(u_tag)::value;
-    constexpr int UN = (U + 1) % NB;  // buffer of stage s+1
-    if (s > 0) {
-      // own copies of stage s+1 landed: at most those of stages s+2 .. s+D-1 remain
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm((D - 2) * C::PER_WAVE));
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    }
-    uint8_t* here = buf_of(u_tag);
-    uint8_t* next = buf_of(std::integral_constant<int, UN>{});
-    uint8_t* refill = buf_of(std::integral_constant<int, (U + D) % NB>{});
-    const int next_half = (U + 1) & 1;
-    StepData<MODE> nxt;
-    StageScales nxt_sc;
-    if constexpr (C::BPL == 2) {
-      // step 0: MFMAs on `cur`; between them the reads of step 1's fragments
-      // (early, they are needed next) and the copies of stage s+D
-      mfma_step(cur, cur_sc, std::integral_constant<int, 0>{}, [&](int k) {
-        if (k < DATA_ITEMS) read_item(here, 1, 0, kStepOrder[MODE][k], nxt, nxt_sc);
-        if (k < C::PER_WAVE) issue_one(k, s + D, refill);
-      });
-      // step 1: MFMAs on `nxt`; between them the reads of stage s+1's step-0
-      // fragments and scales, in the order the next stage consumes them
-      const StageScales sc1 = cur_sc;
-      mfma_step(nxt, sc1, std::integral_constant<int, 1>{}, [&](int k) {
-        read_item(next, 0, next_half, kStageOrder[MODE][k], cur, cur_sc);
-      });
-    } else {
-      mfma_step(cur, cur_sc, std::integral_constant<int, 0>{}, [&](int k) {
-        read_item(next, 0, next_half, kStageOrder[MODE][k], nxt, nxt_sc);
-        if (k < C::PER_WAVE) issue_one(k, s + D, refill);
-      });
-      cur = nxt;
-      cur_sc = nxt_sc;
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  };
-
-  for (int s0 = 0; s0 < n_stages; s0 += NB) {
-    [&]<int... Q>(std::integer_sequence<int, Q...>) {
-      ((s0 + Q < n_stages ? stage(s0 + Q, std::integral_constant<int, Q>{}) : void()), ...);
-    }(std::make_integer_sequence<int, NB>{});
-  }
-  // ---- epilogue. The ring is free once every copy has landed (own copies:
-  // vmcnt(0); the others': the barrier) and every wave is past its last read.
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
-
+  // ---- epilogue of one tile, staged through the slot of its last stage.
   // Accumulator q of lane (r, g) in a 32x32 tile holds n = 8 (q / 4) + 4 g +
-  // (q % 4), m = r. Per group of 32 token rows (j) the wave writes its fp32
-  // accumulators to LDS (rows of 128 values, 528-byte pitch: conflict-free
-  // 16-byte writes and reads), then reads them back with 16 lanes per row,
-  // 8 consecutive columns per lane, applies scale, bias and GELU and stores
-  // 16 bytes of bf16. The per-element work sits in one short loop: the
-  // epilogue stays small enough to remain in the instruction cache next to
-  // the main loop. Region: half of ring buffer sb0 (waves 0, 1) or sb1 (2, 3).
-  constexpr int EP = 528;
-  static_assert(2 * 32 * EP <= C::STAGE, "epilogue staging fits in one ring buffer per wave pair");
-  uint8_t* region = (wm == 0 ? sb0 : sb1) + wn * (32 * EP);
-  const float* tok_scale = static_cast<const float*>(asc);
-  const int lrow = lane >> 4;         // row within a group of 4 (read phase)
-  const int lcol = (lane & 15) * 8;   // first of the lane's 8 columns (read phase)
-  const int n0 = n_base + wn * 128 + lcol;
-  const bool vec16 = (N & 7) == 0;    // 16-byte aligned output rows
-  const bool has_bias = bias != nullptr;
-  float bv[8];
+  // (q % 4), m = r. Pass p = 2 j + h takes row group j (32 token rows) and
+  // column half h (MFMA tiles i = 2h, 2h+1: 64 columns): every lane writes its
+  // accumulators to LDS (rows of 64 fp32, 272-byte pitch: conflict-free
+  // 16-byte writes and reads), then reads
+  // them back 8 lanes per row, 8 consecutive columns per lane, applies scale,
+  // bias and GELU, converts to bf16 and stores 16 bytes (a 128-byte run per
+  // row). Exactly EPI_STORES stores per wave, whatever the shape: rows past M
+  // and columns past N get an offset the range check drops.
+  constexpr int EP = 272;
+  constexpr int EPI_STORES = 32;
+  constexpr int EPI_OPS = EPI_STORES + EPI_PARAM_OPS;
+  static_assert(4 * 32 * EP <= C::STAGE, "epilogue staging fits in one ring slot");
+  const i32x4 ry = make_rsrc(y, (uint32_t)M * (uint32_t)N * 2u);
+  const int lrow = lane >> 3;        // row within a group of 8 (read phase)
+  const int lcol = (lane & 7) * 8;   // first of the lane's 8 columns (read phase)
+  auto write_pass = [&](uint8_t* wbase, auto p_tag) {
+    constexpr int J = decltype(p_tag)::value >> 1, H = decltype(p_tag)::value & 1;
 #pragma unroll
-  for (int u = 0; u < 8; ++u) bv[u] = has_bias && n0 + u < N ? as_float((uint32_t)bias[n0 + u] << 16) : 0.0f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i2 = 0; i2 < 2; ++i2)
 #pragma unroll
       for (int qq = 0; qq < 4; ++qq)
-        *reinterpret_cast<float4*>(region + r * EP + (32 * i + 8 * qq + 4 * g) * 4) =
-            make_float4(acc[i][j][4 * qq], acc[i][j][4 * qq + 1], acc[i][j][4 * qq + 2], acc[i][j][4 * qq + 3]);
+        *reinterpret_cast<float4*>(wbase + (32 * i2 + 8 * qq) * 4) =
+            make_float4(acc[2 * H + i2][J][4 * qq], acc[2 * H + i2][J][4 * qq + 1], acc[2 * H + i2][J][4 * qq + 2],
+                        acc[2 * H + i2][J][4 * qq + 3]);
+  };
+  auto epilogue = [&](int k, int slot) {
+    int tm, tn;
+    tile_of(first + k * stride, tiles_m, tiles_n, tm, tn);
+    const int m_base = tm * 256, n_base = tn * 256;
+    // every wave is done with this slot's operands
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    const int m_grp = m_base + wm * 128 + 32 * j;
-#pragma unroll 1
-    for (int k = 0; k < 8; ++k) {
-      const int row = 4 * k + lrow;
-      const int m = m_grp + row;
-      const float4 lo = *reinterpret_cast<const float4*>(region + row * EP + lcol * 4);
-      const float4 hi = *reinterpret_cast<const float4*>(region + row * EP + lcol * 4 + 16);
-      if (m < M) {
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    const int region_off = slot * C::STAGE + wave * (32 * EP);
+    uint8_t* region = ring + region_off;
+    uint8_t* wbase = region + r * EP + 16 * g;
+    const uint8_t* params = ring + PARAM_OFF + (k & 1) * PARAM_BYTES;
+    const bool has_bias = bias != nullptr;
+    auto pass = [&](auto p_tag) {
+      constexpr int p = decltype(p_tag)::value;
+      write_pass(wbase, p_tag);
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      const int row_grp = wm * 128 + 32 * (p >> 1);
+      const int ncol = wn * 128 + 64 * (p & 1) + lcol;  // column within the tile
+      const int n = n_base + ncol;
+      const uint4 braw = *reinterpret_cast<const uint4*>(params + P_BIAS + ncol * 2);
+      const uint32_t bw[4] = {braw.x, braw.y, braw.z, braw.w};
+#pragma unroll 2
+      for (int it = 0; it < 4; ++it) {
+        const int row = 8 * it + lrow;
+        const int m = m_base + row_grp + row;
+        const float4 lo = *reinterpret_cast<const float4*>(region + row * EP + lcol * 4);
+        const float4 hi = *reinterpret_cast<const float4*>(region + row * EP + lcol * 4 + 16);
         float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
         if constexpr (MODE == 1) {
-          const float sm = tok_scale[m];
+          const float sm = *reinterpret_cast<const float*>(params + P_TOK + (row_grp + row) * 4);
 #pragma unroll
           for (int u = 0; u < 8; ++u) v[u] *= sm;
         }
         if (has_bias) {
 #pragma unroll
-          for (int u = 0; u < 8; ++u) v[u] += bv[u];
+          for (int u = 0; u < 8; ++u) v[u] += as_float((u & 1) ? (bw[u >> 1] & 0xFFFF0000u) : (bw[u >> 1] << 16));
         }
         if (epi == 1) {
 #pragma unroll
           for (int u = 0; u < 8; ++u) v[u] = gelu_tanh_dev(v[u]);
         }
-        uint32_t h[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) h[u] = bf16_rne(v[2 * u]) | (bf16_rne(v[2 * u + 1]) << 16);
-        uint16_t* dst = y + (int64_t)m * N + n0;
-        if (vec16 && n0 + 8 <= N) {
-          *reinterpret_cast<uint4*>(dst) = make_uint4(h[0], h[1], h[2], h[3]);
-        } else {
-          if (n0 + 4 <= N) *reinterpret_cast<uint2*>(dst) = make_uint2(h[0], h[1]);
-          if (n0 + 8 <= N) *reinterpret_cast<uint2*>(dst + 4) = make_uint2(h[2], h[3]);
-        }
+        uint4 h;
+        h.x = pack_bf16x2(v[0], v[1]);
+        h.y = pack_bf16x2(v[2], v[3]);
+        h.z = pack_bf16x2(v[4], v[5]);
+        h.w = pack_bf16x2(v[6], v[7]);
+        const bool in = m < M && n < N;
+        buf_store16(ry, in ? ((uint32_t)m * (uint32_t)N + (uint32_t)n) * 2u : 0x80000000u, h);
       }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    };
+    // the accumulator indices are static: one copy of the pass per (j, h)
+    [&]<int... Q>(std::integer_sequence<int, Q...>) {
+      (pass(std::integral_constant<int, Q>{}), ...);
+    }(std::make_integer_sequence<int, 8>{});
+    // parameters of the next tile (its block was last read two tiles ago)
+    issue_params(k + 1);
+    // the copy cursor is in tile k+1 by now (it runs fewer than n_stages
+    // stages ahead); the tile it moves to next is k+2
+    cp_next = tile_off(cp_k + 1);
+  };
+
+  constexpr int D = NB - 1;  // copies run D stages ahead of the stage computed
+  constexpr int WAIT_BASE = (D - 2) * C::PER_WAVE;
+  static_assert(WAIT_BASE + EPI_OPS <= 63, "vmcnt range");
+
+  // prologue: tile parameters of the first tile, copies of stages 0 .. D-1;
+  // stages 0 and 1 must have landed before the first fragments are read
+  issue_params(0);
+#pragma unroll
+  for (int st = 0; st < D; ++st) {
+#pragma unroll
+    for (int q = 0; q < C::PER_WAVE; ++q) issue_one(q, st);
+    advance_cursor();
   }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(WAIT_BASE));
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  StepData<MODE> cur;
+  StageScales cur_sc;
+#pragma unroll
+  for (int k = 0; k < STAGE_ITEMS; ++k) read_item(ring, 0, 0, kStageOrder[MODE][k], cur, cur_sc);
+
+  int slot = 0;          // ring slot of the stage being computed
+  int since_epi = D;     // stages since the last epilogue, minus one (D: none pending)
+  for (int tile_k = 0; tile_k < count; ++tile_k) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+    for (int s_in = 0; s_in < n_stages; ++s_in) {
+      if (tile_k > 0 || s_in > 0) {
+        if (since_epi < D - 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(WAIT_BASE + EPI_OPS));
+        else __builtin_amdgcn_s_waitcnt(waitcnt_vm(WAIT_BASE));
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      }
+      const int G = tile_k * n_stages + s_in;
+      const int slot_next = slot + 1 == NB ? 0 : slot + 1;
+      const int slot_refill = slot == 0 ? NB - 1 : slot - 1;  // (G + D) mod NB
+      const uint8_t* here = ring + slot * C::STAGE;
+      const uint8_t* next = ring + slot_next * C::STAGE;
+      const int next_half = (G + 1) & 1;
+      StepData<MODE> nxt;
+      StageScales nxt_sc;
+      if constexpr (C::BPL == 2) {
+        // step 0: MFMAs on `cur`; between them the reads of step 1's fragments
+        // (early, they are needed next) and the copies of stage G+D
+        mfma_step(cur, cur_sc, std::integral_constant<int, 0>{}, [&](int k) {
+          if (k < DATA_ITEMS) read_item(here, 1, 0, kStepOrder[MODE][k], nxt, nxt_sc);
+          if (k < C::PER_WAVE) issue_one(k, slot_refill);
+        });
+        advance_cursor();
+        // step 1: MFMAs on `nxt`; between them the reads of stage G+1's step-0
+        // fragments and scales, in the order the next stage consumes them
+        const StageScales sc1 = cur_sc;
+        mfma_step(nxt, sc1, std::integral_constant<int, 1>{}, [&](int k) {
+          read_item(next, 0, next_half, kStageOrder[MODE][k], cur, cur_sc);
+        });
+      } else {
+        mfma_step(cur, cur_sc, std::integral_constant<int, 0>{}, [&](int k) {
+          read_item(next, 0, next_half, kStageOrder[MODE][k], nxt, nxt_sc);
+          if (k < C::PER_WAVE) issue_one(k, slot_refill);
+        });
+        advance_cursor();
+        cur = nxt;
+        cur_sc = nxt_sc;
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+
+      ++since_epi;
+      if (s_in + 1 < n_stages) slot = slot_next;
+    }
+    epilogue(tile_k, slot);
+    since_epi = 0;
+    slot = slot + 1 == NB ? 0 : slot + 1;
+  }
+  // no copy or store may still be in flight when the workgroup retires
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+}
+
+// One workgroup per CU (the kernel holds a whole CU's LDS and registers),
+// each walking its share of the tiles.
+static int device_cu_count() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    return 256;
+  return cus;
 }
 
 template <int MODE, int KT, int NB>
 static hipError_t launch_pipe(const void* aq, const void* as, const void* wq, const void* ws, const void* bias,
                               int epi, void* y, int64_t M, int64_t N, int64_t K, hipStream_t s) {
+  static const int cus = device_cu_count();
   const int tiles_m = (int)((M + 255) / 256);
   const int tiles_n = (int)((N + 255) / 256);
-  hipLaunchKernelGGL((gemm_pipe_kernel<MODE, KT, NB>), dim3(tiles_m * tiles_n), dim3(256), 0, s,
+  const int total = tiles_m * tiles_n;
+  const int grid = total < cus ? total : cus;
+  hipLaunchKernelGGL((gemm_pipe_kernel<MODE, KT, NB>), dim3(grid), dim3(256), 0, s,
                      static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws),
                      static_cast<const uint8_t*>(aq), as, static_cast<const uint16_t*>(bias),
                      static_cast<uint16_t*>(y), (int)M, (int)N, (int)K, epi, tiles_m, tiles_n);
@@ -704,13 +825,15 @@ static hipError_t launch_direct(const void* aq, const void* as, const void* wq, 
 constexpr int kPipeKT[2] = {128, 128};
 constexpr int kPipeNB[2] = {4, 3};
 
-// The pipelined kernel needs whole stages along K and N in multiples of 4
-// (8-byte stores); every Wan2.2 linear qualifies. Everything else takes the
-// direct kernel. 32-bit buffer offsets bound every operand below 2^31 bytes.
+// The pipelined kernel needs whole stages along K, at least NB of them (one
+// tile's epilogue is over before the next one starts), and N in multiples of 8
+// (16-byte stores); every Wan2.2 linear qualifies. Everything else takes the
+// direct kernel. 32-bit buffer offsets, and the out-of-range offset 2^31 that
+// must exceed every size, bound every operand and the output below 2^31 bytes.
 static bool use_lds(int mode, int64_t M, int64_t N, int64_t K) {
   const int64_t a_bytes = mode == 0 ? M * (K / 2) : M * K;
-  return K % kPipeKT[mode] == 0 && N % 4 == 0 && M >= 256 && N >= 256 && a_bytes < (int64_t(1) << 31) &&
-         N * (K / 2) < (int64_t(1) << 31);
+  return K % kPipeKT[mode] == 0 && K / kPipeKT[mode] >= kPipeNB[mode] && N % 8 == 0 && M >= 256 && N >= 256 &&
+         a_bytes < (int64_t(1) << 31) && N * (K / 2) < (int64_t(1) << 31) && M * N * 2 < (int64_t(1) << 31) - 256;
 }
 
 hipError_t launch_gemm(int mode, const void* a_codes, const void* a_scales,

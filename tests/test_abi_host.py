@@ -25,7 +25,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = mxq.lib()
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 11, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(mxq._SIGS)
@@ -137,3 +137,20 @@ def test_python_binding_refuses_cpu_tensors():
     torch = pytest.importorskip("torch")
     with pytest.raises(TypeError):
         mxq.quantize_weight_mxfp4(torch.zeros((4, 64), dtype=torch.bfloat16))
+
+
+def test_gemm_kernel_selection():
+    """The pipelined kernel takes the workload shapes; everything else the direct kernel."""
+    pipe = [(0, 75600, 5120, 5120), (0, 75600, 13824, 5120), (1, 75600, 5120, 13824), (0, 32760, 15360, 5120),
+            (1, 11440, 3072, 14336), (0, 512, 5120, 5120), (0, 256, 256, 512), (1, 256, 256, 384)]
+    direct = [(0, 255, 512, 512),     # M below one tile
+              (0, 512, 260, 512),     # N not a multiple of 8
+              (0, 512, 512, 384),     # fewer stages than the W4A4 ring
+              (1, 512, 512, 256),     # fewer stages than the W4A8 ring
+              (0, 512, 512, 544),     # K not a multiple of 128
+              (0, 75600, 15360, 5120)]  # output of 2^31 bytes or more
+    for mode, m, n, k in pipe:
+        assert mxq.gemm_kernel_name(mode, m, n, k).startswith("pipe_"), (mode, m, n, k)
+    for mode, m, n, k in direct:
+        assert mxq.gemm_kernel_name(mode, m, n, k).startswith("direct_"), (mode, m, n, k)
+    assert mxq.gemm_kernel_name(2, 512, 512, 512) == "invalid"

@@ -128,6 +128,7 @@ def _single_linear_case(config_id, mode, name, seed):
     policy = mxq.Policy(wl.policy())
     assert policy.mode(e, b) == mode
     policy.close()
+    assert mxq.gemm_kernel_name(mode, m, lin.n, lin.k).startswith("pipe_")
     x = _host_activation(config_id, lin.m_role)
     w, wc, ws = _pack_weight(wl, lin, li, e, b)
     codes, scales = mxq.quantize_act(mode, _to_dev(x))
@@ -153,6 +154,8 @@ def _ffn_case(config_id, mode, seed):
     what = f"config{config_id} e{e} b{b} ffn mode={mode} [{m}x{up.n}x{up.k} -> {m}x{dn.n}x{dn.k}]"
     say(what)
     assert up.epilogue == mxq.EPI_GELU_TANH and dn.k == up.n
+    assert mxq.gemm_kernel_name(mode, m, up.n, up.k).startswith("pipe_")
+    assert mxq.gemm_kernel_name(mode, m, dn.n, dn.k).startswith("pipe_")
     x = _host_activation(config_id, "video")
     rows = sample_rows(m, N_ROWS, seed)
 

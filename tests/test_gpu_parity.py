@@ -105,26 +105,32 @@ def test_gemm_matches_oracle(mode, m, n, k):
     assert_output_close(y, y_ref, f"gemm mode={mode} {m}x{n}x{k}")
 
 
-# Shapes that take the LDS-pipelined kernel (M, N >= 256, K % 128 == 0): one
-# stage (fewer than the ring holds), stage counts that are not multiples of the
-# ring depth, partial M and N tiles, and a full A14B-width K.
-PIPE_SHAPES = [(256, 256, 128), (300, 260, 640), (600, 512, 384), (257, 768, 1024), (512, 256, 5120),
-               (1000, 1280, 896)]
+# Shapes that take the LDS-pipelined persistent kernel: exactly one ring of
+# stages (4 for W4A4, more than the W4A8 ring), stage counts that are not
+# multiples of the ring depth (the ring slot rotates from tile to tile),
+# partial M and N tiles, a full A14B-width K, and grids with more tiles than
+# CUs, so that workgroups walk several tiles and the copies run across tile
+# boundaries (2250 x 7424: 261 tiles, not a multiple of 8; 4352 x 4096: 272).
+PIPE_SHAPES = [(256, 256, 512), (300, 264, 640), (600, 512, 512), (257, 768, 1024), (512, 256, 5120),
+               (1000, 1280, 896), (2250, 7424, 512), (4352, 4096, 640)]
 
 
 @pytest.mark.parametrize("mode", [mxq.W4A4, mxq.W4A8])
 @pytest.mark.parametrize("m,n,k", PIPE_SHAPES)
 def test_gemm_pipelined_kernel_matches_oracle(mode, m, n, k):
     say("gemm pipe", mode, m, n, k)
+    assert mxq.gemm_kernel_name(mode, m, n, k).startswith("pipe_")
     y, y_ref = _gemm_case(mode, m, n, k, seed=m + 3 * n + k)
     assert_output_close(y, y_ref, f"gemm pipe mode={mode} {m}x{n}x{k}")
 
 
 @pytest.mark.parametrize("mode", [mxq.W4A4, mxq.W4A8])
-def test_gemm_pipelined_bias_and_gelu(mode):
-    say("gemm pipe epilogue", mode)
-    y, y_ref = _gemm_case(mode, 300, 512, 640, seed=8, epilogue=mxq.EPI_GELU_TANH, bias=True)
-    assert_output_close(y, y_ref, "pipe bias+gelu")
+@pytest.mark.parametrize("m,n,k", [(300, 512, 640), (4352, 4096, 640)])
+def test_gemm_pipelined_bias_and_gelu(mode, m, n, k):
+    say("gemm pipe epilogue", mode, m, n, k)
+    assert mxq.gemm_kernel_name(mode, m, n, k).startswith("pipe_")
+    y, y_ref = _gemm_case(mode, m, n, k, seed=8, epilogue=mxq.EPI_GELU_TANH, bias=True)
+    assert_output_close(y, y_ref, f"pipe bias+gelu {m}x{n}x{k}")
 
 
 @pytest.mark.parametrize("mode", [mxq.W4A4, mxq.W4A8])
