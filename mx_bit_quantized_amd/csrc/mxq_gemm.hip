@@ -24,6 +24,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <array>
+
 #include "mxq_convert.h"
 #include "mxq_internal.h"
 
@@ -565,6 +567,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
        KA + 2, KWS + 2, KA + 3, KWS + 3},
       {KA + 0, KBX + 0, KBX + 1, KWS + 0, KBX + 2, KBX + 3, KBX + 4, KBX + 5, KBX + 6, KBX + 7, KA + 1, KWS + 1,
        KA + 2, KWS + 2, KA + 3, KWS + 3}};
+  // Copy q of a stage goes after MFMA slot floor(SPAN q / PER_WAVE). With
+  // copies three or more stages ahead they spread over all 32 slots (a burst
+  // would fill the vector memory queue and stall the wave that also feeds the
+  // matrix pipe); two stages ahead, a copy issued late in its stage would be
+  // waited for almost at once, so they go out first.
+  constexpr int COPY_SPAN = NB - 1 >= 3 ? 32 : C::PER_WAVE;
+  constexpr auto kCopyAt = [] {
+    std::array<int, 32> at{};
+    for (int t = 0; t < 32; ++t) at[t] = -1;
+    for (int q = 0; q < C::PER_WAVE; ++q) at[(COPY_SPAN * q) / C::PER_WAVE] = q;
+    return at;
+  }();
+  static_assert(C::PER_WAVE <= 32, "one copy per MFMA slot at most");
   auto read_item = [&](const uint8_t* base, int kk, int half, int code, StepData<MODE>& f, StageScales& sc) {
     const int kind = code & ~15, idx = code & 15;
     if (kind == KA) {
@@ -749,18 +764,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       StageScales nxt_sc;
       if constexpr (C::BPL == 2) {
         // step 0: MFMAs on `cur`; between them the reads of step 1's fragments
-        // (early, they are needed next) and the copies of stage G+D
+        // (early, they are needed next) and the first copies of stage G+D
         mfma_step(cur, cur_sc, std::integral_constant<int, 0>{}, [&](int k) {
           if (k < DATA_ITEMS) read_item(here, 1, 0, kStepOrder[MODE][k], nxt, nxt_sc);
-          if (k < C::PER_WAVE) issue_one(k, slot_refill);
+          if (kCopyAt[k] >= 0) issue_one(kCopyAt[k], slot_refill);
         });
-        advance_cursor();
         // step 1: MFMAs on `nxt`; between them the reads of stage G+1's step-0
-        // fragments and scales, in the order the next stage consumes them
+        // fragments and scales, in the order the next stage consumes them, and
+        // the rest of the copies
         const StageScales sc1 = cur_sc;
         mfma_step(nxt, sc1, std::integral_constant<int, 1>{}, [&](int k) {
           read_item(next, 0, next_half, kStageOrder[MODE][k], cur, cur_sc);
+          if (kCopyAt[16 + k] >= 0) issue_one(kCopyAt[16 + k], slot_refill);
         });
+        advance_cursor();
       } else {
         mfma_step(cur, cur_sc, std::integral_constant<int, 0>{}, [&](int k) {
           read_item(next, 0, next_half, kStageOrder[MODE][k], nxt, nxt_sc);
