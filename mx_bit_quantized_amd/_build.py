@@ -15,6 +15,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmxq.so")
 HOSTCHECK_LIB = os.path.join(HERE, "libmxq_hostcheck.so")
+# test-only GPU library: exhaustive checks of the conversion instructions
+CONVCHECK_SRC = os.path.join(ROOT, "tests", "hip", "conversion_check.hip")
+CONVCHECK_LIB = os.path.join(ROOT, "tests", "hip", "libmxq_convcheck.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -53,7 +56,7 @@ def _run(cmd, verbose):
 
 
 def build(verbose=True):
-    """Compile both libraries; raises RuntimeError on a compiler error."""
+    """Compile the libraries (and the test-only conversion check); raises RuntimeError on a compiler error."""
     tmp = LIB + ".tmp"
     cmd = [HIPCC] + DEVICE_FLAGS + COMMON_FLAGS + ["-o", tmp] + [os.path.join(CSRC, s) for s in DEVICE_SOURCES]
     _run(cmd, verbose)
@@ -63,6 +66,11 @@ def build(verbose=True):
                                                                        os.path.join(CSRC, "mxq_hostcheck.cpp")]
     _run(cmd, verbose)
     os.replace(tmp, HOSTCHECK_LIB)
+    if os.path.exists(CONVCHECK_SRC):
+        tmp = CONVCHECK_LIB + ".tmp"
+        cmd = [HIPCC] + DEVICE_FLAGS + COMMON_FLAGS + ["-o", tmp, CONVCHECK_SRC]
+        _run(cmd, verbose)
+        os.replace(tmp, CONVCHECK_LIB)
     return LIB
 
 
