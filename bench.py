@@ -140,7 +140,9 @@ class Stack:
                         self.records.append(("gemm", mode, 2 * m * lin.n * lin.k, gbytes, e1, e2))
 
 
-KERNEL_SYMBOL = {0: "gemm_pipe_kernel<0>", 1: "gemm_pipe_kernel<1>"}
+# the pipelined GEMM's symbol per mode, as the profile summaries write it
+# (template arguments: mode, K elements per stage, ring depth; no spaces)
+KERNEL_SYMBOL = {0: "gemm_pipe_kernel<0,128,4>", 1: "gemm_pipe_kernel<1,128,3>"}
 
 
 def profiled_traffic(workload_tag, mode):
