@@ -395,9 +395,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 
 // Range-checked 16-byte store: offsets at or past the resource size are dropped.
+// A store of more than 8 bytes reads its data registers one cycle late, so a
+// VALU write to them right after it would change what is stored; the compiler
+// guards that only for stores it knows about, so the wait state is part of the
+// asm block.
 __device__ __forceinline__ void buf_store16(const i32x4& rs, uint32_t voff, const uint4& v) {
   const i32x4 d = {(int)v.x, (int)v.y, (int)v.z, (int)v.w};
-  asm volatile("buffer_store_dwordx4 %0, %1, %2, 0 offen" :: "v"(d), "v"(voff), "s"(rs) : "memory");
+  asm volatile("buffer_store_dwordx4 %0, %1, %2, 0 offen\n\ts_nop 1" :: "v"(d), "v"(voff), "s"(rs) : "memory");
 }
 
 template <int MODE, int KT, int NB>
