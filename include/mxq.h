@@ -12,10 +12,19 @@
  *     per-expert, per-block policy artifact lets the runtime keep most blocks
  *     on W4A4 and spend W4A8 only on the blocks calibration flagged.
  *
- * Data formats (all row-major, K contiguous):
- *   bf16 tensor      uint16 bit patterns, [rows][ld] with ld >= K.
- *   MXFP4 codes      uint8 [rows][K/2]; element 2t of a row in the low
- *                    nibble of byte t, element 2t+1 in the high nibble.
+ * Data formats:
+ *   bf16 tensor      uint16 bit patterns, [rows][ld] with ld >= K, row-major.
+ *   Code panels      Codes are stored K-panel-major: K is cut into panels of
+ *                    128 elements (the last one narrower, w = K - 128p, when
+ *                    K % 128 != 0), and panel p holds every row's codes of
+ *                    elements 128p .. 128p + w_p - 1, row after row. With B
+ *                    bytes per element, element k of row r is at byte
+ *                      128 p rows B + r w_p B + (k - 128 p) B,  p = k / 128.
+ *                    The buffer has rows * K * B bytes, as a row-major one
+ *                    would; a GEMM stage of 256 rows is then one contiguous
+ *                    block (the pipelined GEMM copies it with 1 KiB loads).
+ *   MXFP4 codes      B = 1/2, in code panels; element 2t of a row in the low
+ *                    nibble of its byte, element 2t+1 in the high nibble.
  *                    Each nibble is E2M1 (sign bit 3; magnitudes 0, .5, 1,
  *                    1.5, 2, 3, 4, 6).
  *   MXFP4 scales     E8M0 bytes (value 2^(u-127)), one per 32 consecutive
@@ -25,7 +34,7 @@
  *                    j%4; bytes of blocks past K/32 are zero. One K stage of
  *                    a row tile is then one contiguous run (the GEMM copies
  *                    it with a few wide loads).
- *   FP8 codes        uint8 [M][K], E4M3FN (max 448, 0x7F/0xFF NaN).
+ *   FP8 codes        B = 1, in code panels, E4M3FN (max 448, 0x7F/0xFF NaN).
  *   FP8 scales       float32 [M], one per row (token).
  *
  * Quantization rules:
@@ -103,7 +112,7 @@ int mxq_version(void);
  * nn.Linear layout) - the RTN weight quantization of the page's "Results"
  * table, in the MXFP4 format of "Quantization formats".
  *   w       device, bf16 [N][ldw]
- *   codes   device, uint8 [N][K/2]   (output)
+ *   codes   device, uint8, N * K/2 bytes in code panels   (output)
  *   scales  device, uint8 [ceil(K/128)][N][4]  (output, E8M0, group-major)
  */
 int mxq_quantize_weight_mxfp4(const void* w, int64_t N, int64_t K, int64_t ldw,
@@ -111,8 +120,9 @@ int mxq_quantize_weight_mxfp4(const void* w, int64_t N, int64_t K, int64_t ldw,
 
 /*
  * Dynamic activation quantization ("Quantization formats"): MXQ_W4A4 gives
- * MXFP4 codes [M][K/2] + E8M0 scales [ceil(K/128)][M][4] (group-major);
- * MXQ_W4A8 gives E4M3FN codes [M][K] + float32 per-token scales [M].
+ * MXFP4 codes (M * K/2 bytes in code panels) + E8M0 scales [ceil(K/128)][M][4]
+ * (group-major); MXQ_W4A8 gives E4M3FN codes (M * K bytes in code panels) +
+ * float32 per-token scales [M].
  *   x       device, bf16 [M][ldx]
  *   codes   device (output), scales device (output)
  */
@@ -165,7 +175,7 @@ int mxq_qlinear_workspace_bytes(int mode, int64_t M, int64_t K, size_t* bytes);
  * then runs the scaled GEMM into y. Exactly mxq_quantize_act followed by
  * mxq_gemm.
  *   x          device bf16 [M][K] (dense)
- *   w_codes    device uint8 [N][K/2], w_scales device uint8 [ceil(K/128)][N][4]
+ *   w_codes    device uint8, N * K/2 bytes in code panels, w_scales device uint8 [ceil(K/128)][N][4]
  *   bias       device bf16 [N] or null
  *   y          device bf16 [M][N] (output)
  *   workspace  device, at least mxq_qlinear_workspace_bytes(mode, M, K)

@@ -125,7 +125,11 @@ def mx_scale_shape(rows, K):
 
 
 def act_buffers(mode, M, K, device):
-    """Empty (codes, scales) tensors for quantize_act in ``mode``."""
+    """Empty (codes, scales) tensors for quantize_act in ``mode``.
+
+    Codes are byte buffers shaped [M, K/2] (MXFP4) or [M, K] (FP8) whose
+    contents are laid out in K-panels of 128 elements (include/mxq.h).
+    """
     torch = _torch()
     if mode == W4A4:
         return (torch.empty((M, K // 2), dtype=torch.uint8, device=device),
@@ -137,7 +141,11 @@ def act_buffers(mode, M, K, device):
 
 
 def quantize_weight_mxfp4(w, codes=None, scales=None, stream=None):
-    """RTN MXFP4 packing of bf16 weights [N, K] -> (codes uint8 [N, K/2], scales uint8 [ceil(K/128), N, 4])."""
+    """RTN MXFP4 packing of bf16 weights [N, K] -> (codes, scales).
+
+    codes: uint8 tensor of N * K/2 bytes, shaped [N, K/2] but laid out in
+    K-panels of 128 elements (include/mxq.h); scales: uint8 [ceil(K/128), N, 4].
+    """
     torch = _torch()
     n, k = _rows_k(w, "w")
     if codes is None:

@@ -46,13 +46,24 @@ struct FragFp8 {  // one lane, one K tile: 4 steps x two 16-byte halves
   uint4 d[8];
 };
 
+// Codes are K-panel-major: panel p (elements 128p .. 128p + 127, fewer in a
+// ragged last panel) holds every row's codes of that range contiguously. The
+// codes of panel p of `row` start at byte p * 128 * rows * B + row * w_p * B,
+// B = bytes per element (1/2 for FP4, 1 for FP8), w_p the panel's width.
+__device__ __forceinline__ const uint8_t* panel_row(const uint8_t* q, int p, int row, int64_t rows, int K,
+                                                    int bits) {
+  const int w = K - 128 * p < 128 ? K - 128 * p : 128;
+  return q + (((int64_t)p * 128 * rows + (int64_t)row * (w > 0 ? w : 0)) * bits >> 3);
+}
+
 // Scales are group-major: the dword of group gi (blocks 4gi .. 4gi+3) of row
 // `row` sits at sc[gi * rows + row]. A lane slot's four blocks of a 256-wide
-// tile are exactly one group, so one dword load serves 4 MFMA steps.
+// tile are exactly one group (= one code panel), so one dword load serves 4
+// MFMA steps.
 template <bool TAIL>
 __device__ __forceinline__ void load_fp4(FragFp4& f, const uint8_t* q, const uint32_t* sc, int64_t rows, int row,
-                                         int gi, int n_groups, int b0, int KB) {
-  const uint4* p = reinterpret_cast<const uint4*>(q) + b0;
+                                         int gi, int n_groups, int b0, int KB, int K) {
+  const uint4* p = reinterpret_cast<const uint4*>(panel_row(q, gi, row, rows, K, 4));
 #pragma unroll
   for (int t = 0; t < 4; ++t) f.d[t] = (!TAIL || b0 + t < KB) ? p[t] : make_uint4(0, 0, 0, 0);
   f.sc = (!TAIL || gi < n_groups) ? sc[(int64_t)gi * rows + row] : 0u;
@@ -65,14 +76,17 @@ __device__ __forceinline__ void load_fp4(FragFp4& f, const uint8_t* q, const uin
 // With block kk on FP4 slot 0 and block 4+kk on FP4 slot 1 (see above), FP8
 // slot h therefore carries half h of block kk, then half h of block 4+kk.
 template <bool TAIL>
-__device__ __forceinline__ void load_fp8(FragFp8& f, const uint8_t* q, int kt, int h, int KB) {
-  const uint4* p = reinterpret_cast<const uint4*>(q);
+__device__ __forceinline__ void load_fp8(FragFp8& f, const uint8_t* q, int64_t rows, int row, int kt, int h, int KB,
+                                         int K) {
+  // blocks kt*8 + t lie in panel 2 kt, blocks kt*8 + 4 + t in panel 2 kt + 1
+  const uint4* p0 = reinterpret_cast<const uint4*>(panel_row(q, 2 * kt, row, rows, K, 8));
+  const uint4* p1 = reinterpret_cast<const uint4*>(panel_row(q, 2 * kt + 1, row, rows, K, 8));
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int b0 = kt * 8 + t;
     const int b1 = kt * 8 + 4 + t;
-    f.d[2 * t] = (!TAIL || b0 < KB) ? p[2 * b0 + h] : make_uint4(0, 0, 0, 0);
-    f.d[2 * t + 1] = (!TAIL || b1 < KB) ? p[2 * b1 + h] : make_uint4(0, 0, 0, 0);
+    f.d[2 * t] = (!TAIL || b0 < KB) ? p0[2 * t + h] : make_uint4(0, 0, 0, 0);
+    f.d[2 * t + 1] = (!TAIL || b1 < KB) ? p1[2 * t + h] : make_uint4(0, 0, 0, 0);
   }
 }
 
@@ -126,25 +140,16 @@ __global__ __launch_bounds__(256) void gemm_direct_kernel(
   const int n0 = blockIdx.x * (64 * TN) + (wave & 1) * (32 * TN);
   const int m0 = blockIdx.y * (64 * TM) + (wave >> 1) * (32 * TM);
   const int KB = K >> 5;
-  const int64_t a_row_bytes = MODE == 0 ? (K >> 1) : K;
 
   const int n_groups = (KB + 3) >> 2;
   const uint32_t* wsc = reinterpret_cast<const uint32_t*>(ws);
   const uint32_t* xsc = static_cast<const uint32_t*>(asc);
-  const uint8_t* wrow[TN];
   int wn_row[TN];
 #pragma unroll
-  for (int i = 0; i < TN; ++i) {
-    wn_row[i] = min(n0 + 32 * i + r, N - 1);  // rows past the edge re-read the last row
-    wrow[i] = wq + (int64_t)wn_row[i] * (K >> 1);
-  }
-  const uint8_t* xrow[TM];
+  for (int i = 0; i < TN; ++i) wn_row[i] = min(n0 + 32 * i + r, N - 1);  // rows past the edge re-read the last row
   int xm_row[TM];
 #pragma unroll
-  for (int j = 0; j < TM; ++j) {
-    xm_row[j] = min(m0 + 32 * j + r, M - 1);
-    xrow[j] = aq + (int64_t)xm_row[j] * a_row_bytes;
-  }
+  for (int j = 0; j < TM; ++j) xm_row[j] = min(m0 + 32 * j + r, M - 1);
 
   v16f acc[TN][TM];
 #pragma unroll
@@ -162,14 +167,14 @@ __global__ __launch_bounds__(256) void gemm_direct_kernel(
     XFrag xf[TM];
     uint32_t xs[TM];
 #pragma unroll
-    for (int i = 0; i < TN; ++i) load_fp4<TAIL>(wf[i], wrow[i], wsc, N, wn_row[i], gi, n_groups, b0, KB);
+    for (int i = 0; i < TN; ++i) load_fp4<TAIL>(wf[i], wq, wsc, N, wn_row[i], gi, n_groups, b0, KB, K);
 #pragma unroll
     for (int j = 0; j < TM; ++j) {
       if constexpr (MODE == 0) {
-        load_fp4<TAIL>(reinterpret_cast<FragFp4&>(xf[j]), xrow[j], xsc, M, xm_row[j], gi, n_groups, b0, KB);
+        load_fp4<TAIL>(reinterpret_cast<FragFp4&>(xf[j]), aq, xsc, M, xm_row[j], gi, n_groups, b0, KB, K);
         xs[j] = reinterpret_cast<FragFp4&>(xf[j]).sc;
       } else {
-        load_fp8<TAIL>(reinterpret_cast<FragFp8&>(xf[j]), xrow[j], kt, g, KB);
+        load_fp8<TAIL>(reinterpret_cast<FragFp8&>(xf[j]), aq, M, xm_row[j], kt, g, KB, K);
         xs[j] = kUnitScales;
       }
     }
@@ -450,20 +455,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   count = __builtin_amdgcn_readfirstlane(count);
   const int total_stages = count * n_stages;
 
-  // Per-lane source offsets inside a tile (stage 0); stage s adds s * RB.
+  // Codes are K-panel-major with 128-element panels, one panel per stage:
+  // stage s of a tile is the tile's 256 consecutive rows of panel s, one
+  // contiguous block (16 or 32 KiB), so each wave-wide copy reads 1 KiB of
+  // consecutive memory. Per-lane source offsets inside a tile's stage block;
+  // stage s adds s times the panel size.
+  static_assert(KT == 128, "a stage is one 128-element code panel");
   uint32_t vw[C::W_INSTR], vx[C::X_INSTR];
 #pragma unroll
   for (int q = 0; q < C::W_INSTR; ++q) {
     int row, c;
     unswz<C::W_RB>((wave * C::W_INSTR + q) * 64 + lane, row, c);
-    vw[q] = (uint32_t)row * w_row + (uint32_t)c * 16;
+    vw[q] = (uint32_t)row * C::W_RB + (uint32_t)c * 16;
   }
 #pragma unroll
   for (int q = 0; q < C::X_INSTR; ++q) {
     int row, c;
     unswz<C::X_RB>((wave * C::X_INSTR + q) * 64 + lane, row, c);
-    vx[q] = (uint32_t)row * x_row + (uint32_t)c * 16;
+    vx[q] = (uint32_t)row * C::X_RB + (uint32_t)c * 16;
   }
+  const uint32_t w_panel = (uint32_t)N * C::W_RB;  // bytes of one code panel
+  const uint32_t x_panel = (uint32_t)M * C::X_RB;
   // Scales (group-major, 128-element groups): the tile's 256 dwords of group
   // gi are contiguous at byte (gi * rows + base) * 4; wave w copies dwords
   // 64 w .. 64 w + 63. A 64-element stage uses half of its group's bytes.
@@ -493,7 +505,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     int tm = 0, tn = 0;
     if (k < count) tile_of(first + k * stride, tiles_m, tiles_n, tm, tn);
     const uint32_t nb = (uint32_t)tn * 256u, mb = (uint32_t)tm * 256u;
-    return TileOff{nb * w_row, mb * x_row, nb * 4u, mb * 4u};
+    return TileOff{nb * C::W_RB, mb * C::X_RB, nb * 4u, mb * 4u};
   };
   int cp_k = 0, cp_s = 0;
   TileOff cp_off = tile_off(0), cp_next = tile_off(1);
@@ -509,11 +521,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const uint32_t base = lds_ring + (uint32_t)slot * C::STAGE;
     if (q < C::W_INSTR) {
       lds_dma16(rw, base + C::W_OFF + (wave * C::W_INSTR + q) * 1024,
-                live ? vw[q] + cp_off.w + (uint32_t)cp_s * C::W_RB : oob);
+                live ? vw[q] + cp_off.w + (uint32_t)cp_s * w_panel : oob);
     } else if (q < C::W_INSTR + C::X_INSTR) {
       const int qx = q - C::W_INSTR;
       lds_dma16(rx, base + C::X_OFF + (wave * C::X_INSTR + qx) * 1024,
-                live ? vx[qx] + cp_off.x + (uint32_t)cp_s * C::X_RB : oob);
+                live ? vx[qx] + cp_off.x + (uint32_t)cp_s * x_panel : oob);
     } else if (q == C::W_INSTR + C::X_INSTR) {
       lds_dma4(rws, base + C::WS_OFF + wave * 256,
                live ? vs + cp_off.ws + (uint32_t)(cp_s * KT / 128) * ws_group : oob);

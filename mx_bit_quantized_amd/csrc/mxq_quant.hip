@@ -14,6 +14,20 @@
 
 namespace mxq {
 
+// ------------------------------------------------------------ codes -------
+//
+// Codes are stored K-panel-major: K is cut into panels of 128 elements (the
+// last one narrower when K % 128 != 0), and panel p holds every row's codes
+// of elements 128p .. 128p + w_p - 1 contiguously, row after row. One GEMM
+// stage of a 256-row tile is then one contiguous block. Byte offset of
+// element k (a multiple of 8 here) of `row`, for codes of `bits` bits:
+//   p * 128 * rows * bits / 8 + row * w_p * bits / 8 + (k - 128 p) * bits / 8.
+__device__ __forceinline__ int64_t panel_offset(int64_t k, int64_t row, int64_t rows, int64_t K, int bits) {
+  const int64_t p = k >> 7;
+  const int64_t w = K - 128 * p < 128 ? K - 128 * p : 128;
+  return ((p * 128 * rows + row * w + (k & 127)) * bits) >> 3;
+}
+
 // ------------------------------------------------------------ MXFP4 -------
 //
 // Mapping: a wave walks one row at a time; each lane owns one 16-byte chunk
@@ -79,7 +93,6 @@ __global__ __launch_bounds__(64 * kQuantWaves) void mxfp4_quant_kernel(
   const int64_t chunks = K >> 3;  // 8 bf16 per chunk, 4 chunks per block
   for (int64_t row = wave_id; row < rows; row += n_waves) {
     const uint4* src = reinterpret_cast<const uint4*>(x + row * ld);
-    uint32_t* dst = reinterpret_cast<uint32_t*>(codes + row * (K >> 1));
     for (int64_t c0 = 0; c0 < chunks; c0 += 64 * B) {
       uint4 v[B];
 #pragma unroll
@@ -105,7 +118,7 @@ __global__ __launch_bounds__(64 * kQuantWaves) void mxfp4_quant_kernel(
         const uint32_t s2 = (uint32_t)__shfl_down((int)mine, 8);
         const uint32_t s3 = (uint32_t)__shfl_down((int)mine, 12);
         if (ok) {
-          dst[c] = packed;
+          *reinterpret_cast<uint32_t*>(codes + panel_offset(c * 8, row, rows, K, 4)) = packed;
           if ((lane & 15) == 0) scales[(c >> 4) * rows + row] = mine | (s1 << 8) | (s2 << 16) | (s3 << 24);
         }
       }
@@ -175,11 +188,10 @@ __global__ __launch_bounds__(64 * kQuantWaves) void fp8_quant_row_kernel(
     for (int i = 0; i < MAXC; ++i) amax = umax(amax, chunk_amax(v[i]));
     amax = wave_max(amax);
     const Fp8Row r = fp8_row_setup(amax);
-    uint2* dst = reinterpret_cast<uint2*>(codes + row * K);
 #pragma unroll
     for (int i = 0; i < MAXC; ++i) {
       const int c = 64 * i + lane;
-      if (c < chunks) dst[c] = pack8_fp8(v[i], r);
+      if (c < chunks) *reinterpret_cast<uint2*>(codes + panel_offset((int64_t)c * 8, row, rows, K, 8)) = pack8_fp8(v[i], r);
     }
     if (lane == 0) scales[row] = r.s;
   }
@@ -198,8 +210,8 @@ __global__ __launch_bounds__(64 * kQuantWaves) void fp8_quant_kernel(
     for (int64_t c = lane; c < chunks; c += 64) amax = umax(amax, chunk_amax(src[c]));
     amax = wave_max(amax);
     const Fp8Row r = fp8_row_setup(amax);
-    uint2* dst = reinterpret_cast<uint2*>(codes + row * K);
-    for (int64_t c = lane; c < chunks; c += 64) dst[c] = pack8_fp8(src[c], r);
+    for (int64_t c = lane; c < chunks; c += 64)
+      *reinterpret_cast<uint2*>(codes + panel_offset(c * 8, row, rows, K, 8)) = pack8_fp8(src[c], r);
     if (lane == 0) scales[row] = r.s;
   }
 }

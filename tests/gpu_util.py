@@ -36,6 +36,31 @@ def group_major_scales(scales_rows):
     return np.ascontiguousarray(pad.reshape(rows, g, 4).transpose(1, 0, 2))
 
 
+def panel_index(n_rows, K, bits, rows=None):
+    """Byte indices of K-panel-major codes, as [len(rows), K * bits / 8] in row-major order.
+
+    The library stores codes in panels of 128 elements along K (the last one
+    narrower when K % 128 != 0); panel p holds every row's codes of its range,
+    row after row. This is the documented permutation the tests undo before
+    comparing with the oracle's row-major codes.
+    """
+    rows = np.arange(n_rows, dtype=np.int64) if rows is None else np.asarray(rows, np.int64)
+    full = 128 * bits // 8
+    parts = []
+    for p in range((K + 127) // 128):
+        w = min(128, K - 128 * p) * bits // 8
+        parts.append(p * full * n_rows + rows[:, None] * w + np.arange(w, dtype=np.int64)[None, :])
+    return np.concatenate(parts, axis=1)
+
+
+def code_rows(codes, n_rows, K, bits, rows=None):
+    """Host row-major codes [len(rows), K * bits / 8] of a device K-panel-major code buffer."""
+    idx = panel_index(n_rows, K, bits, rows)
+    flat = codes.reshape(-1)
+    got = flat[torch.from_numpy(idx.reshape(-1)).to(flat.device)]
+    return got.cpu().numpy().view(np.uint8).reshape(idx.shape)
+
+
 def sample_rows(m, n_sample, seed, tile=256):
     """Seeded row sample that always holds row 0, row m-1 and rows of the last tile."""
     g = np.random.default_rng(seed)

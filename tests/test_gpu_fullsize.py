@@ -8,7 +8,7 @@ to one token), so:
 
 * weight codes and scales of sampled weight rows must match the oracle byte
   for byte (every row of the FFN's first projection, which the second stage
-  needs whole);
+  needs whole), after undoing the library's K-panel-major code layout;
 * activation codes and scales of sampled token rows likewise;
 * y on the grid (sampled token rows) x (sampled output columns) must satisfy
   |y - y_ref| <= 2^-7 |y_ref| + 1e-3 rms(y_ref) against the oracle's float64
@@ -34,7 +34,7 @@ import torch
 import mx_bit_quantized_amd as mxq
 import oracle
 import synth
-from gpu_util import assert_codes_equal, assert_output_close, host_bits, host_f32, host_u8, sample_rows
+from gpu_util import assert_codes_equal, assert_output_close, code_rows, host_bits, host_f32, host_u8, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -79,7 +79,10 @@ def _scales_rows(scales_gm, rows, kb):
 
 
 def _check_act(mode, codes, scales, rows, o_codes, o_scales, what):
-    assert_codes_equal(host_u8(codes.index_select(0, _idx(rows))), o_codes, f"{what} act codes")
+    bits = 4 if mode == mxq.W4A4 else 8
+    n_rows, K = codes.shape[0], codes.shape[1] * 8 // bits  # byte buffer [rows, K * bits / 8]
+    got = code_rows(codes, n_rows, K, bits, rows)
+    assert_codes_equal(got, o_codes, f"{what} act codes")
     if mode == mxq.W4A4:
         assert_codes_equal(_scales_rows(scales, rows, o_scales.shape[1]), o_scales, f"{what} act scales")
     else:
@@ -91,7 +94,7 @@ def _check_weight_rows(w_dev, wc, ws, rows, k, what):
     """Oracle-pack the sampled weight rows and compare with the device pack; returns the oracle's."""
     w_rows = host_bits(w_dev.index_select(0, _idx(rows)))
     owc, ows = oracle.mxfp4_quantize(w_rows)
-    assert_codes_equal(host_u8(wc.index_select(0, _idx(rows))), owc, f"{what} weight codes")
+    assert_codes_equal(code_rows(wc, wc.shape[0], k, 4, rows), owc, f"{what} weight codes")
     assert_codes_equal(_scales_rows(ws, rows, k // 32), ows, f"{what} weight scales")
     return owc, ows
 

@@ -14,7 +14,7 @@ import torch
 import mx_bit_quantized_amd as mxq
 import oracle
 import synth
-from gpu_util import (assert_codes_equal, assert_output_close, dev_bf16, group_major_scales, host_bits,
+from gpu_util import (assert_codes_equal, assert_output_close, code_rows, dev_bf16, group_major_scales, host_bits,
                       host_f32, host_u8, sample_rows)
 
 pytestmark = pytest.mark.gpu
@@ -61,7 +61,7 @@ def test_weight_pack_bit_exact(n, k):
     torch.cuda.synchronize()
     want_c, want_s = oracle.mxfp4_quantize(w)
     assert_codes_equal(host_u8(scales), group_major_scales(want_s), "weight scales")
-    assert_codes_equal(host_u8(codes), want_c, "weight codes")
+    assert_codes_equal(code_rows(codes, n, k, 4), want_c, "weight codes")
 
 
 @pytest.mark.parametrize("mode", [mxq.W4A4, mxq.W4A8])
@@ -76,7 +76,7 @@ def test_quantize_act_bit_exact(mode, m, k):
         assert_codes_equal(host_u8(scales), group_major_scales(want_s), "mxfp4 scales")
     else:
         assert_codes_equal(host_f32(scales).view(np.uint32), want_s.view(np.uint32), "fp8 scales")
-    assert_codes_equal(host_u8(codes), want_c, "act codes")
+    assert_codes_equal(code_rows(codes, m, k, 4 if mode == mxq.W4A4 else 8), want_c, "act codes")
 
 
 # -------------------------------------------------------------------- GEMM
@@ -176,7 +176,7 @@ def test_config1_qlinear_both_modes_through_policy():
     wc, ws = mxq.quantize_weight_mxfp4(dev_bf16(w))
     xd = dev_bf16(x)
     owc, ows = oracle.mxfp4_quantize(w)
-    assert_codes_equal(host_u8(wc), owc, "config1 weight codes")
+    assert_codes_equal(code_rows(wc, 512, 512, 4), owc, "config1 weight codes")
     assert_codes_equal(host_u8(ws), group_major_scales(ows), "config1 weight scales")
     for block in range(2):
         mode = policy.mode(0, block)
@@ -188,7 +188,8 @@ def test_config1_qlinear_both_modes_through_policy():
         y_ref, oac, oas = oracle.qlinear(mode, x, owc, ows)
         # the workspace holds the activation codes the GEMM consumed
         codes_len = oac.size
-        assert_codes_equal(host_u8(work[:codes_len]).reshape(oac.shape), oac, f"config1 act codes mode={mode}")
+        got = code_rows(work[:codes_len], 256, 512, 4 if mode == mxq.W4A4 else 8)
+        assert_codes_equal(got, oac, f"config1 act codes mode={mode}")
         assert_output_close(host_bits(y), y_ref, f"config1 mode={mode}")
     policy.close()
 
