@@ -14,7 +14,7 @@
  *
  * Data formats:
  *   bf16 tensor      uint16 bit patterns, [rows][ld] with ld >= K, row-major.
- *   Code panels      Codes are stored K-panel-major: K is cut into panels of
+ *   Code panels      MXFP4 codes are stored K-panel-major: K is cut into panels of
  *                    128 elements (the last one narrower, w = K - 128p, when
  *                    K % 128 != 0), and panel p holds every row's codes of
  *                    elements 128p .. 128p + w_p - 1, row after row. With B
@@ -34,7 +34,9 @@
  *                    j%4; bytes of blocks past K/32 are zero. One K stage of
  *                    a row tile is then one contiguous run (the GEMM copies
  *                    it with a few wide loads).
- *   FP8 codes        B = 1, in code panels, E4M3FN (max 448, 0x7F/0xFF NaN).
+ *   FP8 codes        uint8 [M][K] row-major, E4M3FN (max 448, 0x7F/0xFF NaN).
+ *                    (A GEMM stage already takes a full 128-byte line of each
+ *                    FP8 row, so these stay row-major.)
  *   FP8 scales       float32 [M], one per row (token).
  *
  * Quantization rules:
@@ -121,8 +123,8 @@ int mxq_quantize_weight_mxfp4(const void* w, int64_t N, int64_t K, int64_t ldw,
 /*
  * Dynamic activation quantization ("Quantization formats"): MXQ_W4A4 gives
  * MXFP4 codes (M * K/2 bytes in code panels) + E8M0 scales [ceil(K/128)][M][4]
- * (group-major); MXQ_W4A8 gives E4M3FN codes (M * K bytes in code panels) +
- * float32 per-token scales [M].
+ * (group-major); MXQ_W4A8 gives E4M3FN codes [M][K] (row-major) + float32
+ * per-token scales [M].
  *   x       device, bf16 [M][ldx]
  *   codes   device (output), scales device (output)
  */

@@ -127,8 +127,8 @@ def mx_scale_shape(rows, K):
 def act_buffers(mode, M, K, device):
     """Empty (codes, scales) tensors for quantize_act in ``mode``.
 
-    Codes are byte buffers shaped [M, K/2] (MXFP4) or [M, K] (FP8) whose
-    contents are laid out in K-panels of 128 elements (include/mxq.h).
+    MXFP4 codes are a byte buffer shaped [M, K/2] whose contents are laid out
+    in K-panels of 128 elements (include/mxq.h); FP8 codes are row-major [M, K].
     """
     torch = _torch()
     if mode == W4A4:

@@ -46,10 +46,10 @@ struct FragFp8 {  // one lane, one K tile: 4 steps x two 16-byte halves
   uint4 d[8];
 };
 
-// Codes are K-panel-major: panel p (elements 128p .. 128p + 127, fewer in a
-// ragged last panel) holds every row's codes of that range contiguously. The
-// codes of panel p of `row` start at byte p * 128 * rows * B + row * w_p * B,
-// B = bytes per element (1/2 for FP4, 1 for FP8), w_p the panel's width.
+// MXFP4 codes are K-panel-major: panel p (elements 128p .. 128p + 127, fewer
+// in a ragged last panel) holds every row's codes of that range contiguously.
+// The codes of panel p of `row` start at byte p * 64 * rows + row * w_p / 2,
+// w_p the panel's width (the helper also takes other code widths in bits).
 __device__ __forceinline__ const uint8_t* panel_row(const uint8_t* q, int p, int row, int64_t rows, int K,
                                                     int bits) {
   const int w = K - 128 * p < 128 ? K - 128 * p : 128;
@@ -75,18 +75,16 @@ __device__ __forceinline__ void load_fp4(FragFp4& f, const uint8_t* q, const uin
 // pair with K 16h .. 16h+15 and bytes 16..31 with K 32+16h .. 32+16h+15.
 // With block kk on FP4 slot 0 and block 4+kk on FP4 slot 1 (see above), FP8
 // slot h therefore carries half h of block kk, then half h of block 4+kk.
+// FP8 codes are row-major [rows][K].
 template <bool TAIL>
-__device__ __forceinline__ void load_fp8(FragFp8& f, const uint8_t* q, int64_t rows, int row, int kt, int h, int KB,
-                                         int K) {
-  // blocks kt*8 + t lie in panel 2 kt, blocks kt*8 + 4 + t in panel 2 kt + 1
-  const uint4* p0 = reinterpret_cast<const uint4*>(panel_row(q, 2 * kt, row, rows, K, 8));
-  const uint4* p1 = reinterpret_cast<const uint4*>(panel_row(q, 2 * kt + 1, row, rows, K, 8));
+__device__ __forceinline__ void load_fp8(FragFp8& f, const uint8_t* q, int row, int kt, int h, int KB, int K) {
+  const uint4* p = reinterpret_cast<const uint4*>(q + (int64_t)row * K);
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int b0 = kt * 8 + t;
     const int b1 = kt * 8 + 4 + t;
-    f.d[2 * t] = (!TAIL || b0 < KB) ? p0[2 * t + h] : make_uint4(0, 0, 0, 0);
-    f.d[2 * t + 1] = (!TAIL || b1 < KB) ? p1[2 * t + h] : make_uint4(0, 0, 0, 0);
+    f.d[2 * t] = (!TAIL || b0 < KB) ? p[2 * b0 + h] : make_uint4(0, 0, 0, 0);
+    f.d[2 * t + 1] = (!TAIL || b1 < KB) ? p[2 * b1 + h] : make_uint4(0, 0, 0, 0);
   }
 }
 
@@ -174,7 +172,7 @@ __global__ __launch_bounds__(256) void gemm_direct_kernel(
         load_fp4<TAIL>(reinterpret_cast<FragFp4&>(xf[j]), aq, xsc, M, xm_row[j], gi, n_groups, b0, KB, K);
         xs[j] = reinterpret_cast<FragFp4&>(xf[j]).sc;
       } else {
-        load_fp8<TAIL>(reinterpret_cast<FragFp8&>(xf[j]), aq, M, xm_row[j], kt, g, KB, K);
+        load_fp8<TAIL>(reinterpret_cast<FragFp8&>(xf[j]), aq, xm_row[j], kt, g, KB, K);
         xs[j] = kUnitScales;
       }
     }
@@ -455,11 +453,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   count = __builtin_amdgcn_readfirstlane(count);
   const int total_stages = count * n_stages;
 
-  // Codes are K-panel-major with 128-element panels, one panel per stage:
-  // stage s of a tile is the tile's 256 consecutive rows of panel s, one
-  // contiguous block (16 or 32 KiB), so each wave-wide copy reads 1 KiB of
-  // consecutive memory. Per-lane source offsets inside a tile's stage block;
-  // stage s adds s times the panel size.
+  // MXFP4 codes are K-panel-major with 128-element panels, one panel per
+  // stage: stage s of a tile is the tile's 256 consecutive rows of panel s, one
+  // contiguous 16 KiB block, so each wave-wide copy reads 1 KiB of consecutive
+  // memory. FP8 activation codes are row-major, and a stage takes a full
+  // 128-byte line of each row. Per-lane source offsets inside a tile's stage;
+  // stage s adds s times the panel size (FP4) or the stage's row bytes (FP8).
   static_assert(KT == 128, "a stage is one 128-element code panel");
   uint32_t vw[C::W_INSTR], vx[C::X_INSTR];
 #pragma unroll
@@ -472,10 +471,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   for (int q = 0; q < C::X_INSTR; ++q) {
     int row, c;
     unswz<C::X_RB>((wave * C::X_INSTR + q) * 64 + lane, row, c);
-    vx[q] = (uint32_t)row * C::X_RB + (uint32_t)c * 16;
+    vx[q] = (uint32_t)row * (MODE == 0 ? (uint32_t)C::X_RB : x_row) + (uint32_t)c * 16;
   }
   const uint32_t w_panel = (uint32_t)N * C::W_RB;  // bytes of one code panel
-  const uint32_t x_panel = (uint32_t)M * C::X_RB;
+  const uint32_t x_stage = MODE == 0 ? (uint32_t)M * C::X_RB : (uint32_t)C::X_RB;
   // Scales (group-major, 128-element groups): the tile's 256 dwords of group
   // gi are contiguous at byte (gi * rows + base) * 4; wave w copies dwords
   // 64 w .. 64 w + 63. A 64-element stage uses half of its group's bytes.
@@ -505,7 +504,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     int tm = 0, tn = 0;
     if (k < count) tile_of(first + k * stride, tiles_m, tiles_n, tm, tn);
     const uint32_t nb = (uint32_t)tn * 256u, mb = (uint32_t)tm * 256u;
-    return TileOff{nb * C::W_RB, mb * C::X_RB, nb * 4u, mb * 4u};
+    return TileOff{nb * C::W_RB, mb * (MODE == 0 ? (uint32_t)C::X_RB : x_row), nb * 4u, mb * 4u};
   };
   int cp_k = 0, cp_s = 0;
   TileOff cp_off = tile_off(0), cp_next = tile_off(1);
@@ -525,7 +524,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     } else if (q < C::W_INSTR + C::X_INSTR) {
       const int qx = q - C::W_INSTR;
       lds_dma16(rx, base + C::X_OFF + (wave * C::X_INSTR + qx) * 1024,
-                live ? vx[qx] + cp_off.x + (uint32_t)cp_s * x_panel : oob);
+                live ? vx[qx] + cp_off.x + (uint32_t)cp_s * x_stage : oob);
     } else if (q == C::W_INSTR + C::X_INSTR) {
       lds_dma4(rws, base + C::WS_OFF + wave * 256,
                live ? vs + cp_off.ws + (uint32_t)(cp_s * KT / 128) * ws_group : oob);

@@ -14,41 +14,32 @@
 
 namespace mxq {
 
-// ------------------------------------------------------------ codes -------
-//
-// Codes are stored K-panel-major: K is cut into panels of 128 elements (the
-// last one narrower when K % 128 != 0), and panel p holds every row's codes
-// of elements 128p .. 128p + w_p - 1 contiguously, row after row. One GEMM
-// stage of a 256-row tile is then one contiguous block. Byte offset of
-// element k (a multiple of 8 here) of `row`, for codes of `bits` bits:
-//   p * 128 * rows * bits / 8 + row * w_p * bits / 8 + (k - 128 p) * bits / 8.
-__device__ __forceinline__ int64_t panel_offset(int64_t k, int64_t row, int64_t rows, int64_t K, int bits) {
-  const int64_t p = k >> 7;
-  const int64_t w = K - 128 * p < 128 ? K - 128 * p : 128;
-  return ((p * 128 * rows + row * w + (k & 127)) * bits) >> 3;
-}
-
 // ------------------------------------------------------------ MXFP4 -------
 //
-// Mapping: a wave walks one row at a time; each lane owns one 16-byte chunk
-// (8 bf16) per step, so four neighbouring lanes hold one 32-element block and
-// sixteen lanes one 128-element group. A step reads 1 KiB contiguous per wave
-// and writes 256 contiguous bytes of codes (4 per lane). The block amax is a
-// max over the magnitude bit patterns (sign cleared) across the 4 lanes -
-// exact for finite bf16, no float compare, no denormal flush.
+// MXFP4 codes are stored K-panel-major: K is cut into panels of 128 elements
+// (the last one narrower when K % 128 != 0), and panel p holds every row's
+// codes of elements 128p .. 128p + w_p - 1 contiguously, row after row (64 B
+// per row for a full panel). One GEMM stage of a 256-row tile is then one
+// contiguous block. Scales are group-major, [ceil(K/128)][rows][4]: the four
+// E8M0 bytes of one row's blocks in one panel form one dword, and the dwords
+// of all rows for one panel are contiguous.
 //
-// Scales are stored group-major, [ceil(K/128)][rows][4]: the four E8M0 bytes
-// of the blocks of one 128-element group of one row form one dword, and the
-// dwords of all rows for one group are contiguous. The GEMM then fetches the
-// scales of a 256-row tile for one K stage as 1 KiB of consecutive memory.
-// The first lane of each group assembles the dword from the four block
-// leaders and writes it; bytes of blocks past K/32 in a ragged last group are
-// written as zero.
+// Mapping: a wave unit is 16 consecutive rows times up to 4 panels, in steps
+// of 4 rows per panel. Lane l takes 8-element chunk l % 16 of row l / 16 of a
+// step: one load reads 4 rows x 256 B, four neighbouring lanes hold one
+// 32-element block (a quad-shuffle max gives its amax), and one store writes
+// the 4 rows' codes of the panel, 256 contiguous bytes; the 16 rows' codes of
+// a panel are 1 KiB of consecutive memory. All 16 loads of a unit (16 KiB per
+// wave) are issued before the first conversion. The
+// block amax is a max over the magnitude bit patterns (sign cleared), exact
+// for finite bf16, with no float compare and no denormal flush.
 
-__device__ __forceinline__ uint32_t quad_max(uint32_t v) {
-  v = umax(v, (uint32_t)__shfl_xor((int)v, 1));
-  v = umax(v, (uint32_t)__shfl_xor((int)v, 2));
-  return v;
+__device__ __forceinline__ uint32_t chunk_amax(const uint4 c) {
+  uint32_t m0 = umax(c.x & 0x7FFFu, (c.x >> 16) & 0x7FFFu);
+  uint32_t m1 = umax(c.y & 0x7FFFu, (c.y >> 16) & 0x7FFFu);
+  uint32_t m2 = umax(c.z & 0x7FFFu, (c.z >> 16) & 0x7FFFu);
+  uint32_t m3 = umax(c.w & 0x7FFFu, (c.w >> 16) & 0x7FFFu);
+  return umax(umax(m0, m1), umax(m2, m3));
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -69,57 +60,63 @@ __device__ __forceinline__ uint32_t pack8_fp4(const uint4 c, uint32_t sb) {
   return out;
 }
 
-__device__ __forceinline__ uint32_t chunk_amax(const uint4 c) {
-  uint32_t m0 = umax(c.x & 0x7FFFu, (c.x >> 16) & 0x7FFFu);
-  uint32_t m1 = umax(c.y & 0x7FFFu, (c.y >> 16) & 0x7FFFu);
-  uint32_t m2 = umax(c.z & 0x7FFFu, (c.z >> 16) & 0x7FFFu);
-  uint32_t m3 = umax(c.w & 0x7FFFu, (c.w >> 16) & 0x7FFFu);
-  return umax(umax(m0, m1), umax(m2, m3));
+constexpr int kQuantWaves = 4;  // waves per workgroup
+constexpr int kMxRows = 16;     // rows per wave unit
+constexpr int kMxPanels = 4;    // panels per wave unit (fewer in the last one)
+
+__device__ __forceinline__ uint32_t quad_max(uint32_t v) {
+  v = umax(v, (uint32_t)__shfl_xor((int)v, 1));
+  v = umax(v, (uint32_t)__shfl_xor((int)v, 2));
+  return v;
 }
 
-constexpr int kQuantWaves = 4;  // waves per workgroup
-
-// A wave converts a row in batches of B chunks per lane (B KiB per wave): all
-// loads of a batch are issued before the first conversion, so each wave keeps
-// that much of the stream in flight. The launcher picks B so that a row
-// splits into equal batches of at most 16 chunks per lane.
-template <int B>
 __global__ __launch_bounds__(64 * kQuantWaves) void mxfp4_quant_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t K, int64_t ld,
     uint8_t* __restrict__ codes, uint32_t* __restrict__ scales) {
   const int lane = threadIdx.x & 63;
-  const int64_t wave_id = (int64_t)blockIdx.x * kQuantWaves + (threadIdx.x >> 6);
+  const int64_t unit0 = (int64_t)blockIdx.x * kQuantWaves + (threadIdx.x >> 6);
   const int64_t n_waves = (int64_t)gridDim.x * kQuantWaves;
-  const int64_t chunks = K >> 3;  // 8 bf16 per chunk, 4 chunks per block
-  for (int64_t row = wave_id; row < rows; row += n_waves) {
-    const uint4* src = reinterpret_cast<const uint4*>(x + row * ld);
-    for (int64_t c0 = 0; c0 < chunks; c0 += 64 * B) {
-      uint4 v[B];
+  const int64_t chunks = K >> 3;            // 8-element chunks per row
+  const int n_panels = (int)((K + 127) >> 7);
+  const int pchunks = (n_panels + kMxPanels - 1) / kMxPanels;
+  const int64_t units = (rows + kMxRows - 1) / kMxRows * pchunks;
+  const int rs = lane >> 4, c = lane & 15;  // row within a step of 4, chunk within the panel
+  for (int64_t u = unit0; u < units; u += n_waves) {
+    const int64_t row0 = u / pchunks * kMxRows;
+    const int p0 = (int)(u % pchunks) * kMxPanels;
+    // all loads of the unit first: step (pp, t) covers rows row0 + 4 t + 0..3 of panel p0 + pp
+    uint4 v[kMxPanels][4];
 #pragma unroll
-      for (int b = 0; b < B; ++b) {
-        const int64_t c = c0 + 64 * b + lane;
-        v[b] = c < chunks ? src[c] : make_uint4(0, 0, 0, 0);
+    for (int pp = 0; pp < kMxPanels; ++pp)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int64_t row = row0 + 4 * t + rs;
+        const int64_t ch = 16 * (int64_t)(p0 + pp) + c;
+        const bool ok = row < rows && ch < chunks;
+        v[pp][t] = ok ? reinterpret_cast<const uint4*>(x + row * ld)[ch] : make_uint4(0, 0, 0, 0);
       }
 #pragma unroll
-      for (int b = 0; b < B; ++b) {
-        const int64_t c = c0 + 64 * b + lane;
-        // chunks is a multiple of 4 and c - lane of 64, so a whole 4-lane
-        // block is either in range or out of range: the shuffles stay
-        // uniform per block.
-        const bool ok = c < chunks;
-        const uint32_t amax = quad_max(chunk_amax(v[b]));
-        const uint32_t sb = mx_scale_byte(amax);
-        const uint32_t packed = pack8_fp4(v[b], sb);
-        // gather the 4 block scales of this lane's 128-element group into its
-        // first lane (block leaders sit at lanes +0, +4, +8, +12);
-        // out-of-range blocks contribute zero bytes
-        const uint32_t mine = ok ? sb : 0u;
-        const uint32_t s1 = (uint32_t)__shfl_down((int)mine, 4);
-        const uint32_t s2 = (uint32_t)__shfl_down((int)mine, 8);
-        const uint32_t s3 = (uint32_t)__shfl_down((int)mine, 12);
-        if (ok) {
-          *reinterpret_cast<uint32_t*>(codes + panel_offset(c * 8, row, rows, K, 4)) = packed;
-          if ((lane & 15) == 0) scales[(c >> 4) * rows + row] = mine | (s1 << 8) | (s2 << 16) | (s3 << 24);
+    for (int pp = 0; pp < kMxPanels; ++pp) {
+      const int p = p0 + pp;
+      const int64_t ch = 16 * (int64_t)p + c;
+      // chunks is a multiple of 4 and a panel's first chunk of 16, so a whole
+      // 4-lane block is in or out of range: the shuffles stay uniform per block
+      const bool ch_ok = ch < chunks;
+      const int64_t w = K - 128 * (int64_t)p < 128 ? K - 128 * (int64_t)p : 128;  // panel width
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int64_t row = row0 + 4 * t + rs;
+        const uint32_t amax = quad_max(chunk_amax(v[pp][t]));
+        const uint32_t sb = ch_ok ? mx_scale_byte(amax) : 0u;
+        const uint32_t packed = pack8_fp4(v[pp][t], sb);
+        // the row's 4 block scales (block leaders at lanes +0, +4, +8, +12)
+        const uint32_t s1 = (uint32_t)__shfl_down((int)sb, 4);
+        const uint32_t s2 = (uint32_t)__shfl_down((int)sb, 8);
+        const uint32_t s3 = (uint32_t)__shfl_down((int)sb, 12);
+        if (row < rows && p < n_panels) {
+          // 4 consecutive rows of the panel: 4 x (w / 2) contiguous bytes
+          if (ch_ok) *reinterpret_cast<uint32_t*>(codes + (int64_t)p * 64 * rows + row * (w >> 1) + 4 * c) = packed;
+          if (c == 0) scales[(int64_t)p * rows + row] = sb | (s1 << 8) | (s2 << 16) | (s3 << 24);
         }
       }
     }
@@ -191,7 +188,7 @@ __global__ __launch_bounds__(64 * kQuantWaves) void fp8_quant_row_kernel(
 #pragma unroll
     for (int i = 0; i < MAXC; ++i) {
       const int c = 64 * i + lane;
-      if (c < chunks) *reinterpret_cast<uint2*>(codes + panel_offset((int64_t)c * 8, row, rows, K, 8)) = pack8_fp8(v[i], r);
+      if (c < chunks) reinterpret_cast<uint2*>(codes + row * K)[c] = pack8_fp8(v[i], r);
     }
     if (lane == 0) scales[row] = r.s;
   }
@@ -210,8 +207,8 @@ __global__ __launch_bounds__(64 * kQuantWaves) void fp8_quant_kernel(
     for (int64_t c = lane; c < chunks; c += 64) amax = umax(amax, chunk_amax(src[c]));
     amax = wave_max(amax);
     const Fp8Row r = fp8_row_setup(amax);
-    for (int64_t c = lane; c < chunks; c += 64)
-      *reinterpret_cast<uint2*>(codes + panel_offset(c * 8, row, rows, K, 8)) = pack8_fp8(src[c], r);
+    uint2* dst = reinterpret_cast<uint2*>(codes + row * K);
+    for (int64_t c = lane; c < chunks; c += 64) dst[c] = pack8_fp8(src[c], r);
     if (lane == 0) scales[row] = r.s;
   }
 }
@@ -224,30 +221,15 @@ static int grid_for_rows(int64_t rows) {
   return (int)(blocks < cap ? blocks : cap);
 }
 
-template <int B>
-static void launch_mxfp4_b(const void* x, int64_t rows, int64_t K, int64_t ld, void* codes, void* scales,
-                           hipStream_t s) {
-  hipLaunchKernelGGL(mxfp4_quant_kernel<B>, dim3(grid_for_rows(rows)), dim3(64 * kQuantWaves), 0, s,
-                     static_cast<const uint16_t*>(x), rows, K, ld, static_cast<uint8_t*>(codes),
-                     static_cast<uint32_t*>(scales));
-}
-
 hipError_t launch_mxfp4_quant(const void* x, int64_t rows, int64_t K, int64_t ld,
                               void* codes, void* scales, hipStream_t s) {
-  // chunks per lane, split into equal batches of at most 16, rounded up to even
-  const int64_t per_lane = ((K >> 3) + 63) / 64;
-  const int64_t n_batches = (per_lane + 15) / 16;
-  const int64_t b = ((per_lane + n_batches - 1) / n_batches + 1) & ~int64_t(1);
-  switch (b) {
-    case 2: launch_mxfp4_b<2>(x, rows, K, ld, codes, scales, s); break;
-    case 4: launch_mxfp4_b<4>(x, rows, K, ld, codes, scales, s); break;
-    case 6: launch_mxfp4_b<6>(x, rows, K, ld, codes, scales, s); break;
-    case 8: launch_mxfp4_b<8>(x, rows, K, ld, codes, scales, s); break;
-    case 10: launch_mxfp4_b<10>(x, rows, K, ld, codes, scales, s); break;
-    case 12: launch_mxfp4_b<12>(x, rows, K, ld, codes, scales, s); break;
-    case 14: launch_mxfp4_b<14>(x, rows, K, ld, codes, scales, s); break;
-    default: launch_mxfp4_b<16>(x, rows, K, ld, codes, scales, s); break;
-  }
+  const int64_t pchunks = ((K + 127) / 128 + kMxPanels - 1) / kMxPanels;
+  const int64_t units = (rows + kMxRows - 1) / kMxRows * pchunks;
+  int64_t blocks = (units + kQuantWaves - 1) / kQuantWaves;
+  if (blocks > (1 << 16)) blocks = 1 << 16;  // units loop beyond
+  hipLaunchKernelGGL(mxfp4_quant_kernel, dim3((unsigned)blocks), dim3(64 * kQuantWaves), 0, s,
+                     static_cast<const uint16_t*>(x), rows, K, ld, static_cast<uint8_t*>(codes),
+                     static_cast<uint32_t*>(scales));
   return hipGetLastError();
 }
 

@@ -79,9 +79,10 @@ def _scales_rows(scales_gm, rows, kb):
 
 
 def _check_act(mode, codes, scales, rows, o_codes, o_scales, what):
-    bits = 4 if mode == mxq.W4A4 else 8
-    n_rows, K = codes.shape[0], codes.shape[1] * 8 // bits  # byte buffer [rows, K * bits / 8]
-    got = code_rows(codes, n_rows, K, bits, rows)
+    if mode == mxq.W4A4:  # K-panel-major byte buffer [rows, K/2]
+        got = code_rows(codes, codes.shape[0], codes.shape[1] * 2, 4, rows)
+    else:  # row-major FP8 codes
+        got = host_u8(codes.index_select(0, _idx(rows)))
     assert_codes_equal(got, o_codes, f"{what} act codes")
     if mode == mxq.W4A4:
         assert_codes_equal(_scales_rows(scales, rows, o_scales.shape[1]), o_scales, f"{what} act scales")
