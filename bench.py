@@ -141,16 +141,19 @@ class Stack:
 
 
 # the pipelined GEMM's symbol per mode, as the profile summaries write it
-# (template arguments: mode, K elements per stage, ring depth; no spaces)
-KERNEL_SYMBOL = {0: "gemm_pipe_kernel<0,128,4>", 1: "gemm_pipe_kernel<1,128,3>"}
+# (template arguments: mode, K elements per stage, ring depth, GELU; no
+# spaces): each mode has a plain and a GELU instance, and the roofline covers both
+KERNEL_SYMBOL = {0: "gemm_pipe_kernel<0,128,4,{false,true}>", 1: "gemm_pipe_kernel<1,128,3,{false,true}>"}
+KERNEL_PREFIX = {0: "gemm_pipe_kernel<0,128,4,", 1: "gemm_pipe_kernel<1,128,3,"}
 
 
 def profiled_traffic(workload_tag, mode):
-    """HBM bytes per launch of the mode's GEMM kernel from the committed counter summary.
+    """HBM bytes per launch of the mode's GEMM kernels from the committed counter summary.
 
     profiles/hbm_traffic_<workload>.txt holds calibrated FETCH_SIZE + WRITE_SIZE
     bytes per dispatch and the sha1 of the GEMM source they were taken on; a
-    different source means the numbers describe another kernel: None.
+    different source means the numbers describe another kernel: None. The
+    plain and GELU instances are averaged, weighted by their dispatch counts.
     """
     import hashlib
 
@@ -159,14 +162,17 @@ def profiled_traffic(workload_tag, mode):
     if not os.path.exists(path):
         return None
     sha = hashlib.sha1(open(src, "rb").read()).hexdigest()
-    recorded, traffic = None, None
+    recorded, launches, total = None, 0, 0
     for line in open(path):
         parts = line.split()
         if parts[:1] == ["source_sha1_gemm"]:
             recorded = parts[1]
-        elif parts[:1] == ["kernel"] and parts[1] == KERNEL_SYMBOL[mode]:
-            traffic = int(parts[5])
-    return traffic if recorded == sha else None
+        elif parts[:1] == ["kernel"] and parts[1].startswith(KERNEL_PREFIX[mode]):
+            launches += int(parts[2])
+            total += int(parts[2]) * int(parts[5])
+    if recorded != sha or launches == 0:
+        return None
+    return total // launches
 
 
 def cpu_baseline(wl, sample_rows):

@@ -331,9 +331,11 @@ __device__ __forceinline__ void tile_of(int t, int tiles_m, int tiles_n, int& tm
 }
 
 __device__ __forceinline__ float gelu_tanh_dev(float y) {
-  // 0.5 y (1 + tanh(u)) = y / (1 + exp(-2u)), u = sqrt(2/pi) (y + 0.044715 y^3)
-  const float u = 0.7978845608028654f * y * (1.0f + 0.044715f * y * y);
-  const float e = __builtin_amdgcn_exp2f(-2.0f * 1.4426950408889634f * u);
+  // 0.5 y (1 + tanh(u)) = y / (1 + exp(-2u)), u = sqrt(2/pi) (y + 0.044715 y^3);
+  // exp(-2u) = 2^(y (c0 + c1 y^2)) with the constants folded: 5 VALU
+  // operations and 2 transcendental ones per element
+  constexpr float kL = -2.0f * 1.4426950408889634f * 0.7978845608028654f;  // -2 log2(e) sqrt(2/pi)
+  const float e = __builtin_amdgcn_exp2f(y * __builtin_fmaf(y * y, kL * 0.044715f, kL));
   return y * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
@@ -407,12 +409,12 @@ __device__ __forceinline__ void buf_store16(const i32x4& rs, uint32_t voff, cons
   asm volatile("buffer_store_dwordx4 %0, %1, %2, 0 offen\n\ts_nop 1" :: "v"(d), "v"(voff), "s"(rs) : "memory");
 }
 
-template <int MODE, int KT, int NB>
+template <int MODE, int KT, int NB, bool GELU>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_pipe_kernel(
     const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws,
     const uint8_t* __restrict__ aq, const void* __restrict__ asc,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
-    int M, int N, int K, int epi, int tiles_m, int tiles_n) {
+    int M, int N, int K, int tiles_m, int tiles_n) {
   using C = PipeCfg<MODE, KT, NB>;
   // ring of NB stage slots, then two tile-parameter blocks: bias slice (512
   // bytes), a sink for the unused waves' copies (512), token scales (1024, FP8)
@@ -646,12 +648,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // Accumulator q of lane (r, g) in a 32x32 tile holds n = 8 (q / 4) + 4 g +
   // (q % 4), m = r. Pass p = 2 j + h takes row group j (32 token rows) and
   // column half h (MFMA tiles i = 2h, 2h+1: 64 columns): every lane writes its
-  // accumulators to LDS (rows of 64 fp32, 272-byte pitch: conflict-free
-  // 16-byte writes and reads), then reads
+  // accumulators to LDS straight from the accumulator registers (rows of 64
+  // fp32, 272-byte pitch: conflict-free 16-byte writes and reads), then reads
   // them back 8 lanes per row, 8 consecutive columns per lane, applies scale,
-  // bias and GELU, converts to bf16 and stores 16 bytes (a 128-byte run per
-  // row). Exactly EPI_STORES stores per wave, whatever the shape: rows past M
-  // and columns past N get an offset the range check drops.
+  // bias and GELU, converts to bf16 and stores 16 bytes: each store writes 8
+  // rows x 128 contiguous bytes, whole cache lines. A pass issues all of its
+  // LDS reads before the first use, so the wave waits for LDS once per pass.
+  // The bias slice in LDS holds zeros when there is no bias, so the add needs
+  // no branch. Exactly EPI_STORES stores per wave, whatever the shape: rows
+  // past M and columns past N get an offset the range check drops.
   constexpr int EP = 272;
   constexpr int EPI_STORES = 32;
   constexpr int EPI_OPS = EPI_STORES + EPI_PARAM_OPS;
@@ -680,36 +685,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int region_off = slot * C::STAGE + wave * (32 * EP);
     uint8_t* region = ring + region_off;
     uint8_t* wbase = region + r * EP + 16 * g;
+    const uint8_t* rbase = region + lrow * EP + lcol * 4;
     const uint8_t* params = ring + PARAM_OFF + (k & 1) * PARAM_BYTES;
-    const bool has_bias = bias != nullptr;
     auto pass = [&](auto p_tag) {
       constexpr int p = decltype(p_tag)::value;
+      constexpr int J = p >> 1, H = p & 1;
       write_pass(wbase, p_tag);
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-      const int row_grp = wm * 128 + 32 * (p >> 1);
-      const int ncol = wn * 128 + 64 * (p & 1) + lcol;  // column within the tile
+      const int row_grp = wm * 128 + 32 * J;
+      const int ncol = wn * 128 + 64 * H + lcol;  // column within the tile
       const int n = n_base + ncol;
       const uint4 braw = *reinterpret_cast<const uint4*>(params + P_BIAS + ncol * 2);
-      const uint32_t bw[4] = {braw.x, braw.y, braw.z, braw.w};
-#pragma unroll 2
+      float4 lo[4], hi[4];
+      float sm[4];
+#pragma unroll
       for (int it = 0; it < 4; ++it) {
-        const int row = 8 * it + lrow;
-        const int m = m_base + row_grp + row;
-        const float4 lo = *reinterpret_cast<const float4*>(region + row * EP + lcol * 4);
-        const float4 hi = *reinterpret_cast<const float4*>(region + row * EP + lcol * 4 + 16);
-        float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        if constexpr (MODE == 1) {
-          const float sm = *reinterpret_cast<const float*>(params + P_TOK + (row_grp + row) * 4);
+        lo[it] = *reinterpret_cast<const float4*>(rbase + 8 * it * EP);
+        hi[it] = *reinterpret_cast<const float4*>(rbase + 8 * it * EP + 16);
+        if constexpr (MODE == 1) sm[it] = *reinterpret_cast<const float*>(params + P_TOK + (row_grp + 8 * it + lrow) * 4);
+      }
+      // the next pass overwrites the region: its writes stay behind these reads
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      const uint32_t bw[4] = {braw.x, braw.y, braw.z, braw.w};
+      float b[8];
 #pragma unroll
-          for (int u = 0; u < 8; ++u) v[u] *= sm;
-        }
-        if (has_bias) {
+      for (int u = 0; u < 8; ++u) b[u] = as_float((u & 1) ? (bw[u >> 1] & 0xFFFF0000u) : (bw[u >> 1] << 16));
 #pragma unroll
-          for (int u = 0; u < 8; ++u) v[u] += as_float((u & 1) ? (bw[u >> 1] & 0xFFFF0000u) : (bw[u >> 1] << 16));
-        }
-        if (epi == 1) {
+      for (int it = 0; it < 4; ++it) {
+        const int m = m_base + row_grp + 8 * it + lrow;
+        float v[8] = {lo[it].x, lo[it].y, lo[it].z, lo[it].w, hi[it].x, hi[it].y, hi[it].z, hi[it].w};
 #pragma unroll
-          for (int u = 0; u < 8; ++u) v[u] = gelu_tanh_dev(v[u]);
+        for (int u = 0; u < 8; ++u) {
+          if constexpr (MODE == 1) v[u] = __builtin_fmaf(v[u], sm[it], b[u]);
+          else v[u] += b[u];
+          if constexpr (GELU) v[u] = gelu_tanh_dev(v[u]);
         }
         uint4 h;
         h.x = pack_bf16x2(v[0], v[1]);
@@ -719,7 +728,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const bool in = m < M && n < N;
         buf_store16(ry, in ? ((uint32_t)m * (uint32_t)N + (uint32_t)n) * 2u : 0x80000000u, h);
       }
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     };
     // the accumulator indices are static: one copy of the pass per (j, h)
     [&]<int... Q>(std::integer_sequence<int, Q...>) {
@@ -777,31 +785,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       const int next_half = (G + 1) & 1;
       StepData<MODE> nxt;
       StageScales nxt_sc;
-      if constexpr (C::BPL == 2) {
-        // step 0: MFMAs on `cur`; between them the reads of step 1's fragments
-        // (early, they are needed next) and the first copies of stage G+D
-        mfma_step(cur, cur_sc, std::integral_constant<int, 0>{}, [&](int k) {
-          if (k < DATA_ITEMS) read_item(here, 1, 0, kStepOrder[MODE][k], nxt, nxt_sc);
-          if (kCopyAt[k] >= 0) issue_one(kCopyAt[k], slot_refill);
-        });
-        // step 1: MFMAs on `nxt`; between them the reads of stage G+1's step-0
-        // fragments and scales, in the order the next stage consumes them, and
-        // the rest of the copies
-        const StageScales sc1 = cur_sc;
-        mfma_step(nxt, sc1, std::integral_constant<int, 1>{}, [&](int k) {
-          read_item(next, 0, next_half, kStageOrder[MODE][k], cur, cur_sc);
-          if (kCopyAt[16 + k] >= 0) issue_one(kCopyAt[16 + k], slot_refill);
-        });
-        advance_cursor();
-      } else {
-        mfma_step(cur, cur_sc, std::integral_constant<int, 0>{}, [&](int k) {
-          read_item(next, 0, next_half, kStageOrder[MODE][k], nxt, nxt_sc);
-          if (k < C::PER_WAVE) issue_one(k, slot_refill);
-        });
-        advance_cursor();
-        cur = nxt;
-        cur_sc = nxt_sc;
-      }
+      // step 0: MFMAs on `cur`; between them the reads of step 1's fragments
+      // (early, they are needed next) and the first copies of stage G+D
+      mfma_step(cur, cur_sc, std::integral_constant<int, 0>{}, [&](int k) {
+        if (k < DATA_ITEMS) read_item(here, 1, 0, kStepOrder[MODE][k], nxt, nxt_sc);
+        if (kCopyAt[k] >= 0) issue_one(kCopyAt[k], slot_refill);
+      });
+      // step 1: MFMAs on `nxt`; between them the reads of stage G+1's step-0
+      // fragments and scales, in the order the next stage consumes them, and
+      // the rest of the copies
+      const StageScales sc1 = cur_sc;
+      mfma_step(nxt, sc1, std::integral_constant<int, 1>{}, [&](int k) {
+        read_item(next, 0, next_half, kStageOrder[MODE][k], cur, cur_sc);
+        if (kCopyAt[16 + k] >= 0) issue_one(kCopyAt[16 + k], slot_refill);
+      });
+      advance_cursor();
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
 
       ++since_epi;
@@ -833,10 +831,17 @@ static hipError_t launch_pipe(const void* aq, const void* as, const void* wq, co
   const int tiles_n = (int)((N + 255) / 256);
   const int total = tiles_m * tiles_n;
   const int grid = total < cus ? total : cus;
-  hipLaunchKernelGGL((gemm_pipe_kernel<MODE, KT, NB>), dim3(grid), dim3(256), 0, s,
-                     static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws),
-                     static_cast<const uint8_t*>(aq), as, static_cast<const uint16_t*>(bias),
-                     static_cast<uint16_t*>(y), (int)M, (int)N, (int)K, epi, tiles_m, tiles_n);
+  // GELU is a kernel parameter, so that the plain kernel carries no GELU code
+  if (epi == 1)
+    hipLaunchKernelGGL((gemm_pipe_kernel<MODE, KT, NB, true>), dim3(grid), dim3(256), 0, s,
+                       static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws),
+                       static_cast<const uint8_t*>(aq), as, static_cast<const uint16_t*>(bias),
+                       static_cast<uint16_t*>(y), (int)M, (int)N, (int)K, tiles_m, tiles_n);
+  else
+    hipLaunchKernelGGL((gemm_pipe_kernel<MODE, KT, NB, false>), dim3(grid), dim3(256), 0, s,
+                       static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws),
+                       static_cast<const uint8_t*>(aq), as, static_cast<const uint16_t*>(bias),
+                       static_cast<uint16_t*>(y), (int)M, (int)N, (int)K, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
