@@ -404,12 +404,20 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // VALU write to them right after it would change what is stored; the compiler
 // guards that only for stores it knows about, so the wait state is part of the
 // asm block.
+// One accumulator register read into a VGPR at the point of use (left to the
+// compiler, all 256 accumulators are copied out at once and spill).
+__device__ __forceinline__ float acc_read(float a) {
+  float v;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(v) : "a"(a));
+  return v;
+}
+
 __device__ __forceinline__ void buf_store16(const i32x4& rs, uint32_t voff, const uint4& v) {
   const i32x4 d = {(int)v.x, (int)v.y, (int)v.z, (int)v.w};
   asm volatile("buffer_store_dwordx4 %0, %1, %2, 0 offen\n\ts_nop 1" :: "v"(d), "v"(voff), "s"(rs) : "memory");
 }
 
-template <int MODE, int KT, int NB, bool GELU>
+template <int MODE, int KT, int NB, bool GELU, bool BIAS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_pipe_kernel(
     const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws,
     const uint8_t* __restrict__ aq, const void* __restrict__ asc,
@@ -421,7 +429,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int P_BIAS = 0, P_SINK = 512, P_TOK = 1024;
   constexpr int PARAM_BYTES = MODE == 1 ? 2048 : 1024;
   constexpr int PARAM_OFF = NB * C::STAGE;
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[NB * C::STAGE + 2 * PARAM_BYTES];
+  // W4A4 stages its results through a small area of its own (the epilogue
+  // runs while the ring is busy, see below): 32 rows x 144 bytes per wave
+  constexpr int EV_PITCH = 144;
+  constexpr int EV_BYTES = 32 * EV_PITCH;
+  constexpr int EV_OFF = PARAM_OFF + 2 * PARAM_BYTES;
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[EV_OFF + (MODE == 0 ? 4 * EV_BYTES : 0)];
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -499,50 +512,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // a few scalar selects and no branch: a branch between the MFMA steps
   // would split the block the reads and copies are interleaved in.
   const uint32_t lds_ring = lds_addr(ring);
-  struct TileOff {
-    uint32_t w, x, ws, xs;
-  };
-  auto tile_off = [&](int k) {
+  // first output column (nb) and row (mb) of tile k; zeros past the last tile
+  auto tile_base = [&](int k, uint32_t& nb, uint32_t& mb) {
     int tm = 0, tn = 0;
     if (k < count) tile_of(first + k * stride, tiles_m, tiles_n, tm, tn);
-    const uint32_t nb = (uint32_t)tn * 256u, mb = (uint32_t)tm * 256u;
-    return TileOff{nb * C::W_RB, mb * (MODE == 0 ? (uint32_t)C::X_RB : x_row), nb * 4u, mb * 4u};
+    nb = (uint32_t)tn * 256u;
+    mb = (uint32_t)tm * 256u;
   };
   int cp_k = 0, cp_s = 0;
-  TileOff cp_off = tile_off(0), cp_next = tile_off(1);
+  uint32_t cp_nb, cp_mb, nx_nb, nx_mb;  // the cursor's tile and the tile after it
+  tile_base(0, cp_nb, cp_mb);
+  tile_base(1, nx_nb, nx_mb);
   // Copy q (0 .. PER_WAVE-1) of the cursor's stage into ring slot `slot`.
   // Past the last tile the copies are still issued (so the wait counts stay
-  // constant and the issue has no branch) but with an offset beyond every
-  // resource's size: the hardware then writes zeros to LDS without reading
-  // memory. Offsets stay in the per-lane operand, the part the range check
-  // covers.
+  // constant and the issue has no branch) but with 2^31 added to the offset,
+  // beyond every resource's size (all below 2^31; the per-lane part is too,
+  // so the sum does not wrap): the hardware then writes zeros to LDS without
+  // reading memory. Offsets stay in the per-lane operand, the part the range
+  // check covers; the scalar part is chosen with a scalar select.
   auto issue_one = [&](int q, int slot) {
     const bool live = cp_k < count;
-    const uint32_t oob = 0x80000000u;
+    constexpr uint32_t oob = 0x80000000u;
     const uint32_t base = lds_ring + (uint32_t)slot * C::STAGE;
     if (q < C::W_INSTR) {
-      lds_dma16(rw, base + C::W_OFF + (wave * C::W_INSTR + q) * 1024,
-                live ? vw[q] + cp_off.w + (uint32_t)cp_s * w_panel : oob);
+      const uint32_t so = live ? cp_nb * (uint32_t)C::W_RB + (uint32_t)cp_s * w_panel : oob;
+      lds_dma16(rw, base + C::W_OFF + (wave * C::W_INSTR + q) * 1024, vw[q] + so);
     } else if (q < C::W_INSTR + C::X_INSTR) {
       const int qx = q - C::W_INSTR;
-      lds_dma16(rx, base + C::X_OFF + (wave * C::X_INSTR + qx) * 1024,
-                live ? vx[qx] + cp_off.x + (uint32_t)cp_s * x_stage : oob);
+      const uint32_t so =
+          live ? cp_mb * (MODE == 0 ? (uint32_t)C::X_RB : x_row) + (uint32_t)cp_s * x_stage : oob;
+      lds_dma16(rx, base + C::X_OFF + (wave * C::X_INSTR + qx) * 1024, vx[qx] + so);
     } else if (q == C::W_INSTR + C::X_INSTR) {
-      lds_dma4(rws, base + C::WS_OFF + wave * 256,
-               live ? vs + cp_off.ws + (uint32_t)(cp_s * KT / 128) * ws_group : oob);
+      const uint32_t so = live ? cp_nb * 4u + (uint32_t)(cp_s * KT / 128) * ws_group : oob;
+      lds_dma4(rws, base + C::WS_OFF + wave * 256, vs + so);
     } else {
-      lds_dma4(rxs, base + C::XS_OFF + wave * 256,
-               live ? vs + cp_off.xs + (uint32_t)(cp_s * KT / 128) * xs_group : oob);
+      const uint32_t so = live ? cp_mb * 4u + (uint32_t)(cp_s * KT / 128) * xs_group : oob;
+      lds_dma4(rxs, base + C::XS_OFF + wave * 256, vs + so);
     }
   };
   auto advance_cursor = [&] {
     const bool wrap = ++cp_s == n_stages;
     cp_s = wrap ? 0 : cp_s;
     cp_k += wrap ? 1 : 0;
-    cp_off.w = wrap ? cp_next.w : cp_off.w;
-    cp_off.x = wrap ? cp_next.x : cp_off.x;
-    cp_off.ws = wrap ? cp_next.ws : cp_off.ws;
-    cp_off.xs = wrap ? cp_next.xs : cp_off.xs;
+    // a select on the values (written as a mask: the compiler turns the
+    // conditional form into a select of addresses, which keeps them in memory)
+    const uint32_t take = 0u - (uint32_t)wrap;
+    cp_nb = (nx_nb & take) | (cp_nb & ~take);
+    cp_mb = (nx_mb & take) | (cp_mb & ~take);
   };
   // Tile parameters of tile k into parameter block k & 1: the bias slice
   // (waves 0, 1: 256 bytes each; waves 2, 3 copy nothing into the sink) and,
@@ -624,24 +640,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // The 16 MFMAs of one step; after MFMA number k (0..15) `between(k)` may
   // issue one deferred operation, and the order is pinned by a scheduling
   // barrier so that the reads stay spread between the MFMAs.
-  auto mfma_step = [&](const StepData<MODE>& f, const StageScales& sc, auto kk_tag, auto&& between) {
+  // `before(k)` runs before MFMA k; with `zero_tag` true the step starts the
+  // tile's sums (accumulator input 0, an inline constant).
+  // With `pin_tag` true each MFMA result passes through an empty asm
+  // statement right after it: ordered with the other asm statements of the
+  // step, the MFMA cannot be moved away from the work interleaved with it.
+  auto mfma_step_x = [&](const StepData<MODE>& f, const StageScales& sc, auto kk_tag, auto zero_tag, auto pin_tag,
+                         auto&& before, auto&& between) {
     constexpr int KK = decltype(kk_tag)::value;
+    constexpr bool ZERO = decltype(zero_tag)::value;
+    constexpr bool PIN = decltype(pin_tag)::value;
     constexpr int SEL = KT == 128 ? KK : 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
+        before(i * 4 + j);
         const v8i a = op_fp4(f.a[i]);
         if constexpr (MODE == 0)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, op_fp4(f.b[j]), acc[i][j], kFmtFp4, kFmtFp4,
-                                                                      SEL, (int)sc.ws[i], SEL, (int)sc.xs[j]);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, op_fp4(f.b[j]), ZERO ? v16f{} : acc[i][j],
+                                                                      kFmtFp4, kFmtFp4, SEL, (int)sc.ws[i], SEL,
+                                                                      (int)sc.xs[j]);
         else
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, op_fp8(f.b[2 * j], f.b[2 * j + 1]), acc[i][j],
                                                                       kFmtFp4, kFmtFp8, SEL, (int)sc.ws[i], SEL,
                                                                       (int)kUnitScales);
+        if constexpr (PIN) asm volatile("" ::"a"(acc[i][j]));
         between(i * 4 + j);
         __builtin_amdgcn_sched_barrier(0);
       }
+  };
+  auto mfma_step = [&](const StepData<MODE>& f, const StageScales& sc, auto kk_tag, auto&& between) {
+    mfma_step_x(f, sc, kk_tag, std::false_type{}, std::false_type{}, [](int) {}, between);
   };
 
   // ---- epilogue of one tile, staged through the slot of its last stage.
@@ -716,8 +746,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         float v[8] = {lo[it].x, lo[it].y, lo[it].z, lo[it].w, hi[it].x, hi[it].y, hi[it].z, hi[it].w};
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          if constexpr (MODE == 1) v[u] = __builtin_fmaf(v[u], sm[it], b[u]);
-          else v[u] += b[u];
+          if constexpr (MODE == 1) v[u] = BIAS ? __builtin_fmaf(v[u], sm[it], b[u]) : v[u] * sm[it];
+          else if constexpr (BIAS) v[u] += b[u];
           if constexpr (GELU) v[u] = gelu_tanh_dev(v[u]);
         }
         uint4 h;
@@ -737,7 +767,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     issue_params(k + 1);
     // the copy cursor is in tile k+1 by now (it runs fewer than n_stages
     // stages ahead); the tile it moves to next is k+2
-    cp_next = tile_off(cp_k + 1);
+    tile_base(cp_k + 1, nx_nb, nx_mb);
   };
 
   constexpr int D = NB - 1;  // copies run D stages ahead of the stage computed
@@ -761,18 +791,82 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
   for (int k = 0; k < STAGE_ITEMS; ++k) read_item(ring, 0, 0, kStageOrder[MODE][k], cur, cur_sc);
 
-  int slot = 0;          // ring slot of the stage being computed
-  int since_epi = D;     // stages since the last epilogue, minus one (D: none pending)
-  for (int tile_k = 0; tile_k < count; ++tile_k) {
+  if constexpr (MODE == 0) {
+    // ---- W4A4: the epilogue of tile t-1 runs inside the first stage of
+    // tile t. Before MFMA (i, j) of that stage's first step (which starts the
+    // new sums from zero) the lane reads accumulator tile (i, j) of tile t-1
+    // out of its registers, adds the bias, applies GELU and packs bf16 pairs;
+    // v_permlane32_swap then gives each lane 16 contiguous bytes of one row
+    // (columns 16 u + 8 g .. + 7 of the 32-column tile). When both tiles of a
+    // column pair (i = 2h, 2h+1) of row group j are ready they go through the
+    // wave's staging area (32 rows x 64 columns) and leave as 4 stores of 8
+    // rows x 128 contiguous bytes, one MFMA slot later. The matrix pipe keeps
+    // working while the vector unit does this. Tile 0's first stage has no
+    // previous tile (its stores are dropped), and one extra stage after the
+    // last tile, computing on zeros, carries the last tile's epilogue.
+    uint8_t* ev_region = ring + EV_OFF + wave * EV_BYTES;
+    // bias of the lane's 16 columns of MFMA tile row group i, in accumulator
+    // order (q = 4 t + c: column 32 i + 8 t + 4 g + c)
+    auto ev_bias = [&](const uint8_t* prm, int i, v16f& b) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int t2 = 0; t2 < 4; ++t2) {
+        const uint2 bb = *reinterpret_cast<const uint2*>(prm + P_BIAS + (wn * 128 + 32 * i + 8 * t2 + 4 * g) * 2);
+        b[4 * t2 + 0] = as_float(bb.x << 16);
+        b[4 * t2 + 1] = as_float(bb.x & 0xFFFF0000u);
+        b[4 * t2 + 2] = as_float(bb.y << 16);
+        b[4 * t2 + 3] = as_float(bb.y & 0xFFFF0000u);
+      }
+    };
+    // accumulator tile (i, j) of the finished tile (+ bias) -> 8 bf16 pairs:
+    // pair h of run t holds columns 8 t + 4 g + 2 h, + 1
+    auto ev_tile = [&](int i, int j, const v16f& b, uint32_t (&pk)[4][2]) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
+      for (int t2 = 0; t2 < 4; ++t2)
 #pragma unroll
-        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
-    for (int s_in = 0; s_in < n_stages; ++s_in) {
+        for (int h = 0; h < 2; ++h) {
+          float v0 = acc_read(acc[i][j][4 * t2 + 2 * h]);
+          float v1 = acc_read(acc[i][j][4 * t2 + 2 * h + 1]);
+          if constexpr (BIAS) {
+            v0 += b[4 * t2 + 2 * h];
+            v1 += b[4 * t2 + 2 * h + 1];
+          }
+          if constexpr (GELU) {
+            v0 = gelu_tanh_dev(v0);
+            v1 = gelu_tanh_dev(v1);
+          }
+          pk[t2][h] = pack_bf16x2(v0, v1);
+        }
+    };
+    // staging area: row r holds the 64 columns of tiles 2h, 2h+1; the lane's
+    // run t of tile ii is 8 bytes at column 32 ii + 8 t + 4 g
+    auto ev_unit_write = [&](const uint32_t (&p0)[4][2], const uint32_t (&p1)[4][2]) {
+#pragma unroll
+      for (int t2 = 0; t2 < 4; ++t2) {
+        *reinterpret_cast<uint2*>(ev_region + r * EV_PITCH + 16 * t2 + 8 * g) = make_uint2(p0[t2][0], p0[t2][1]);
+        *reinterpret_cast<uint2*>(ev_region + r * EV_PITCH + 64 + 16 * t2 + 8 * g) = make_uint2(p1[t2][0], p1[t2][1]);
+      }
+    };
+    auto ev_unit_read = [&](uint4 (&rd)[4]) {
+#pragma unroll
+      for (int it = 0; it < 4; ++it)
+        rd[it] = *reinterpret_cast<const uint4*>(ev_region + (8 * it + (lane >> 3)) * EV_PITCH + (lane & 7) * 16);
+    };
+
+    constexpr int D_SLACK1 = EPI_OPS;        // a wait that every op of the first stage may outlast
+    constexpr int D_SLACK2 = EPI_PARAM_OPS;  // ops of the first stage issued after its last copy
+    // every epilogue store of the first stage comes before its last copy
+    constexpr int kLastCopySlot = COPY_SPAN * (C::PER_WAVE - 1) / C::PER_WAVE;
+    static_assert(kLastCopySlot > 16, "epilogue stores end in slot 16");
+
+    int slot = 0;  // ring slot of the stage being computed
+    auto run_stage = [&](int tile_k, int s_in, auto first_tag) {
+      constexpr bool FIRST = decltype(first_tag)::value;
       if (tile_k > 0 || s_in > 0) {
-        if (since_epi < D - 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(WAIT_BASE + EPI_OPS));
+        // the stage after the first one may leave all of the first stage's
+        // operations outstanding; the one after that, those issued after its
+        // last copy
+        if (s_in >= 1 && s_in <= D - 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(WAIT_BASE + D_SLACK1));
+        else if (s_in == D - 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(WAIT_BASE + D_SLACK2));
         else __builtin_amdgcn_s_waitcnt(waitcnt_vm(WAIT_BASE));
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
@@ -785,29 +879,140 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       const int next_half = (G + 1) & 1;
       StepData<MODE> nxt;
       StageScales nxt_sc;
-      // step 0: MFMAs on `cur`; between them the reads of step 1's fragments
-      // (early, they are needed next) and the first copies of stage G+D
-      mfma_step(cur, cur_sc, std::integral_constant<int, 0>{}, [&](int k) {
+      auto between0 = [&](int k) {
         if (k < DATA_ITEMS) read_item(here, 1, 0, kStepOrder[MODE][k], nxt, nxt_sc);
         if (kCopyAt[k] >= 0) issue_one(kCopyAt[k], slot_refill);
-      });
-      // step 1: MFMAs on `nxt`; between them the reads of stage G+1's step-0
-      // fragments and scales, in the order the next stage consumes them, and
-      // the rest of the copies
-      const StageScales sc1 = cur_sc;
-      mfma_step(nxt, sc1, std::integral_constant<int, 1>{}, [&](int k) {
+      };
+      auto between1 = [&](int k) {
         read_item(next, 0, next_half, kStageOrder[MODE][k], cur, cur_sc);
         if (kCopyAt[16 + k] >= 0) issue_one(kCopyAt[16 + k], slot_refill);
-      });
+      };
+      if constexpr (!FIRST) {
+        mfma_step(cur, cur_sc, std::integral_constant<int, 0>{}, between0);
+        const StageScales sc1 = cur_sc;
+        mfma_step(nxt, sc1, std::integral_constant<int, 1>{}, between1);
+      } else {
+        // the cursor is in this tile (stage D): the tile it moves to next is
+        // tile_k + 1
+        tile_base(cp_k + 1, nx_nb, nx_mb);
+        const bool ev_live = tile_k > 0;
+        int ptm = 0, ptn = 0;
+        if (ev_live) tile_of(first + (tile_k - 1) * stride, tiles_m, tiles_n, ptm, ptn);
+        // byte offset of the lane's first store (+ 32 j rows + 8 it rows + 64 h
+        // columns); rows past M fall past the end of the output, which the
+        // range check drops, and columns past N (or no tile at all) get the
+        // offset's top bit, past every output of fewer than 2^31 bytes
+        const int ev_m0 = ptm * 256 + wm * 128 + (lane >> 3);
+        const int ev_n0 = ptn * 256 + wn * 128 + (lane & 7) * 8;
+        const uint32_t ev_off0 = ((uint32_t)ev_m0 * (uint32_t)N + (uint32_t)ev_n0) * 2u;
+        const uint32_t ev_bad0 = ev_live && ev_n0 < N ? 0u : 0x80000000u;
+        const uint32_t ev_bad1 = ev_live && ev_n0 + 64 < N ? 0u : 0x80000000u;
+        const uint32_t row8 = (uint32_t)N * 16u;  // 8 rows of bf16
+        // bias of the finished tile (zeros when there is none)
+        const uint8_t* prm = ring + PARAM_OFF + ((tile_k - 1) & 1) * PARAM_BYTES;
+        v16f c_cur, c_nxt;
+        if constexpr (BIAS) ev_bias(prm, 0, c_cur);
+        uint32_t evd[4][4][4][2];
+        uint4 rd[4];
+        auto unit_store = [&](int j, int h) {
+#pragma unroll
+          for (int it = 0; it < 4; ++it)
+            buf_store16(ry, (ev_off0 + (uint32_t)(4 * j + it) * row8 + 128u * h) | (h ? ev_bad1 : ev_bad0), rd[it]);
+        };
+        auto before0 = [&](int k) {
+          const int i = k >> 2, j = k & 3;
+          if (BIAS && j == 0 && i > 0) c_cur = c_nxt;
+          ev_tile(i, j, c_cur, evd[i][j]);
+        };
+        auto after0 = [&](int k) {
+          const int i = k >> 2, j = k & 3;
+          between0(k);
+          // stores of the pair staged in the previous slot
+          if ((k - 1) >> 2 == 1 || (k - 1) >> 2 == 3) unit_store((k - 1) & 3, (k - 1) >> 3);
+          if (i & 1) {
+            ev_unit_write(evd[i - 1][j], evd[i][j]);
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            ev_unit_read(rd);
+            // the next pair's writes stay behind these reads
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+          }
+          if (BIAS && j == 1 && i < 3) ev_bias(prm, i + 1, c_nxt);
+        };
+        mfma_step_x(cur, cur_sc, std::integral_constant<int, 0>{}, std::true_type{}, std::true_type{}, before0,
+                    after0);
+        const StageScales sc1 = cur_sc;
+        mfma_step_x(nxt, sc1, std::integral_constant<int, 1>{}, std::false_type{}, std::true_type{}, [](int) {},
+                    [&](int k) {
+                      between1(k);
+                      if (k == 0) unit_store(3, 1);
+                    });
+        // parameters of the next tile go into the block just read: wait for those reads
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+        issue_params(tile_k + 1);
+      }
       advance_cursor();
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      slot = slot_next;
+    };
 
-      ++since_epi;
-      if (s_in + 1 < n_stages) slot = slot_next;
+    // one more first stage after the last tile: it carries that tile's
+    // epilogue (its own MFMAs work on zeros); the loop test is the only exit,
+    // at the end of an iteration, so no path leaves between a first stage's
+    // MFMAs and the stages that use their sums
+    for (int tile_k = 0; tile_k <= count; ++tile_k) {
+      run_stage(tile_k, 0, std::true_type{});
+      const int s_end = tile_k < count ? n_stages : 1;
+      for (int s_in = 1; s_in < s_end; ++s_in) run_stage(tile_k, s_in, std::false_type{});
     }
-    epilogue(tile_k, slot);
-    since_epi = 0;
-    slot = slot + 1 == NB ? 0 : slot + 1;
+  } else {
+  int slot = 0;          // ring slot of the stage being computed
+    int since_epi = D;     // stages since the last epilogue, minus one (D: none pending)
+    for (int tile_k = 0; tile_k < count; ++tile_k) {
+  #pragma unroll
+      for (int i = 0; i < 4; ++i)
+  #pragma unroll
+        for (int j = 0; j < 4; ++j)
+  #pragma unroll
+          for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+      for (int s_in = 0; s_in < n_stages; ++s_in) {
+        if (tile_k > 0 || s_in > 0) {
+          if (since_epi < D - 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(WAIT_BASE + EPI_OPS));
+          else __builtin_amdgcn_s_waitcnt(waitcnt_vm(WAIT_BASE));
+          __builtin_amdgcn_s_barrier();
+          __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+        }
+        const int G = tile_k * n_stages + s_in;
+        const int slot_next = slot + 1 == NB ? 0 : slot + 1;
+        const int slot_refill = slot == 0 ? NB - 1 : slot - 1;  // (G + D) mod NB
+        const uint8_t* here = ring + slot * C::STAGE;
+        const uint8_t* next = ring + slot_next * C::STAGE;
+        const int next_half = (G + 1) & 1;
+        StepData<MODE> nxt;
+        StageScales nxt_sc;
+        // step 0: MFMAs on `cur`; between them the reads of step 1's fragments
+        // (early, they are needed next) and the first copies of stage G+D
+        mfma_step(cur, cur_sc, std::integral_constant<int, 0>{}, [&](int k) {
+          if (k < DATA_ITEMS) read_item(here, 1, 0, kStepOrder[MODE][k], nxt, nxt_sc);
+          if (kCopyAt[k] >= 0) issue_one(kCopyAt[k], slot_refill);
+        });
+        // step 1: MFMAs on `nxt`; between them the reads of stage G+1's step-0
+        // fragments and scales, in the order the next stage consumes them, and
+        // the rest of the copies
+        const StageScales sc1 = cur_sc;
+        mfma_step(nxt, sc1, std::integral_constant<int, 1>{}, [&](int k) {
+          read_item(next, 0, next_half, kStageOrder[MODE][k], cur, cur_sc);
+          if (kCopyAt[16 + k] >= 0) issue_one(kCopyAt[16 + k], slot_refill);
+        });
+        advance_cursor();
+        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+  
+        ++since_epi;
+        if (s_in + 1 < n_stages) slot = slot_next;
+      }
+      epilogue(tile_k, slot);
+      since_epi = 0;
+      slot = slot + 1 == NB ? 0 : slot + 1;
+    }
   }
   // no copy or store may still be in flight when the workgroup retires
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
@@ -831,17 +1036,22 @@ static hipError_t launch_pipe(const void* aq, const void* as, const void* wq, co
   const int tiles_n = (int)((N + 255) / 256);
   const int total = tiles_m * tiles_n;
   const int grid = total < cus ? total : cus;
-  // GELU is a kernel parameter, so that the plain kernel carries no GELU code
-  if (epi == 1)
-    hipLaunchKernelGGL((gemm_pipe_kernel<MODE, KT, NB, true>), dim3(grid), dim3(256), 0, s,
-                       static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws),
-                       static_cast<const uint8_t*>(aq), as, static_cast<const uint16_t*>(bias),
-                       static_cast<uint16_t*>(y), (int)M, (int)N, (int)K, tiles_m, tiles_n);
-  else
-    hipLaunchKernelGGL((gemm_pipe_kernel<MODE, KT, NB, false>), dim3(grid), dim3(256), 0, s,
-                       static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws),
-                       static_cast<const uint8_t*>(aq), as, static_cast<const uint16_t*>(bias),
-                       static_cast<uint16_t*>(y), (int)M, (int)N, (int)K, tiles_m, tiles_n);
+  // GELU and bias are kernel parameters, so that each kernel carries only
+  // the epilogue work it does
+  auto go = [&](auto gelu_tag, auto bias_tag) {
+    hipLaunchKernelGGL((gemm_pipe_kernel<MODE, KT, NB, decltype(gelu_tag)::value, decltype(bias_tag)::value>),
+                       dim3(grid), dim3(256), 0, s, static_cast<const uint8_t*>(wq),
+                       static_cast<const uint8_t*>(ws), static_cast<const uint8_t*>(aq), as,
+                       static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), (int)M, (int)N, (int)K, tiles_m,
+                       tiles_n);
+  };
+  if (epi == 1) {
+    if (bias != nullptr) go(std::true_type{}, std::true_type{});
+    else go(std::true_type{}, std::false_type{});
+  } else {
+    if (bias != nullptr) go(std::false_type{}, std::true_type{});
+    else go(std::false_type{}, std::false_type{});
+  }
   return hipGetLastError();
 }
 

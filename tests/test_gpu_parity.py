@@ -125,13 +125,17 @@ def test_gemm_pipelined_kernel_matches_oracle(mode, m, n, k):
     assert_output_close(y, y_ref, f"gemm pipe mode={mode} {m}x{n}x{k}")
 
 
+# Each combination of bias and GELU is a kernel of its own (the one without
+# either is covered above).
 @pytest.mark.parametrize("mode", [mxq.W4A4, mxq.W4A8])
 @pytest.mark.parametrize("m,n,k", [(300, 512, 640), (4352, 4096, 640)])
-def test_gemm_pipelined_bias_and_gelu(mode, m, n, k):
-    say("gemm pipe epilogue", mode, m, n, k)
+@pytest.mark.parametrize("epilogue,bias", [(mxq.EPI_GELU_TANH, True), (mxq.EPI_NONE, True),
+                                           (mxq.EPI_GELU_TANH, False)])
+def test_gemm_pipelined_bias_and_gelu(mode, m, n, k, epilogue, bias):
+    say("gemm pipe epilogue", mode, m, n, k, epilogue, bias)
     assert mxq.gemm_kernel_name(mode, m, n, k).startswith("pipe_")
-    y, y_ref = _gemm_case(mode, m, n, k, seed=8, epilogue=mxq.EPI_GELU_TANH, bias=True)
-    assert_output_close(y, y_ref, f"pipe bias+gelu {m}x{n}x{k}")
+    y, y_ref = _gemm_case(mode, m, n, k, seed=8, epilogue=epilogue, bias=bias)
+    assert_output_close(y, y_ref, f"pipe epilogue={epilogue} bias={bias} {m}x{n}x{k}")
 
 
 @pytest.mark.parametrize("mode", [mxq.W4A4, mxq.W4A8])
