@@ -91,21 +91,25 @@ class Stack:
         self.h = torch.empty((wl.m_video * max(wl.ffn, 1),), dtype=torch.bfloat16, device=dev)
         ws = max(mxq.qlinear_workspace_bytes(md, m_max, l.k) for md in (0, 1) for l in wl.linears)
         self.codes_buf = torch.empty((ws,), dtype=torch.uint8, device=dev)
+        # W4A4 FFN: the first projection writes the second one's MXFP4 input here
+        self.codes_buf2 = torch.empty((ws,), dtype=torch.uint8, device=dev)
         self.records = []  # (kind, mode, flops, bytes, ev_start, ev_end)
+        self.down_ready = False  # the W4A4 FFN's second projection has its input codes in codes_buf2
 
-    def _act_views(self, mode, m, k):
+    def _act_views(self, mode, m, k, buf=None):
         torch = self.torch
+        buf = self.codes_buf if buf is None else buf
         if mode == 0:
             cb = m * k // 2
-            codes = self.codes_buf[:cb].view(m, k // 2)
+            codes = buf[:cb].view(m, k // 2)
             off = (cb + 255) // 256 * 256
             shape = self.mxq.mx_scale_shape(m, k)
-            scales = self.codes_buf[off:off + shape[0] * m * 4].view(shape)
+            scales = buf[off:off + shape[0] * m * 4].view(shape)
         else:
             cb = m * k
-            codes = self.codes_buf[:cb].view(m, k)
+            codes = buf[:cb].view(m, k)
             off = (cb + 255) // 256 * 256
-            scales = self.codes_buf[off:off + 4 * m].view(torch.float32)
+            scales = buf[off:off + 4 * m].view(torch.float32)
         return codes, scales
 
     def step(self, timed):
@@ -122,21 +126,39 @@ class Stack:
                     else:
                         x = self.h[: m * lin.k].view(m, lin.k)
                     out = (self.h if lin.epilogue == 1 else self.y)[: m * lin.n].view(m, lin.n)
-                    codes, scales = self._act_views(mode, m, lin.k)
                     wc, wsc = self.weights[(e, b, li)]
+                    # W4A4 FFN: the first projection quantizes its GELU output
+                    # for the second one in its epilogue (same codes as
+                    # quantize_act of its bf16 output), the second one reads
+                    # them as they are
+                    fused_up = mode == 0 and lin.name == "ffn_up" and mxq.gemm_mxfp4_out_supported(m, lin.n, lin.k)
+                    fed = mode == 0 and lin.name == "ffn_down" and self.down_ready
+                    if fed:
+                        codes, scales = self._act_views(mode, m, lin.k, self.codes_buf2)
+                    else:
+                        codes, scales = self._act_views(mode, m, lin.k)
                     if timed:
                         e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
                         e0.record()
-                    mxq.quantize_act(mode, x, codes, scales)
+                    if not fed:
+                        mxq.quantize_act(mode, x, codes, scales)
                     if timed:
                         e1.record()
-                    mxq.gemm(mode, codes, scales, wc, wsc, None, lin.epilogue, out)
+                    if fused_up:
+                        oc, osc = self._act_views(mode, m, lin.n, self.codes_buf2)
+                        mxq.gemm_mxfp4_out(codes, scales, wc, wsc, None, lin.epilogue, oc, osc)
+                        out_bytes = m * lin.n // 2 + m * lin.n // 32
+                    else:
+                        mxq.gemm(mode, codes, scales, wc, wsc, None, lin.epilogue, out)
+                        out_bytes = m * lin.n * 2
+                    self.down_ready = fused_up
                     if timed:
                         e2.record()
                         qbytes = m * lin.k * 2 + (m * lin.k // 2 + m * lin.k // 32 if mode == 0 else m * lin.k + 4 * m)
                         gbytes = ((m * lin.k // 2 + m * lin.k // 32) if mode == 0 else (m * lin.k + 4 * m)) \
-                            + lin.n * lin.k // 2 + lin.n * lin.k // 32 + m * lin.n * 2
-                        self.records.append(("quant", mode, 0, qbytes, e0, e1))
+                            + lin.n * lin.k // 2 + lin.n * lin.k // 32 + out_bytes
+                        if not fed:
+                            self.records.append(("quant", mode, 0, qbytes, e0, e1))
                         self.records.append(("gemm", mode, 2 * m * lin.n * lin.k, gbytes, e1, e2))
 
 

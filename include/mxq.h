@@ -146,6 +146,29 @@ int mxq_gemm(int mode, const void* a_codes, const void* a_scales,
              hipStream_t stream);
 
 /*
+ * W4A4 GEMM whose output is the W4A4 activation of a next layer: the FFN of a
+ * W4A4 block takes the first projection (with tanh-GELU), quantizes the
+ * hidden state to MXFP4 ("Quantization formats") and feeds it to the second
+ * projection. This entry point does the first two in one kernel, without the
+ * bf16 hidden state in memory. The result is exactly that of mxq_gemm(
+ * MXQ_W4A4, ...) into a bf16 [M][N] buffer followed by mxq_quantize_act(
+ * MXQ_W4A4, that buffer): the same bf16 values, quantized by the same rule.
+ *   a_codes/a_scales  device, from mxq_quantize_act(MXQ_W4A4, ...)
+ *   w_codes/w_scales  device, from mxq_quantize_weight_mxfp4
+ *   bias              device bf16 [N], or null for none
+ *   y_codes           device uint8, M * N/2 bytes in code panels (output;
+ *                     its K is N)
+ *   y_scales          device uint8 [N/128][M][4] (output)
+ * Only for the shapes of the pipelined kernel (mxq_gemm_kernel_name(MXQ_W4A4,
+ * M, N, K) starts with "pipe_") with N a multiple of 128: MXQ_ERR_SHAPE
+ * otherwise, and nothing is written (use mxq_gemm and mxq_quantize_act).
+ */
+int mxq_gemm_mxfp4_out(const void* a_codes, const void* a_scales,
+                       const void* w_codes, const void* w_scales, const void* bias,
+                       int epilogue, void* y_codes, void* y_scales,
+                       int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/*
  * Name of the kernel that mxq_gemm runs for (mode, M, N, K), as a static
  * string: "pipe_..." for the LDS-pipelined persistent kernel (M, N >= 256,
  * N a multiple of 8, K a multiple of 128 with at least one ring of stages),

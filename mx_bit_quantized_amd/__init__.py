@@ -39,6 +39,7 @@ _SIGS = {
     "mxq_quantize_weight_mxfp4": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "mxq_quantize_act": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, _I64, _P, _P, _P]),
     "mxq_gemm": (ctypes.c_int, [ctypes.c_int, _P, _P, _P, _P, _P, ctypes.c_int, _P, _I64, _I64, _I64, _P]),
+    "mxq_gemm_mxfp4_out": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int, _P, _P, _I64, _I64, _I64, _P]),
     "mxq_gemm_kernel_name": (ctypes.c_char_p, [ctypes.c_int, _I64, _I64, _I64]),
     "mxq_policy_create": (ctypes.c_int, [_P, _I32, _I32, ctypes.POINTER(_P)]),
     "mxq_policy_destroy": (ctypes.c_int, [_P]),
@@ -185,6 +186,33 @@ def gemm(mode, a_codes, a_scales, w_codes, w_scales, bias=None, epilogue=EPI_NON
                          _dev_ptr(y, "y", torch.bfloat16), m, n, k, _stream_handle(stream))
     _check(st, "gemm")
     return y
+
+
+def gemm_mxfp4_out(a_codes, a_scales, w_codes, w_scales, bias=None, epilogue=EPI_NONE, y_codes=None,
+                   y_scales=None, stream=None):
+    """W4A4 GEMM whose output is quantized straight to the W4A4 activation format.
+
+    Returns (y_codes, y_scales), equal to quantize_act(W4A4, gemm(W4A4, ...)).
+    """
+    torch = _torch()
+    m = int(a_codes.shape[0])
+    n = int(w_codes.shape[0])
+    k = int(w_codes.shape[1]) * 2
+    if y_codes is None or y_scales is None:
+        y_codes, y_scales = act_buffers(W4A4, m, n, w_codes.device)
+    st = lib().mxq_gemm_mxfp4_out(_dev_ptr(a_codes, "a_codes"), _dev_ptr(a_scales, "a_scales"),
+                                   _dev_ptr(w_codes, "w_codes", torch.uint8),
+                                   _dev_ptr(w_scales, "w_scales", torch.uint8),
+                                   _dev_ptr(bias, "bias", torch.bfloat16), int(epilogue),
+                                   _dev_ptr(y_codes, "y_codes", torch.uint8),
+                                   _dev_ptr(y_scales, "y_scales", torch.uint8), m, n, k, _stream_handle(stream))
+    _check(st, "gemm_mxfp4_out")
+    return y_codes, y_scales
+
+
+def gemm_mxfp4_out_supported(M, N, K):
+    """Whether gemm_mxfp4_out takes (M, N, K): the pipelined kernel's shapes with N % 128 == 0."""
+    return gemm_kernel_name(W4A4, M, N, K).startswith("pipe_") and N % 128 == 0
 
 
 def gemm_kernel_name(mode, M, N, K):

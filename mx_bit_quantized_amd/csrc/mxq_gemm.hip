@@ -414,17 +414,27 @@ __device__ __forceinline__ float acc_read(float a) {
   return v;
 }
 
+// Range-checked 4-byte store (one data register: no late read).
+__device__ __forceinline__ void buf_store4(const i32x4& rs, uint32_t voff, uint32_t v) {
+  asm volatile("buffer_store_dword %0, %1, %2, 0 offen" :: "v"(v), "v"(voff), "s"(rs) : "memory");
+}
+
 __device__ __forceinline__ void buf_store16(const i32x4& rs, uint32_t voff, const uint4& v) {
   const i32x4 d = {(int)v.x, (int)v.y, (int)v.z, (int)v.w};
   asm volatile("buffer_store_dwordx4 %0, %1, %2, 0 offen\n\ts_nop 1" :: "v"(d), "v"(voff), "s"(rs) : "memory");
 }
 
-template <int MODE, int KT, int NB, bool GELU, bool BIAS>
+// QOUT (W4A4 only): instead of y in bf16 the kernel writes the MXFP4
+// quantization of those bf16 values, the activation format of a next W4A4
+// layer: codes in code panels of width 128 along N (y = codes, M N / 2 bytes)
+// and group-major scales [N/128][M][4] (y_scales). N % 128 == 0.
+template <int MODE, int KT, int NB, bool GELU, bool BIAS, bool QOUT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_pipe_kernel(
     const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws,
     const uint8_t* __restrict__ aq, const void* __restrict__ asc,
-    const uint16_t* __restrict__ bias, uint16_t* __restrict__ y,
+    const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, uint8_t* __restrict__ y_scales,
     int M, int N, int K, int tiles_m, int tiles_n) {
+  static_assert(!QOUT || MODE == 0, "quantized output is the W4A4 activation format");
   using C = PipeCfg<MODE, KT, NB>;
   // ring of NB stage slots, then two tile-parameter blocks: bias slice (512
   // bytes), a sink for the unused waves' copies (512), token scales (1024, FP8)
@@ -661,17 +671,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // With `pin_tag` true each MFMA result passes through an empty asm
   // statement right after it: ordered with the other asm statements of the
   // step, the MFMA cannot be moved away from the work interleaved with it.
+  // `order_tag` true takes the MFMAs j-outer (slot s = 4 j + i), so that a
+  // 32-row group of the output is complete every 4 slots.
   auto mfma_step_x = [&](const StepData<MODE>& f, const StageScales& sc, auto kk_tag, auto zero_tag, auto pin_tag,
-                         auto&& before, auto&& between) {
+                         auto order_tag, auto&& before, auto&& between) {
     constexpr int KK = decltype(kk_tag)::value;
     constexpr bool ZERO = decltype(zero_tag)::value;
     constexpr bool PIN = decltype(pin_tag)::value;
+    constexpr bool JOUT = decltype(order_tag)::value;
     constexpr int SEL = KT == 128 ? KK : 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        before(i * 4 + j);
+    for (int s = 0; s < 16; ++s) {
+      const int i = JOUT ? (s & 3) : (s >> 2), j = JOUT ? (s >> 2) : (s & 3);
+      {
+        before(s);
         const v8i a = op_fp4(f.a[i]);
         if constexpr (MODE == 0)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, op_fp4(f.b[j]), ZERO ? v16f{} : acc[i][j],
@@ -682,12 +695,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                                                                       kFmtFp4, kFmtFp8, SEL, (int)sc.ws[i], SEL,
                                                                       (int)kUnitScales);
         if constexpr (PIN) asm volatile("" ::"a"(acc[i][j]));
-        between(i * 4 + j);
+        between(s);
         __builtin_amdgcn_sched_barrier(0);
       }
+    }
   };
   auto mfma_step = [&](const StepData<MODE>& f, const StageScales& sc, auto kk_tag, auto&& between) {
-    mfma_step_x(f, sc, kk_tag, std::false_type{}, std::false_type{}, [](int) {}, between);
+    mfma_step_x(f, sc, kk_tag, std::false_type{}, std::false_type{}, std::false_type{}, [](int) {}, between);
   };
 
   // ---- epilogue of one tile, staged through the slot of its last stage.
@@ -704,7 +718,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // no branch. Exactly EPI_STORES stores per wave, whatever the shape: rows
   // past M and columns past N get an offset the range check drops.
   constexpr int EP = 272;
-  constexpr int EPI_STORES = 32;
+  // W4A4 with QOUT: per 32-row group two 1 KiB code stores and one scale store
+  constexpr int EPI_STORES = QOUT ? 12 : 32;
   constexpr int EPI_OPS = EPI_STORES + EPI_PARAM_OPS;
   static_assert(4 * 32 * EP <= C::STAGE, "epilogue staging fits in one ring slot");
   const i32x4 ry = make_rsrc(y, (uint32_t)M * (uint32_t)N * 2u);
@@ -914,54 +929,151 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const bool ev_live = tile_k > 0;
         int ptm = 0, ptn = 0;
         if (ev_live) tile_of(first + (tile_k - 1) * stride, tiles_m, tiles_n, ptm, ptn);
-        // byte offset of the lane's first store (+ 32 j rows + 8 it rows + 64 h
-        // columns); rows past M fall past the end of the output, which the
-        // range check drops, and columns past N (or no tile at all) get the
-        // offset's top bit, past every output of fewer than 2^31 bytes
-        const int ev_m0 = ptm * 256 + wm * 128 + (lane >> 3);
-        const int ev_n0 = ptn * 256 + wn * 128 + (lane & 7) * 8;
-        const uint32_t ev_off0 = ((uint32_t)ev_m0 * (uint32_t)N + (uint32_t)ev_n0) * 2u;
-        const uint32_t ev_bad0 = ev_live && ev_n0 < N ? 0u : 0x80000000u;
-        const uint32_t ev_bad1 = ev_live && ev_n0 + 64 < N ? 0u : 0x80000000u;
-        const uint32_t row8 = (uint32_t)N * 16u;  // 8 rows of bf16
-        // bias of the finished tile (zeros when there is none)
-        const uint8_t* prm = ring + PARAM_OFF + ((tile_k - 1) & 1) * PARAM_BYTES;
-        v16f c_cur, c_nxt;
-        if constexpr (BIAS) ev_bias(prm, 0, c_cur);
-        uint32_t evd[4][4][4][2];
-        uint4 rd[4];
-        auto unit_store = [&](int j, int h) {
+        if constexpr (QOUT) {
+          // MXFP4 output. The wave's 128 columns are one code panel of the
+          // output (64 bytes per row, rows contiguous) and one scale dword per
+          // row. The first step runs j-outer: before MFMA (i, j) the lane turns
+          // accumulator tile (i, j) into bf16 pairs (bias, GELU) exactly as
+          // the bf16 epilogue would, takes the block amax over its 16 values and
+          // its partner lane's 16 (lane +- 32: together the 32 columns of the
+          // tile's row), and converts them with the quantizer's scaled
+          // conversion. A lane swap and two byte permutes leave each lane 8
+          // contiguous code bytes of its row; they go into the staging area
+          // (32 rows x 64 bytes), and after the 4 tiles of row group j the
+          // group's 2 KiB leave as two 1 KiB stores, with the 32 scale dwords,
+          // one slot later.
+          constexpr int QP = 80;  // staging pitch: 64 bytes + 16 (16-byte aligned rows)
+          const int n_q = ptn * 256 + wn * 128;
+          const uint32_t q_bad = ev_live && n_q < N ? 0u : 0x80000000u;
+          const uint32_t q_pan = (uint32_t)(n_q >> 7);
+          const int m_q = ptm * 256 + wm * 128;
+          const i32x4 rq = make_rsrc(y, (uint32_t)M * (uint32_t)N / 2u);
+          const i32x4 rsq = make_rsrc(y_scales, (uint32_t)(N >> 7) * (uint32_t)M * 4u);
+          const uint8_t* prm = ring + PARAM_OFF + ((tile_k - 1) & 1) * PARAM_BYTES;
+          v16f bq[4];
+          if constexpr (BIAS) {
 #pragma unroll
-          for (int it = 0; it < 4; ++it)
-            buf_store16(ry, (ev_off0 + (uint32_t)(4 * j + it) * row8 + 128u * h) | (h ? ev_bad1 : ev_bad0), rd[it]);
-        };
-        auto before0 = [&](int k) {
-          const int i = k >> 2, j = k & 3;
-          if (BIAS && j == 0 && i > 0) c_cur = c_nxt;
-          ev_tile(i, j, c_cur, evd[i][j]);
-        };
-        auto after0 = [&](int k) {
-          const int i = k >> 2, j = k & 3;
-          between0(k);
-          // stores of the pair staged in the previous slot
-          if ((k - 1) >> 2 == 1 || (k - 1) >> 2 == 3) unit_store((k - 1) & 3, (k - 1) >> 3);
-          if (i & 1) {
-            ev_unit_write(evd[i - 1][j], evd[i][j]);
-            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-            ev_unit_read(rd);
-            // the next pair's writes stay behind these reads
-            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            for (int i = 0; i < 4; ++i) ev_bias(prm, i, bq[i]);
           }
-          if (BIAS && j == 1 && i < 3) ev_bias(prm, i + 1, c_nxt);
-        };
-        mfma_step_x(cur, cur_sc, std::integral_constant<int, 0>{}, std::true_type{}, std::true_type{}, before0,
-                    after0);
-        const StageScales sc1 = cur_sc;
-        mfma_step_x(nxt, sc1, std::integral_constant<int, 1>{}, std::false_type{}, std::true_type{}, [](int) {},
-                    [&](int k) {
-                      between1(k);
-                      if (k == 0) unit_store(3, 1);
-                    });
+          uint4 rd[2];
+          uint32_t sbs = 0, sbs_done = 0;
+          auto group_store = [&](int j) {
+#pragma unroll
+            for (int it = 0; it < 2; ++it) {
+              const int row = m_q + 32 * j + 16 * it + (lane >> 2);
+              const uint32_t off = q_pan * 64u * (uint32_t)M + (uint32_t)row * 64u + (uint32_t)(lane & 3) * 16u;
+              buf_store16(rq, row < M ? (off | q_bad) : 0x80000000u, rd[it]);
+            }
+            const int srow = m_q + 32 * j + r;
+            const uint32_t soff = (q_pan * (uint32_t)M + (uint32_t)srow) * 4u;
+            buf_store4(rsq, g == 0 && srow < M ? (soff | q_bad) : 0x80000000u, sbs_done);
+          };
+          auto beforeq = [&](int sl) {
+            const int i = sl & 3, j = sl >> 2;
+            uint32_t pk[4][2];
+            ev_tile(i, j, bq[i], pk);
+            typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+            u16x2 m2 = {0, 0};
+#pragma unroll
+            for (int t2 = 0; t2 < 4; ++t2)
+#pragma unroll
+              for (int h = 0; h < 2; ++h)
+                m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, pk[t2][h] & 0x7FFF7FFFu));
+            uint32_t am = umax((uint32_t)m2.x, (uint32_t)m2.y);
+            const auto sw = __builtin_amdgcn_permlane32_swap(am, am, false, false);
+            am = umax(am, g ? (uint32_t)sw[0] : (uint32_t)sw[1]);
+            const uint32_t sb = mx_scale_byte(am);
+            const float scq = as_float(sb << 23);
+            uint32_t e0 = 0, e1 = 0;
+            e0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(e0, __builtin_bit_cast(bf16x2, pk[0][0]), scq, 0);
+            e0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(e0, __builtin_bit_cast(bf16x2, pk[0][1]), scq, 1);
+            e0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(e0, __builtin_bit_cast(bf16x2, pk[1][0]), scq, 2);
+            e0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(e0, __builtin_bit_cast(bf16x2, pk[1][1]), scq, 3);
+            e1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(e1, __builtin_bit_cast(bf16x2, pk[2][0]), scq, 0);
+            e1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(e1, __builtin_bit_cast(bf16x2, pk[2][1]), scq, 1);
+            e1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(e1, __builtin_bit_cast(bf16x2, pk[3][0]), scq, 2);
+            e1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(e1, __builtin_bit_cast(bf16x2, pk[3][1]), scq, 3);
+            // lane g = 0 holds code bytes 4t + {0, 1} (t = 0..3) of the row's 16
+            // bytes of tile i, lane g = 1 bytes 4t + {2, 3}: after the swap the
+            // lower lane has both halves' t = 0, 1 bytes, the upper lane t = 2, 3
+            const auto pq = __builtin_amdgcn_permlane32_swap(e0, e1, false, false);
+            const uint32_t wlo = __builtin_amdgcn_perm((uint32_t)pq[1], (uint32_t)pq[0], 0x05040100u);
+            const uint32_t whi = __builtin_amdgcn_perm((uint32_t)pq[1], (uint32_t)pq[0], 0x07060302u);
+            *reinterpret_cast<uint2*>(ev_region + r * QP + 16 * i + 8 * g) = make_uint2(wlo, whi);
+            sbs |= sb << (8 * i);
+          };
+          auto afterq = [&](int sl) {
+            between0(sl);
+            if (sl >= 4 && (sl & 3) == 0) group_store((sl >> 2) - 1);
+            if ((sl & 3) == 3) {
+              __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+#pragma unroll
+              for (int it = 0; it < 2; ++it)
+                rd[it] = *reinterpret_cast<const uint4*>(ev_region + (16 * it + (lane >> 2)) * QP + (lane & 3) * 16);
+              // the next group's writes stay behind these reads
+              __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+              sbs_done = sbs;
+              sbs = 0;
+            }
+          };
+          mfma_step_x(cur, cur_sc, std::integral_constant<int, 0>{}, std::true_type{}, std::true_type{},
+                      std::true_type{}, beforeq, afterq);
+          const StageScales sc1 = cur_sc;
+          mfma_step_x(nxt, sc1, std::integral_constant<int, 1>{}, std::false_type{}, std::true_type{},
+                      std::false_type{}, [](int) {}, [&](int k) {
+                        between1(k);
+                        if (k == 0) group_store(3);
+                      });
+        } else {
+          // byte offset of the lane's first store (+ 32 j rows + 8 it rows + 64 h
+          // columns); rows past M fall past the end of the output, which the
+          // range check drops, and columns past N (or no tile at all) get the
+          // offset's top bit, past every output of fewer than 2^31 bytes
+          const int ev_m0 = ptm * 256 + wm * 128 + (lane >> 3);
+          const int ev_n0 = ptn * 256 + wn * 128 + (lane & 7) * 8;
+          const uint32_t ev_off0 = ((uint32_t)ev_m0 * (uint32_t)N + (uint32_t)ev_n0) * 2u;
+          const uint32_t ev_bad0 = ev_live && ev_n0 < N ? 0u : 0x80000000u;
+          const uint32_t ev_bad1 = ev_live && ev_n0 + 64 < N ? 0u : 0x80000000u;
+          const uint32_t row8 = (uint32_t)N * 16u;  // 8 rows of bf16
+          // bias of the finished tile (zeros when there is none)
+          const uint8_t* prm = ring + PARAM_OFF + ((tile_k - 1) & 1) * PARAM_BYTES;
+          v16f c_cur, c_nxt;
+          if constexpr (BIAS) ev_bias(prm, 0, c_cur);
+          uint32_t evd[4][4][4][2];
+          uint4 rd[4];
+          auto unit_store = [&](int j, int h) {
+  #pragma unroll
+            for (int it = 0; it < 4; ++it)
+              buf_store16(ry, (ev_off0 + (uint32_t)(4 * j + it) * row8 + 128u * h) | (h ? ev_bad1 : ev_bad0), rd[it]);
+          };
+          auto before0 = [&](int k) {
+            const int i = k >> 2, j = k & 3;
+            if (BIAS && j == 0 && i > 0) c_cur = c_nxt;
+            ev_tile(i, j, c_cur, evd[i][j]);
+          };
+          auto after0 = [&](int k) {
+            const int i = k >> 2, j = k & 3;
+            between0(k);
+            // stores of the pair staged in the previous slot
+            if ((k - 1) >> 2 == 1 || (k - 1) >> 2 == 3) unit_store((k - 1) & 3, (k - 1) >> 3);
+            if (i & 1) {
+              ev_unit_write(evd[i - 1][j], evd[i][j]);
+              __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+              ev_unit_read(rd);
+              // the next pair's writes stay behind these reads
+              __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            }
+            if (BIAS && j == 1 && i < 3) ev_bias(prm, i + 1, c_nxt);
+          };
+          mfma_step_x(cur, cur_sc, std::integral_constant<int, 0>{}, std::true_type{}, std::true_type{},
+                      std::false_type{}, before0, after0);
+          const StageScales sc1 = cur_sc;
+          mfma_step_x(nxt, sc1, std::integral_constant<int, 1>{}, std::false_type{}, std::true_type{},
+                      std::false_type{}, [](int) {}, [&](int k) {
+                        between1(k);
+                        if (k == 0) unit_store(3, 1);
+                      });
+        }
         // parameters of the next tile go into the block just read: wait for those reads
         __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
         issue_params(tile_k + 1);
@@ -1044,9 +1156,10 @@ static int device_cu_count() {
   return cus;
 }
 
-template <int MODE, int KT, int NB>
+template <int MODE, int KT, int NB, bool QOUT = false>
 static hipError_t launch_pipe(const void* aq, const void* as, const void* wq, const void* ws, const void* bias,
-                              int epi, void* y, int64_t M, int64_t N, int64_t K, hipStream_t s) {
+                              int epi, void* y, int64_t M, int64_t N, int64_t K, hipStream_t s,
+                              void* y_scales = nullptr) {
   static const int cus = device_cu_count();
   const int tiles_m = (int)((M + 255) / 256);
   const int tiles_n = (int)((N + 255) / 256);
@@ -1055,11 +1168,11 @@ static hipError_t launch_pipe(const void* aq, const void* as, const void* wq, co
   // GELU and bias are kernel parameters, so that each kernel carries only
   // the epilogue work it does
   auto go = [&](auto gelu_tag, auto bias_tag) {
-    hipLaunchKernelGGL((gemm_pipe_kernel<MODE, KT, NB, decltype(gelu_tag)::value, decltype(bias_tag)::value>),
+    hipLaunchKernelGGL((gemm_pipe_kernel<MODE, KT, NB, decltype(gelu_tag)::value, decltype(bias_tag)::value, QOUT>),
                        dim3(grid), dim3(256), 0, s, static_cast<const uint8_t*>(wq),
                        static_cast<const uint8_t*>(ws), static_cast<const uint8_t*>(aq), as,
-                       static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y), (int)M, (int)N, (int)K, tiles_m,
-                       tiles_n);
+                       static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y),
+                       static_cast<uint8_t*>(y_scales), (int)M, (int)N, (int)K, tiles_m, tiles_n);
   };
   if (epi == 1) {
     if (bias != nullptr) go(std::true_type{}, std::true_type{});
@@ -1112,6 +1225,15 @@ hipError_t launch_gemm(int mode, const void* a_codes, const void* a_scales,
   if (mode == 0)
     return launch_direct<0, 2, 2>(a_codes, a_scales, w_codes, w_scales, bias, epilogue, y, M, N, K, s);
   return launch_direct<1, 2, 2>(a_codes, a_scales, w_codes, w_scales, bias, epilogue, y, M, N, K, s);
+}
+
+bool gemm_mxfp4_out_supported(int64_t M, int64_t N, int64_t K) { return use_lds(0, M, N, K) && N % 128 == 0; }
+
+hipError_t launch_gemm_mxfp4_out(const void* a_codes, const void* a_scales, const void* w_codes,
+                                 const void* w_scales, const void* bias, int epilogue, void* y_codes,
+                                 void* y_scales, int64_t M, int64_t N, int64_t K, hipStream_t s) {
+  return launch_pipe<0, kPipeKT[0], kPipeNB[0], true>(a_codes, a_scales, w_codes, w_scales, bias, epilogue, y_codes,
+                                                      M, N, K, s, y_scales);
 }
 
 const char* gemm_variant_name(int mode, int64_t M, int64_t N, int64_t K) {

@@ -19,6 +19,14 @@ hipError_t launch_gemm(int mode, const void* a_codes, const void* a_scales,
                        int epilogue, void* y, int64_t M, int64_t N, int64_t K,
                        hipStream_t s);
 
+// W4A4 GEMM whose bf16 output goes straight into the MXFP4 activation
+// format (codes in code panels along N, scales [N/128][M][4]); only for shapes
+// where gemm_mxfp4_out_supported holds.
+bool gemm_mxfp4_out_supported(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_mxfp4_out(const void* a_codes, const void* a_scales, const void* w_codes,
+                                 const void* w_scales, const void* bias, int epilogue, void* y_codes,
+                                 void* y_scales, int64_t M, int64_t N, int64_t K, hipStream_t s);
+
 // Name of the GEMM kernel variant launch_gemm picks for a shape (for logs).
 const char* gemm_variant_name(int mode, int64_t M, int64_t N, int64_t K);
 

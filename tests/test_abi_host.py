@@ -25,7 +25,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = mxq.lib()
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(mxq._SIGS)
@@ -85,6 +85,37 @@ def test_weight_pack_and_gemm_validation():
     empty[7] = 0
     empty[0] = None
     assert L.mxq_gemm(mxq.W4A8, *empty) == mxq.OK
+
+
+def test_gemm_mxfp4_out_validation():
+    """Host-side checks of the fused GEMM -> MXFP4 entry point (nothing is enqueued)."""
+    L = mxq.lib()
+    S = None
+    # a0 as0 w0 ws0 bias epi yc ys M N K stream
+    ok = [FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, FAKE, 512, 1024, 1024, S]
+    bad_epi = list(ok)
+    bad_epi[5] = 2
+    assert L.mxq_gemm_mxfp4_out(*bad_epi) == mxq.ERR_MODE
+    bad_k = list(ok)
+    bad_k[10] = 100
+    assert L.mxq_gemm_mxfp4_out(*bad_k) == mxq.ERR_SHAPE
+    # shapes the pipelined kernel does not take, or N not a multiple of 128
+    for m, n, k in [(255, 1024, 1024), (512, 1024, 384), (512, 1000, 1024), (512, 1088, 1024)]:
+        args = list(ok)
+        args[8:11] = [m, n, k]
+        assert L.mxq_gemm_mxfp4_out(*args) == mxq.ERR_SHAPE, (m, n, k)
+    for pos in (0, 1, 2, 3, 6, 7):
+        args = list(ok)
+        args[pos] = None
+        assert L.mxq_gemm_mxfp4_out(*args) == mxq.ERR_NULL, pos
+    for pos in (0, 4, 6, 7):
+        args = list(ok)
+        args[pos] = FAKE_ODD
+        assert L.mxq_gemm_mxfp4_out(*args) == mxq.ERR_ALIGN, pos
+    empty = list(ok)
+    empty[8] = 0
+    empty[0] = empty[6] = empty[7] = None
+    assert L.mxq_gemm_mxfp4_out(*empty) == mxq.OK
 
 
 def test_policy_table_roundtrip_and_errors():
