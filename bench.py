@@ -163,9 +163,10 @@ class Stack:
 
 
 # the pipelined GEMM's symbol per mode, as the profile summaries write it
-# (template arguments: mode, K elements per stage, ring depth, GELU; no
-# spaces): each mode has a plain and a GELU instance, and the roofline covers both
-KERNEL_SYMBOL = {0: "gemm_pipe_kernel<0,128,4,{false,true}>", 1: "gemm_pipe_kernel<1,128,3,{false,true}>"}
+# (template arguments: mode, K elements per stage, ring depth, GELU, bias,
+# MXFP4 output; no spaces): each mode has several instances, and the
+# roofline covers all of them
+KERNEL_SYMBOL = {0: "gemm_pipe_kernel<0,128,4,*>", 1: "gemm_pipe_kernel<1,128,3,*>"}
 KERNEL_PREFIX = {0: "gemm_pipe_kernel<0,128,4,", 1: "gemm_pipe_kernel<1,128,3,"}
 
 
@@ -175,7 +176,7 @@ def profiled_traffic(workload_tag, mode):
     profiles/hbm_traffic_<workload>.txt holds calibrated FETCH_SIZE + WRITE_SIZE
     bytes per dispatch and the sha1 of the GEMM source they were taken on; a
     different source means the numbers describe another kernel: None. The
-    plain and GELU instances are averaged, weighted by their dispatch counts.
+    instances of a mode are averaged, weighted by their dispatch counts.
     """
     import hashlib
 
