@@ -15,7 +15,8 @@ quantize-dequantize emulation):
                  rounding), the E2M1 / E4M3FN / E8M0 code tables and a
                  generic round-to-nearest-even into a small binary float format.
 * ``quant``    - MXFP4 block quantizer (one E8M0 scale per 32 elements along K)
-                 and FP8 E4M3FN per-token quantizer (scale = row amax / 448).
+                 and FP8 E4M3FN quantizers: per-token (scale = row amax / 448)
+                 and static (one calibrated scale per tensor, saturating).
 * ``linear``   - dequantize-then-fp64 matmul (the QDQ result), tanh-GELU, the
                  per-block policy lookup and the output tolerance check.
 
@@ -45,6 +46,9 @@ from .quant import (
     fp8_dequantize_per_token,
     fp8_per_token_scale,
     fp8_scaled_quotient,
+    fp8_calibration_amax,
+    fp8_static_scale,
+    fp8_quantize_static,
     unpack_nibbles,
 )
 from .linear import (

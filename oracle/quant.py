@@ -21,6 +21,18 @@ m with largest magnitude amax_m:
     code = E4M3FN RNE of fp32(x / s_m), saturating at 448 (two roundings:
            the fp32 quotient first, then E4M3FN)
     an all-zero row has s_m = 0 and every code is a signed zero.
+
+FP8 static (the same page's format table names the W4A8 activations FP8 E4M3
+"static"; its experimental setup runs a calibration set through the model).
+One scale per activation tensor, fixed before inference from the largest
+magnitude seen on calibration data:
+
+    amax = max |x| over every calibration batch of the tensor (fp32)
+    s    = fp32(amax) / fp32(448)
+    code = E4M3FN RNE of fp32(x / s), saturating at +-448: unlike the
+           per-token scale, a static one can be exceeded at run time
+    s = 0 (all-zero calibration data) gives signed-zero codes, as a zero row
+    does per token.
 """
 
 import numpy as np
@@ -99,7 +111,7 @@ def fp8_scaled_quotient(x32, s):
     """IEEE fp32 quotients x / s_m (signed zeros for rows whose scale is 0)."""
     x32 = np.asarray(x32, dtype=np.float32)
     s = np.asarray(s, dtype=np.float32)
-    with np.errstate(divide="ignore", invalid="ignore"):
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
         r = (x32 / s[:, None]).astype(np.float32)
     zero_row = (s == 0)[:, None]
     return np.where(zero_row, np.copysign(np.float32(0.0), x32), r).astype(np.float32)
@@ -119,3 +131,35 @@ def fp8_dequantize_per_token(codes, scales):
     """E4M3FN codes [M, K] + float32 scales [M] -> float64 [M, K]."""
     vals = e4m3fn_decode(codes)
     return vals * np.asarray(scales, dtype=np.float32).astype(np.float64)[:, None]
+
+
+def fp8_calibration_amax(batches):
+    """Largest magnitude over calibration batches of bf16 [M, K] (uint16 bits), as float32.
+
+    Every bf16 magnitude is exact in float32, so the result is one of the inputs'
+    magnitudes (0 when there is none)."""
+    amax = np.float32(0.0)
+    for b in batches:
+        x32 = bf16_bits_to_f32(_check_rows(b))
+        if x32.size:
+            amax = max(amax, np.float32(np.abs(x32).max()))
+    return np.float32(amax)
+
+
+def fp8_static_scale(amax):
+    """Static per-tensor scale s = fp32(amax) / fp32(448)."""
+    return np.float32(np.float32(amax) / np.float32(448.0))
+
+
+def fp8_quantize_static(x_bits, amax):
+    """bf16 [M, K] (uint16 bits) and a calibrated amax -> (codes uint8 [M, K], scales float32 [M]).
+
+    Every row takes the same scale s = amax / 448, so the scale vector is s
+    repeated; quotients beyond 448 (and infinite ones, from a tiny s) saturate
+    in the E4M3FN encoder."""
+    x_bits = _check_rows(x_bits)
+    x32 = bf16_bits_to_f32(x_bits)
+    s = np.full(x32.shape[0], fp8_static_scale(amax), np.float32)
+    r = fp8_scaled_quotient(x32, s)
+    codes = e4m3fn_encode(r.astype(np.float64))
+    return codes, s

@@ -244,3 +244,101 @@ def test_fp8_quotient_is_correctly_rounded_division():
                 assert err <= abs(Fraction(float(nb)) - exact), (i, j)
             recip_differs += int(np.float32(x32[i, j] * (np.float32(1) / s[i])) != q)
     assert recip_differs > 0  # the sample does separate the two forms
+
+
+# ----------------------------------------------------------- FP8 static ----
+
+def _static_golden():
+    groups, cur = [], None
+    for row in golden_lines("fp8_static.txt"):
+        if row[0] == "amax":
+            cur = {"amax": int(row[1], 16), "scale": None if row[3] == "-" else float(row[3]), "elems": []}
+            groups.append(cur)
+        else:
+            cur["elems"].append((int(row[0], 16), int(row[1], 16)))
+    return groups
+
+
+def test_fp8_static_golden():
+    groups = _static_golden()
+    assert len(groups) == 6
+    for gr in groups:
+        amax = oracle.bf16_bits_to_f32(np.array([gr["amax"]], np.uint16))[0]
+        x = np.zeros((1, 32), np.uint16)
+        for i, (b, _) in enumerate(gr["elems"]):
+            x[0, i] = b
+        codes, scales = oracle.fp8_quantize_static(x, amax)
+        if gr["scale"] is not None:
+            assert scales[0] == np.float32(gr["scale"])
+        for i, (b, c) in enumerate(gr["elems"]):
+            assert codes[0, i] == c, (hex(gr["amax"]), hex(b), hex(codes[0, i]), hex(c))
+
+
+def test_fp8_static_equals_per_token_when_every_row_has_the_amax():
+    """Rows whose own amax is the calibrated one: the static rule is the per-token rule."""
+    g = np.random.default_rng(31)
+    x = g.standard_normal((40, 256)) * 2.0
+    x[:, 0] = 9.0
+    x[1::2, 0] = -9.0  # the amax may come with either sign
+    bits = _bits_from_f64(np.clip(x, -9.0, 9.0))
+    c_tok, s_tok = oracle.fp8_quantize_per_token(bits)
+    c_st, s_st = oracle.fp8_quantize_static(bits, np.float32(9.0))
+    assert np.array_equal(s_tok, s_st) and np.array_equal(c_tok, c_st)
+
+
+def test_fp8_static_matches_torch_below_saturation():
+    """Independent route: torch fp32 division and torch's E4M3FN cast where |x / s| < 464,
+    and the saturated code where it is not (torch's cast turns those into NaN)."""
+    g = np.random.default_rng(32)
+    x = (g.standard_normal((48, 512)) * np.ldexp(1.0, g.integers(-20, 20, (48, 1)))).astype(np.float32)
+    bits = _bits_from_f64(x)
+    xt = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float32)
+    for frac in (1.0, 0.3, 1e-3, 7.5):
+        amax = np.float32(float(xt.abs().max()) * frac)
+        codes, scales = oracle.fp8_quantize_static(bits, amax)
+        s = torch.tensor(amax, dtype=torch.float32) / torch.tensor(448.0, dtype=torch.float32)
+        assert np.all(scales == s.numpy())
+        q = xt / s
+        small = q.abs() < 464
+        want = q.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        sat = np.where(np.signbit(q.numpy()), 0xFE, 0x7E).astype(np.uint8)
+        want = np.where(small.numpy(), want, sat)
+        assert np.array_equal(codes, want), frac
+        if frac < 1:
+            assert np.count_nonzero(~small.numpy()) > 0  # saturation is exercised
+
+
+def test_fp8_static_monotone_and_saturating_over_all_bf16():
+    """Over every finite bf16 x (one amax), the decoded code is a non-decreasing
+    function of x, odd, at most 448, and 448 exactly from x / s >= 432 on."""
+    pos = np.arange(0, 0x7F80, dtype=np.uint32).astype(np.uint16)
+    bits = np.concatenate([pos, pos | 0x8000]).reshape(-1, 32)
+    amax = np.float32(3.296875)  # a bf16 value that is no power of two
+    codes, s = oracle.fp8_quantize_static(bits, amax)
+    codes = codes.reshape(-1)
+    x = oracle.bf16_bits_to_f64(bits.reshape(-1))
+    v = oracle.e4m3fn_decode(codes)
+    n = len(pos)
+    assert np.all(np.diff(v[:n]) >= 0)                      # positive half, increasing x
+    assert np.array_equal(v[n:], -v[:n])                    # sign symmetry
+    assert np.abs(v).max() == 448.0
+    ratio = x[:n] / float(s[0])
+    assert np.all(v[:n][ratio >= 432] == 448.0) and np.all(v[:n][ratio < 431] < 448.0)
+
+
+def test_fp8_calibration_amax_brute_force():
+    vals = [[1.0, -3.0, 0.5], [2.5, -0.25], [-3.25, 0.0]]
+    batches = []
+    for row in vals:
+        x = np.zeros((2, 32), np.float64)
+        x[1, : len(row)] = row
+        batches.append(_bits_from_f64(x))
+    want = max(abs(v) for row in vals for v in row)
+    assert oracle.fp8_calibration_amax(batches) == np.float32(want) == np.float32(3.25)
+    assert oracle.fp8_calibration_amax(batches[:2]) == np.float32(3.0)
+    assert oracle.fp8_calibration_amax([]) == 0.0
+    assert oracle.fp8_calibration_amax([np.zeros((3, 64), np.uint16)]) == 0.0
+    # the order of the batches does not matter, and -0 counts as 0
+    assert oracle.fp8_calibration_amax(batches[::-1]) == np.float32(3.25)
+    neg0 = np.full((1, 32), 0x8000, np.uint16)
+    assert oracle.fp8_calibration_amax([neg0]) == 0.0
