@@ -132,6 +132,36 @@ int mxq_quantize_act(int mode, const void* x, int64_t M, int64_t K, int64_t ldx,
                      void* codes, void* scales, hipStream_t stream);
 
 /*
+ * Calibration for static FP8 activations. The page's format table calls the
+ * W4A8 activations FP8 E4M3 "static", and its experimental setup runs a
+ * calibration set (prompts x denoising steps) through the model: a static
+ * scale is fixed from the largest activation magnitude seen there. This call
+ * folds one calibration batch into a running maximum:
+ *   *amax = max(*amax, max |x|)   over x [M][K] (bf16 [M][ldx], device)
+ *   amax   device float32, one value; the caller sets it to 0 before the
+ *          first batch and may call this any number of times (in any
+ *          order: the result depends only on the set of batches). It is
+ *          always the magnitude of one input element, exactly.
+ * Finite inputs only (a NaN or infinity makes the result unspecified).
+ */
+int mxq_fp8_calibrate(const void* x, int64_t M, int64_t K, int64_t ldx, float* amax, hipStream_t stream);
+
+/*
+ * Static FP8 activation quantization (W4A8 with a calibrated per-tensor
+ * scale): s = fp32(*amax) / 448 (IEEE), code = E4M3FN round-half-to-even of
+ * the IEEE fp32 quotient x / s, saturating at +-448 (values past the
+ * calibrated range clamp); *amax == 0 gives s = 0 and signed-zero codes.
+ *   x       device, bf16 [M][ldx]
+ *   amax    device float32 (e.g. from mxq_fp8_calibrate), finite, >= 0; read
+ *           by the kernel, so it may be produced earlier on the same stream
+ *   codes   device uint8 [M][K] E4M3FN (output)
+ *   scales  device float32 [M] (output): s in every row, so the pair feeds
+ *           mxq_gemm(MXQ_W4A8, ...) exactly as per-token activations do
+ */
+int mxq_quantize_act_fp8_static(const void* x, int64_t M, int64_t K, int64_t ldx, const float* amax,
+                                void* codes, void* scales, hipStream_t stream);
+
+/*
  * Scaled GEMM on quantized operands (the native MXFP4 / W4A8 execution of
  * "Quantization formats", kernel note): y [M][N] bf16 =
  *   epilogue( sum_k deqA[m][k] deqW[n][k] + bias[n] ).

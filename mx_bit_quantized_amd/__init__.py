@@ -38,6 +38,8 @@ _SIGS = {
     "mxq_version": (ctypes.c_int, []),
     "mxq_quantize_weight_mxfp4": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "mxq_quantize_act": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, _I64, _P, _P, _P]),
+    "mxq_fp8_calibrate": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P]),
+    "mxq_quantize_act_fp8_static": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "mxq_gemm": (ctypes.c_int, [ctypes.c_int, _P, _P, _P, _P, _P, ctypes.c_int, _P, _I64, _I64, _I64, _P]),
     "mxq_gemm_mxfp4_out": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int, _P, _P, _I64, _I64, _I64, _P]),
     "mxq_gemm_kernel_name": (ctypes.c_char_p, [ctypes.c_int, _I64, _I64, _I64]),
@@ -169,6 +171,31 @@ def quantize_act(mode, x, codes=None, scales=None, stream=None):
     st = lib().mxq_quantize_act(int(mode), _dev_ptr(x, "x", torch.bfloat16), m, k, k,
                                  _dev_ptr(codes, "codes"), _dev_ptr(scales, "scales"), _stream_handle(stream))
     _check(st, "quantize_act")
+    return codes, scales
+
+
+def fp8_calibrate(x, amax=None, stream=None):
+    """Fold bf16 x [M, K] into a running amax (device float32 [1], created as 0 when None) -> amax."""
+    torch = _torch()
+    m, k = _rows_k(x, "x")
+    if amax is None:
+        amax = torch.zeros((1,), dtype=torch.float32, device=x.device)
+    st = lib().mxq_fp8_calibrate(_dev_ptr(x, "x", torch.bfloat16), m, k, k, _dev_ptr(amax, "amax", torch.float32),
+                                  _stream_handle(stream))
+    _check(st, "fp8_calibrate")
+    return amax
+
+
+def quantize_act_fp8_static(x, amax, codes=None, scales=None, stream=None):
+    """Static FP8 quantization of bf16 x [M, K] with the calibrated amax (device float32 [1]) -> (codes, scales)."""
+    torch = _torch()
+    m, k = _rows_k(x, "x")
+    if codes is None or scales is None:
+        codes, scales = act_buffers(W4A8, m, k, x.device)
+    st = lib().mxq_quantize_act_fp8_static(_dev_ptr(x, "x", torch.bfloat16), m, k, k,
+                                            _dev_ptr(amax, "amax", torch.float32), _dev_ptr(codes, "codes"),
+                                            _dev_ptr(scales, "scales"), _stream_handle(stream))
+    _check(st, "quantize_act_fp8_static")
     return codes, scales
 
 

@@ -102,6 +102,29 @@ int mxq_quantize_act(int mode, const void* x, int64_t M, int64_t K, int64_t ldx,
   return hip_status(mxq::launch_fp8_quant(x, M, K, ldx, codes, scales, stream));
 }
 
+int mxq_fp8_calibrate(const void* x, int64_t M, int64_t K, int64_t ldx, float* amax, hipStream_t stream) {
+  int st = check_mk(M, K, ldx);
+  if (st != MXQ_OK) return st;
+  if (M == 0) return MXQ_OK;
+  if (x == nullptr || amax == nullptr) return MXQ_ERR_NULL;
+  if (!aligned16(x) || ldx % 8 != 0 || (reinterpret_cast<uintptr_t>(amax) & 3u) != 0) return MXQ_ERR_ALIGN;
+  if (log_enabled()) fprintf(stderr, "[mxq] fp8_calibrate M=%lld K=%lld\n", (long long)M, (long long)K);
+  return hip_status(mxq::launch_fp8_amax(x, M, K, ldx, amax, stream));
+}
+
+int mxq_quantize_act_fp8_static(const void* x, int64_t M, int64_t K, int64_t ldx, const float* amax,
+                                void* codes, void* scales, hipStream_t stream) {
+  int st = check_mk(M, K, ldx);
+  if (st != MXQ_OK) return st;
+  if (M == 0) return MXQ_OK;
+  if (x == nullptr || amax == nullptr || codes == nullptr || scales == nullptr) return MXQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(codes) || !aligned16(scales) || ldx % 8 != 0 ||
+      (reinterpret_cast<uintptr_t>(amax) & 3u) != 0)
+    return MXQ_ERR_ALIGN;
+  if (log_enabled()) fprintf(stderr, "[mxq] quantize_act fp8_static M=%lld K=%lld\n", (long long)M, (long long)K);
+  return hip_status(mxq::launch_fp8_static_quant(x, M, K, ldx, amax, codes, scales, stream));
+}
+
 int mxq_gemm(int mode, const void* a_codes, const void* a_scales,
              const void* w_codes, const void* w_scales, const void* bias,
              int epilogue, void* y, int64_t M, int64_t N, int64_t K,

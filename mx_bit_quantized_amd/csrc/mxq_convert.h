@@ -109,21 +109,26 @@ MXQ_HD uint32_t e4m3fn_code(float q) {
 // rounding, unchanged. The host build of this code is compared with IEEE
 // division for every bf16 amax and every bf16 x of its row.
 struct Fp8Row {
-  float s;       // the stored per-token scale fp32(amax) / 448
+  float s;       // the stored scale fp32(amax) / 448
   float pre;     // 1, or 2^64 when s < 2^-64
   float ss;      // s * pre
   float y;       // RN(1 / ss)
+  float hi;      // RN(448 ss): the static quotient's clamp (see below)
 };
 
-MXQ_HD Fp8Row fp8_row_setup(uint32_t amax_mag_bits) {
+// Setup from an fp32 amax: a row's bf16 amax (exact in fp32) for per-token
+// scales, or a calibrated amax for a static one.
+MXQ_HD Fp8Row fp8_scale_setup(float amax) {
   Fp8Row r;
-  float amax = as_float(amax_mag_bits << 16);
   r.s = amax / 448.0f;
   r.pre = r.s < 5.42101086242752217e-20f ? 18446744073709551616.0f : 1.0f;  // 2^-64, 2^64
   r.ss = r.s * r.pre;
   r.y = 1.0f / r.ss;
+  r.hi = 448.0f * r.ss;
   return r;
 }
+
+MXQ_HD Fp8Row fp8_row_setup(uint32_t amax_mag_bits) { return fp8_scale_setup(as_float(amax_mag_bits << 16)); }
 
 MXQ_HD float fp8_quotient(float x, const Fp8Row& r) {
   float xs = x * r.pre;
@@ -140,6 +145,29 @@ MXQ_HD uint32_t fp8_code_bf16(uint32_t bits16, const Fp8Row& r) {
   const uint32_t sign = (bits16 >> 8) & 0x80u;
   if (r.s == 0.0f) return sign;
   return e4m3fn_code(fp8_quotient(as_float((bits16 & 0x7FFFu) << 16), r)) | sign;
+}
+
+// Static (per-tensor) scale: x may exceed the calibrated amax, and quotients
+// beyond 448 saturate. The pre-scaled |x| is first clamped at hi = RN(448 ss)
+// (an overflow of |x| * 2^64 to infinity clamps too): below hi nothing
+// changes, so the quotient is the IEEE one and at most hi / ss < 448 (1 + 2^-23);
+// at or above hi the true quotient is at least 448 (1 - 2^-24), above E4M3FN's
+// last rounding boundary 432, and so is that of hi itself. Either way the code
+// is the saturating RNE code of the IEEE quotient, and every quotient handed
+// to the conversion stays within the range where the hardware conversion is
+// exact (|q| <= 464).
+MXQ_HD float fp8_static_quotient(float x_abs, const Fp8Row& r) {
+  float xs = fminf(x_abs * r.pre, r.hi);
+  float q0 = xs * r.y;
+  float rem = __builtin_fmaf(-q0, r.ss, xs);
+  return __builtin_fmaf(rem, r.y, q0);
+}
+
+// E4M3FN code of a bf16 element under a static scale (s == 0: signed zero).
+MXQ_HD uint32_t fp8_static_code_bf16(uint32_t bits16, const Fp8Row& r) {
+  const uint32_t sign = (bits16 >> 8) & 0x80u;
+  if (r.s == 0.0f) return sign;
+  return e4m3fn_code(fp8_static_quotient(as_float((bits16 & 0x7FFFu) << 16), r)) | sign;
 }
 
 // --------------------------------------------------------------- bf16 -----

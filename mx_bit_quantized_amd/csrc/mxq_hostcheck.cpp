@@ -89,6 +89,49 @@ void mxq_host_fp8_division_sweep(int32_t amax_lo, int32_t amax_hi, int64_t* pair
   *code_mismatch = nc;
 }
 
+// Static scales: for each fp32 amax in the list and every finite bf16 x (both
+// signs), compare the kernel code with the saturating E4M3FN code of the IEEE
+// quotient x / s (infinite quotients included), and the kernel quotient with
+// the IEEE one wherever |x / s| lies in [2^-10, 448].
+void mxq_host_fp8_static_sweep(const float* amax, int64_t n_amax, int64_t* pairs, int64_t* quotient_mismatch,
+                               int64_t* code_mismatch) {
+  int64_t np = 0, nq = 0, nc = 0;
+  for (int64_t i = 0; i < n_amax; ++i) {
+    const Fp8Row row = fp8_scale_setup(amax[i]);
+    for (uint32_t m = 0; m < 0x7F80u; ++m) {
+      for (int sgn = 0; sgn < 2; ++sgn) {
+        const uint32_t bits = m | (sgn ? 0x8000u : 0u);
+        const float x = as_float(bits << 16);
+        const uint32_t sign = sgn ? 0x80u : 0u;
+        uint32_t want;
+        if (row.s == 0.0f) {
+          want = sign;
+        } else {
+          const float ref = fabsf(x) / row.s;
+          want = e4m3fn_code(ref) | sign;
+          if (ref >= 0.0009765625f && ref <= 448.0f &&
+              as_uint(ref) != as_uint(fp8_static_quotient(fabsf(x), row)))
+            ++nq;
+        }
+        ++np;
+        if (want != fp8_static_code_bf16(bits, row)) ++nc;
+      }
+    }
+  }
+  *pairs = np;
+  *quotient_mismatch = nq;
+  *code_mismatch = nc;
+}
+
+void mxq_host_fp8_quantize_static(const uint16_t* x, int64_t rows, int64_t K, float amax, uint8_t* codes,
+                                  float* scales) {
+  const Fp8Row row = fp8_scale_setup(amax);
+  for (int64_t r = 0; r < rows; ++r) {
+    for (int64_t i = 0; i < K; ++i) codes[r * K + i] = (uint8_t)fp8_static_code_bf16(x[r * K + i], row);
+    scales[r] = row.s;
+  }
+}
+
 void mxq_host_bf16_rne(const float* f, int64_t n, uint16_t* out) {
   for (int64_t i = 0; i < n; ++i) out[i] = (uint16_t)bf16_rne(f[i]);
 }

@@ -13,6 +13,14 @@ hipError_t launch_mxfp4_quant(const void* x, int64_t rows, int64_t K, int64_t ld
 hipError_t launch_fp8_quant(const void* x, int64_t rows, int64_t K, int64_t ld,
                             void* codes, void* scales, hipStream_t s);
 
+// Static FP8: codes with the one scale amax / 448 (amax: device fp32), every
+// row's scale slot set to it.
+hipError_t launch_fp8_static_quant(const void* x, int64_t rows, int64_t K, int64_t ld, const float* amax,
+                                   void* codes, void* scales, hipStream_t s);
+
+// *amax = max(*amax, max |x|) over a [rows, K] bf16 matrix (device fp32, >= 0).
+hipError_t launch_fp8_amax(const void* x, int64_t rows, int64_t K, int64_t ld, float* amax, hipStream_t s);
+
 // y[M][N] = epilogue(A * W^T + bias); mode 0 = W4A4, 1 = W4A8.
 hipError_t launch_gemm(int mode, const void* a_codes, const void* a_scales,
                        const void* w_codes, const void* w_scales, const void* bias,

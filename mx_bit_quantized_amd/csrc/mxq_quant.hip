@@ -213,6 +213,107 @@ __global__ __launch_bounds__(64 * kQuantWaves) void fp8_quant_kernel(
   }
 }
 
+// ------------------------------------------------------ FP8 static -------
+//
+// Static (per-tensor) FP8: one scale s = amax / 448 for the whole tensor,
+// from an amax gathered beforehand over calibration data. The quantizer needs
+// no reduction: each lane turns 8 elements (16 bytes read) into 8 codes (8
+// bytes written), and every row's scale slot gets s, so the W4A8 GEMM takes
+// the result as it takes per-token activations. Quotients beyond 448
+// saturate (a static scale can be exceeded at run time).
+
+__device__ __forceinline__ float fp8_static_signed_quotient(uint32_t bits16, const Fp8Row& r) {
+  const float q = r.s == 0.0f ? 0.0f : fp8_static_quotient(as_float((bits16 & 0x7FFFu) << 16), r);
+  return as_float(as_uint(q) | ((bits16 & 0x8000u) << 16));
+}
+
+__device__ __forceinline__ uint2 pack8_fp8_static(const uint4 c, const Fp8Row& r) {
+  const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+  uint32_t out[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const float q0 = fp8_static_signed_quotient(w[2 * i] & 0xFFFFu, r);
+    const float q1 = fp8_static_signed_quotient(w[2 * i] >> 16, r);
+    const float q2 = fp8_static_signed_quotient(w[2 * i + 1] & 0xFFFFu, r);
+    const float q3 = fp8_static_signed_quotient(w[2 * i + 1] >> 16, r);
+    uint32_t o = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
+    o = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, (int)o, true);
+    out[i] = o;
+  }
+  return make_uint2(out[0], out[1]);
+}
+
+constexpr int kStaticUnroll = 4;  // 16-byte loads in flight per lane
+
+// One wave per row (rows loop beyond the grid); lanes walk the row's 8-element
+// chunks, kStaticUnroll loads ahead of the conversions.
+__global__ __launch_bounds__(64 * kQuantWaves) void fp8_static_quant_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t K, int64_t ld, const float* __restrict__ amax,
+    uint8_t* __restrict__ codes, float* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int64_t wave_id = (int64_t)blockIdx.x * kQuantWaves + (threadIdx.x >> 6);
+  const int64_t n_waves = (int64_t)gridDim.x * kQuantWaves;
+  const int64_t chunks = K >> 3;
+  const Fp8Row r = fp8_scale_setup(*amax);
+  for (int64_t row = wave_id; row < rows; row += n_waves) {
+    const uint4* src = reinterpret_cast<const uint4*>(x + row * ld);
+    uint2* dst = reinterpret_cast<uint2*>(codes + row * K);
+    for (int64_t c0 = lane; c0 < chunks; c0 += 64 * kStaticUnroll) {
+      uint4 v[kStaticUnroll];
+#pragma unroll
+      for (int i = 0; i < kStaticUnroll; ++i) {
+        const int64_t c = c0 + 64 * i;
+        v[i] = c < chunks ? src[c] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < kStaticUnroll; ++i) {
+        const int64_t c = c0 + 64 * i;
+        if (c < chunks) dst[c] = pack8_fp8_static(v[i], r);
+      }
+    }
+    if (lane == 0) scales[row] = r.s;
+  }
+}
+
+// Calibration: largest |x| of a [rows, K] bf16 matrix, folded into a running
+// maximum. Magnitude bit patterns order like the values (finite inputs), and
+// a bf16 pattern shifted left by 16 is the fp32 pattern of the same value, so
+// the running maximum is an fp32 updated with an unsigned atomic max (max is
+// order-free: the result does not depend on the schedule). Each wave keeps a
+// maximum over its rows; one atomic per workgroup.
+__global__ __launch_bounds__(64 * kQuantWaves) void fp8_amax_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t K, int64_t ld, uint32_t* __restrict__ amax_bits) {
+  __shared__ uint32_t wave_max_lds[kQuantWaves];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int64_t wave_id = (int64_t)blockIdx.x * kQuantWaves + wave;
+  const int64_t n_waves = (int64_t)gridDim.x * kQuantWaves;
+  const int64_t chunks = K >> 3;
+  uint32_t m = 0;
+  for (int64_t row = wave_id; row < rows; row += n_waves) {
+    const uint4* src = reinterpret_cast<const uint4*>(x + row * ld);
+    for (int64_t c0 = lane; c0 < chunks; c0 += 64 * kStaticUnroll) {
+      uint4 v[kStaticUnroll];
+#pragma unroll
+      for (int i = 0; i < kStaticUnroll; ++i) {
+        const int64_t c = c0 + 64 * i;
+        v[i] = c < chunks ? src[c] : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < kStaticUnroll; ++i) m = umax(m, chunk_amax(v[i]));
+    }
+  }
+  m = wave_max(m);
+  if (lane == 0) wave_max_lds[wave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t b = wave_max_lds[0];
+#pragma unroll
+    for (int w = 1; w < kQuantWaves; ++w) b = umax(b, wave_max_lds[w]);
+    if (b != 0) atomicMax(amax_bits, b << 16);
+  }
+}
+
 // ------------------------------------------------------------ launch ------
 
 static int grid_for_rows(int64_t rows) {
@@ -248,6 +349,30 @@ hipError_t launch_fp8_quant(const void* x, int64_t rows, int64_t K, int64_t ld,
     hipLaunchKernelGGL(fp8_quant_row_kernel<28>, grid, block, 0, s, xs, rows, K, ld, cs, ss);
   else
     hipLaunchKernelGGL(fp8_quant_kernel, grid, block, 0, s, xs, rows, K, ld, cs, ss);
+  return hipGetLastError();
+}
+
+// Static FP8 and calibration grids: a few workgroups per CU, rows loop.
+static int grid_for_static(int64_t rows) {
+  const int64_t blocks = (rows + kQuantWaves - 1) / kQuantWaves;
+  const int64_t cap = 4096;
+  return (int)(blocks < cap ? (blocks > 0 ? blocks : 1) : cap);
+}
+
+hipError_t launch_fp8_static_quant(const void* x, int64_t rows, int64_t K, int64_t ld, const float* amax,
+                                   void* codes, void* scales, hipStream_t s) {
+  hipLaunchKernelGGL(fp8_static_quant_kernel, dim3(grid_for_static(rows)), dim3(64 * kQuantWaves), 0, s,
+                     static_cast<const uint16_t*>(x), rows, K, ld, amax, static_cast<uint8_t*>(codes),
+                     static_cast<float*>(scales));
+  return hipGetLastError();
+}
+
+hipError_t launch_fp8_amax(const void* x, int64_t rows, int64_t K, int64_t ld, float* amax, hipStream_t s) {
+  const int64_t cap = 1024;  // workgroups: one atomic each
+  int64_t blocks = (rows + kQuantWaves - 1) / kQuantWaves;
+  blocks = blocks < cap ? blocks : cap;
+  hipLaunchKernelGGL(fp8_amax_kernel, dim3((unsigned)blocks), dim3(64 * kQuantWaves), 0, s,
+                     static_cast<const uint16_t*>(x), rows, K, ld, reinterpret_cast<uint32_t*>(amax));
   return hipGetLastError();
 }
 

@@ -28,6 +28,9 @@ def lib():
         l.mxq_host_fp8_quantize.argtypes = [_P, _I64, _I64, _P, _P]
         l.mxq_host_fp8_division_sweep.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(_I64),
                                                   ctypes.POINTER(_I64), ctypes.POINTER(_I64)]
+        l.mxq_host_fp8_static_sweep.argtypes = [_P, _I64, ctypes.POINTER(_I64), ctypes.POINTER(_I64),
+                                                ctypes.POINTER(_I64)]
+        l.mxq_host_fp8_quantize_static.argtypes = [_P, _I64, _I64, ctypes.c_float, _P, _P]
         l.mxq_host_bf16_rne.argtypes = [_P, _I64, _P]
         l.mxq_host_gelu_tanh.argtypes = [_P, _I64, _P]
         _lib = l
@@ -95,3 +98,19 @@ def gelu_tanh(f):
     out = np.empty(a.shape, np.float32)
     lib().mxq_host_gelu_tanh(_p(a), a.size, _p(out))
     return out
+
+
+def fp8_static_sweep(amax):
+    a = np.ascontiguousarray(amax, np.float32)
+    pairs, qm, cm = _I64(), _I64(), _I64()
+    lib().mxq_host_fp8_static_sweep(_p(a), a.size, ctypes.byref(pairs), ctypes.byref(qm), ctypes.byref(cm))
+    return pairs.value, qm.value, cm.value
+
+
+def fp8_quantize_static(x_bits, amax):
+    x = np.ascontiguousarray(x_bits, np.uint16)
+    r, k = x.shape
+    codes = np.empty((r, k), np.uint8)
+    scales = np.empty((r,), np.float32)
+    lib().mxq_host_fp8_quantize_static(_p(x), r, k, float(amax), _p(codes), _p(scales))
+    return codes, scales

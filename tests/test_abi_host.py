@@ -25,7 +25,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = mxq.lib()
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(mxq._SIGS)
@@ -116,6 +116,33 @@ def test_gemm_mxfp4_out_validation():
     empty[8] = 0
     empty[0] = empty[6] = empty[7] = None
     assert L.mxq_gemm_mxfp4_out(*empty) == mxq.OK
+
+
+def test_static_fp8_validation():
+    """Host-side checks of the static FP8 quantizer and its calibration (nothing is enqueued)."""
+    L = mxq.lib()
+    S = None
+    FAKE_F32_ODD = ctypes.c_void_p(0x10002)  # not 4-byte aligned
+    # x M K ld codes scales
+    for k in (0, 16, 48):
+        assert L.mxq_quantize_act_fp8_static(FAKE, 4, k, 64, FAKE, FAKE, FAKE, S) == mxq.ERR_SHAPE
+        assert L.mxq_fp8_calibrate(FAKE, 4, k, 64, FAKE, S) == mxq.ERR_SHAPE
+    assert L.mxq_quantize_act_fp8_static(FAKE, 4, 64, 32, FAKE, FAKE, FAKE, S) == mxq.ERR_SHAPE  # ld < K
+    assert L.mxq_fp8_calibrate(FAKE, -1, 64, 64, FAKE, S) == mxq.ERR_SHAPE
+    for pos in (0, 4, 5, 6):
+        args = [FAKE, 4, 64, 64, FAKE, FAKE, FAKE, S]
+        args[pos] = None
+        assert L.mxq_quantize_act_fp8_static(*args) == mxq.ERR_NULL, pos
+    assert L.mxq_fp8_calibrate(None, 4, 64, 64, FAKE, S) == mxq.ERR_NULL
+    assert L.mxq_fp8_calibrate(FAKE, 4, 64, 64, None, S) == mxq.ERR_NULL
+    assert L.mxq_quantize_act_fp8_static(FAKE_ODD, 4, 64, 64, FAKE, FAKE, FAKE, S) == mxq.ERR_ALIGN
+    assert L.mxq_quantize_act_fp8_static(FAKE, 4, 64, 64, FAKE_F32_ODD, FAKE, FAKE, S) == mxq.ERR_ALIGN
+    assert L.mxq_quantize_act_fp8_static(FAKE, 4, 64, 68, FAKE, FAKE, FAKE, S) == mxq.ERR_ALIGN  # ld % 8
+    assert L.mxq_fp8_calibrate(FAKE_ODD, 4, 64, 64, FAKE, S) == mxq.ERR_ALIGN
+    assert L.mxq_fp8_calibrate(FAKE, 4, 64, 64, FAKE_F32_ODD, S) == mxq.ERR_ALIGN
+    # empty inputs enqueue nothing
+    assert L.mxq_quantize_act_fp8_static(None, 0, 64, 64, None, None, None, S) == mxq.OK
+    assert L.mxq_fp8_calibrate(None, 0, 64, 64, None, S) == mxq.OK
 
 
 def test_policy_table_roundtrip_and_errors():

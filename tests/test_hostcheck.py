@@ -129,3 +129,37 @@ def test_gelu_tanh_fp32_close_to_oracle():
     got = hostcheck.gelu_tanh(y).astype(np.float64)
     want = oracle.gelu_tanh(y.astype(np.float64))
     assert np.all(np.abs(got - want) <= 4e-7 * np.abs(want) + 1e-7)
+
+
+def _static_amax_set():
+    g = np.random.default_rng(77)
+    vals = [np.float32(v) for v in (448.0, 224.0, 1.0, 3.296875, 0.0, 1e-44, 1e-40, 2.4e-17, 2.43e-17, 1e-30,
+                                     3.3895314e38, 3.0e38, 65504.0, 5.27e-36)]
+    rnd = np.ldexp(g.uniform(1, 2, 160), g.integers(-149, 127, 160)).astype(np.float32)
+    pow2 = np.ldexp(1.0, np.arange(-140, 127, 9)).astype(np.float32)
+    a = np.concatenate([np.array(vals, np.float32), rnd, pow2])
+    return a[np.isfinite(a)]
+
+
+def test_fp8_static_quotient_and_code_sweep():
+    """Static scales (any fp32 amax, subnormal and huge ones too) against every finite bf16 x:
+    the kernel's clamped quotient and code equal IEEE division followed by saturating RNE."""
+    amax = _static_amax_set()
+    chunks = np.array_split(amax, 8)
+    with ThreadPoolExecutor(8) as ex:
+        res = list(ex.map(hostcheck.fp8_static_sweep, chunks))
+    pairs = sum(r[0] for r in res)
+    assert pairs == len(amax) * 0x7F80 * 2
+    assert sum(r[1] for r in res) == 0, "quotient differs from IEEE x / s"
+    assert sum(r[2] for r in res) == 0, "E4M3FN code differs"
+
+
+@pytest.mark.parametrize("k", [32, 96, 512])
+def test_fp8_static_composition_matches_oracle(k):
+    x = _edge_rows(k)
+    true_amax = float(np.abs(oracle.bf16_bits_to_f64(x)).max())
+    for amax in (true_amax, true_amax * 1e-3, 0.0, 1e-42, 3.0e38):
+        got = hostcheck.fp8_quantize_static(x, np.float32(amax))
+        want = oracle.fp8_quantize_static(x, np.float32(amax))
+        assert np.array_equal(got[1].view(np.uint32), want[1].view(np.uint32)), amax
+        assert np.array_equal(got[0], want[0]), amax
