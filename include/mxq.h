@@ -199,6 +199,30 @@ int mxq_gemm_mxfp4_out(const void* a_codes, const void* a_scales,
                        int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 /*
+ * W4A8 GEMM whose output is the static FP8 activation of a next W4A8 layer:
+ * the FFN of a W4A8 block takes the first projection (with tanh-GELU),
+ * quantizes the hidden state with its calibrated static scale (the FP8 E4M3
+ * static activations of "Quantization formats") and feeds it to the second
+ * projection. With a static scale no amax pass over the hidden state is
+ * needed, so this entry point does the first two in one kernel. The result
+ * is exactly that of mxq_gemm(MXQ_W4A8, ...) into a bf16 [M][N] buffer
+ * followed by mxq_quantize_act_fp8_static(that buffer, out_amax).
+ *   a_codes/a_scales  device, W4A8 activations (per-token or static scales)
+ *   w_codes/w_scales  device, from mxq_quantize_weight_mxfp4
+ *   bias              device bf16 [N], or null for none
+ *   out_amax          device float32, the output's calibrated amax (>= 0)
+ *   y_codes           device uint8 [M][N] E4M3FN (output)
+ *   y_scales          device float32 [M] (output): out_amax / 448 in every row
+ * Only for the shapes of the pipelined kernel (mxq_gemm_kernel_name(MXQ_W4A8,
+ * M, N, K) starts with "pipe_") with N a multiple of 32 (N is the next
+ * layer's K): MXQ_ERR_SHAPE otherwise, and nothing is written.
+ */
+int mxq_gemm_fp8_static_out(const void* a_codes, const void* a_scales,
+                            const void* w_codes, const void* w_scales, const void* bias,
+                            int epilogue, const float* out_amax, void* y_codes, void* y_scales,
+                            int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/*
  * Name of the kernel that mxq_gemm runs for (mode, M, N, K), as a static
  * string: "pipe_..." for the LDS-pipelined persistent kernel (M, N >= 256,
  * N a multiple of 8, K a multiple of 128 with at least one ring of stages),

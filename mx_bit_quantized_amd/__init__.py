@@ -42,6 +42,8 @@ _SIGS = {
     "mxq_quantize_act_fp8_static": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "mxq_gemm": (ctypes.c_int, [ctypes.c_int, _P, _P, _P, _P, _P, ctypes.c_int, _P, _I64, _I64, _I64, _P]),
     "mxq_gemm_mxfp4_out": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int, _P, _P, _I64, _I64, _I64, _P]),
+    "mxq_gemm_fp8_static_out": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int, _P, _P, _P, _I64, _I64, _I64,
+                                                _P]),
     "mxq_gemm_kernel_name": (ctypes.c_char_p, [ctypes.c_int, _I64, _I64, _I64]),
     "mxq_policy_create": (ctypes.c_int, [_P, _I32, _I32, ctypes.POINTER(_P)]),
     "mxq_policy_destroy": (ctypes.c_int, [_P]),
@@ -240,6 +242,35 @@ def gemm_mxfp4_out(a_codes, a_scales, w_codes, w_scales, bias=None, epilogue=EPI
 def gemm_mxfp4_out_supported(M, N, K):
     """Whether gemm_mxfp4_out takes (M, N, K): the pipelined kernel's shapes with N % 128 == 0."""
     return gemm_kernel_name(W4A4, M, N, K).startswith("pipe_") and N % 128 == 0
+
+
+def gemm_fp8_static_out(a_codes, a_scales, w_codes, w_scales, out_amax, bias=None, epilogue=EPI_NONE,
+                        y_codes=None, y_scales=None, stream=None):
+    """W4A8 GEMM whose output is quantized straight to static FP8 with the calibrated ``out_amax``.
+
+    Returns (y_codes, y_scales), equal to quantize_act_fp8_static(gemm(W4A8, ...), out_amax).
+    """
+    torch = _torch()
+    m = int(a_codes.shape[0])
+    n = int(w_codes.shape[0])
+    k = int(w_codes.shape[1]) * 2
+    if y_codes is None or y_scales is None:
+        y_codes, y_scales = act_buffers(W4A8, m, n, w_codes.device)
+    st = lib().mxq_gemm_fp8_static_out(_dev_ptr(a_codes, "a_codes"), _dev_ptr(a_scales, "a_scales"),
+                                        _dev_ptr(w_codes, "w_codes", torch.uint8),
+                                        _dev_ptr(w_scales, "w_scales", torch.uint8),
+                                        _dev_ptr(bias, "bias", torch.bfloat16), int(epilogue),
+                                        _dev_ptr(out_amax, "out_amax", torch.float32),
+                                        _dev_ptr(y_codes, "y_codes", torch.uint8),
+                                        _dev_ptr(y_scales, "y_scales", torch.float32), m, n, k,
+                                        _stream_handle(stream))
+    _check(st, "gemm_fp8_static_out")
+    return y_codes, y_scales
+
+
+def gemm_fp8_static_out_supported(M, N, K):
+    """Whether gemm_fp8_static_out takes (M, N, K): the pipelined W4A8 kernel's shapes with N % 32 == 0."""
+    return gemm_kernel_name(W4A8, M, N, K).startswith("pipe_") and N % 32 == 0
 
 
 def gemm_kernel_name(mode, M, N, K):

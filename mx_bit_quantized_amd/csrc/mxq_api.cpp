@@ -168,6 +168,30 @@ int mxq_gemm_mxfp4_out(const void* a_codes, const void* a_scales, const void* w_
                                                y_scales, M, N, K, stream));
 }
 
+
+int mxq_gemm_fp8_static_out(const void* a_codes, const void* a_scales, const void* w_codes, const void* w_scales,
+                            const void* bias, int epilogue, const float* out_amax, void* y_codes, void* y_scales,
+                            int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  if (epilogue != MXQ_EPI_NONE && epilogue != MXQ_EPI_GELU_TANH) return MXQ_ERR_MODE;
+  int st = check_mk(M, K, K);
+  if (st != MXQ_OK) return st;
+  if (N < 0 || N >= kMaxDim) return MXQ_ERR_SHAPE;
+  if (M == 0 || N == 0) return MXQ_OK;
+  if (!mxq::gemm_fp8_static_out_supported(M, N, K)) return MXQ_ERR_SHAPE;
+  if (a_codes == nullptr || a_scales == nullptr || w_codes == nullptr || w_scales == nullptr ||
+      out_amax == nullptr || y_codes == nullptr || y_scales == nullptr)
+    return MXQ_ERR_NULL;
+  if (!aligned16(a_codes) || !aligned16(a_scales) || !aligned16(w_codes) || !aligned16(w_scales) ||
+      !aligned16(y_codes) || !aligned16(y_scales) || (bias != nullptr && !aligned16(bias)) ||
+      (reinterpret_cast<uintptr_t>(out_amax) & 3u) != 0)
+    return MXQ_ERR_ALIGN;
+  if (log_enabled())
+    fprintf(stderr, "[mxq] gemm w4a8 -> fp8 static M=%lld N=%lld K=%lld epi=%d\n", (long long)M, (long long)N,
+            (long long)K, epilogue);
+  return hip_status(mxq::launch_gemm_fp8_static_out(a_codes, a_scales, w_codes, w_scales, bias, epilogue, out_amax,
+                                                    y_codes, y_scales, M, N, K, stream));
+}
+
 const char* mxq_gemm_kernel_name(int mode, int64_t M, int64_t N, int64_t K) {
   if (mode != MXQ_W4A4 && mode != MXQ_W4A8) return "invalid";
   return mxq::gemm_variant_name(mode, M, N, K);

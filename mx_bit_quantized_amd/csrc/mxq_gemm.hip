@@ -393,6 +393,38 @@ struct StageScales {
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t v2u __attribute__((ext_vector_type(2)));
+
+// Static FP8 output (W4A8 GEMM writing the next W4A8 layer's activations):
+// the division setup of the static quantizer, arranged for signed inputs. A
+// zero scale maps every value to a signed zero (y = 0, hi = 0).
+struct Fp8Out {
+  float s, pre, ss, y, hi;
+};
+
+__device__ __forceinline__ Fp8Out fp8_out_setup(float amax) {
+  const Fp8Row r = fp8_scale_setup(amax);
+  Fp8Out o;
+  o.s = r.s;
+  o.pre = r.pre;
+  o.ss = r.s == 0.0f ? 1.0f : r.ss;
+  o.y = r.s == 0.0f ? 0.0f : r.y;
+  o.hi = r.s == 0.0f ? 0.0f : r.hi;
+  return o;
+}
+
+// Quotient x / s of a value that is exact in fp32 (a bf16 output), with the
+// static quantizer's clamp at RN(448 ss) applied to both signs and x's sign
+// put back afterwards (the correction step turns -0 into +0; for a nonzero
+// quotient the sign is already x's). The magnitude equals that quantizer's
+// quotient of |x|, so the E4M3FN codes are the same.
+__device__ __forceinline__ float fp8_out_quotient(float x, const Fp8Out& o) {
+  const float xs = __builtin_amdgcn_fmed3f(x * o.pre, -o.hi, o.hi);
+  const float q0 = xs * o.y;
+  const float rem = __builtin_fmaf(-q0, o.ss, xs);
+  const float q = __builtin_fmaf(rem, o.y, q0);
+  return as_float((as_uint(q) & 0x7FFFFFFFu) | (as_uint(x) & 0x80000000u));
+}
 
 // Two floats to packed bf16 (low half = a), round to nearest even: one
 // v_cvt_pk_bf16_f32 on gfx950.
@@ -419,22 +451,29 @@ __device__ __forceinline__ void buf_store4(const i32x4& rs, uint32_t voff, uint3
   asm volatile("buffer_store_dword %0, %1, %2, 0 offen" :: "v"(v), "v"(voff), "s"(rs) : "memory");
 }
 
+// Range-checked 8-byte store (no late read of its data registers).
+__device__ __forceinline__ void buf_store8(const i32x4& rs, uint32_t voff, uint32_t lo, uint32_t hi) {
+  const v2u d = {lo, hi};
+  asm volatile("buffer_store_dwordx2 %0, %1, %2, 0 offen" :: "v"(d), "v"(voff), "s"(rs) : "memory");
+}
+
 __device__ __forceinline__ void buf_store16(const i32x4& rs, uint32_t voff, const uint4& v) {
   const i32x4 d = {(int)v.x, (int)v.y, (int)v.z, (int)v.w};
   asm volatile("buffer_store_dwordx4 %0, %1, %2, 0 offen\n\ts_nop 1" :: "v"(d), "v"(voff), "s"(rs) : "memory");
 }
 
-// QOUT (W4A4 only): instead of y in bf16 the kernel writes the MXFP4
-// quantization of those bf16 values, the activation format of a next W4A4
-// layer: codes in code panels of width 128 along N (y = codes, M N / 2 bytes)
-// and group-major scales [N/128][M][4] (y_scales). N % 128 == 0.
+// QOUT: instead of y in bf16 the kernel writes the quantization of those bf16
+// values in the activation format of a next layer of the same mode.
+//   W4A4: MXFP4 codes in code panels of width 128 along N (y = codes, M N / 2
+//         bytes) and group-major scales [N/128][M][4] (y_scales); N % 128 == 0.
+//   W4A8: static FP8 with the scale out_amax / 448: codes [M][N] (y) and the
+//         scale in every row of y_scales (float [M]).
 template <int MODE, int KT, int NB, bool GELU, bool BIAS, bool QOUT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_pipe_kernel(
     const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws,
     const uint8_t* __restrict__ aq, const void* __restrict__ asc,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, uint8_t* __restrict__ y_scales,
-    int M, int N, int K, int tiles_m, int tiles_n) {
-  static_assert(!QOUT || MODE == 0, "quantized output is the W4A4 activation format");
+    const float* __restrict__ out_amax, int M, int N, int K, int tiles_m, int tiles_n) {
   using C = PipeCfg<MODE, KT, NB>;
   // ring of NB stage slots, then two tile-parameter blocks: bias slice (512
   // bytes), a sink for the unused waves' copies (512), token scales (1024, FP8)
@@ -718,11 +757,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // no branch. Exactly EPI_STORES stores per wave, whatever the shape: rows
   // past M and columns past N get an offset the range check drops.
   constexpr int EP = 272;
-  // W4A4 with QOUT: per 32-row group two 1 KiB code stores and one scale store
-  constexpr int EPI_STORES = QOUT ? 12 : 32;
+  // W4A4 with QOUT: per 32-row group two 1 KiB code stores and one scale
+  // store; W4A8 with QOUT: the 32 code stores and one store of row scales
+  constexpr int EPI_STORES = MODE == 0 ? (QOUT ? 12 : 32) : (QOUT ? 33 : 32);
   constexpr int EPI_OPS = EPI_STORES + EPI_PARAM_OPS;
   static_assert(4 * 32 * EP <= C::STAGE, "epilogue staging fits in one ring slot");
-  const i32x4 ry = make_rsrc(y, (uint32_t)M * (uint32_t)N * 2u);
+  const i32x4 ry = make_rsrc(y, (uint32_t)M * (uint32_t)N * (MODE == 1 && QOUT ? 1u : 2u));
+  Fp8Out fo{};
+  if constexpr (MODE == 1 && QOUT) fo = fp8_out_setup(*out_amax);
   const int lrow = lane >> 3;        // row within a group of 8 (read phase)
   const int lcol = (lane & 7) * 8;   // first of the lane's 8 columns (read phase)
   auto write_pass = [&](uint8_t* wbase, auto p_tag) {
@@ -787,13 +829,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         h.z = pack_bf16x2(v[4], v[5]);
         h.w = pack_bf16x2(v[6], v[7]);
         const bool in = m < M && n < N;
-        buf_store16(ry, in ? ((uint32_t)m * (uint32_t)N + (uint32_t)n) * 2u : 0x80000000u, h);
+        if constexpr (MODE == 1 && QOUT) {
+          // the bf16 values as the next layer would read them, then their
+          // static FP8 codes: 8 bytes of row m
+          const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
+          uint32_t cw[2];
+#pragma unroll
+          for (int c2 = 0; c2 < 2; ++c2) {
+            const float q0 = fp8_out_quotient(as_float(hw[2 * c2] << 16), fo);
+            const float q1 = fp8_out_quotient(as_float(hw[2 * c2] & 0xFFFF0000u), fo);
+            const float q2 = fp8_out_quotient(as_float(hw[2 * c2 + 1] << 16), fo);
+            const float q3 = fp8_out_quotient(as_float(hw[2 * c2 + 1] & 0xFFFF0000u), fo);
+            uint32_t o = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
+            o = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, (int)o, true);
+            cw[c2] = o;
+          }
+          buf_store8(ry, in ? (uint32_t)m * (uint32_t)N + (uint32_t)n : 0x80000000u, cw[0], cw[1]);
+        } else {
+          buf_store16(ry, in ? ((uint32_t)m * (uint32_t)N + (uint32_t)n) * 2u : 0x80000000u, h);
+        }
       }
     };
     // the accumulator indices are static: one copy of the pass per (j, h)
     [&]<int... Q>(std::integer_sequence<int, Q...>) {
       (pass(std::integral_constant<int, Q>{}), ...);
     }(std::make_integer_sequence<int, 8>{});
+    if constexpr (MODE == 1 && QOUT) {
+      // the row scales: thread t writes that of the tile's row t, from the
+      // tiles of the first column only (one store per wave either way)
+      const int m = m_base + t;
+      const i32x4 rs = make_rsrc(y_scales, (uint32_t)M * 4u);
+      buf_store4(rs, tn == 0 && m < M ? (uint32_t)m * 4u : 0x80000000u, as_uint(fo.s));
+    }
     // parameters of the next tile (its block was last read two tiles ago)
     issue_params(k + 1);
     // the copy cursor is in tile k+1 by now (it runs fewer than n_stages
@@ -1159,7 +1226,7 @@ static int device_cu_count() {
 template <int MODE, int KT, int NB, bool QOUT = false>
 static hipError_t launch_pipe(const void* aq, const void* as, const void* wq, const void* ws, const void* bias,
                               int epi, void* y, int64_t M, int64_t N, int64_t K, hipStream_t s,
-                              void* y_scales = nullptr) {
+                              void* y_scales = nullptr, const float* out_amax = nullptr) {
   static const int cus = device_cu_count();
   const int tiles_m = (int)((M + 255) / 256);
   const int tiles_n = (int)((N + 255) / 256);
@@ -1172,7 +1239,7 @@ static hipError_t launch_pipe(const void* aq, const void* as, const void* wq, co
                        dim3(grid), dim3(256), 0, s, static_cast<const uint8_t*>(wq),
                        static_cast<const uint8_t*>(ws), static_cast<const uint8_t*>(aq), as,
                        static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y),
-                       static_cast<uint8_t*>(y_scales), (int)M, (int)N, (int)K, tiles_m, tiles_n);
+                       static_cast<uint8_t*>(y_scales), out_amax, (int)M, (int)N, (int)K, tiles_m, tiles_n);
   };
   if (epi == 1) {
     if (bias != nullptr) go(std::true_type{}, std::true_type{});
@@ -1234,6 +1301,17 @@ hipError_t launch_gemm_mxfp4_out(const void* a_codes, const void* a_scales, cons
                                  void* y_scales, int64_t M, int64_t N, int64_t K, hipStream_t s) {
   return launch_pipe<0, kPipeKT[0], kPipeNB[0], true>(a_codes, a_scales, w_codes, w_scales, bias, epilogue, y_codes,
                                                       M, N, K, s, y_scales);
+}
+
+// N is the next layer's K: a multiple of 32
+bool gemm_fp8_static_out_supported(int64_t M, int64_t N, int64_t K) { return use_lds(1, M, N, K) && N % 32 == 0; }
+
+hipError_t launch_gemm_fp8_static_out(const void* a_codes, const void* a_scales, const void* w_codes,
+                                      const void* w_scales, const void* bias, int epilogue, const float* out_amax,
+                                      void* y_codes, void* y_scales, int64_t M, int64_t N, int64_t K,
+                                      hipStream_t s) {
+  return launch_pipe<1, kPipeKT[1], kPipeNB[1], true>(a_codes, a_scales, w_codes, w_scales, bias, epilogue, y_codes,
+                                                      M, N, K, s, y_scales, out_amax);
 }
 
 const char* gemm_variant_name(int mode, int64_t M, int64_t N, int64_t K) {

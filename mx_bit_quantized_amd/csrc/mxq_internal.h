@@ -35,6 +35,15 @@ hipError_t launch_gemm_mxfp4_out(const void* a_codes, const void* a_scales, cons
                                  const void* w_scales, const void* bias, int epilogue, void* y_codes,
                                  void* y_scales, int64_t M, int64_t N, int64_t K, hipStream_t s);
 
+// W4A8 GEMM whose bf16 output goes straight into static FP8 with the scale
+// out_amax / 448 (device fp32): codes [M][N], the scale in every row of
+// y_scales (float [M]); only where gemm_fp8_static_out_supported holds.
+bool gemm_fp8_static_out_supported(int64_t M, int64_t N, int64_t K);
+hipError_t launch_gemm_fp8_static_out(const void* a_codes, const void* a_scales, const void* w_codes,
+                                      const void* w_scales, const void* bias, int epilogue, const float* out_amax,
+                                      void* y_codes, void* y_scales, int64_t M, int64_t N, int64_t K,
+                                      hipStream_t s);
+
 // Name of the GEMM kernel variant launch_gemm picks for a shape (for logs).
 const char* gemm_variant_name(int mode, int64_t M, int64_t N, int64_t K);
 

@@ -25,7 +25,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = mxq.lib()
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(mxq._SIGS)
@@ -116,6 +116,38 @@ def test_gemm_mxfp4_out_validation():
     empty[8] = 0
     empty[0] = empty[6] = empty[7] = None
     assert L.mxq_gemm_mxfp4_out(*empty) == mxq.OK
+
+
+def test_gemm_fp8_static_out_validation():
+    """Host-side checks of the fused W4A8 GEMM -> static FP8 entry point (nothing is enqueued)."""
+    L = mxq.lib()
+    S = None
+    FAKE_F32_ODD = ctypes.c_void_p(0x10002)
+    # a0 as0 w0 ws0 bias epi amax yc ys M N K stream
+    ok = [FAKE, FAKE, FAKE, FAKE, None, 1, FAKE, FAKE, FAKE, 512, 1024, 1024, S]
+    bad_epi = list(ok)
+    bad_epi[5] = 3
+    assert L.mxq_gemm_fp8_static_out(*bad_epi) == mxq.ERR_MODE
+    # shapes the pipelined W4A8 kernel does not take
+    for m, n, k in [(255, 1024, 1024), (512, 1024, 256), (512, 1020, 1024), (512, 1024, 100), (512, 1000, 1024)]:
+        args = list(ok)
+        args[9:12] = [m, n, k]
+        assert L.mxq_gemm_fp8_static_out(*args) == mxq.ERR_SHAPE, (m, n, k)
+    for pos in (0, 1, 2, 3, 6, 7, 8):
+        args = list(ok)
+        args[pos] = None
+        assert L.mxq_gemm_fp8_static_out(*args) == mxq.ERR_NULL, pos
+    for pos in (0, 4, 7, 8):
+        args = list(ok)
+        args[pos] = FAKE_ODD
+        assert L.mxq_gemm_fp8_static_out(*args) == mxq.ERR_ALIGN, pos
+    args = list(ok)
+    args[6] = FAKE_F32_ODD
+    assert L.mxq_gemm_fp8_static_out(*args) == mxq.ERR_ALIGN
+    empty = list(ok)
+    empty[10] = 0
+    empty[0] = empty[6] = empty[7] = empty[8] = None
+    assert L.mxq_gemm_fp8_static_out(*empty) == mxq.OK
 
 
 def test_static_fp8_validation():

@@ -210,3 +210,103 @@ def test_a14b_ffn_720p_static_full_size():
     y_got = host_bits(y.index_select(0, torch.from_numpy(rows).cuda()).index_select(1, torch.from_numpy(cols).cuda()))
     rep = assert_output_close(y_got, y_ref, what + " down")
     say(f"{what}: worst/bound {rep['worst_ratio']:.3f}")
+
+
+# -------------------------------------- fused W4A8 GEMM -> static FP8 -------
+#
+# mxq_gemm_fp8_static_out is defined as the static FP8 quantization of the bf16
+# output the plain W4A8 GEMM writes: it must equal that two-step path byte for
+# byte over the whole buffers, and, wherever the GPU's bf16 output equals the
+# oracle's bf16 rounding of its QDQ result, the oracle's static codes.
+
+def _fused_paths(m, n, k, seed, epilogue, bias, amax_frac):
+    x = synth.activation_bf16(seed, m, k, ("student_t",))
+    w = synth.weight_bf16(seed + 1, n, k)
+    b = synth.f32_to_bf16_bits((np.random.default_rng(seed).standard_normal(n) * 0.1).astype(np.float32)) \
+        if bias else None
+    ac, asc = mxq.quantize_act(mxq.W4A8, dev_bf16(x))
+    wc, ws = mxq.quantize_weight_mxfp4(dev_bf16(w))
+    bd = dev_bf16(b) if bias else None
+    y = mxq.gemm(mxq.W4A8, ac, asc, wc, ws, bd, epilogue)
+    torch.cuda.synchronize()
+    # the output's static amax: a fraction of the oracle's largest |h| over a few
+    # rows (a calibration value, so some outputs may exceed it)
+    owc, ows = oracle.mxfp4_quantize(w)
+    oac, oas = oracle.fp8_quantize_per_token(x)
+    b64 = oracle.bf16_bits_to_f64(b) if bias else None
+    h_ref = oracle.f64_to_bf16_bits(oracle.qdq_matmul(mxq.W4A8, oac, oas, owc, ows, b64, epilogue))
+    amax = np.float32(float(oracle.fp8_calibration_amax([h_ref])) * amax_frac)
+    ad = _amax_dev(amax)
+    rc, rs = mxq.quantize_act_fp8_static(y, ad)
+    fc, fs = mxq.gemm_fp8_static_out(ac, asc, wc, ws, ad, bd, epilogue)
+    torch.cuda.synchronize()
+    return y, h_ref, amax, (rc, rs), (fc, fs)
+
+
+FUSED_FP8_SHAPES = [(256, 512, 512), (300, 288, 384), (600, 1280, 896), (2250, 7424, 512)]
+
+
+@pytest.mark.parametrize("m,n,k", FUSED_FP8_SHAPES)
+@pytest.mark.parametrize("epilogue,bias,amax_frac", [(mxq.EPI_GELU_TANH, False, 1.0), (mxq.EPI_NONE, True, 0.25),
+                                                     (mxq.EPI_GELU_TANH, True, 0.5), (mxq.EPI_NONE, False, 0.0)])
+def test_fused_fp8_static_equals_gemm_then_quantize(m, n, k, epilogue, bias, amax_frac):
+    say("fused fp8 vs two-step", m, n, k, epilogue, bias, amax_frac)
+    assert mxq.gemm_fp8_static_out_supported(m, n, k)
+    y, h_ref, amax, (rc, rs), (fc, fs) = _fused_paths(m, n, k, 41 + m + n, epilogue, bias, amax_frac)
+    assert torch.equal(fs, rs), "row scales differ"
+    bad = int((fc != rc).sum())
+    assert bad == 0, f"{bad} code bytes differ"
+    # tie to the oracle where the bf16 outputs agree
+    agree = host_bits(y) == h_ref
+    assert agree.mean() > 0.9, f"only {agree.mean():.3f} of the outputs agree in bf16"
+    want_c, want_s = oracle.fp8_quantize_static(h_ref, amax)
+    got = host_u8(fc)
+    assert np.all(host_f32(fs).view(np.uint32) == want_s.view(np.uint32))
+    bad = np.argwhere(agree & (got != want_c))
+    assert bad.size == 0, f"{len(bad)} codes of agreeing outputs differ from the oracle, first {bad[:5].tolist()}"
+    if 0 < amax_frac < 1:
+        assert np.any((got & 0x7F) == 0x7E)  # saturation is exercised
+
+
+def test_fused_fp8_static_tiny_scale():
+    """A tiny static amax (pre-scaled divisor): every nonzero output saturates, zeros keep their sign."""
+    m, n, k = 256, 512, 512
+    say("fused fp8 tiny scale", m, n, k)
+    x = synth.activation_bf16(97, m, k, ("student_t",))
+    w = synth.weight_bf16(98, n, k)
+    ac, asc = mxq.quantize_act(mxq.W4A8, dev_bf16(x))
+    wc, ws = mxq.quantize_weight_mxfp4(dev_bf16(w))
+    y = mxq.gemm(mxq.W4A8, ac, asc, wc, ws, None, mxq.EPI_GELU_TANH)
+    ad = _amax_dev(1e-38)
+    rc, rs = mxq.quantize_act_fp8_static(y, ad)
+    fc, fs = mxq.gemm_fp8_static_out(ac, asc, wc, ws, ad, None, mxq.EPI_GELU_TANH)
+    torch.cuda.synchronize()
+    assert torch.equal(fc, rc) and torch.equal(fs, rs)
+    yb = host_bits(y)
+    got = host_u8(fc)
+    nz = (yb & 0x7FFF) != 0
+    assert np.all((got[nz] & 0x7F) == 0x7E) and np.all((got[~nz] & 0x7F) == 0)
+    assert np.all((got >> 7) == (yb >> 15))  # signs, zeros included
+
+
+def test_fused_fp8_static_a14b_ffn_up_full_size():
+    """A14B FFN first projection at 720p (75600 x 13824 x 5120, GELU), whole buffers against the two-step path."""
+    wl = synth.workload(3)
+    up = wl.linears[0]
+    m, n, k = wl.m_video, up.n, up.k
+    say("fused fp8 full size", m, n, k)
+    assert up.name == "ffn_up" and mxq.gemm_fp8_static_out_supported(m, n, k)
+    g = torch.Generator(device="cuda:0").manual_seed(7)
+    x = (torch.randn((m, k), generator=g, device="cuda:0") * 0.5).to(torch.bfloat16)
+    ac, asc = mxq.quantize_act(mxq.W4A8, x)
+    del x
+    w = synth.weight_bf16_device(3, n, k, 0, 0, 0)
+    wc, ws = mxq.quantize_weight_mxfp4(w)
+    del w
+    y = mxq.gemm(mxq.W4A8, ac, asc, wc, ws, None, up.epilogue)
+    amax = mxq.fp8_calibrate(y[: m // 3])  # calibrated on a third of the tokens
+    rc, rs = mxq.quantize_act_fp8_static(y, amax)
+    del y
+    fc, fs = mxq.gemm_fp8_static_out(ac, asc, wc, ws, amax, None, up.epilogue)
+    torch.cuda.synchronize()
+    assert torch.equal(fc, rc) and torch.equal(fs, rs)
