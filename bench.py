@@ -7,6 +7,12 @@ inputs and packed weights already resident in HBM. Weight packing is offline
 and is timed separately (reported, not part of the step).
 
     python bench.py [--steps K] [--warmup W] [--workload a14b_stack|a14b_ffn|qkv|ti2v|tiny]
+                    [--act-scale per_token|static]
+
+--act-scale static runs the W4A8 linears on static (per-tensor) FP8
+activations: each input's amax is calibrated once, untimed, on the same
+synthetic inputs, and the FFN's first projection of a W4A8 block writes the
+hidden state's static FP8 codes itself. The default is the per-token scale.
 
 Prints one JSON line. Per-launch kernel durations come from HIP events
 recorded on the launch stream around every kernel inside the timed steps.
@@ -37,6 +43,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=3)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="a14b_stack", choices=sorted(WORKLOADS))
+    ap.add_argument("--act-scale", default="per_token", choices=["per_token", "static"],
+                    help="W4A8 activation scale: per token (amax/448 of each row) or static per tensor (calibrated)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=512)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -51,8 +59,9 @@ def log(*a):
 class Stack:
     """Packed weights, inputs and buffers of one workload on the device."""
 
-    def __init__(self, wl, torch, mxq):
+    def __init__(self, wl, torch, mxq, static=False):
         self.wl, self.torch, self.mxq = wl, torch, mxq
+        self.static = static
         dev = "cuda:0"
         t0 = time.time()
         self.policy_table = wl.policy()
@@ -94,7 +103,42 @@ class Stack:
         # W4A4 FFN: the first projection writes the second one's MXFP4 input here
         self.codes_buf2 = torch.empty((ws,), dtype=torch.uint8, device=dev)
         self.records = []  # (kind, mode, flops, bytes, ev_start, ev_end)
-        self.down_ready = False  # the W4A4 FFN's second projection has its input codes in codes_buf2
+        self.down_ready = False  # the FFN's second projection has its input codes in codes_buf2
+        if static:
+            self._calibrate()
+
+    def _calibrate(self):
+        """Static FP8 scales (untimed): the amax of each W4A8 input tensor over the synthetic inputs.
+
+        Video and text activations are shared by every linear that reads them;
+        the FFN hidden state of each W4A8 block is calibrated on the output of
+        its first projection, run once on static activations."""
+        torch, mxq, wl = self.torch, self.mxq, self.wl
+        t0 = time.time()
+        self.amax = {"video": mxq.fp8_calibrate(self.x_video)}
+        if self.x_text is not None:
+            self.amax["text"] = mxq.fp8_calibrate(self.x_text)
+        self.amax_h = {}
+        for e in range(wl.n_experts):
+            for b in range(wl.n_blocks):
+                if self.policy.mode(e, b) != 1:
+                    continue
+                for li, lin in enumerate(wl.linears):
+                    if lin.name != "ffn_up":
+                        continue
+                    m = wl.m_of(lin)
+                    codes, scales = self._act_views(1, m, lin.k)
+                    mxq.quantize_act_fp8_static(self.x_video if lin.m_role == "video" else self.x_text,
+                                                self.amax[lin.m_role], codes, scales)
+                    h = self.h[: m * lin.n].view(m, lin.n)
+                    wc, wsc = self.weights[(e, b, li)]
+                    mxq.gemm(1, codes, scales, wc, wsc, None, lin.epilogue, h)
+                    self.amax_h[(e, b)] = mxq.fp8_calibrate(h)
+        torch.cuda.synchronize()
+        log(f"static FP8 scales calibrated in {time.time() - t0:.1f}s ({len(self.amax_h)} FFN hidden states)")
+
+    def _input_amax(self, e, b, role):
+        return self.amax_h[(e, b)] if role == "ffn_hidden" else self.amax[role]
 
     def _act_views(self, mode, m, k, buf=None):
         torch = self.torch
@@ -127,12 +171,16 @@ class Stack:
                         x = self.h[: m * lin.k].view(m, lin.k)
                     out = (self.h if lin.epilogue == 1 else self.y)[: m * lin.n].view(m, lin.n)
                     wc, wsc = self.weights[(e, b, li)]
-                    # W4A4 FFN: the first projection quantizes its GELU output
-                    # for the second one in its epilogue (same codes as
-                    # quantize_act of its bf16 output), the second one reads
-                    # them as they are
-                    fused_up = mode == 0 and lin.name == "ffn_up" and mxq.gemm_mxfp4_out_supported(m, lin.n, lin.k)
-                    fed = mode == 0 and lin.name == "ffn_down" and self.down_ready
+                    # FFN: the first projection quantizes its GELU output for
+                    # the second one in its epilogue (same codes as quantizing
+                    # its bf16 output), the second one reads them as they are.
+                    # W4A4: MXFP4; W4A8: only with static scales (a per-token
+                    # scale needs the row's amax first)
+                    static8 = mode == 1 and self.static
+                    fused_up = lin.name == "ffn_up" and (
+                        (mode == 0 and mxq.gemm_mxfp4_out_supported(m, lin.n, lin.k))
+                        or (static8 and mxq.gemm_fp8_static_out_supported(m, lin.n, lin.k)))
+                    fed = lin.name == "ffn_down" and self.down_ready
                     if fed:
                         codes, scales = self._act_views(mode, m, lin.k, self.codes_buf2)
                     else:
@@ -141,13 +189,21 @@ class Stack:
                         e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
                         e0.record()
                     if not fed:
-                        mxq.quantize_act(mode, x, codes, scales)
+                        if static8:
+                            mxq.quantize_act_fp8_static(x, self._input_amax(e, b, lin.m_role), codes, scales)
+                        else:
+                            mxq.quantize_act(mode, x, codes, scales)
                     if timed:
                         e1.record()
-                    if fused_up:
+                    if fused_up and mode == 0:
                         oc, osc = self._act_views(mode, m, lin.n, self.codes_buf2)
                         mxq.gemm_mxfp4_out(codes, scales, wc, wsc, None, lin.epilogue, oc, osc)
                         out_bytes = m * lin.n // 2 + m * lin.n // 32
+                    elif fused_up:
+                        oc, osc = self._act_views(mode, m, lin.n, self.codes_buf2)
+                        mxq.gemm_fp8_static_out(codes, scales, wc, wsc, self.amax_h[(e, b)], None, lin.epilogue,
+                                                oc, osc)
+                        out_bytes = m * lin.n + 4 * m
                     else:
                         mxq.gemm(mode, codes, scales, wc, wsc, None, lin.epilogue, out)
                         out_bytes = m * lin.n * 2
@@ -198,8 +254,11 @@ def profiled_traffic(workload_tag, mode):
     return total // launches
 
 
-def cpu_baseline(wl, sample_rows):
-    """Oracle throughput on a bounded sample: `sample_rows` token rows through one block's linears."""
+def cpu_baseline(wl, sample_rows, static=False):
+    """Oracle throughput on a bounded sample: `sample_rows` token rows through one block's linears.
+
+    With ``static`` the W4A8 linears quantize with the oracle's static FP8 rule,
+    the scale calibrated on the sample (untimed)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -223,8 +282,14 @@ def cpu_baseline(wl, sample_rows):
                 continue
             w = synth.weight_bf16(wl.config_id, lin.n, lin.k, 0, b, li)
             wq, wsc = oracle.mxfp4_quantize(w)  # offline on both sides; not timed
+            xs = x[:, : lin.k]
+            amax = oracle.fp8_calibration_amax([xs]) if static else None
             t0 = time.perf_counter()
-            y, _, _ = oracle.qlinear(md, x[:, : lin.k], wq, wsc, epilogue=lin.epilogue)
+            if md == 1 and static:
+                ac, asc = oracle.fp8_quantize_static(xs, amax)
+                y = oracle.qdq_matmul(md, ac, asc, wq, wsc, None, lin.epilogue)
+            else:
+                y, _, _ = oracle.qlinear(md, xs, wq, wsc, epilogue=lin.epilogue)
             secs += time.perf_counter() - t0
             flops += 2 * rows * lin.n * lin.k
             if secs > 10:
@@ -233,7 +298,8 @@ def cpu_baseline(wl, sample_rows):
             break
     return {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{rows} token rows through the first W4A4 and first W4A8 block's video-token linears "
-                      f"(quantize + float64 QDQ matmul), {flops / 1e9:.1f} GFLOP in {secs:.1f} s"}
+                      f"(quantize{' (W4A8: static FP8)' if static else ''} + float64 QDQ matmul), "
+                      f"{flops / 1e9:.1f} GFLOP in {secs:.1f} s"}
 
 
 def main():
@@ -258,7 +324,8 @@ def main():
         return
     mxq.lib()
     wl = synth.workload(WORKLOADS[args.workload])
-    stack = Stack(wl, torch, mxq)
+    static = args.act_scale == "static"
+    stack = Stack(wl, torch, mxq, static)
     for _ in range(args.warmup):
         stack.step(timed=False)
     torch.cuda.synchronize()
@@ -296,7 +363,7 @@ def main():
     dom = max((k for k in agg if k[0] == "gemm"), key=lambda k: agg[k]["ms"])
     a = agg[dom]
     achieved = a["flops"] / (a["ms"] * 1e-3) / 1e12
-    tag = [k for k, v in WORKLOADS.items() if v == wl.config_id][0]
+    tag = [k for k, v in WORKLOADS.items() if v == wl.config_id][0] + ("_static" if static else "")
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_TFLOPS[dom[1]], "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_TFLOPS[dom[1]], 4),
                 "traffic": profiled_traffic(tag, dom[1]),
@@ -316,17 +383,19 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "+".join(x for x, md in (("mxfp4xmxfp4", 0), ("fp8e4m3xmxfp4", 1)) if md in modes) + "->fp32acc->bf16",
-        "data": "synthetic (seeded activations with Student-t outlier channels; N(0,0.02) weights, RTN MXFP4)",
+        "data": "synthetic (seeded activations with Student-t outlier channels; N(0,0.02) weights, RTN MXFP4"
+                + ("; static FP8 scales calibrated, untimed, on the same inputs)" if static else ")"),
         "config": {"workload": wl.name, "m_video": wl.m_video, "m_text": wl.m_text, "dim": wl.dim, "ffn": wl.ffn,
                    "experts": wl.n_experts, "blocks": wl.n_blocks,
                    "w4a8_blocks": int((stack.policy_table == 1).sum()),
+                   "w4a8_activations": "fp8_static_per_tensor" if static else "fp8_per_token",
                    "linears_per_block": len(wl.linears), "tflop_per_step": round(wl.total_flops() / 1e12, 2)},
         "roofline": roofline,
         "kernels": kernels,
         "weight_pack_gbs": round(stack.pack_gbs, 1),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_rows)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_rows, static)
     print(json.dumps(out), flush=True)
 
 
