@@ -17,6 +17,8 @@ quantize-dequantize emulation):
 * ``quant``    - MXFP4 block quantizer (one E8M0 scale per 32 elements along K)
                  and FP8 E4M3FN quantizers: per-token (scale = row amax / 448)
                  and static (one calibrated scale per tensor, saturating).
+* ``transform`` - the transform_on mode: block-diagonal 128-point Hadamard
+                 rotation (fp32 butterflies) and SmoothQuant factors ahead of MXFP4.
 * ``linear``   - dequantize-then-fp64 matmul (the QDQ result), tanh-GELU, the
                  per-block policy lookup and the output tolerance check.
 
@@ -50,6 +52,14 @@ from .quant import (
     fp8_static_scale,
     fp8_quantize_static,
     unpack_nibbles,
+)
+from .transform import (
+    fwht128_f32,
+    hadamard_channel_amax,
+    smoothquant_factors,
+    hadamard_transform_bf16,
+    mxfp4_quantize_hadamard,
+    INV_SQRT_BLOCK,
 )
 from .linear import (
     W4A4,
