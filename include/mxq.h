@@ -94,9 +94,11 @@ enum {
   MXQ_ERR_RANGE = 7      /* policy index (expert, block) out of range       */
 };
 
-/* Precision modes: values of the policy table. The page's policy artifact
- * also has "bf16" and "transform_on" entries; they are not modes of this
- * layer and are rejected with MXQ_ERR_MODE. */
+/* Precision modes: values of the policy table (the page's policy artifact,
+ * "Practical workflow" step 6). MXQ_POLICY_TRANSFORM_ON is W4A4 with the
+ * fixed Hadamard rotation + SmoothQuant transform ("Calibration-driven block
+ * selection"): the policy accepts it, mxq_qlinear_transform runs it. The
+ * artifact's "bf16" entry is not a mode of this layer (MXQ_ERR_MODE). */
 enum { MXQ_W4A4 = 0, MXQ_W4A8 = 1, MXQ_POLICY_BF16 = 2, MXQ_POLICY_TRANSFORM_ON = 3 };
 
 /* GEMM epilogues. The FFN's first projection is followed by tanh-GELU:
@@ -159,6 +161,41 @@ int mxq_fp8_calibrate(const void* x, int64_t M, int64_t K, int64_t ldx, float* a
  *           mxq_gemm(MXQ_W4A8, ...) exactly as per-token activations do
  */
 int mxq_quantize_act_fp8_static(const void* x, int64_t M, int64_t K, int64_t ldx, const float* amax,
+                                void* codes, void* scales, hipStream_t stream);
+
+/*
+ * transform_on (sections "Calibration-driven block selection" and
+ * "Mixed-Precision selection": fixed Hadamard rotation followed by
+ * SmoothQuant, MXFP4 W4A4). For a linear y = x W^T the K dimension is rotated
+ * by a block-diagonal Walsh-Hadamard matrix (one 128-point block per 128
+ * consecutive elements, the MXFP4 code panel) and each channel is rescaled:
+ *   x_t = (x H) / lambda (online),  W_t = (W H) * lambda (offline),
+ * so x_t W_t^T = x W^T. The arithmetic is fp32 in a fixed order: the
+ * unnormalized transform by butterflies (h = 1, 2, 4, ..., 64, each a + b and
+ * a - b of the elements h apart), one multiply by the channel factor `mult`,
+ * rounding to bf16, then the MXFP4 rule. K must be a multiple of 128.
+ *
+ * mxq_hadamard_channel_amax: SmoothQuant calibration statistic,
+ *   amax[k] = max(amax[k], max over rows |unnormalized transform of x|[k])
+ *   x      device bf16 [M][ldx]; amax device float32 [K], set to 0 by the
+ *          caller before the first batch, then folded batch after batch (in
+ *          any order). Use it on calibration activations, and on the bf16
+ *          weight [N][K] for the weight's statistic.
+ * mxq_smoothquant_factors: lambda = sqrt(act_amax / w_amax) (migration
+ *   strength 0.5; 1 where either maximum is 0), then
+ *   act_mult = RN(RN(1 / lambda) * c), w_mult = RN(lambda * c), c = RN(1 /
+ *   sqrt(128)) (IEEE fp32 division and square root). All device float32 [K].
+ * mxq_quantize_mxfp4_hadamard: MXFP4 codes (M * K/2 bytes in code panels) and
+ *   E8M0 scales [K/128][M][4] of RN_bf16(transform(x) * mult). With act_mult
+ *   it is the transform_on activation quantizer; with w_mult on the bf16
+ *   weight [N][K] it packs the weight offline (use these codes with mxq_gemm(
+ *   MXQ_W4A4, ...)). mult: device float32 [K], 16-byte aligned.
+ * Finite inputs whose transform stays finite only.
+ */
+int mxq_hadamard_channel_amax(const void* x, int64_t M, int64_t K, int64_t ldx, float* amax, hipStream_t stream);
+int mxq_smoothquant_factors(const float* act_amax, const float* w_amax, int64_t K, float* act_mult,
+                            float* w_mult, hipStream_t stream);
+int mxq_quantize_mxfp4_hadamard(const void* x, int64_t M, int64_t K, int64_t ldx, const float* mult,
                                 void* codes, void* scales, hipStream_t stream);
 
 /*
@@ -264,6 +301,22 @@ int mxq_qlinear(const void* policy, int32_t expert, int32_t block,
                 const void* w_codes, const void* w_scales, int64_t N,
                 const void* bias, int epilogue, void* y,
                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * mxq_qlinear for tables that hold MXQ_POLICY_TRANSFORM_ON blocks. A
+ * transform_on block quantizes x with mxq_quantize_mxfp4_hadamard(act_mult)
+ * and multiplies with the weight packed by the same call on w_mult; its
+ * workspace is the W4A4 one. Other blocks ignore act_mult and behave as
+ * mxq_qlinear. (mxq_qlinear itself returns MXQ_ERR_MODE on a transform_on
+ * block: it has no factors for it.)
+ *   act_mult  device float32 [K] (16-byte aligned); required (MXQ_ERR_NULL)
+ *             on a transform_on block; K a multiple of 128 there.
+ */
+int mxq_qlinear_transform(const void* policy, int32_t expert, int32_t block,
+                          const void* x, int64_t M, int64_t K,
+                          const void* w_codes, const void* w_scales, int64_t N,
+                          const void* bias, int epilogue, const float* act_mult, void* y,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -39,6 +39,9 @@ _SIGS = {
     "mxq_quantize_weight_mxfp4": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "mxq_quantize_act": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, _I64, _P, _P, _P]),
     "mxq_fp8_calibrate": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P]),
+    "mxq_hadamard_channel_amax": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P]),
+    "mxq_smoothquant_factors": (ctypes.c_int, [_P, _P, _I64, _P, _P, _P]),
+    "mxq_quantize_mxfp4_hadamard": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "mxq_quantize_act_fp8_static": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "mxq_gemm": (ctypes.c_int, [ctypes.c_int, _P, _P, _P, _P, _P, ctypes.c_int, _P, _I64, _I64, _I64, _P]),
     "mxq_gemm_mxfp4_out": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int, _P, _P, _I64, _I64, _I64, _P]),
@@ -51,6 +54,8 @@ _SIGS = {
     "mxq_qlinear_workspace_bytes": (ctypes.c_int, [ctypes.c_int, _I64, _I64, ctypes.POINTER(ctypes.c_size_t)]),
     "mxq_qlinear": (ctypes.c_int, [_P, _I32, _I32, _P, _I64, _I64, _P, _P, _I64, _P, ctypes.c_int, _P,
                                    _P, ctypes.c_size_t, _P]),
+    "mxq_qlinear_transform": (ctypes.c_int, [_P, _I32, _I32, _P, _I64, _I64, _P, _P, _I64, _P, ctypes.c_int, _P,
+                                             _P, _P, ctypes.c_size_t, _P]),
 }
 
 
@@ -201,6 +206,47 @@ def quantize_act_fp8_static(x, amax, codes=None, scales=None, stream=None):
     return codes, scales
 
 
+def hadamard_channel_amax(x, amax=None, stream=None):
+    """Fold bf16 x [M, K] into the running per-channel max |transform(x)| (device float32 [K]) -> amax."""
+    torch = _torch()
+    m, k = _rows_k(x, "x")
+    if amax is None:
+        amax = torch.zeros((k,), dtype=torch.float32, device=x.device)
+    st = lib().mxq_hadamard_channel_amax(_dev_ptr(x, "x", torch.bfloat16), m, k, k,
+                                          _dev_ptr(amax, "amax", torch.float32), _stream_handle(stream))
+    _check(st, "hadamard_channel_amax")
+    return amax
+
+
+def smoothquant_factors(act_amax, w_amax, act_mult=None, w_mult=None, stream=None):
+    """SmoothQuant factor vectors (act_mult, w_mult), device float32 [K], from the two rotated maxima."""
+    torch = _torch()
+    k = int(act_amax.numel())
+    if act_mult is None:
+        act_mult = torch.empty((k,), dtype=torch.float32, device=act_amax.device)
+    if w_mult is None:
+        w_mult = torch.empty((k,), dtype=torch.float32, device=act_amax.device)
+    st = lib().mxq_smoothquant_factors(_dev_ptr(act_amax, "act_amax", torch.float32),
+                                        _dev_ptr(w_amax, "w_amax", torch.float32), k,
+                                        _dev_ptr(act_mult, "act_mult", torch.float32),
+                                        _dev_ptr(w_mult, "w_mult", torch.float32), _stream_handle(stream))
+    _check(st, "smoothquant_factors")
+    return act_mult, w_mult
+
+
+def quantize_mxfp4_hadamard(x, mult, codes=None, scales=None, stream=None):
+    """MXFP4 of the transformed bf16 x [M, K] (rotation, channel factor ``mult``, bf16) -> (codes, scales)."""
+    torch = _torch()
+    m, k = _rows_k(x, "x")
+    if codes is None or scales is None:
+        codes, scales = act_buffers(W4A4, m, k, x.device)
+    st = lib().mxq_quantize_mxfp4_hadamard(_dev_ptr(x, "x", torch.bfloat16), m, k, k,
+                                            _dev_ptr(mult, "mult", torch.float32), _dev_ptr(codes, "codes"),
+                                            _dev_ptr(scales, "scales"), _stream_handle(stream))
+    _check(st, "quantize_mxfp4_hadamard")
+    return codes, scales
+
+
 def gemm(mode, a_codes, a_scales, w_codes, w_scales, bias=None, epilogue=EPI_NONE, y=None, stream=None):
     """Scaled GEMM on quantized operands -> y bf16 [M, N]."""
     torch = _torch()
@@ -348,4 +394,28 @@ def qlinear(policy, expert, block, x, w_codes, w_scales, bias=None, epilogue=EPI
                             _dev_ptr(y, "y", torch.bfloat16), _dev_ptr(workspace, "workspace", torch.uint8),
                             int(workspace.numel()), _stream_handle(stream))
     _check(st, "qlinear")
+    return y
+
+
+def qlinear_transform(policy, expert, block, x, w_codes, w_scales, act_mult=None, bias=None, epilogue=EPI_NONE,
+                      y=None, workspace=None, stream=None):
+    """qlinear for tables with transform_on blocks: such a block quantizes x with its ``act_mult``."""
+    torch = _torch()
+    handle = policy.handle if isinstance(policy, Policy) else policy
+    m, k = _rows_k(x, "x")
+    n = int(w_codes.shape[0])
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=x.device)
+    if workspace is None:
+        mode = policy_mode(handle, expert, block)
+        workspace = torch.empty((max(qlinear_workspace_bytes(mode, m, k), 1),), dtype=torch.uint8,
+                                device=x.device)
+    st = lib().mxq_qlinear_transform(handle, int(expert), int(block), _dev_ptr(x, "x", torch.bfloat16), m, k,
+                                      _dev_ptr(w_codes, "w_codes", torch.uint8),
+                                      _dev_ptr(w_scales, "w_scales", torch.uint8), n,
+                                      _dev_ptr(bias, "bias", torch.bfloat16), int(epilogue),
+                                      _dev_ptr(act_mult, "act_mult", torch.float32),
+                                      _dev_ptr(y, "y", torch.bfloat16), _dev_ptr(workspace, "workspace", torch.uint8),
+                                      int(workspace.numel()), _stream_handle(stream))
+    _check(st, "qlinear_transform")
     return y

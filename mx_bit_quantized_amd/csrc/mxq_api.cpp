@@ -102,6 +102,40 @@ int mxq_quantize_act(int mode, const void* x, int64_t M, int64_t K, int64_t ldx,
   return hip_status(mxq::launch_fp8_quant(x, M, K, ldx, codes, scales, stream));
 }
 
+int mxq_hadamard_channel_amax(const void* x, int64_t M, int64_t K, int64_t ldx, float* amax, hipStream_t stream) {
+  int st = check_mk(M, K, ldx);
+  if (st != MXQ_OK) return st;
+  if (K % 128 != 0) return MXQ_ERR_SHAPE;
+  if (M == 0) return MXQ_OK;
+  if (x == nullptr || amax == nullptr) return MXQ_ERR_NULL;
+  if (!aligned16(x) || ldx % 8 != 0 || (reinterpret_cast<uintptr_t>(amax) & 3u) != 0) return MXQ_ERR_ALIGN;
+  if (log_enabled()) fprintf(stderr, "[mxq] hadamard_channel_amax M=%lld K=%lld\n", (long long)M, (long long)K);
+  return hip_status(mxq::launch_hadamard_amax(x, M, K, ldx, amax, stream));
+}
+
+int mxq_smoothquant_factors(const float* act_amax, const float* w_amax, int64_t K, float* act_mult,
+                            float* w_mult, hipStream_t stream) {
+  if (K < 0 || K >= kMaxDim) return MXQ_ERR_SHAPE;
+  if (K == 0) return MXQ_OK;
+  if (act_amax == nullptr || w_amax == nullptr || act_mult == nullptr || w_mult == nullptr) return MXQ_ERR_NULL;
+  for (const void* p : {(const void*)act_amax, (const void*)w_amax, (const void*)act_mult, (const void*)w_mult})
+    if ((reinterpret_cast<uintptr_t>(p) & 3u) != 0) return MXQ_ERR_ALIGN;
+  return hip_status(mxq::launch_smoothquant_factors(act_amax, w_amax, K, act_mult, w_mult, stream));
+}
+
+int mxq_quantize_mxfp4_hadamard(const void* x, int64_t M, int64_t K, int64_t ldx, const float* mult,
+                                void* codes, void* scales, hipStream_t stream) {
+  int st = check_mk(M, K, ldx);
+  if (st != MXQ_OK) return st;
+  if (K % 128 != 0) return MXQ_ERR_SHAPE;
+  if (M == 0) return MXQ_OK;
+  if (x == nullptr || mult == nullptr || codes == nullptr || scales == nullptr) return MXQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(mult) || !aligned16(codes) || !aligned16(scales) || ldx % 8 != 0)
+    return MXQ_ERR_ALIGN;
+  if (log_enabled()) fprintf(stderr, "[mxq] quantize_mxfp4_hadamard M=%lld K=%lld\n", (long long)M, (long long)K);
+  return hip_status(mxq::launch_mxfp4_hadamard_quant(x, M, K, ldx, mult, codes, scales, stream));
+}
+
 int mxq_fp8_calibrate(const void* x, int64_t M, int64_t K, int64_t ldx, float* amax, hipStream_t stream) {
   int st = check_mk(M, K, ldx);
   if (st != MXQ_OK) return st;
@@ -204,7 +238,7 @@ int mxq_policy_create(const uint8_t* modes, int32_t n_experts, int32_t n_blocks,
   if (modes == nullptr) return MXQ_ERR_NULL;
   const size_t n = (size_t)n_experts * (size_t)n_blocks;
   for (size_t i = 0; i < n; ++i)
-    if (modes[i] != MXQ_W4A4 && modes[i] != MXQ_W4A8) return MXQ_ERR_MODE;
+    if (modes[i] != MXQ_W4A4 && modes[i] != MXQ_W4A8 && modes[i] != MXQ_POLICY_TRANSFORM_ON) return MXQ_ERR_MODE;
   Policy* p = new (std::nothrow) Policy;
   if (p == nullptr) return MXQ_ERR_HIP;
   p->n_experts = n_experts;
@@ -229,12 +263,47 @@ int mxq_policy_mode(const void* policy, int32_t expert, int32_t block, int* mode
 
 int mxq_qlinear_workspace_bytes(int mode, int64_t M, int64_t K, size_t* bytes) {
   if (bytes == nullptr) return MXQ_ERR_NULL;
-  if (mode != MXQ_W4A4 && mode != MXQ_W4A8) return MXQ_ERR_MODE;
+  if (mode != MXQ_W4A4 && mode != MXQ_W4A8 && mode != MXQ_POLICY_TRANSFORM_ON) return MXQ_ERR_MODE;
   int st = check_mk(M, K, K);
   if (st != MXQ_OK) return st;
   size_t cb = 0;
-  workspace_layout(mode, M, K, &cb, bytes);
+  workspace_layout(mode == MXQ_W4A8 ? MXQ_W4A8 : MXQ_W4A4, M, K, &cb, bytes);
   return MXQ_OK;
+}
+
+// Shared body of mxq_qlinear and mxq_qlinear_transform: `allow_transform`
+// says whether a transform_on block may run (with act_mult).
+static int qlinear_impl(const void* policy, int32_t expert, int32_t block, const void* x, int64_t M, int64_t K,
+                        const void* w_codes, const void* w_scales, int64_t N, const void* bias, int epilogue,
+                        bool allow_transform, const float* act_mult, void* y, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  int mode = 0;
+  int st = mxq_policy_mode(policy, expert, block, &mode);
+  if (st != MXQ_OK) return st;
+  const bool transform = mode == MXQ_POLICY_TRANSFORM_ON;
+  if (transform && !allow_transform) return MXQ_ERR_MODE;
+  if (epilogue != MXQ_EPI_NONE && epilogue != MXQ_EPI_GELU_TANH) return MXQ_ERR_MODE;
+  st = check_mk(M, K, K);
+  if (st != MXQ_OK) return st;
+  if (transform && K % 128 != 0) return MXQ_ERR_SHAPE;
+  if (N < 0 || N >= kMaxDim) return MXQ_ERR_SHAPE;
+  if (M == 0 || N == 0) return MXQ_OK;
+  if (x == nullptr || w_codes == nullptr || w_scales == nullptr || y == nullptr) return MXQ_ERR_NULL;
+  if (transform && act_mult == nullptr) return MXQ_ERR_NULL;
+  if (workspace == nullptr) return MXQ_ERR_WORKSPACE;
+  const int gemm_mode = mode == MXQ_W4A8 ? MXQ_W4A8 : MXQ_W4A4;
+  size_t codes_bytes = 0, need = 0;
+  workspace_layout(gemm_mode, M, K, &codes_bytes, &need);
+  if (workspace_bytes < need) return MXQ_ERR_WORKSPACE;
+  if (!aligned16(x) || !aligned16(w_codes) || !aligned16(w_scales) || !aligned16(y) ||
+      !aligned16(workspace) || (bias != nullptr && !aligned16(bias)) || (transform && !aligned16(act_mult)))
+    return MXQ_ERR_ALIGN;
+  void* a_codes = workspace;
+  void* a_scales = static_cast<uint8_t*>(workspace) + codes_bytes;
+  st = transform ? mxq_quantize_mxfp4_hadamard(x, M, K, K, act_mult, a_codes, a_scales, stream)
+                 : mxq_quantize_act(mode, x, M, K, K, a_codes, a_scales, stream);
+  if (st != MXQ_OK) return st;
+  return mxq_gemm(gemm_mode, a_codes, a_scales, w_codes, w_scales, bias, epilogue, y, M, N, K, stream);
 }
 
 int mxq_qlinear(const void* policy, int32_t expert, int32_t block,
@@ -242,27 +311,17 @@ int mxq_qlinear(const void* policy, int32_t expert, int32_t block,
                 const void* w_codes, const void* w_scales, int64_t N,
                 const void* bias, int epilogue, void* y,
                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  int mode = 0;
-  int st = mxq_policy_mode(policy, expert, block, &mode);
-  if (st != MXQ_OK) return st;
-  if (epilogue != MXQ_EPI_NONE && epilogue != MXQ_EPI_GELU_TANH) return MXQ_ERR_MODE;
-  st = check_mk(M, K, K);
-  if (st != MXQ_OK) return st;
-  if (N < 0 || N >= kMaxDim) return MXQ_ERR_SHAPE;
-  if (M == 0 || N == 0) return MXQ_OK;
-  if (x == nullptr || w_codes == nullptr || w_scales == nullptr || y == nullptr) return MXQ_ERR_NULL;
-  if (workspace == nullptr) return MXQ_ERR_WORKSPACE;
-  size_t codes_bytes = 0, need = 0;
-  workspace_layout(mode, M, K, &codes_bytes, &need);
-  if (workspace_bytes < need) return MXQ_ERR_WORKSPACE;
-  if (!aligned16(x) || !aligned16(w_codes) || !aligned16(w_scales) || !aligned16(y) ||
-      !aligned16(workspace) || (bias != nullptr && !aligned16(bias)))
-    return MXQ_ERR_ALIGN;
-  void* a_codes = workspace;
-  void* a_scales = static_cast<uint8_t*>(workspace) + codes_bytes;
-  st = mxq_quantize_act(mode, x, M, K, K, a_codes, a_scales, stream);
-  if (st != MXQ_OK) return st;
-  return mxq_gemm(mode, a_codes, a_scales, w_codes, w_scales, bias, epilogue, y, M, N, K, stream);
+  return qlinear_impl(policy, expert, block, x, M, K, w_codes, w_scales, N, bias, epilogue, false, nullptr, y,
+                      workspace, workspace_bytes, stream);
+}
+
+int mxq_qlinear_transform(const void* policy, int32_t expert, int32_t block,
+                          const void* x, int64_t M, int64_t K,
+                          const void* w_codes, const void* w_scales, int64_t N,
+                          const void* bias, int epilogue, const float* act_mult, void* y,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return qlinear_impl(policy, expert, block, x, M, K, w_codes, w_scales, N, bias, epilogue, true, act_mult, y,
+                      workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

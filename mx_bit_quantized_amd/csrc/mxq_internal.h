@@ -13,6 +13,15 @@ hipError_t launch_mxfp4_quant(const void* x, int64_t rows, int64_t K, int64_t ld
 hipError_t launch_fp8_quant(const void* x, int64_t rows, int64_t K, int64_t ld,
                             void* codes, void* scales, hipStream_t s);
 
+// transform_on: MXFP4 codes and scales of RN_bf16(hadamard128(x) * mult)
+// (K % 128 == 0); the per-channel rotated amax for SmoothQuant calibration
+// (running maximum, amax [K]); the SmoothQuant factor vectors from two of them.
+hipError_t launch_mxfp4_hadamard_quant(const void* x, int64_t rows, int64_t K, int64_t ld, const float* mult,
+                                       void* codes, void* scales, hipStream_t s);
+hipError_t launch_hadamard_amax(const void* x, int64_t rows, int64_t K, int64_t ld, float* amax, hipStream_t s);
+hipError_t launch_smoothquant_factors(const float* act_amax, const float* w_amax, int64_t K, float* act_mult,
+                                      float* w_mult, hipStream_t s);
+
 // Static FP8: codes with the one scale amax / 448 (amax: device fp32), every
 // row's scale slot set to it.
 hipError_t launch_fp8_static_quant(const void* x, int64_t rows, int64_t K, int64_t ld, const float* amax,

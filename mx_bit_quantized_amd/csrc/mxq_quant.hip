@@ -9,6 +9,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "mxq_convert.h"
 #include "mxq_internal.h"
 
@@ -64,9 +66,10 @@ constexpr int kQuantWaves = 4;  // waves per workgroup
 constexpr int kMxRows = 16;     // rows per wave unit
 constexpr int kMxPanels = 4;    // panels per wave unit (fewer in the last one)
 
+// Max over the 4 lanes of a quad, by DPP quad permutations (lane ^ 1, lane ^ 2).
 __device__ __forceinline__ uint32_t quad_max(uint32_t v) {
-  v = umax(v, (uint32_t)__shfl_xor((int)v, 1));
-  v = umax(v, (uint32_t)__shfl_xor((int)v, 2));
+  v = umax(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));
+  v = umax(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));
   return v;
 }
 
@@ -213,6 +216,241 @@ __global__ __launch_bounds__(64 * kQuantWaves) void fp8_quant_kernel(
   }
 }
 
+// ---------------------------------------------------- transform_on -------
+//
+// The transform_on mode keeps a block on W4A4 but rotates the K dimension of
+// each linear's input by a fixed block-diagonal Walsh-Hadamard matrix (one
+// 128-point block per MXFP4 code panel) and rescales each channel
+// (SmoothQuant), the weight offline with the inverse rescale; see section
+// "Mixed-Precision selection" of the page. The arithmetic is fp32 in a fixed
+// order: butterflies for h = 1, 2, 4 (inside a lane's 8 elements), then
+// h = 8, 16, 32, 64 (lanes whose chunk index differs in bit h / 8), each an
+// fp32 a + b or a - b; then one fp32 multiply by the channel's factor (which
+// holds 1 / sqrt(128)); then rounding to bf16 and the MXFP4 rule above.
+
+constexpr uint32_t kInvSqrt128Bits = 0x3DB504F3u;  // RN(1 / sqrt(128)) in fp32
+
+// 128-point transform of one row panel held by 16 lanes, 8 elements each:
+// lane chunk c holds elements 8c .. 8c + 7. Every lane of the wave takes part
+// in the exchanges (no lane may be inactive here).
+//
+// Stages h = 1, 2, 4 run inside the lane. Stages h = 8, 16, 32, 64 pair the
+// lanes whose chunk index differs in bit 1, 2, 4, 8 (lane ^ 1, ^ 2, ^ 4, ^ 8
+// within the 16-lane row). They keep a known sign per lane: afterwards the
+// lane holds (-1)^popcount(c) times the transform (callers fold that sign
+// into the channel factor, an exact change). In that form each stage is one
+// fused multiply-add of the partner's value, read through DPP, into the
+// lane's own: with u = s v (the partner's sign equal to the lane's s before
+// the stage), the lane whose bit is clear computes u_p + u = s (a + b) and
+// keeps its sign, the other computes u - u_p = -s (a - b) and flips it. Each
+// is one rounding of a + b or a - b, up to that sign; only the sign of an
+// exact zero is lost, and callers turn every exact zero into +0.
+// The DPP patterns: lane ^ 1 and ^ 2 are quad permutations, ^ 8 the row
+// rotation by 8, ^ 4 the half-row mirror (lane ^ 7) then the quad
+// permutation lane ^ 3. All are their own inverses, so no direction
+// convention matters. A DPP read of a register needs two wait states after
+// a VALU write of it: the block opens with them, and inside it every DPP
+// source was written eight instructions earlier.
+__device__ __forceinline__ void fwht128_lanes(float (&f)[8], int c) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if ((e & h) == 0) {
+        const float a = f[e], b = f[e + h];
+        f[e] = a + b;
+        f[e + h] = a - b;
+      }
+  const float s1 = (c & 1) ? -1.0f : 1.0f, s2 = (c & 2) ? -1.0f : 1.0f;
+  const float s4 = (c & 4) ? -1.0f : 1.0f, s8 = (c & 8) ? -1.0f : 1.0f;
+  float t0, t1, t2, t3, t4, t5, t6, t7;
+#define MXQ_DPP_FMAC(D, S, SG, PAT) "v_fmac_f32_dpp " D ", " S ", " SG " " PAT " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+#define MXQ_DPP_MOV(D, S, PAT) "v_mov_b32_dpp " D ", " S " " PAT " row_mask:0xf bank_mask:0xf bound_ctrl:1\n\t"
+#define MXQ_STAGE8(SG, PAT)                                                                                   \
+  MXQ_DPP_FMAC("%0", "%0", SG, PAT) MXQ_DPP_FMAC("%1", "%1", SG, PAT) MXQ_DPP_FMAC("%2", "%2", SG, PAT)      \
+  MXQ_DPP_FMAC("%3", "%3", SG, PAT) MXQ_DPP_FMAC("%4", "%4", SG, PAT) MXQ_DPP_FMAC("%5", "%5", SG, PAT)      \
+  MXQ_DPP_FMAC("%6", "%6", SG, PAT) MXQ_DPP_FMAC("%7", "%7", SG, PAT)
+  asm volatile(
+      "s_nop 1\n\t"
+      MXQ_STAGE8("%16", "quad_perm:[1,0,3,2]")
+      MXQ_STAGE8("%17", "quad_perm:[2,3,0,1]")
+      MXQ_DPP_MOV("%8", "%0", "row_half_mirror") MXQ_DPP_MOV("%9", "%1", "row_half_mirror")
+      MXQ_DPP_MOV("%10", "%2", "row_half_mirror") MXQ_DPP_MOV("%11", "%3", "row_half_mirror")
+      MXQ_DPP_MOV("%12", "%4", "row_half_mirror") MXQ_DPP_MOV("%13", "%5", "row_half_mirror")
+      MXQ_DPP_MOV("%14", "%6", "row_half_mirror") MXQ_DPP_MOV("%15", "%7", "row_half_mirror")
+      MXQ_DPP_FMAC("%0", "%8", "%18", "quad_perm:[3,2,1,0]") MXQ_DPP_FMAC("%1", "%9", "%18", "quad_perm:[3,2,1,0]")
+      MXQ_DPP_FMAC("%2", "%10", "%18", "quad_perm:[3,2,1,0]") MXQ_DPP_FMAC("%3", "%11", "%18", "quad_perm:[3,2,1,0]")
+      MXQ_DPP_FMAC("%4", "%12", "%18", "quad_perm:[3,2,1,0]") MXQ_DPP_FMAC("%5", "%13", "%18", "quad_perm:[3,2,1,0]")
+      MXQ_DPP_FMAC("%6", "%14", "%18", "quad_perm:[3,2,1,0]") MXQ_DPP_FMAC("%7", "%15", "%18", "quad_perm:[3,2,1,0]")
+      MXQ_STAGE8("%19", "row_ror:8")
+      : "+v"(f[0]), "+v"(f[1]), "+v"(f[2]), "+v"(f[3]), "+v"(f[4]), "+v"(f[5]), "+v"(f[6]), "+v"(f[7]),
+        "=&v"(t0), "=&v"(t1), "=&v"(t2), "=&v"(t3), "=&v"(t4), "=&v"(t5), "=&v"(t6), "=&v"(t7)
+      : "v"(s1), "v"(s2), "v"(s4), "v"(s8));
+#undef MXQ_STAGE8
+#undef MXQ_DPP_MOV
+#undef MXQ_DPP_FMAC
+}
+
+__device__ __forceinline__ void bf16x8_to_f32(const uint4 v, float (&f)[8]) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[2 * i] = as_float(w[i] << 16);
+    f[2 * i + 1] = as_float(w[i] & 0xFFFF0000u);
+  }
+}
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  const f32x2_t f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+// The MXFP4 quantizer's mapping and stores, on transformed rows: each step's
+// 16 lanes of a row panel transform their 128 elements together, apply the
+// channel factors as RN(t * mult + 0), round to bf16, and continue exactly as
+// the plain quantizer. K is a multiple of 128 (whole panels).
+__global__ __launch_bounds__(64 * kQuantWaves) void mxfp4_hadamard_quant_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t K, int64_t ld, const float* __restrict__ mult,
+    uint8_t* __restrict__ codes, uint32_t* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int64_t unit0 = (int64_t)blockIdx.x * kQuantWaves + (threadIdx.x >> 6);
+  const int64_t n_waves = (int64_t)gridDim.x * kQuantWaves;
+  const int n_panels = (int)(K >> 7);
+  const int pchunks = (n_panels + kMxPanels - 1) / kMxPanels;
+  const int64_t units = (rows + kMxRows - 1) / kMxRows * pchunks;
+  const int rs = lane >> 4, c = lane & 15;
+  for (int64_t u = unit0; u < units; u += n_waves) {
+    const int64_t row0 = u / pchunks * kMxRows;
+    const int p0 = (int)(u % pchunks) * kMxPanels;
+    uint4 v[kMxPanels][4];
+#pragma unroll
+    for (int pp = 0; pp < kMxPanels; ++pp)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int64_t row = row0 + 4 * t + rs;
+        const bool ok = row < rows && p0 + pp < n_panels;
+        v[pp][t] = ok ? reinterpret_cast<const uint4*>(x + row * ld)[16 * (int64_t)(p0 + pp) + c]
+                      : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+    for (int pp = 0; pp < kMxPanels; ++pp) {
+      const int p = p0 + pp;
+      float m[8];
+      if (p < n_panels) {
+        // the factors with the lane's sign from the transform folded in
+        const uint32_t neg = (uint32_t)(__builtin_popcount(c) & 1) << 31;
+        const float4 m0 = reinterpret_cast<const float4*>(mult + 128 * (int64_t)p + 8 * c)[0];
+        const float4 m1 = reinterpret_cast<const float4*>(mult + 128 * (int64_t)p + 8 * c)[1];
+        m[0] = m0.x; m[1] = m0.y; m[2] = m0.z; m[3] = m0.w;
+        m[4] = m1.x; m[5] = m1.y; m[6] = m1.z; m[7] = m1.w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m[e] = as_float(as_uint(m[e]) ^ neg);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m[e] = 0.0f;
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int64_t row = row0 + 4 * t + rs;
+        float f[8];
+        bf16x8_to_f32(v[pp][t], f);
+        fwht128_lanes(f, c);
+        // RN(t * mult + 0): exact zeros become +0 (their sign is not known here)
+        float q[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) q[e] = __builtin_fmaf(f[e], m[e], 0.0f);
+        uint4 tv;
+        tv.x = bf16x2_rne(q[0], q[1]);
+        tv.y = bf16x2_rne(q[2], q[3]);
+        tv.z = bf16x2_rne(q[4], q[5]);
+        tv.w = bf16x2_rne(q[6], q[7]);
+        const uint32_t amax = quad_max(chunk_amax(tv));
+        const uint32_t sb = mx_scale_byte(amax);
+        const uint32_t packed = pack8_fp4(tv, sb);
+        const uint32_t s1 = (uint32_t)__shfl_down((int)sb, 4);
+        const uint32_t s2 = (uint32_t)__shfl_down((int)sb, 8);
+        const uint32_t s3 = (uint32_t)__shfl_down((int)sb, 12);
+        if (row < rows && p < n_panels) {
+          *reinterpret_cast<uint32_t*>(codes + (int64_t)p * 64 * rows + row * 64 + 4 * c) = packed;
+          if (c == 0) scales[(int64_t)p * rows + row] = sb | (s1 << 8) | (s2 << 16) | (s3 << 24);
+        }
+      }
+    }
+  }
+}
+
+// Calibration for SmoothQuant: per-channel max |transform(x)| (unnormalized
+// butterflies, no factor) over the rows, folded into a running maximum
+// amax[K] (fp32 bit patterns, non-negative: unsigned atomic max). Workgroup
+// (panel p, row split): its 4 waves take 4 rows per step each; lane chunk c
+// keeps the maxima of channels 128p + 8c .. + 7; one atomic per channel per
+// workgroup.
+constexpr int kAmaxRowsUnroll = 4;
+
+__global__ __launch_bounds__(64 * kQuantWaves) void hadamard_amax_kernel(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t K, int64_t ld, int64_t rows_per_split,
+    uint32_t* __restrict__ amax_bits) {
+  __shared__ uint32_t red[kQuantWaves][128];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int rs = lane >> 4, c = lane & 15;
+  const int p = blockIdx.x;
+  const int64_t r_begin = (int64_t)blockIdx.y * rows_per_split;
+  const int64_t r_end = r_begin + rows_per_split < rows ? r_begin + rows_per_split : rows;
+  uint32_t m[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  constexpr int STEP = 4 * kQuantWaves;  // rows per workgroup step
+  for (int64_t r0 = r_begin + 4 * wave; r0 < r_end; r0 += STEP * kAmaxRowsUnroll) {
+    uint4 v[kAmaxRowsUnroll];
+#pragma unroll
+    for (int i = 0; i < kAmaxRowsUnroll; ++i) {
+      const int64_t row = r0 + STEP * i + rs;
+      v[i] = row < r_end ? reinterpret_cast<const uint4*>(x + row * ld)[16 * (int64_t)p + c] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kAmaxRowsUnroll; ++i) {
+      float f[8];
+      bf16x8_to_f32(v[i], f);
+      fwht128_lanes(f, c);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m[e] = umax(m[e], as_uint(f[e]) & 0x7FFFFFFFu);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    m[e] = umax(m[e], (uint32_t)__shfl_xor((int)m[e], 16));
+    m[e] = umax(m[e], (uint32_t)__shfl_xor((int)m[e], 32));
+  }
+  if (rs == 0) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[wave][8 * c + e] = m[e];
+  }
+  __syncthreads();
+  if (threadIdx.x < 128) {
+    uint32_t b = red[0][threadIdx.x];
+#pragma unroll
+    for (int w = 1; w < kQuantWaves; ++w) b = umax(b, red[w][threadIdx.x]);
+    if (b != 0) atomicMax(amax_bits + 128 * (int64_t)p + threadIdx.x, b);
+  }
+}
+
+// SmoothQuant factors at migration strength 0.5: lambda = sqrt(ax / aw) (1
+// where either maximum is 0), act_mult = RN(RN(1 / lambda) / sqrt(128)),
+// w_mult = RN(lambda / sqrt(128)), with 1 / sqrt(128) the fp32 constant above
+// (IEEE division and square root).
+__global__ void smoothquant_factor_kernel(const float* __restrict__ ax, const float* __restrict__ aw, int64_t K,
+                                          float* __restrict__ act_mult, float* __restrict__ w_mult) {
+  const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (k >= K) return;
+  const float a = ax[k], w = aw[k];
+  const float lam = (a > 0.0f && w > 0.0f) ? __builtin_sqrtf(a / w) : 1.0f;
+  const float c0 = as_float(kInvSqrt128Bits);
+  const float inv = 1.0f / lam;
+  act_mult[k] = inv * c0;
+  w_mult[k] = lam * c0;
+}
+
 // ------------------------------------------------------ FP8 static -------
 //
 // Static (per-tensor) FP8: one scale s = amax / 448 for the whole tensor,
@@ -349,6 +587,41 @@ hipError_t launch_fp8_quant(const void* x, int64_t rows, int64_t K, int64_t ld,
     hipLaunchKernelGGL(fp8_quant_row_kernel<28>, grid, block, 0, s, xs, rows, K, ld, cs, ss);
   else
     hipLaunchKernelGGL(fp8_quant_kernel, grid, block, 0, s, xs, rows, K, ld, cs, ss);
+  return hipGetLastError();
+}
+
+hipError_t launch_mxfp4_hadamard_quant(const void* x, int64_t rows, int64_t K, int64_t ld, const float* mult,
+                                       void* codes, void* scales, hipStream_t s) {
+  const int64_t pchunks = (K / 128 + kMxPanels - 1) / kMxPanels;
+  const int64_t units = (rows + kMxRows - 1) / kMxRows * pchunks;
+  int64_t blocks = (units + kQuantWaves - 1) / kQuantWaves;
+  if (blocks > (1 << 16)) blocks = 1 << 16;  // units loop beyond
+  hipLaunchKernelGGL(mxfp4_hadamard_quant_kernel, dim3((unsigned)blocks), dim3(64 * kQuantWaves), 0, s,
+                     static_cast<const uint16_t*>(x), rows, K, ld, mult, static_cast<uint8_t*>(codes),
+                     static_cast<uint32_t*>(scales));
+  return hipGetLastError();
+}
+
+hipError_t launch_hadamard_amax(const void* x, int64_t rows, int64_t K, int64_t ld, float* amax, hipStream_t s) {
+  const int64_t panels = K / 128;
+  const int64_t step = 4 * kQuantWaves;
+  // about 2048 workgroups in all; each split a multiple of the workgroup step
+  int64_t splits = (2048 + panels - 1) / panels;
+  const int64_t max_splits = (rows + step - 1) / step;
+  splits = splits < max_splits ? splits : max_splits;
+  splits = splits > 0 ? splits : 1;
+  int64_t per = (rows + splits - 1) / splits;
+  per = (per + step - 1) / step * step;
+  splits = (rows + per - 1) / per;
+  hipLaunchKernelGGL(hadamard_amax_kernel, dim3((unsigned)panels, (unsigned)splits), dim3(64 * kQuantWaves), 0, s,
+                     static_cast<const uint16_t*>(x), rows, K, ld, per, reinterpret_cast<uint32_t*>(amax));
+  return hipGetLastError();
+}
+
+hipError_t launch_smoothquant_factors(const float* act_amax, const float* w_amax, int64_t K, float* act_mult,
+                                      float* w_mult, hipStream_t s) {
+  hipLaunchKernelGGL(smoothquant_factor_kernel, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, s, act_amax,
+                     w_amax, K, act_mult, w_mult);
   return hipGetLastError();
 }
 

@@ -64,6 +64,7 @@ from .transform import (
 from .linear import (
     W4A4,
     W4A8,
+    TRANSFORM_ON,
     EPI_NONE,
     EPI_GELU_TANH,
     gelu_tanh,
@@ -71,6 +72,7 @@ from .linear import (
     quantize_act,
     dequantize_act,
     qlinear,
+    qlinear_transform,
     policy_mode,
     output_tolerance_ok,
     output_error_report,

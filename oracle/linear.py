@@ -30,6 +30,7 @@ from .quant import (
 
 W4A4 = 0
 W4A8 = 1
+TRANSFORM_ON = 3  # W4A4 behind the Hadamard + SmoothQuant transform (policy value)
 EPI_NONE = 0
 EPI_GELU_TANH = 1
 
@@ -73,13 +74,17 @@ def qdq_matmul(mode, a_codes, a_scales, w_codes, w_scales, bias=None, epilogue=E
 
 
 def policy_mode(table, expert, block):
-    """Mode of (expert, block) in a [n_experts, n_blocks] table; rejects non-linear modes."""
+    """Mode of (expert, block) in a [n_experts, n_blocks] table.
+
+    W4A4, W4A8 and transform_on (the artifact's third quantized value) are
+    modes of the layer; the artifact's bf16 entry (2) and anything else are
+    rejected."""
     table = np.asarray(table)
     if not (0 <= expert < table.shape[0] and 0 <= block < table.shape[1]):
         raise IndexError("policy index out of range")
     mode = int(table[expert, block])
-    if mode not in (W4A4, W4A8):
-        raise ValueError(f"policy mode {mode} is not W4A4 or W4A8")
+    if mode not in (W4A4, W4A8, TRANSFORM_ON):
+        raise ValueError(f"policy mode {mode} is not W4A4, W4A8 or transform_on")
     return mode
 
 
@@ -115,3 +120,18 @@ def output_tolerance_ok(y, y_ref):
     """True iff y is finite and |y - y_ref| <= 2^-7 |y_ref| + 1e-3 rms(y_ref) everywhere."""
     rep = output_error_report(y, y_ref)
     return rep["finite"] and rep["worst_ratio"] <= 1.0
+
+
+def qlinear_transform(mode, x_bits, w_codes, w_scales, act_mult=None, bias=None, epilogue=EPI_NONE):
+    """qlinear for a policy that may hold transform_on blocks.
+
+    transform_on quantizes x with the transformed MXFP4 quantizer (act_mult) and
+    multiplies with the weight packed by it (w_mult); the product is the W4A4
+    QDQ matmul of those codes. Other modes are qlinear. Returns (y, a_codes, a_scales)."""
+    if mode != TRANSFORM_ON:
+        return qlinear(mode, x_bits, w_codes, w_scales, bias, epilogue)
+    from .transform import mxfp4_quantize_hadamard
+
+    a_codes, a_scales = mxfp4_quantize_hadamard(x_bits, act_mult)
+    y = qdq_matmul(W4A4, a_codes, a_scales, w_codes, w_scales, bias, epilogue)
+    return y, a_codes, a_scales

@@ -27,6 +27,11 @@ Readings recorded in the design notes:
   activation, w_mult_k = RN(lambda_k * RN(1 / sqrt(128))) for the weight), and
   the result is rounded to bf16, the activation dtype, before the usual MXFP4
   quantizer.
+* An output of the rotation that cancels exactly is +0: the factor is applied
+  as RN(t * mult + 0), which leaves every nonzero product (and the sign of one
+  that underflows) as RN(t * mult) and turns an exact zero into +0. The sign of
+  an exactly cancelling sum says nothing about the data, and the IEEE rules
+  would tie it to the order of the butterflies.
 """
 
 import numpy as np
@@ -88,9 +93,13 @@ def smoothquant_factors(act_amax, w_amax):
 
 
 def hadamard_transform_bf16(x_bits, mult):
-    """bf16 [R, K] -> the transformed tensor in bf16: RN_bf16(fwht128_f32(x) * mult) (uint16 bits)."""
-    t = fwht128_f32(bf16_bits_to_f32(_check_k(x_bits)))
-    t = (t * np.asarray(mult, dtype=np.float32)[None, :]).astype(np.float32)
+    """bf16 [R, K] -> the transformed tensor in bf16: RN_bf16(RN_fp32(fwht128_f32(x) * mult + 0)) (uint16 bits).
+
+    The fp32 product is exact in float64, so adding +0 there and rounding once
+    to fp32 is RN(t * mult + 0): an exact zero becomes +0, anything else is the
+    fp32 product."""
+    t = fwht128_f32(bf16_bits_to_f32(_check_k(x_bits))).astype(np.float64)
+    t = (t * np.asarray(mult, dtype=np.float32).astype(np.float64)[None, :] + 0.0).astype(np.float32)
     return f64_to_bf16_bits(t.astype(np.float64))
 
 

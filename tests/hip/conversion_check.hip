@@ -9,6 +9,9 @@
 //   mxq_check_fp8(counts, first): v_cvt_pk_fp8_f32 against e4m3fn_code for
 //     every fp32 with |q| <= 464 (the quotients of the FP8 quantizer stay
 //     below 448 (1 + 2^-22)), both signs.
+//   mxq_check_bf16(counts, first): v_cvt_pk_bf16_f32 against bf16_rne for
+//     every non-NaN fp32 (infinities, subnormals and zeros included), both
+//     signs (the transformed MXFP4 quantizer rounds its fp32 values with it).
 // counts[0] receives the number of mismatches, counts[1] the number of cases;
 // first[] the first (input, reference, result) triples. Returns 0, or 1/2 on
 // a HIP error.
@@ -59,6 +62,21 @@ __global__ void fp8_kernel(unsigned long long* counts, uint32_t* first, uint32_t
   if (hw != ref) note(counts, first, a, ref, hw);
 }
 
+typedef float v2f_t __attribute__((ext_vector_type(2)));
+
+__global__ void bf16_kernel(unsigned long long* counts, uint32_t* first) {
+  const uint32_t a = blockIdx.x * 256u + threadIdx.x;  // every pattern with the sign bit clear
+  const bool live = a <= 0x7F800000u;                   // not NaN
+  const int n_live = __syncthreads_count(live);
+  if (threadIdx.x == 0) atomicAdd(&counts[1], 2ull * (unsigned long long)n_live);
+  if (!live) return;
+  const float q = as_float(a), nq = as_float(a | 0x80000000u);
+  const uint32_t ref = bf16_rne(q) | (bf16_rne(nq) << 16);
+  const v2f_t f = {q, nq};
+  const uint32_t hw = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+  if (hw != ref) note(counts, first, a, ref, hw);
+}
+
 static int finish(unsigned long long* d_counts, uint32_t* d_first, unsigned long long* counts, uint32_t* first) {
   if (hipDeviceSynchronize() != hipSuccess) return 2;
   if (hipMemcpy(counts, d_counts, 16, hipMemcpyDeviceToHost) != hipSuccess) return 2;
@@ -89,6 +107,15 @@ extern "C" int mxq_check_fp8(unsigned long long* counts, uint32_t* first) {
   if (setup(&dc, &df)) return 1;
   const uint32_t limit = 0x43E80000u;  // 464.0f
   hipLaunchKernelGGL(fp8_kernel, dim3(limit / 256u + 1u), dim3(256), 0, 0, dc, df, limit);
+  if (hipGetLastError() != hipSuccess) return 1;
+  return finish(dc, df, counts, first);
+}
+
+extern "C" int mxq_check_bf16(unsigned long long* counts, uint32_t* first) {
+  unsigned long long* dc;
+  uint32_t* df;
+  if (setup(&dc, &df)) return 1;
+  hipLaunchKernelGGL(bf16_kernel, dim3(0x80000000u / 256u), dim3(256), 0, 0, dc, df);
   if (hipGetLastError() != hipSuccess) return 1;
   return finish(dc, df, counts, first);
 }

@@ -25,7 +25,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = mxq.lib()
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 19, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(mxq._SIGS)
@@ -150,6 +150,53 @@ def test_gemm_fp8_static_out_validation():
     assert L.mxq_gemm_fp8_static_out(*empty) == mxq.OK
 
 
+def test_transform_validation():
+    """Host-side checks of the transform_on entry points (nothing is enqueued)."""
+    L = mxq.lib()
+    S = None
+    F4 = ctypes.c_void_p(0x10004)  # 4-byte aligned only
+    # K must be a multiple of 128
+    for k in (0, 32, 96, 160):
+        assert L.mxq_quantize_mxfp4_hadamard(FAKE, 4, k, 256, FAKE, FAKE, FAKE, S) == mxq.ERR_SHAPE, k
+        assert L.mxq_hadamard_channel_amax(FAKE, 4, k, 256, FAKE, S) == mxq.ERR_SHAPE, k
+    assert L.mxq_quantize_mxfp4_hadamard(FAKE, 4, 128, 64, FAKE, FAKE, FAKE, S) == mxq.ERR_SHAPE  # ld < K
+    for pos in (0, 4, 5, 6):
+        args = [FAKE, 4, 128, 128, FAKE, FAKE, FAKE, S]
+        args[pos] = None
+        assert L.mxq_quantize_mxfp4_hadamard(*args) == mxq.ERR_NULL, pos
+    for pos in (0, 4, 5, 6):
+        args = [FAKE, 4, 128, 128, FAKE, FAKE, FAKE, S]
+        args[pos] = FAKE_ODD if pos != 4 else F4
+        assert L.mxq_quantize_mxfp4_hadamard(*args) == mxq.ERR_ALIGN, pos
+    assert L.mxq_hadamard_channel_amax(None, 4, 128, 128, FAKE, S) == mxq.ERR_NULL
+    assert L.mxq_hadamard_channel_amax(FAKE, 4, 128, 128, None, S) == mxq.ERR_NULL
+    assert L.mxq_hadamard_channel_amax(FAKE, 4, 128, 132, FAKE, S) == mxq.ERR_ALIGN  # ld % 8
+    for pos in (0, 1, 3, 4):
+        args = [FAKE, FAKE, 128, FAKE, FAKE, S]
+        args[pos] = None
+        assert L.mxq_smoothquant_factors(*args) == mxq.ERR_NULL, pos
+        args[pos] = ctypes.c_void_p(0x10002)
+        assert L.mxq_smoothquant_factors(*args) == mxq.ERR_ALIGN, pos
+    assert L.mxq_smoothquant_factors(FAKE, FAKE, -1, FAKE, FAKE, S) == mxq.ERR_SHAPE
+    assert L.mxq_smoothquant_factors(None, None, 0, None, None, S) == mxq.OK
+    assert L.mxq_quantize_mxfp4_hadamard(None, 0, 128, 128, None, None, None, S) == mxq.OK
+    # qlinear on a transform_on block: mxq_qlinear refuses (no factors); the transform
+    # entry point wants act_mult and K % 128 == 0
+    p = mxq.Policy([[3, 0]])
+    ws = mxq.qlinear_workspace_bytes(mxq.POLICY_TRANSFORM_ON, 4, 128)
+    assert ws == mxq.qlinear_workspace_bytes(mxq.W4A4, 4, 128)
+    assert L.mxq_qlinear(p.handle, 0, 0, FAKE, 4, 128, FAKE, FAKE, 8, None, 0, FAKE, FAKE, ws, S) == mxq.ERR_MODE
+    assert L.mxq_qlinear_transform(p.handle, 0, 0, FAKE, 4, 128, FAKE, FAKE, 8, None, 0, None, FAKE, FAKE, ws,
+                                   S) == mxq.ERR_NULL
+    assert L.mxq_qlinear_transform(p.handle, 0, 0, FAKE, 4, 96, FAKE, FAKE, 8, None, 0, FAKE, FAKE, FAKE, ws,
+                                   S) == mxq.ERR_SHAPE
+    assert L.mxq_qlinear_transform(p.handle, 0, 0, FAKE, 4, 128, FAKE, FAKE, 8, None, 0, F4, FAKE, FAKE, ws,
+                                   S) == mxq.ERR_ALIGN
+    assert L.mxq_qlinear_transform(p.handle, 0, 0, FAKE, 4, 128, FAKE, FAKE, 8, None, 0, FAKE, FAKE, FAKE, ws - 1,
+                                   S) == mxq.ERR_WORKSPACE
+    p.close()
+
+
 def test_static_fp8_validation():
     """Host-side checks of the static FP8 quantizer and its calibration (nothing is enqueued)."""
     L = mxq.lib()
@@ -188,7 +235,11 @@ def test_policy_table_roundtrip_and_errors():
             p.mode(e, b)
         assert ei.value.status == mxq.ERR_RANGE
     p.close()
-    for bad in ([[0, 2]], [[3, 0]], [[9]]):
+    # transform_on is a policy value (W4A4 with the Hadamard + SmoothQuant transform); bf16 is not
+    pt = mxq.Policy([[3, 0]])
+    assert pt.mode(0, 0) == mxq.POLICY_TRANSFORM_ON
+    pt.close()
+    for bad in ([[0, 2]], [[4, 0]], [[9]]):
         with pytest.raises(mxq.MxqError) as ei:
             mxq.Policy(bad)
         assert ei.value.status == mxq.ERR_MODE

@@ -1,7 +1,8 @@
 """Exhaustive GPU checks of the conversion instructions the quantizers use.
 
-The MXFP4 quantizer rounds with gfx950's scaled bf16 -> FP4 conversion and
-the FP8 quantizer with its fp32 -> E4M3 conversion. Each is compared on the
+The MXFP4 quantizer rounds with gfx950's scaled bf16 -> FP4 conversion, the
+FP8 quantizer with its fp32 -> E4M3 conversion, and the transformed MXFP4
+quantizer (and every bf16 output) with its fp32 -> bf16 conversion. Each is compared on the
 GPU with the software rounding of mxq_convert.h over its whole input domain
 (every finite bf16 at every block scale that can hold it; every fp32 quotient
 the FP8 quantizer can produce, both signs). The host build of that software
@@ -49,4 +50,11 @@ def test_fp8_conversion_matches_rounding_rule(lib):
     print("[case] fp8 conversion, every fp32 with |q| <= 464", flush=True)
     bad, cases, first = _run(lib, "mxq_check_fp8")
     assert cases == 2 * (0x43E80000 + 1), cases  # every fp32 pattern from +0 to 464.0, and its negative
+    assert bad == 0, f"{bad} mismatches of {cases}; first (case, want, got): {first[:min(bad, 8)].tolist()}"
+
+
+def test_bf16_conversion_matches_rounding_rule(lib):
+    print("[case] bf16 conversion, every non-NaN fp32", flush=True)
+    bad, cases, first = _run(lib, "mxq_check_bf16")
+    assert cases == 2 * (0x7F800000 + 1), cases  # +0 .. +inf and their negatives
     assert bad == 0, f"{bad} mismatches of {cases}; first (case, want, got): {first[:min(bad, 8)].tolist()}"

@@ -122,10 +122,11 @@ def test_policy_table_from_page_counts():
 
 
 def test_policy_rejects_other_modes_and_indices():
-    table = np.array([[0, 1, 2, 3]], np.uint8)
+    table = np.array([[0, 1, 2, 3, 4]], np.uint8)
     assert oracle.policy_mode(table, 0, 0) == oracle.W4A4
     assert oracle.policy_mode(table, 0, 1) == oracle.W4A8
-    for b in (2, 3):
+    assert oracle.policy_mode(table, 0, 3) == oracle.TRANSFORM_ON
+    for b in (2, 4):
         try:
             oracle.policy_mode(table, 0, b)
             raise AssertionError("accepted a non-linear mode")

@@ -149,6 +149,26 @@ def test_transform_lifts_sqnr_on_outlier_channels():
     assert sqnr(y_t) > sqnr(y_plain) + 1.0, (sqnr(y_t), sqnr(y_plain))
 
 
+def test_exact_zero_outputs_are_positive_and_underflow_keeps_its_sign():
+    """An exactly cancelling rotation output is +0 whatever the IEEE signs of the
+    butterflies; a nonzero product that rounds to zero keeps its sign."""
+    x = np.zeros((3, 128), np.float32)
+    x[0, :] = -0.0                  # every sum of -0's is -0 under IEEE; here it is +0
+    x[1, 0], x[1, 1] = 3.0, 3.0     # outputs with (-1)^k in bit 0 cancel exactly
+    x[2, 0] = -1.0                  # every output is -1 (times its sign pattern)
+    bits = synth.f32_to_bf16_bits(x)
+    bits[0, :] = 0x8000
+    t_raw = oracle.fwht128_f32(oracle.bf16_bits_to_f32(bits))
+    assert np.signbit(t_raw[0, 0])  # the butterflies alone give -0
+    tiny = np.full(128, np.float32(2.0 ** -140), np.float32)  # -1 * 2^-140 underflows bf16 to -0
+    out = oracle.hadamard_transform_bf16(bits, tiny)
+    assert np.all(out[0] == 0x0000)
+    assert np.all(out[1, 1::2] == 0x0000)                       # 3 - 3
+    # row 2 transforms to -1 everywhere; times 2^-140 it is a nonzero fp32 that
+    # rounds to zero in bf16 (below half of 2^-133), keeping its sign
+    assert np.all(out[2] == 0x8000)
+
+
 def test_rejects_k_not_multiple_of_128():
     with pytest.raises(ValueError):
         oracle.fwht128_f32(np.zeros((2, 96), np.float32))
