@@ -7,12 +7,18 @@ inputs and packed weights already resident in HBM. Weight packing is offline
 and is timed separately (reported, not part of the step).
 
     python bench.py [--steps K] [--warmup W] [--workload a14b_stack|a14b_ffn|qkv|ti2v|tiny]
-                    [--act-scale per_token|static]
+                    [--act-scale per_token|static] [--transform-on]
 
 --act-scale static runs the W4A8 linears on static (per-tensor) FP8
 activations: each input's amax is calibrated once, untimed, on the same
 synthetic inputs, and the FFN's first projection of a W4A8 block writes the
 hidden state's static FP8 codes itself. The default is the per-token scale.
+
+--transform-on runs every W4A4 block as transform_on: block Hadamard rotation
+plus SmoothQuant ahead of MXFP4. The factors are calibrated once, untimed, on
+the same synthetic inputs and on each weight, and the weights are packed
+transformed. Such a block's FFN runs up-projection -> bf16 h -> transformed
+quantizer -> down-projection (the fused MXFP4 epilogue does not rotate).
 
 Prints one JSON line. Per-launch kernel durations come from HIP events
 recorded on the launch stream around every kernel inside the timed steps.
@@ -45,6 +51,8 @@ def parse():
     ap.add_argument("--workload", default="a14b_stack", choices=sorted(WORKLOADS))
     ap.add_argument("--act-scale", default="per_token", choices=["per_token", "static"],
                     help="W4A8 activation scale: per token (amax/448 of each row) or static per tensor (calibrated)")
+    ap.add_argument("--transform-on", action="store_true",
+                    help="run the W4A4 blocks as transform_on (Hadamard rotation + SmoothQuant, calibrated)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=512)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -59,9 +67,10 @@ def log(*a):
 class Stack:
     """Packed weights, inputs and buffers of one workload on the device."""
 
-    def __init__(self, wl, torch, mxq, static=False):
+    def __init__(self, wl, torch, mxq, static=False, transform=False):
         self.wl, self.torch, self.mxq = wl, torch, mxq
         self.static = static
+        self.transform = transform
         dev = "cuda:0"
         t0 = time.time()
         self.policy_table = wl.policy()
@@ -74,6 +83,21 @@ class Stack:
             self.x_text = to_dev(synth.activation_bf16(wl.config_id, wl.m_text, wl.dim, wl.outliers,
                                                        tensor_id=synth.T_X_TEXT))
         log(f"activations ready in {time.time() - t0:.1f}s")
+        m_max = wl.m_video
+        n_max = max(l.n for l in wl.linears)
+        self.y = torch.empty((m_max * n_max,), dtype=torch.bfloat16, device=dev)
+        self.h = torch.empty((wl.m_video * max(wl.ffn, 1),), dtype=torch.bfloat16, device=dev)
+        ws = max(mxq.qlinear_workspace_bytes(md, m_max, l.k) for md in (0, 1) for l in wl.linears)
+        self.codes_buf = torch.empty((ws,), dtype=torch.uint8, device=dev)
+        # W4A4 FFN: the first projection writes the second one's MXFP4 input here
+        self.codes_buf2 = torch.empty((ws,), dtype=torch.uint8, device=dev)
+        # transform_on: rotated per-channel maxima of the shared inputs, and each
+        # linear's activation factors
+        self.act_mult = {}
+        if transform:
+            self.ax_role = {"video": mxq.hadamard_channel_amax(self.x_video)}
+            if self.x_text is not None:
+                self.ax_role["text"] = mxq.hadamard_channel_amax(self.x_text)
         # packed weights: drawn on the device per linear, packed, bf16 copy freed
         self.weights = {}
         pack_bytes, pack_ms = 0, 0.0
@@ -84,24 +108,36 @@ class Stack:
                     w = synth.weight_bf16_device(wl.config_id, lin.n, lin.k, e, b, li)
                     codes = torch.empty((lin.n, lin.k // 2), dtype=torch.uint8, device=dev)
                     scales = torch.empty(mxq.mx_scale_shape(lin.n, lin.k), dtype=torch.uint8, device=dev)
+                    tr = transform and self.policy.mode(e, b) == 0
+                    if tr:
+                        # calibration (untimed): the input's and the weight's rotated
+                        # maxima give the factors; the weight is packed transformed
+                        aw = mxq.hadamard_channel_amax(w)
+                        ax = ax_h if lin.m_role == "ffn_hidden" else self.ax_role[lin.m_role]
+                        am, wm = mxq.smoothquant_factors(ax, aw)
+                        self.act_mult[(e, b, li)] = am
                     ev0.record()
-                    mxq.quantize_weight_mxfp4(w, codes, scales)
+                    if tr:
+                        mxq.quantize_mxfp4_hadamard(w, wm, codes, scales)
+                    else:
+                        mxq.quantize_weight_mxfp4(w, codes, scales)
                     ev1.record()
                     torch.cuda.synchronize()
+                    if tr and lin.name == "ffn_up":
+                        # the hidden state of this block, for the second projection's maxima
+                        m = wl.m_of(lin)
+                        ac, asc = self._act_views(0, m, lin.k)
+                        xin = self.x_video if lin.m_role == "video" else self.x_text
+                        mxq.quantize_mxfp4_hadamard(xin, am, ac, asc)
+                        hv = self.h[: m * lin.n].view(m, lin.n)
+                        mxq.gemm(0, ac, asc, codes, scales, None, lin.epilogue, hv)
+                        ax_h = mxq.hadamard_channel_amax(hv)
                     pack_ms += ev0.elapsed_time(ev1)
                     pack_bytes += lin.n * lin.k * 2 + lin.n * lin.k // 2 + lin.n * lin.k // 32
                     self.weights[(e, b, li)] = (codes, scales)
                     del w
         self.pack_gbs = pack_bytes / (pack_ms * 1e-3) / 1e9
         log(f"weights packed in {time.time() - t0:.1f}s ({pack_bytes / 1e9:.1f} GB traffic, {self.pack_gbs:.0f} GB/s)")
-        m_max = wl.m_video
-        n_max = max(l.n for l in wl.linears)
-        self.y = torch.empty((m_max * n_max,), dtype=torch.bfloat16, device=dev)
-        self.h = torch.empty((wl.m_video * max(wl.ffn, 1),), dtype=torch.bfloat16, device=dev)
-        ws = max(mxq.qlinear_workspace_bytes(md, m_max, l.k) for md in (0, 1) for l in wl.linears)
-        self.codes_buf = torch.empty((ws,), dtype=torch.uint8, device=dev)
-        # W4A4 FFN: the first projection writes the second one's MXFP4 input here
-        self.codes_buf2 = torch.empty((ws,), dtype=torch.uint8, device=dev)
         self.records = []  # (kind, mode, flops, bytes, ev_start, ev_end)
         self.down_ready = False  # the FFN's second projection has its input codes in codes_buf2
         if static:
@@ -177,7 +213,8 @@ class Stack:
                     # W4A4: MXFP4; W4A8: only with static scales (a per-token
                     # scale needs the row's amax first)
                     static8 = mode == 1 and self.static
-                    fused_up = lin.name == "ffn_up" and (
+                    tr = mode == 0 and self.transform
+                    fused_up = lin.name == "ffn_up" and not tr and (
                         (mode == 0 and mxq.gemm_mxfp4_out_supported(m, lin.n, lin.k))
                         or (static8 and mxq.gemm_fp8_static_out_supported(m, lin.n, lin.k)))
                     fed = lin.name == "ffn_down" and self.down_ready
@@ -189,7 +226,9 @@ class Stack:
                         e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
                         e0.record()
                     if not fed:
-                        if static8:
+                        if tr:
+                            mxq.quantize_mxfp4_hadamard(x, self.act_mult[(e, b, li)], codes, scales)
+                        elif static8:
                             mxq.quantize_act_fp8_static(x, self._input_amax(e, b, lin.m_role), codes, scales)
                         else:
                             mxq.quantize_act(mode, x, codes, scales)
@@ -254,11 +293,13 @@ def profiled_traffic(workload_tag, mode):
     return total // launches
 
 
-def cpu_baseline(wl, sample_rows, static=False):
+def cpu_baseline(wl, sample_rows, static=False, transform=False):
     """Oracle throughput on a bounded sample: `sample_rows` token rows through one block's linears.
 
     With ``static`` the W4A8 linears quantize with the oracle's static FP8 rule,
-    the scale calibrated on the sample (untimed)."""
+    the scale calibrated on the sample (untimed). With ``transform`` the W4A4
+    linears run the oracle's transform_on path, calibrated on the sample and the
+    weight (untimed, like the weight packing)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -281,11 +322,18 @@ def cpu_baseline(wl, sample_rows, static=False):
             if lin.m_role == "ffn_hidden":
                 continue
             w = synth.weight_bf16(wl.config_id, lin.n, lin.k, 0, b, li)
-            wq, wsc = oracle.mxfp4_quantize(w)  # offline on both sides; not timed
             xs = x[:, : lin.k]
+            if md == 0 and transform:
+                am, wm = oracle.smoothquant_factors(oracle.hadamard_channel_amax([xs]),
+                                                    oracle.hadamard_channel_amax([w]))
+                wq, wsc = oracle.mxfp4_quantize_hadamard(w, wm)  # offline on both sides; not timed
+            else:
+                wq, wsc = oracle.mxfp4_quantize(w)  # offline on both sides; not timed
             amax = oracle.fp8_calibration_amax([xs]) if static else None
             t0 = time.perf_counter()
-            if md == 1 and static:
+            if md == 0 and transform:
+                y, _, _ = oracle.qlinear_transform(oracle.TRANSFORM_ON, xs, wq, wsc, am, epilogue=lin.epilogue)
+            elif md == 1 and static:
                 ac, asc = oracle.fp8_quantize_static(xs, amax)
                 y = oracle.qdq_matmul(md, ac, asc, wq, wsc, None, lin.epilogue)
             else:
@@ -298,7 +346,8 @@ def cpu_baseline(wl, sample_rows, static=False):
             break
     return {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{rows} token rows through the first W4A4 and first W4A8 block's video-token linears "
-                      f"(quantize{' (W4A8: static FP8)' if static else ''} + float64 QDQ matmul), "
+                      f"(quantize{' (W4A8: static FP8)' if static else ''}"
+                      f"{' (W4A4: transform_on)' if transform else ''} + float64 QDQ matmul), "
                       f"{flops / 1e9:.1f} GFLOP in {secs:.1f} s"}
 
 
@@ -325,7 +374,8 @@ def main():
     mxq.lib()
     wl = synth.workload(WORKLOADS[args.workload])
     static = args.act_scale == "static"
-    stack = Stack(wl, torch, mxq, static)
+    transform = args.transform_on
+    stack = Stack(wl, torch, mxq, static, transform)
     for _ in range(args.warmup):
         stack.step(timed=False)
     torch.cuda.synchronize()
@@ -363,7 +413,8 @@ def main():
     dom = max((k for k in agg if k[0] == "gemm"), key=lambda k: agg[k]["ms"])
     a = agg[dom]
     achieved = a["flops"] / (a["ms"] * 1e-3) / 1e12
-    tag = [k for k, v in WORKLOADS.items() if v == wl.config_id][0] + ("_static" if static else "")
+    tag = [k for k, v in WORKLOADS.items() if v == wl.config_id][0] + ("_static" if static else "") + \
+        ("_transform" if transform else "")
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_TFLOPS[dom[1]], "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_TFLOPS[dom[1]], 4),
                 "traffic": profiled_traffic(tag, dom[1]),
@@ -384,18 +435,21 @@ def main():
         "vs_baseline": None,
         "dtype": "+".join(x for x, md in (("mxfp4xmxfp4", 0), ("fp8e4m3xmxfp4", 1)) if md in modes) + "->fp32acc->bf16",
         "data": "synthetic (seeded activations with Student-t outlier channels; N(0,0.02) weights, RTN MXFP4"
-                + ("; static FP8 scales calibrated, untimed, on the same inputs)" if static else ")"),
+                + ("; static FP8 scales calibrated, untimed, on the same inputs" if static else "")
+                + ("; transform_on factors calibrated, untimed, on the same inputs and weights" if transform else "")
+                + ")",
         "config": {"workload": wl.name, "m_video": wl.m_video, "m_text": wl.m_text, "dim": wl.dim, "ffn": wl.ffn,
                    "experts": wl.n_experts, "blocks": wl.n_blocks,
                    "w4a8_blocks": int((stack.policy_table == 1).sum()),
                    "w4a8_activations": "fp8_static_per_tensor" if static else "fp8_per_token",
+                   "w4a4_transform": "hadamard128+smoothquant" if transform else "none",
                    "linears_per_block": len(wl.linears), "tflop_per_step": round(wl.total_flops() / 1e12, 2)},
         "roofline": roofline,
         "kernels": kernels,
         "weight_pack_gbs": round(stack.pack_gbs, 1),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_rows, static)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_rows, static, transform)
     print(json.dumps(out), flush=True)
 
 
