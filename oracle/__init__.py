@@ -19,6 +19,9 @@ quantize-dequantize emulation):
                  and static (one calibrated scale per tensor, saturating).
 * ``transform`` - the transform_on mode: block-diagonal 128-point Hadamard
                  rotation (fp32 butterflies) and SmoothQuant factors ahead of MXFP4.
+* ``select``   - calibration-driven block selection: block-replay SQNR (OFF
+                 = plain MXFP4, ON = transform) and the tiered rule ladder that
+                 emits the policy artifact.
 * ``linear``   - dequantize-then-fp64 matmul (the QDQ result), tanh-GELU, the
                  per-block policy lookup and the output tolerance check.
 
@@ -60,6 +63,15 @@ from .transform import (
     hadamard_transform_bf16,
     mxfp4_quantize_hadamard,
     INV_SQRT_BLOCK,
+)
+from .select import (
+    TIERS,
+    BF16_MODE,
+    sqnr_sums,
+    sqnr_db,
+    select_mode,
+    select_policy,
+    block_replay_sums,
 )
 from .linear import (
     W4A4,
