@@ -199,6 +199,51 @@ int mxq_quantize_mxfp4_hadamard(const void* x, int64_t M, int64_t K, int64_t ldx
                                 void* codes, void* scales, hipStream_t stream);
 
 /*
+ * Calibration-driven block selection (section "Calibration-driven block
+ * selection"): captured BF16 block inputs are replayed through two quantized
+ * versions of each block, OFF = plain dynamic MXFP4 and ON = MXFP4 behind the
+ * transform above, and the block output's SQNR against the captured BF16
+ * output decides the block by a rule ladder with three tiers of thresholds.
+ * A block here is its quantized linears; their outputs together are the
+ * block output. SQNR = 10 log10(sum y_ref^2 / sum (y - y_ref)^2) dB.
+ *
+ * mxq_sqnr_accumulate: sums[0] += sum y_ref^2, sums[1] += sum (y - y_ref)^2
+ *   over n elements of two bf16 device buffers (16-byte aligned), in fp64.
+ *   sums: device double [2], set to 0 by the caller, then folded over any
+ *   number of calls (the order of fp64 additions is not fixed).
+ * mxq_block_replay_sqnr: one block's replay. For each linear, OFF quantizes
+ *   x (mxq_quantize_act, MXQ_W4A4) and w (mxq_quantize_weight_mxfp4) and ON
+ *   calibrates the transform on this x and w (mxq_hadamard_channel_amax,
+ *   mxq_smoothquant_factors) and quantizes both with
+ *   mxq_quantize_mxfp4_hadamard; both run mxq_gemm(MXQ_W4A4) into bf16 and
+ *   fold their output against y_ref into sums_off / sums_on (device double
+ *   [2] each, running). K % 128 == 0 for every linear. All inputs are
+ *   validated before anything is enqueued; the linears run in order on
+ *   `stream`, sharing the workspace (size from mxq_replay_workspace_bytes).
+ *   linears is a host array.
+ * mxq_policy_select: host only. From the host copies of per-block sums
+ *   (double [n_experts][n_blocks][2] each) it writes the policy artifact
+ *   modes [n_experts][n_blocks] (host): with best = max(SQNR_off, SQNR_on),
+ *   best < floor -> MXQ_POLICY_BF16; best < w4a8 -> MXQ_W4A8;
+ *   SQNR_on - SQNR_off > margin -> MXQ_POLICY_TRANSFORM_ON; else MXQ_W4A4.
+ *   Tiers (floor, w4a8, margin) in dB: low (8, 21, 0.5), mid (10, 23, 0.5),
+ *   high (12, 25, 0.5). No noise counts as +inf dB, no signal as -inf.
+ */
+enum { MXQ_TIER_LOW = 0, MXQ_TIER_MID = 1, MXQ_TIER_HIGH = 2 };
+typedef struct mxq_replay_linear {
+  const void* x;     /* device bf16 [M][K]: the captured input */
+  const void* w;     /* device bf16 [N][K]: the linear's weight */
+  const void* y_ref; /* device bf16 [M][N]: the captured BF16 output */
+  int64_t M, N, K;
+} mxq_replay_linear;
+int mxq_sqnr_accumulate(const void* y, const void* y_ref, int64_t n, double* sums, hipStream_t stream);
+int mxq_replay_workspace_bytes(const mxq_replay_linear* linears, int32_t n_linears, size_t* bytes);
+int mxq_block_replay_sqnr(const mxq_replay_linear* linears, int32_t n_linears, void* workspace,
+                          size_t workspace_bytes, double* sums_off, double* sums_on, hipStream_t stream);
+int mxq_policy_select(const double* sums_off, const double* sums_on, int32_t n_experts, int32_t n_blocks,
+                      int32_t tier, uint8_t* modes);
+
+/*
  * Scaled GEMM on quantized operands (the native MXFP4 / W4A8 execution of
  * "Quantization formats", kernel note): y [M][N] bf16 =
  *   epilogue( sum_k deqA[m][k] deqW[n][k] + bias[n] ).

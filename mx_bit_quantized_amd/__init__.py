@@ -27,18 +27,29 @@ LIB_PATH = os.path.join(_HERE, "libmxq.so")
 # status codes, modes and epilogues (include/mxq.h)
 OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_MODE, ERR_WORKSPACE, ERR_HIP, ERR_RANGE = range(8)
 W4A4, W4A8, POLICY_BF16, POLICY_TRANSFORM_ON = 0, 1, 2, 3
+TIER_LOW, TIER_MID, TIER_HIGH = 0, 1, 2
 EPI_NONE, EPI_GELU_TANH = 0, 1
 
 # every function the header declares, with its ctypes signature
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _I32 = ctypes.c_int32
+
+
+class ReplayLinear(ctypes.Structure):
+    """mxq_replay_linear: one linear of a block replay (device pointers, sizes)."""
+    _fields_ = [("x", _P), ("w", _P), ("y_ref", _P), ("M", _I64), ("N", _I64), ("K", _I64)]
+
 _SIGS = {
     "mxq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "mxq_version": (ctypes.c_int, []),
     "mxq_quantize_weight_mxfp4": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "mxq_quantize_act": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, _I64, _P, _P, _P]),
     "mxq_fp8_calibrate": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P]),
+    "mxq_sqnr_accumulate": (ctypes.c_int, [_P, _P, _I64, _P, _P]),
+    "mxq_replay_workspace_bytes": (ctypes.c_int, [_P, _I32, ctypes.POINTER(ctypes.c_size_t)]),
+    "mxq_block_replay_sqnr": (ctypes.c_int, [_P, _I32, _P, ctypes.c_size_t, _P, _P, _P]),
+    "mxq_policy_select": (ctypes.c_int, [_P, _P, _I32, _I32, _I32, _P]),
     "mxq_hadamard_channel_amax": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P]),
     "mxq_smoothquant_factors": (ctypes.c_int, [_P, _P, _I64, _P, _P, _P]),
     "mxq_quantize_mxfp4_hadamard": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
@@ -419,3 +430,62 @@ def qlinear_transform(policy, expert, block, x, w_codes, w_scales, act_mult=None
                                       int(workspace.numel()), _stream_handle(stream))
     _check(st, "qlinear_transform")
     return y
+
+
+# ----------------------------------------------------------- selection ----
+
+def sqnr_accumulate(y, y_ref, sums, stream=None):
+    """Fold bf16 y against bf16 y_ref (same size) into sums (device float64 [2]: signal, noise)."""
+    torch = _torch()
+    if y.numel() != y_ref.numel():
+        raise ValueError("y and y_ref differ in size")
+    st = lib().mxq_sqnr_accumulate(_dev_ptr(y, "y", torch.bfloat16), _dev_ptr(y_ref, "y_ref", torch.bfloat16),
+                                    int(y.numel()), _dev_ptr(sums, "sums", torch.float64), _stream_handle(stream))
+    _check(st, "sqnr_accumulate")
+    return sums
+
+
+def _replay_array(linears):
+    torch = _torch()
+    arr = (ReplayLinear * len(linears))()
+    for i, (x, w, y_ref) in enumerate(linears):
+        m, k = _rows_k(x, "x")
+        n = int(w.shape[0])
+        if tuple(w.shape) != (n, k) or tuple(y_ref.shape) != (m, n):
+            raise ValueError("replay linear shapes must be x [M, K], w [N, K], y_ref [M, N]")
+        arr[i] = ReplayLinear(_dev_ptr(x, "x", torch.bfloat16), _dev_ptr(w, "w", torch.bfloat16),
+                              _dev_ptr(y_ref, "y_ref", torch.bfloat16), m, n, k)
+    return arr
+
+
+def replay_workspace_bytes(linears):
+    arr = _replay_array(linears)
+    out = ctypes.c_size_t()
+    _check(lib().mxq_replay_workspace_bytes(arr, len(linears), ctypes.byref(out)), "replay_workspace_bytes")
+    return out.value
+
+
+def block_replay_sqnr(linears, sums_off, sums_on, workspace=None, stream=None):
+    """Replay one block's linears [(x, w, y_ref), ...] OFF and ON, folding into sums_off / sums_on."""
+    torch = _torch()
+    arr = _replay_array(linears)
+    if workspace is None:
+        workspace = torch.empty((max(replay_workspace_bytes(linears), 1),), dtype=torch.uint8,
+                                device=sums_off.device)
+    st = lib().mxq_block_replay_sqnr(arr, len(linears), _dev_ptr(workspace, "workspace", torch.uint8),
+                                      int(workspace.numel()), _dev_ptr(sums_off, "sums_off", torch.float64),
+                                      _dev_ptr(sums_on, "sums_on", torch.float64), _stream_handle(stream))
+    _check(st, "block_replay_sqnr")
+
+
+def policy_select(sums_off, sums_on, tier=TIER_HIGH):
+    """Host float64 [n_experts, n_blocks, 2] sums (OFF, ON) -> uint8 policy artifact [n_experts, n_blocks]."""
+    off = np.ascontiguousarray(sums_off, np.float64)
+    on = np.ascontiguousarray(sums_on, np.float64)
+    if off.ndim != 3 or off.shape[2] != 2 or on.shape != off.shape:
+        raise ValueError("sums must be float64 [n_experts, n_blocks, 2]")
+    modes = np.empty(off.shape[:2], np.uint8)
+    st = lib().mxq_policy_select(off.ctypes.data_as(_P), on.ctypes.data_as(_P), off.shape[0], off.shape[1],
+                                  int(tier), modes.ctypes.data_as(_P))
+    _check(st, "policy_select")
+    return modes

@@ -11,6 +11,8 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <math.h>
+
 #include <new>
 #include <vector>
 
@@ -54,6 +56,50 @@ void workspace_layout(int mode, int64_t M, int64_t K, size_t* codes_bytes, size_
   size_t sb = mode == MXQ_W4A4 ? (size_t)M * 4 * (size_t)((K + 127) / 128) : (size_t)M * sizeof(float);
   *codes_bytes = round_up(cb, 256);
   *total = *codes_bytes + round_up(sb, 256);
+}
+
+// Workspace layout of mxq_block_replay_sqnr for one linear: activation codes
+// and scales, weight codes and scales (W4A4 layouts), y (bf16), then four fp32
+// vectors of K (x maxima, w maxima, act factors, w factors); 256-byte aligned.
+struct ReplayLayout {
+  size_t a_codes, a_scales, w_codes, w_scales, y, ax, aw, am, wm, total;
+};
+
+ReplayLayout replay_layout(int64_t M, int64_t N, int64_t K) {
+  ReplayLayout L{};
+  size_t cb = 0, tot = 0, off = 0;
+  workspace_layout(MXQ_W4A4, M, K, &cb, &tot);
+  L.a_codes = off;
+  L.a_scales = off + cb;
+  off += tot;
+  workspace_layout(MXQ_W4A4, N, K, &cb, &tot);
+  L.w_codes = off;
+  L.w_scales = off + cb;
+  off += tot;
+  L.y = off;
+  off += round_up((size_t)M * (size_t)N * 2, 256);
+  const size_t kv = round_up((size_t)K * 4, 256);
+  L.ax = off;
+  L.aw = off + kv;
+  L.am = off + 2 * kv;
+  L.wm = off + 3 * kv;
+  L.total = off + 4 * kv;
+  return L;
+}
+
+int check_replay_linear(const mxq_replay_linear& l) {
+  int st = check_mk(l.M, l.K, l.K);
+  if (st != MXQ_OK) return st;
+  if (l.M < 1 || l.N < 1 || l.N >= kMaxDim || l.K % 128 != 0) return MXQ_ERR_SHAPE;
+  if (l.x == nullptr || l.w == nullptr || l.y_ref == nullptr) return MXQ_ERR_NULL;
+  if (!aligned16(l.x) || !aligned16(l.w) || !aligned16(l.y_ref)) return MXQ_ERR_ALIGN;
+  return MXQ_OK;
+}
+
+double sqnr_of(const double* sums) {
+  if (sums[1] == 0.0) return INFINITY;
+  if (sums[0] == 0.0) return -INFINITY;
+  return 10.0 * log10(sums[0] / sums[1]);
 }
 
 }  // namespace
@@ -134,6 +180,101 @@ int mxq_quantize_mxfp4_hadamard(const void* x, int64_t M, int64_t K, int64_t ldx
     return MXQ_ERR_ALIGN;
   if (log_enabled()) fprintf(stderr, "[mxq] quantize_mxfp4_hadamard M=%lld K=%lld\n", (long long)M, (long long)K);
   return hip_status(mxq::launch_mxfp4_hadamard_quant(x, M, K, ldx, mult, codes, scales, stream));
+}
+
+int mxq_sqnr_accumulate(const void* y, const void* y_ref, int64_t n, double* sums, hipStream_t stream) {
+  if (n < 0) return MXQ_ERR_SHAPE;
+  if (n == 0) return MXQ_OK;
+  if (y == nullptr || y_ref == nullptr || sums == nullptr) return MXQ_ERR_NULL;
+  if (!aligned16(y) || !aligned16(y_ref) || (reinterpret_cast<uintptr_t>(sums) & 7u) != 0) return MXQ_ERR_ALIGN;
+  return hip_status(mxq::launch_sqnr_sums(y, y_ref, n, sums, stream));
+}
+
+int mxq_replay_workspace_bytes(const mxq_replay_linear* linears, int32_t n_linears, size_t* bytes) {
+  if (bytes == nullptr) return MXQ_ERR_NULL;
+  if (n_linears < 0) return MXQ_ERR_SHAPE;
+  if (n_linears > 0 && linears == nullptr) return MXQ_ERR_NULL;
+  size_t need = 0;
+  for (int32_t i = 0; i < n_linears; ++i) {
+    const mxq_replay_linear& l = linears[i];
+    if (check_mk(l.M, l.K, l.K) != MXQ_OK || l.M < 1 || l.N < 1 || l.N >= kMaxDim || l.K % 128 != 0)
+      return MXQ_ERR_SHAPE;
+    const size_t t = replay_layout(l.M, l.N, l.K).total;
+    need = t > need ? t : need;
+  }
+  *bytes = need;
+  return MXQ_OK;
+}
+
+int mxq_block_replay_sqnr(const mxq_replay_linear* linears, int32_t n_linears, void* workspace,
+                          size_t workspace_bytes, double* sums_off, double* sums_on, hipStream_t stream) {
+  if (n_linears < 0) return MXQ_ERR_SHAPE;
+  if (n_linears == 0) return MXQ_OK;
+  if (linears == nullptr || sums_off == nullptr || sums_on == nullptr) return MXQ_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(sums_off) & 7u) != 0 || (reinterpret_cast<uintptr_t>(sums_on) & 7u) != 0)
+    return MXQ_ERR_ALIGN;
+  size_t need = 0;
+  for (int32_t i = 0; i < n_linears; ++i) {
+    const int st = check_replay_linear(linears[i]);
+    if (st != MXQ_OK) return st;
+  }
+  int st = mxq_replay_workspace_bytes(linears, n_linears, &need);
+  if (st != MXQ_OK) return st;
+  if (workspace == nullptr || workspace_bytes < need) return MXQ_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return MXQ_ERR_ALIGN;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  for (int32_t i = 0; i < n_linears; ++i) {
+    const mxq_replay_linear& l = linears[i];
+    const ReplayLayout L = replay_layout(l.M, l.N, l.K);
+    void* ac = ws + L.a_codes;
+    void* as = ws + L.a_scales;
+    void* wc = ws + L.w_codes;
+    void* wsc = ws + L.w_scales;
+    void* y = ws + L.y;
+    float* ax = reinterpret_cast<float*>(ws + L.ax);
+    float* aw = reinterpret_cast<float*>(ws + L.aw);
+    float* am = reinterpret_cast<float*>(ws + L.am);
+    float* wm = reinterpret_cast<float*>(ws + L.wm);
+    const int64_t n_out = l.M * l.N;
+    // OFF: plain dynamic MXFP4
+    if ((st = mxq_quantize_act(MXQ_W4A4, l.x, l.M, l.K, l.K, ac, as, stream)) != MXQ_OK) return st;
+    if ((st = mxq_quantize_weight_mxfp4(l.w, l.N, l.K, l.K, wc, wsc, stream)) != MXQ_OK) return st;
+    if ((st = mxq_gemm(MXQ_W4A4, ac, as, wc, wsc, nullptr, MXQ_EPI_NONE, y, l.M, l.N, l.K, stream)) != MXQ_OK)
+      return st;
+    if ((st = mxq_sqnr_accumulate(y, l.y_ref, n_out, sums_off, stream)) != MXQ_OK) return st;
+    // ON: the transform calibrated on this input and weight
+    if ((st = hip_status(mxq::launch_fill_zero(ax, 2 * ((L.aw - L.ax) / 4), stream))) != MXQ_OK) return st;
+    if ((st = mxq_hadamard_channel_amax(l.x, l.M, l.K, l.K, ax, stream)) != MXQ_OK) return st;
+    if ((st = mxq_hadamard_channel_amax(l.w, l.N, l.K, l.K, aw, stream)) != MXQ_OK) return st;
+    if ((st = mxq_smoothquant_factors(ax, aw, l.K, am, wm, stream)) != MXQ_OK) return st;
+    if ((st = mxq_quantize_mxfp4_hadamard(l.x, l.M, l.K, l.K, am, ac, as, stream)) != MXQ_OK) return st;
+    if ((st = mxq_quantize_mxfp4_hadamard(l.w, l.N, l.K, l.K, wm, wc, wsc, stream)) != MXQ_OK) return st;
+    if ((st = mxq_gemm(MXQ_W4A4, ac, as, wc, wsc, nullptr, MXQ_EPI_NONE, y, l.M, l.N, l.K, stream)) != MXQ_OK)
+      return st;
+    if ((st = mxq_sqnr_accumulate(y, l.y_ref, n_out, sums_on, stream)) != MXQ_OK) return st;
+  }
+  return MXQ_OK;
+}
+
+int mxq_policy_select(const double* sums_off, const double* sums_on, int32_t n_experts, int32_t n_blocks,
+                      int32_t tier, uint8_t* modes) {
+  static const double kTiers[3][3] = {{8.0, 21.0, 0.5}, {10.0, 23.0, 0.5}, {12.0, 25.0, 0.5}};
+  if (tier < MXQ_TIER_LOW || tier > MXQ_TIER_HIGH) return MXQ_ERR_MODE;
+  if (n_experts <= 0 || n_blocks <= 0) return MXQ_ERR_SHAPE;
+  if (sums_off == nullptr || sums_on == nullptr || modes == nullptr) return MXQ_ERR_NULL;
+  const double floor_db = kTiers[tier][0], w4a8_db = kTiers[tier][1], margin = kTiers[tier][2];
+  const size_t n = (size_t)n_experts * (size_t)n_blocks;
+  for (size_t i = 0; i < n; ++i) {
+    const double off = sqnr_of(sums_off + 2 * i), on = sqnr_of(sums_on + 2 * i);
+    const double best = off > on ? off : on;
+    uint8_t m;
+    if (best < floor_db) m = MXQ_POLICY_BF16;
+    else if (best < w4a8_db) m = MXQ_W4A8;
+    else if (on - off > margin) m = MXQ_POLICY_TRANSFORM_ON;
+    else m = MXQ_W4A4;
+    modes[i] = m;
+  }
+  return MXQ_OK;
 }
 
 int mxq_fp8_calibrate(const void* x, int64_t M, int64_t K, int64_t ldx, float* amax, hipStream_t stream) {

@@ -22,6 +22,11 @@ hipError_t launch_hadamard_amax(const void* x, int64_t rows, int64_t K, int64_t 
 hipError_t launch_smoothquant_factors(const float* act_amax, const float* w_amax, int64_t K, float* act_mult,
                                       float* w_mult, hipStream_t s);
 
+// Block selection: sums[0] += sum r^2, sums[1] += sum (y - r)^2 over n bf16
+// elements (fp64, device [2]); a zero fill of n 4-byte words.
+hipError_t launch_sqnr_sums(const void* y, const void* y_ref, int64_t n, double* sums, hipStream_t s);
+hipError_t launch_fill_zero(void* p, int64_t n_words, hipStream_t s);
+
 // Static FP8: codes with the one scale amax / 448 (amax: device fp32), every
 // row's scale slot set to it.
 hipError_t launch_fp8_static_quant(const void* x, int64_t rows, int64_t K, int64_t ld, const float* amax,

@@ -9,7 +9,8 @@ whose thresholds come in three tiers. Readings recorded in the design notes:
 * SQNR = 10 log10( sum y_ref^2 / sum (y - y_ref)^2 ) in dB, over every output
   element of the block; a block here is its quantized linears (the path holds
   no attention or norms), each fed its captured input, and their outputs
-  together form the block output. No noise gives +inf, no signal -inf.
+  together form the block output. y is the quantized layer's output as the
+  layer produces it, in bf16. No noise gives +inf, no signal -inf.
 * The rules, first match wins, with best = max(sqnr_off, sqnr_on):
       best < floor                 -> bf16 (the block stays unquantized)
       best < w4a8_sqnr             -> W4A8
@@ -20,6 +21,7 @@ whose thresholds come in three tiers. Readings recorded in the design notes:
 
 import numpy as np
 
+from .formats import bf16_bits_to_f64, f64_to_bf16_bits
 from .linear import EPI_NONE, W4A4, W4A8, TRANSFORM_ON, qdq_matmul
 from .quant import mxfp4_quantize
 from .transform import hadamard_channel_amax, mxfp4_quantize_hadamard, smoothquant_factors
@@ -85,11 +87,11 @@ def block_replay_sums(linears):
     for x, w, y_ref in linears:
         xc, xs = mxfp4_quantize(x)
         wc, ws = mxfp4_quantize(w)
-        y_off = qdq_matmul(W4A4, xc, xs, wc, ws, None, EPI_NONE)
+        y_off = bf16_bits_to_f64(f64_to_bf16_bits(qdq_matmul(W4A4, xc, xs, wc, ws, None, EPI_NONE)))
         am, wm = smoothquant_factors(hadamard_channel_amax([x]), hadamard_channel_amax([w]))
         txc, txs = mxfp4_quantize_hadamard(x, am)
         twc, tws = mxfp4_quantize_hadamard(w, wm)
-        y_on = qdq_matmul(W4A4, txc, txs, twc, tws, None, EPI_NONE)
+        y_on = bf16_bits_to_f64(f64_to_bf16_bits(qdq_matmul(W4A4, txc, txs, twc, tws, None, EPI_NONE)))
         s, e_off = sqnr_sums(y_off, y_ref)
         _, e_on = sqnr_sums(y_on, y_ref)
         sig += s

@@ -25,7 +25,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = mxq.lib()
     names = declared_functions()
-    assert len(names) == 19, names
+    assert len(names) == 23, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(mxq._SIGS)
@@ -195,6 +195,58 @@ def test_transform_validation():
     assert L.mxq_qlinear_transform(p.handle, 0, 0, FAKE, 4, 128, FAKE, FAKE, 8, None, 0, FAKE, FAKE, FAKE, ws - 1,
                                    S) == mxq.ERR_WORKSPACE
     p.close()
+
+
+def test_selection_validation_and_host_policy_select():
+    """Selector entry points: host-side checks, and the host-only rule ladder against the oracle."""
+    import oracle
+
+    L = mxq.lib()
+    S = None
+    F8 = ctypes.c_void_p(0x10004)  # not 8-byte aligned
+    assert L.mxq_sqnr_accumulate(FAKE, FAKE, -1, FAKE, S) == mxq.ERR_SHAPE
+    assert L.mxq_sqnr_accumulate(None, None, 0, None, S) == mxq.OK
+    for pos in (0, 1, 3):
+        args = [FAKE, FAKE, 64, FAKE, S]
+        args[pos] = None
+        assert L.mxq_sqnr_accumulate(*args) == mxq.ERR_NULL, pos
+    assert L.mxq_sqnr_accumulate(FAKE_ODD, FAKE, 64, FAKE, S) == mxq.ERR_ALIGN
+    assert L.mxq_sqnr_accumulate(FAKE, FAKE, 64, F8, S) == mxq.ERR_ALIGN
+    # replay: shapes, nulls, workspace
+    good = mxq.ReplayLinear(FAKE, FAKE, FAKE, 64, 96, 256)
+    arr = (mxq.ReplayLinear * 2)(good, good)
+    need = ctypes.c_size_t()
+    assert L.mxq_replay_workspace_bytes(arr, 2, ctypes.byref(need)) == mxq.OK and need.value > 0
+    bad_k = (mxq.ReplayLinear * 1)(mxq.ReplayLinear(FAKE, FAKE, FAKE, 64, 96, 96))
+    assert L.mxq_replay_workspace_bytes(bad_k, 1, ctypes.byref(need)) == mxq.ERR_SHAPE
+    assert L.mxq_block_replay_sqnr(bad_k, 1, FAKE, 1 << 30, FAKE, FAKE, S) == mxq.ERR_SHAPE
+    null_w = (mxq.ReplayLinear * 1)(mxq.ReplayLinear(FAKE, None, FAKE, 64, 96, 256))
+    assert L.mxq_block_replay_sqnr(null_w, 1, FAKE, 1 << 30, FAKE, FAKE, S) == mxq.ERR_NULL
+    odd = (mxq.ReplayLinear * 1)(mxq.ReplayLinear(FAKE, FAKE, FAKE_ODD, 64, 96, 256))
+    assert L.mxq_block_replay_sqnr(odd, 1, FAKE, 1 << 30, FAKE, FAKE, S) == mxq.ERR_ALIGN
+    assert L.mxq_block_replay_sqnr(arr, 2, FAKE, 16, FAKE, FAKE, S) == mxq.ERR_WORKSPACE
+    assert L.mxq_block_replay_sqnr(arr, 2, None, 1 << 30, FAKE, FAKE, S) == mxq.ERR_WORKSPACE
+    assert L.mxq_block_replay_sqnr(arr, 2, FAKE, 1 << 30, None, FAKE, S) == mxq.ERR_NULL
+    assert L.mxq_block_replay_sqnr(arr, 2, FAKE, 1 << 30, FAKE, F8, S) == mxq.ERR_ALIGN
+    assert L.mxq_block_replay_sqnr(arr, -1, FAKE, 1 << 30, FAKE, FAKE, S) == mxq.ERR_SHAPE
+    assert L.mxq_block_replay_sqnr(None, 0, None, 0, None, None, S) == mxq.OK
+    # the rule ladder (host only) against the oracle, on random sums and on exact 10 dB steps
+    g = np.random.default_rng(3)
+    sig = np.ldexp(g.uniform(1, 2, (2, 40)), g.integers(0, 40, (2, 40)))
+    off = np.stack([sig, sig * 10.0 ** (-g.uniform(0.5, 4.0, (2, 40)))], axis=2)
+    on = np.stack([sig, sig * 10.0 ** (-g.uniform(0.5, 4.0, (2, 40)))], axis=2)
+    off[0, 0, 1] = 0.0   # no noise: +inf dB
+    on[1, 3, 0] = 0.0    # no signal: -inf dB
+    off[1, 5] = [100.0, 10.0]    # exactly 10 dB: the mid tier's floor is not crossed
+    on[1, 5] = [100.0, 10.0]
+    for tier, name in ((mxq.TIER_LOW, "low"), (mxq.TIER_MID, "mid"), (mxq.TIER_HIGH, "high")):
+        got = mxq.policy_select(off, on, tier)
+        db = lambda a: np.vectorize(oracle.sqnr_db)(a[..., 0], a[..., 1])
+        want = oracle.select_policy(db(off), db(on), name)
+        assert np.array_equal(got, want), name
+    assert mxq.policy_select(off, on, mxq.TIER_MID)[1, 5] == mxq.W4A8
+    with pytest.raises(mxq.MxqError):
+        mxq.policy_select(off, on, 3)
 
 
 def test_static_fp8_validation():
