@@ -53,6 +53,9 @@ def parse():
                     help="W4A8 activation scale: per token (amax/448 of each row) or static per tensor (calibrated)")
     ap.add_argument("--transform-on", action="store_true",
                     help="run the W4A4 blocks as transform_on (Hadamard rotation + SmoothQuant, calibrated)")
+    ap.add_argument("--select", action="store_true",
+                    help="instead of the step: calibration-driven block selection over the A14B model (one 480p "
+                         "calibration sample), timing the library's block replay")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=512)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -351,6 +354,117 @@ def cpu_baseline(wl, sample_rows, static=False, transform=False):
                       f"{flops / 1e9:.1f} GFLOP in {secs:.1f} s"}
 
 
+SELECT_M = 32760  # one 480p calibration sample: 21 x 30 x 52 latent tokens (the page's 832 x 480, 81 frames)
+
+
+def run_select(args, torch, mxq):
+    """Calibration-driven block selection over the A14B 2-expert, 40-block model.
+
+    The captured BF16 data of one calibration sample (synthetic inputs; every
+    linear's output and the FFN hidden state from torch's bf16 matmul, which is
+    the BF16 path the page compares against) are made untimed. The timed part
+    is the library's block replay (OFF: plain MXFP4; ON: transform calibrated on
+    the sample) with its SQNR reductions, one call per block."""
+    wl = synth.workload(5)
+    dev = "cuda:0"
+    to_dev = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
+    m = SELECT_M
+    x_video = to_dev(synth.activation_bf16(wl.config_id, m, wl.dim, wl.outliers, tensor_id=synth.T_X_VIDEO))
+    x_text = to_dev(synth.activation_bf16(wl.config_id, wl.m_text, wl.dim, wl.outliers, tensor_id=synth.T_X_TEXT))
+    sums_off = torch.zeros((wl.n_experts, wl.n_blocks, 2), dtype=torch.float64, device=dev)
+    sums_on = torch.zeros_like(sums_off)
+    ws = None
+    replay_ms, flops, n_blocks = 0.0, 0, 0
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.time()
+    for e in range(wl.n_experts):
+        for b in range(wl.n_blocks):
+            lins, h = [], None
+            for li, lin in enumerate(wl.linears):
+                w = synth.weight_bf16_device(wl.config_id, lin.n, lin.k, e, b, li)
+                if lin.m_role == "video":
+                    x = x_video
+                elif lin.m_role == "text":
+                    x = x_text
+                else:
+                    x = h
+                y_ref = torch.mm(x, w.t().contiguous())  # the BF16 path's output (captured)
+                if lin.name == "ffn_up":  # the BF16 block's hidden state (captured)
+                    h = torch.nn.functional.gelu(y_ref.float(), approximate="tanh").to(torch.bfloat16)
+                lins.append((x, w, y_ref))
+                flops += 2 * 2 * x.shape[0] * lin.n * lin.k  # OFF and ON GEMMs
+            if ws is None:
+                ws = torch.empty((mxq.replay_workspace_bytes(lins),), dtype=torch.uint8, device=dev)
+            torch.cuda.synchronize()
+            ev0.record()
+            mxq.block_replay_sqnr(lins, sums_off[e, b], sums_on[e, b], ws)
+            ev1.record()
+            torch.cuda.synchronize()
+            replay_ms += ev0.elapsed_time(ev1)
+            n_blocks += 1
+            del lins, h
+        log(f"expert {e} replayed ({time.time() - t0:.1f}s)")
+    off, on = sums_off.cpu().numpy(), sums_on.cpu().numpy()
+    table = mxq.policy_select(off, on, mxq.TIER_HIGH)
+    sq = lambda a: 10 * np.log10(a[..., 0] / a[..., 1])
+    counts = {name: int((table == v).sum()) for name, v in (("w4a4", 0), ("w4a8", 1), ("bf16", 2),
+                                                            ("transform_on", 3))}
+    out = {
+        "metric": "block-replay selection throughput: A14B blocks scored per second (one 480p calibration sample)",
+        "value": round(n_blocks / (replay_ms * 1e-3), 3),
+        "unit": "blocks/s",
+        "n_gpus": 1,
+        "higher_is_better": True,
+        "ms_per_block": round(replay_ms / n_blocks, 3),
+        "replay_tflops": round(flops / (replay_ms * 1e-3) / 1e12, 1),
+        "dtype": "mxfp4xmxfp4->fp32acc->bf16 (OFF and ON), fp64 SQNR sums",
+        "data": "synthetic (seeded activations with Student-t outlier channels, N(0,0.02) weights); BF16 "
+                "reference outputs from torch bf16 matmul, untimed",
+        "config": {"workload": "a14b_40block_2expert_selection", "m_video": m, "m_text": wl.m_text,
+                   "experts": wl.n_experts, "blocks": wl.n_blocks, "linears_per_block": len(wl.linears),
+                   "tier": "high"},
+        "roofline": {"bound": "mfma", "achieved": round(flops / (replay_ms * 1e-3) / 1e12, 1),
+                     "peak": PEAK_TFLOPS[0], "unit": "TFLOP/s",
+                     "frac": round(flops / (replay_ms * 1e-3) / 1e12 / PEAK_TFLOPS[0], 4), "traffic": None,
+                     "kernel": "whole block replay (W4A4 GEMMs OFF and ON, their quantizers, maxima, reductions)"},
+        "policy_counts": counts,
+        "sqnr_db_off": {"min": round(float(sq(off).min()), 2), "max": round(float(sq(off).max()), 2)},
+        "sqnr_db_on": {"min": round(float(sq(on).min()), 2), "max": round(float(sq(on).max()), 2)},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_select_baseline(wl)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_select_baseline(wl):
+    """The oracle's block replay on a bounded sample: 128 tokens through the first block's video linears."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    rows = 128
+    x = synth.activation_bf16(wl.config_id, rows, wl.dim, wl.outliers, tensor_id=synth.T_X_VIDEO)
+    lins = []
+    for li, lin in enumerate(wl.linears):
+        if lin.m_role != "video":
+            continue
+        w = synth.weight_bf16(wl.config_id, lin.n, lin.k, 0, 0, li)
+        y_ref = oracle.bf16_bits_to_f64(oracle.f64_to_bf16_bits(oracle.bf16_bits_to_f64(x) @
+                                                                oracle.bf16_bits_to_f64(w).T))
+        lins.append((x, w, y_ref))
+        if len(lins) == 2:
+            break
+    t0 = time.perf_counter()
+    oracle.block_replay_sums(lins)
+    secs = time.perf_counter() - t0
+    tokens_per_s = rows / secs
+    return {"value": round(tokens_per_s, 2), "unit": "tokens/s through two linears (OFF and ON)",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"{rows} token rows through the first block's first two video linears, {secs:.1f} s"}
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -372,6 +486,9 @@ def main():
         print(json.dumps({"copy_probe_bytes": n}), flush=True)
         return
     mxq.lib()
+    if args.select:
+        run_select(args, torch, mxq)
+        return
     wl = synth.workload(WORKLOADS[args.workload])
     static = args.act_scale == "static"
     transform = args.transform_on
