@@ -19,6 +19,8 @@ quantize-dequantize emulation):
                  and static (one calibrated scale per tensor, saturating).
 * ``transform`` - the transform_on mode: block-diagonal 128-point Hadamard
                  rotation (fp32 butterflies) and SmoothQuant factors ahead of MXFP4.
+* ``lowrank``  - SVDQuant's 16-bit low-rank branch beside the quantized
+                 product: T = bf16(x L1), y = bf16(epilogue(y_pre + T L2)).
 * ``select``   - calibration-driven block selection: block-replay SQNR (OFF
                  = plain MXFP4, ON = transform) and the tiered rule ladder that
                  emits the policy artifact.
@@ -63,6 +65,11 @@ from .transform import (
     hadamard_transform_bf16,
     mxfp4_quantize_hadamard,
     INV_SQRT_BLOCK,
+)
+from .lowrank import (
+    lowrank_down,
+    lowrank_up,
+    svdquant_linear,
 )
 from .select import (
     TIERS,
