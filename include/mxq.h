@@ -244,6 +244,30 @@ int mxq_policy_select(const double* sums_off, const double* sums_on, int32_t n_e
                       int32_t tier, uint8_t* modes);
 
 /*
+ * SVDQuant's low-rank branch (the SVDQuant transform of sections
+ * "Mixed-Precision selection" and "Results"): for a weight W ~ L2 L1^T + R of
+ * rank r, the residual R is packed as MXFP4 like any weight and the layer is
+ *   y = epilogue( Q(x) Q(R)^T + bias + (x L1) L2^T' )
+ * with the branch in bf16 beside the quantized product. Run as: mxq_gemm
+ * (or mxq_qlinear) with MXQ_EPI_NONE into y_pre (the GELU must follow the
+ * whole sum), mxq_lowrank_down, then mxq_lowrank_up with the linear's
+ * epilogue.
+ * mxq_lowrank_down: t [M][r] = RN_bf16(x L1), fp32 accumulation.
+ *   x    device bf16 [M][K] (dense), K a multiple of 64
+ *   l1t  device bf16 [r][K]: L1 transposed (one rank vector per row)
+ *   r    32, 64, 96 or 128
+ *   t    device bf16 [M][r] (output)
+ * mxq_lowrank_up: y [M][N] = RN_bf16(epilogue(y_pre + t L2^T)), fp32.
+ *   y_pre device bf16 [M][N] (dense), N a multiple of 32
+ *   l2    device bf16 [N][r] (one rank vector per output column)
+ *   y     device bf16 [M][N] (output; may be y_pre itself)
+ * All pointers 16-byte aligned.
+ */
+int mxq_lowrank_down(const void* x, int64_t M, int64_t K, const void* l1t, int64_t r, void* t, hipStream_t stream);
+int mxq_lowrank_up(const void* y_pre, const void* t, const void* l2, int64_t M, int64_t N, int64_t r,
+                   int epilogue, void* y, hipStream_t stream);
+
+/*
  * Scaled GEMM on quantized operands (the native MXFP4 / W4A8 execution of
  * "Quantization formats", kernel note): y [M][N] bf16 =
  *   epilogue( sum_k deqA[m][k] deqW[n][k] + bias[n] ).

@@ -46,6 +46,8 @@ _SIGS = {
     "mxq_quantize_weight_mxfp4": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "mxq_quantize_act": (ctypes.c_int, [ctypes.c_int, _P, _I64, _I64, _I64, _P, _P, _P]),
     "mxq_fp8_calibrate": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P]),
+    "mxq_lowrank_down": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P]),
+    "mxq_lowrank_up": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P, _P]),
     "mxq_sqnr_accumulate": (ctypes.c_int, [_P, _P, _I64, _P, _P]),
     "mxq_replay_workspace_bytes": (ctypes.c_int, [_P, _I32, ctypes.POINTER(ctypes.c_size_t)]),
     "mxq_block_replay_sqnr": (ctypes.c_int, [_P, _I32, _P, ctypes.c_size_t, _P, _P, _P]),
@@ -489,3 +491,32 @@ def policy_select(sums_off, sums_on, tier=TIER_HIGH):
                                   int(tier), modes.ctypes.data_as(_P))
     _check(st, "policy_select")
     return modes
+
+
+# ------------------------------------------------------------ low rank ----
+
+def lowrank_down(x, l1t, t=None, stream=None):
+    """SVDQuant branch, first half: t [M, r] = bf16(x [M, K] @ L1), with L1 given transposed as l1t [r, K]."""
+    torch = _torch()
+    m, k = _rows_k(x, "x")
+    r = int(l1t.shape[0])
+    if t is None:
+        t = torch.empty((m, r), dtype=torch.bfloat16, device=x.device)
+    st = lib().mxq_lowrank_down(_dev_ptr(x, "x", torch.bfloat16), m, k, _dev_ptr(l1t, "l1t", torch.bfloat16), r,
+                                 _dev_ptr(t, "t", torch.bfloat16), _stream_handle(stream))
+    _check(st, "lowrank_down")
+    return t
+
+
+def lowrank_up(y_pre, t, l2, epilogue=EPI_NONE, y=None, stream=None):
+    """SVDQuant branch, second half: y = bf16(epilogue(y_pre + t @ l2^T)); l2 [N, r]; y may be y_pre."""
+    torch = _torch()
+    m, n = _rows_k(y_pre, "y_pre")
+    r = int(t.shape[1])
+    if y is None:
+        y = torch.empty_like(y_pre)
+    st = lib().mxq_lowrank_up(_dev_ptr(y_pre, "y_pre", torch.bfloat16), _dev_ptr(t, "t", torch.bfloat16),
+                               _dev_ptr(l2, "l2", torch.bfloat16), m, n, r, int(epilogue),
+                               _dev_ptr(y, "y", torch.bfloat16), _stream_handle(stream))
+    _check(st, "lowrank_up")
+    return y

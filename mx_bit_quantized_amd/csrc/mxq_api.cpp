@@ -182,6 +182,28 @@ int mxq_quantize_mxfp4_hadamard(const void* x, int64_t M, int64_t K, int64_t ldx
   return hip_status(mxq::launch_mxfp4_hadamard_quant(x, M, K, ldx, mult, codes, scales, stream));
 }
 
+static bool lowrank_rank_ok(int64_t r) { return r == 32 || r == 64 || r == 96 || r == 128; }
+
+int mxq_lowrank_down(const void* x, int64_t M, int64_t K, const void* l1t, int64_t r, void* t, hipStream_t stream) {
+  int st = check_mk(M, K, K);
+  if (st != MXQ_OK) return st;
+  if (K % 64 != 0 || !lowrank_rank_ok(r)) return MXQ_ERR_SHAPE;
+  if (M == 0) return MXQ_OK;
+  if (x == nullptr || l1t == nullptr || t == nullptr) return MXQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(l1t) || !aligned16(t)) return MXQ_ERR_ALIGN;
+  return hip_status(mxq::launch_lowrank_down(x, M, K, l1t, r, t, stream));
+}
+
+int mxq_lowrank_up(const void* y_pre, const void* t, const void* l2, int64_t M, int64_t N, int64_t r,
+                   int epilogue, void* y, hipStream_t stream) {
+  if (epilogue != MXQ_EPI_NONE && epilogue != MXQ_EPI_GELU_TANH) return MXQ_ERR_MODE;
+  if (M < 0 || N < 0 || M >= kMaxDim || N >= kMaxDim || N % 32 != 0 || !lowrank_rank_ok(r)) return MXQ_ERR_SHAPE;
+  if (M == 0 || N == 0) return MXQ_OK;
+  if (y_pre == nullptr || t == nullptr || l2 == nullptr || y == nullptr) return MXQ_ERR_NULL;
+  if (!aligned16(y_pre) || !aligned16(t) || !aligned16(l2) || !aligned16(y)) return MXQ_ERR_ALIGN;
+  return hip_status(mxq::launch_lowrank_up(y_pre, t, l2, M, N, r, epilogue, y, stream));
+}
+
 int mxq_sqnr_accumulate(const void* y, const void* y_ref, int64_t n, double* sums, hipStream_t stream) {
   if (n < 0) return MXQ_ERR_SHAPE;
   if (n == 0) return MXQ_OK;

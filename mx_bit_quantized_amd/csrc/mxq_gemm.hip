@@ -27,6 +27,7 @@
 #include <array>
 
 #include "mxq_convert.h"
+#include "mxq_device.h"
 #include "mxq_internal.h"
 
 namespace mxq {
@@ -330,15 +331,6 @@ __device__ __forceinline__ void tile_of(int t, int tiles_m, int tiles_n, int& tm
   const int in = t - group * G * tiles_n;
   tm = first_m + in % gm;
   tn = in / gm;
-}
-
-__device__ __forceinline__ float gelu_tanh_dev(float y) {
-  // 0.5 y (1 + tanh(u)) = y / (1 + exp(-2u)), u = sqrt(2/pi) (y + 0.044715 y^3);
-  // exp(-2u) = 2^(y (c0 + c1 y^2)) with the constants folded: 5 VALU
-  // operations and 2 transcendental ones per element
-  constexpr float kL = -2.0f * 1.4426950408889634f * 0.7978845608028654f;  // -2 log2(e) sqrt(2/pi)
-  const float e = __builtin_amdgcn_exp2f(y * __builtin_fmaf(y * y, kL * 0.044715f, kL));
-  return y * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 #define MXQ_LDS __attribute__((address_space(3)))

@@ -22,6 +22,14 @@ hipError_t launch_hadamard_amax(const void* x, int64_t rows, int64_t K, int64_t 
 hipError_t launch_smoothquant_factors(const float* act_amax, const float* w_amax, int64_t K, float* act_mult,
                                       float* w_mult, hipStream_t s);
 
+// SVDQuant's low-rank branch: t [M][r] = RN_bf16(x L1) from l1t [r][K]
+// (r = 32, 64, 96 or 128; K % 64 == 0); y [M][N] = RN_bf16(epilogue(y_pre +
+// t L2^T)) from l2 [N][r] (N % 32 == 0; y may be y_pre).
+hipError_t launch_lowrank_down(const void* x, int64_t M, int64_t K, const void* l1t, int64_t r, void* t,
+                               hipStream_t s);
+hipError_t launch_lowrank_up(const void* y_pre, const void* t, const void* l2, int64_t M, int64_t N, int64_t r,
+                             int epilogue, void* y, hipStream_t s);
+
 // Block selection: sums[0] += sum r^2, sums[1] += sum (y - r)^2 over n bf16
 // elements (fp64, device [2]); a zero fill of n 4-byte words.
 hipError_t launch_sqnr_sums(const void* y, const void* y_ref, int64_t n, double* sums, hipStream_t s);

@@ -25,7 +25,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = mxq.lib()
     names = declared_functions()
-    assert len(names) == 23, names
+    assert len(names) == 25, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(mxq._SIGS)
@@ -247,6 +247,32 @@ def test_selection_validation_and_host_policy_select():
     assert mxq.policy_select(off, on, mxq.TIER_MID)[1, 5] == mxq.W4A8
     with pytest.raises(mxq.MxqError):
         mxq.policy_select(off, on, 3)
+
+
+def test_lowrank_validation():
+    """Host-side checks of the SVDQuant branch entry points (nothing is enqueued)."""
+    L = mxq.lib()
+    S = None
+    for r in (0, 16, 48, 160, -32):
+        assert L.mxq_lowrank_down(FAKE, 64, 256, FAKE, r, FAKE, S) == mxq.ERR_SHAPE, r
+        assert L.mxq_lowrank_up(FAKE, FAKE, FAKE, 64, 256, r, 0, FAKE, S) == mxq.ERR_SHAPE, r
+    assert L.mxq_lowrank_down(FAKE, 64, 96, FAKE, 32, FAKE, S) == mxq.ERR_SHAPE  # K % 64
+    assert L.mxq_lowrank_up(FAKE, FAKE, FAKE, 64, 48, 32, 0, FAKE, S) == mxq.ERR_SHAPE  # N % 32
+    assert L.mxq_lowrank_up(FAKE, FAKE, FAKE, 64, 256, 32, 2, FAKE, S) == mxq.ERR_MODE
+    for pos in (0, 3, 5):
+        args = [FAKE, 64, 256, FAKE, 32, FAKE, S]
+        args[pos] = None
+        assert L.mxq_lowrank_down(*args) == mxq.ERR_NULL, pos
+        args[pos] = FAKE_ODD
+        assert L.mxq_lowrank_down(*args) == mxq.ERR_ALIGN, pos
+    for pos in (0, 1, 2, 7):
+        args = [FAKE, FAKE, FAKE, 64, 256, 32, 0, FAKE, S]
+        args[pos] = None
+        assert L.mxq_lowrank_up(*args) == mxq.ERR_NULL, pos
+        args[pos] = FAKE_ODD
+        assert L.mxq_lowrank_up(*args) == mxq.ERR_ALIGN, pos
+    assert L.mxq_lowrank_down(None, 0, 256, None, 32, None, S) == mxq.OK
+    assert L.mxq_lowrank_up(None, None, None, 0, 256, 32, 0, None, S) == mxq.OK
 
 
 def test_static_fp8_validation():
