@@ -7,7 +7,7 @@ inputs and packed weights already resident in HBM. Weight packing is offline
 and is timed separately (reported, not part of the step).
 
     python bench.py [--steps K] [--warmup W] [--workload a14b_stack|a14b_ffn|qkv|ti2v|tiny]
-                    [--act-scale per_token|static] [--transform-on]
+                    [--act-scale per_token|static] [--transform-on] [--svdquant-rank R] [--select]
 
 --act-scale static runs the W4A8 linears on static (per-tensor) FP8
 activations: each input's amax is calibrated once, untimed, on the same
@@ -19,6 +19,14 @@ plus SmoothQuant ahead of MXFP4. The factors are calibrated once, untimed, on
 the same synthetic inputs and on each weight, and the weights are packed
 transformed. Such a block's FFN runs up-projection -> bf16 h -> transformed
 quantizer -> down-projection (the fused MXFP4 epilogue does not rotate).
+
+--svdquant-rank R adds SVDQuant's rank-R bf16 branch to every W4A4 linear:
+GEMM on the residual (no epilogue) -> T = x L1 -> y = epilogue(y_pre + T L2).
+The factors are random bf16 of the right shapes (no trained weights to
+decompose); the branch's cost does not depend on their values.
+
+--select replaces the step by the calibration-driven block selection over the
+A14B model (see run_select).
 
 Prints one JSON line. Per-launch kernel durations come from HIP events
 recorded on the launch stream around every kernel inside the timed steps.
@@ -53,6 +61,8 @@ def parse():
                     help="W4A8 activation scale: per token (amax/448 of each row) or static per tensor (calibrated)")
     ap.add_argument("--transform-on", action="store_true",
                     help="run the W4A4 blocks as transform_on (Hadamard rotation + SmoothQuant, calibrated)")
+    ap.add_argument("--svdquant-rank", type=int, default=0, choices=[0, 32, 64, 96, 128],
+                    help="add SVDQuant's low-rank bf16 branch of this rank to every W4A4 linear")
     ap.add_argument("--select", action="store_true",
                     help="instead of the step: calibration-driven block selection over the A14B model (one 480p "
                          "calibration sample), timing the library's block replay")
@@ -70,10 +80,11 @@ def log(*a):
 class Stack:
     """Packed weights, inputs and buffers of one workload on the device."""
 
-    def __init__(self, wl, torch, mxq, static=False, transform=False):
+    def __init__(self, wl, torch, mxq, static=False, transform=False, lr_rank=0):
         self.wl, self.torch, self.mxq = wl, torch, mxq
         self.static = static
         self.transform = transform
+        self.lr_rank = lr_rank
         dev = "cuda:0"
         t0 = time.time()
         self.policy_table = wl.policy()
@@ -141,6 +152,19 @@ class Stack:
                     del w
         self.pack_gbs = pack_bytes / (pack_ms * 1e-3) / 1e9
         log(f"weights packed in {time.time() - t0:.1f}s ({pack_bytes / 1e9:.1f} GB traffic, {self.pack_gbs:.0f} GB/s)")
+        # SVDQuant branch factors of the W4A4 linears (random bf16, seeded) and T's buffer
+        self.lowrank = {}
+        if lr_rank:
+            gen = torch.Generator(device=dev).manual_seed(1234)
+            for e in range(wl.n_experts):
+                for b in range(wl.n_blocks):
+                    if self.policy.mode(e, b) != 0:
+                        continue
+                    for li, lin in enumerate(wl.linears):
+                        l1t = (torch.randn((lr_rank, lin.k), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+                        l2 = (torch.randn((lin.n, lr_rank), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+                        self.lowrank[(e, b, li)] = (l1t, l2)
+            self.t_buf = torch.empty((m_max * lr_rank,), dtype=torch.bfloat16, device=dev)
         self.records = []  # (kind, mode, flops, bytes, ev_start, ev_end)
         self.down_ready = False  # the FFN's second projection has its input codes in codes_buf2
         if static:
@@ -217,7 +241,8 @@ class Stack:
                     # scale needs the row's amax first)
                     static8 = mode == 1 and self.static
                     tr = mode == 0 and self.transform
-                    fused_up = lin.name == "ffn_up" and not tr and (
+                    lr = self.lowrank.get((e, b, li)) if mode == 0 else None
+                    fused_up = lin.name == "ffn_up" and not tr and lr is None and (
                         (mode == 0 and mxq.gemm_mxfp4_out_supported(m, lin.n, lin.k))
                         or (static8 and mxq.gemm_fp8_static_out_supported(m, lin.n, lin.k)))
                     fed = lin.name == "ffn_down" and self.down_ready
@@ -246,18 +271,33 @@ class Stack:
                         mxq.gemm_fp8_static_out(codes, scales, wc, wsc, self.amax_h[(e, b)], None, lin.epilogue,
                                                 oc, osc)
                         out_bytes = m * lin.n + 4 * m
+                    elif lr is not None:
+                        # the quantized product without the epilogue, then the branch and the epilogue
+                        mxq.gemm(mode, codes, scales, wc, wsc, None, 0, out)
+                        out_bytes = m * lin.n * 2
                     else:
                         mxq.gemm(mode, codes, scales, wc, wsc, None, lin.epilogue, out)
                         out_bytes = m * lin.n * 2
-                    self.down_ready = fused_up
                     if timed:
                         e2.record()
+                    if lr is not None:
+                        t = self.t_buf[: m * self.lr_rank].view(m, self.lr_rank)
+                        mxq.lowrank_down(x, lr[0], t)
+                        mxq.lowrank_up(out, t, lr[1], lin.epilogue, y=out)
+                    self.down_ready = fused_up
+                    if timed:
+                        e5 = torch.cuda.Event(enable_timing=True)
+                        e5.record()
                         qbytes = m * lin.k * 2 + (m * lin.k // 2 + m * lin.k // 32 if mode == 0 else m * lin.k + 4 * m)
                         gbytes = ((m * lin.k // 2 + m * lin.k // 32) if mode == 0 else (m * lin.k + 4 * m)) \
                             + lin.n * lin.k // 2 + lin.n * lin.k // 32 + out_bytes
                         if not fed:
                             self.records.append(("quant", mode, 0, qbytes, e0, e1))
                         self.records.append(("gemm", mode, 2 * m * lin.n * lin.k, gbytes, e1, e2))
+                        if lr is not None:
+                            rr = self.lr_rank
+                            self.records.append(("lowrank", mode, 2 * m * rr * (lin.k + lin.n),
+                                                 m * lin.k * 2 + 2 * m * lin.n * 2, e2, e5))
 
 
 # the pipelined GEMM's symbol per mode, as the profile summaries write it
@@ -296,13 +336,14 @@ def profiled_traffic(workload_tag, mode):
     return total // launches
 
 
-def cpu_baseline(wl, sample_rows, static=False, transform=False):
+def cpu_baseline(wl, sample_rows, static=False, transform=False, lr_rank=0):
     """Oracle throughput on a bounded sample: `sample_rows` token rows through one block's linears.
 
     With ``static`` the W4A8 linears quantize with the oracle's static FP8 rule,
     the scale calibrated on the sample (untimed). With ``transform`` the W4A4
     linears run the oracle's transform_on path, calibrated on the sample and the
-    weight (untimed, like the weight packing)."""
+    weight (untimed, like the weight packing). With ``lr_rank`` the W4A4
+    linears add the oracle's SVDQuant branch of that rank (random factors)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -336,6 +377,12 @@ def cpu_baseline(wl, sample_rows, static=False, transform=False):
             t0 = time.perf_counter()
             if md == 0 and transform:
                 y, _, _ = oracle.qlinear_transform(oracle.TRANSFORM_ON, xs, wq, wsc, am, epilogue=lin.epilogue)
+            elif md == 0 and lr_rank:
+                g = np.random.default_rng(li)
+                l1t = synth.f32_to_bf16_bits((g.standard_normal((lr_rank, lin.k)) * 0.02).astype(np.float32))
+                l2 = synth.f32_to_bf16_bits((g.standard_normal((lin.n, lr_rank)) * 0.02).astype(np.float32))
+                ac, asc = oracle.mxfp4_quantize(xs)
+                y = oracle.svdquant_linear(md, ac, asc, wq, wsc, xs, l1t, l2, None, lin.epilogue)[0]
             elif md == 1 and static:
                 ac, asc = oracle.fp8_quantize_static(xs, amax)
                 y = oracle.qdq_matmul(md, ac, asc, wq, wsc, None, lin.epilogue)
@@ -350,7 +397,8 @@ def cpu_baseline(wl, sample_rows, static=False, transform=False):
     return {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{rows} token rows through the first W4A4 and first W4A8 block's video-token linears "
                       f"(quantize{' (W4A8: static FP8)' if static else ''}"
-                      f"{' (W4A4: transform_on)' if transform else ''} + float64 QDQ matmul), "
+                      f"{' (W4A4: transform_on)' if transform else ''}"
+                      f"{f' (W4A4: + rank-{lr_rank} SVDQuant branch)' if lr_rank else ''} + float64 QDQ matmul), "
                       f"{flops / 1e9:.1f} GFLOP in {secs:.1f} s"}
 
 
@@ -492,7 +540,10 @@ def main():
     wl = synth.workload(WORKLOADS[args.workload])
     static = args.act_scale == "static"
     transform = args.transform_on
-    stack = Stack(wl, torch, mxq, static, transform)
+    if transform and args.svdquant_rank:
+        print("--transform-on and --svdquant-rank are separate W4A4 transforms: pick one", file=sys.stderr)
+        sys.exit(2)
+    stack = Stack(wl, torch, mxq, static, transform, args.svdquant_rank)
     for _ in range(args.warmup):
         stack.step(timed=False)
     torch.cuda.synchronize()
@@ -523,6 +574,9 @@ def main():
         if kind == "gemm":
             d["tflops"] = round(a["flops"] / (a["ms"] * 1e-3) / 1e12, 1)
             d["frac_of_peak"] = round(d["tflops"] / PEAK_TFLOPS[mode], 4)
+        elif kind == "lowrank":
+            d["gbs"] = round(a["bytes"] / (a["ms"] * 1e-3) / 1e9, 1)
+            d["frac_of_hbm"] = round(d["gbs"] / PEAK_HBM_GBS, 4)
         else:
             d["gbs"] = round(a["bytes"] / (a["ms"] * 1e-3) / 1e9, 1)
             d["frac_of_hbm"] = round(d["gbs"] / PEAK_HBM_GBS, 4)
@@ -531,7 +585,7 @@ def main():
     a = agg[dom]
     achieved = a["flops"] / (a["ms"] * 1e-3) / 1e12
     tag = [k for k, v in WORKLOADS.items() if v == wl.config_id][0] + ("_static" if static else "") + \
-        ("_transform" if transform else "")
+        ("_transform" if transform else "") + (f"_svdquant{args.svdquant_rank}" if args.svdquant_rank else "")
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_TFLOPS[dom[1]], "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_TFLOPS[dom[1]], 4),
                 "traffic": profiled_traffic(tag, dom[1]),
@@ -559,14 +613,15 @@ def main():
                    "experts": wl.n_experts, "blocks": wl.n_blocks,
                    "w4a8_blocks": int((stack.policy_table == 1).sum()),
                    "w4a8_activations": "fp8_static_per_tensor" if static else "fp8_per_token",
-                   "w4a4_transform": "hadamard128+smoothquant" if transform else "none",
+                   "w4a4_transform": "hadamard128+smoothquant" if transform else
+                   (f"svdquant_rank{args.svdquant_rank}" if args.svdquant_rank else "none"),
                    "linears_per_block": len(wl.linears), "tflop_per_step": round(wl.total_flops() / 1e12, 2)},
         "roofline": roofline,
         "kernels": kernels,
         "weight_pack_gbs": round(stack.pack_gbs, 1),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_rows, static, transform)
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_rows, static, transform, args.svdquant_rank)
     print(json.dumps(out), flush=True)
 
 

@@ -253,7 +253,7 @@ int mxq_policy_select(const double* sums_off, const double* sums_on, int32_t n_e
  * whole sum), mxq_lowrank_down, then mxq_lowrank_up with the linear's
  * epilogue.
  * mxq_lowrank_down: t [M][r] = RN_bf16(x L1), fp32 accumulation.
- *   x    device bf16 [M][K] (dense), K a multiple of 64
+ *   x    device bf16 [M][K] (dense), K a multiple of 128
  *   l1t  device bf16 [r][K]: L1 transposed (one rank vector per row)
  *   r    32, 64, 96 or 128
  *   t    device bf16 [M][r] (output)

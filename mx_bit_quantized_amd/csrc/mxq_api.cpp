@@ -187,7 +187,7 @@ static bool lowrank_rank_ok(int64_t r) { return r == 32 || r == 64 || r == 96 ||
 int mxq_lowrank_down(const void* x, int64_t M, int64_t K, const void* l1t, int64_t r, void* t, hipStream_t stream) {
   int st = check_mk(M, K, K);
   if (st != MXQ_OK) return st;
-  if (K % 64 != 0 || !lowrank_rank_ok(r)) return MXQ_ERR_SHAPE;
+  if (K % 128 != 0 || !lowrank_rank_ok(r)) return MXQ_ERR_SHAPE;
   if (M == 0) return MXQ_OK;
   if (x == nullptr || l1t == nullptr || t == nullptr) return MXQ_ERR_NULL;
   if (!aligned16(x) || !aligned16(l1t) || !aligned16(t)) return MXQ_ERR_ALIGN;

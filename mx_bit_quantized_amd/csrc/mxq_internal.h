@@ -23,7 +23,7 @@ hipError_t launch_smoothquant_factors(const float* act_amax, const float* w_amax
                                       float* w_mult, hipStream_t s);
 
 // SVDQuant's low-rank branch: t [M][r] = RN_bf16(x L1) from l1t [r][K]
-// (r = 32, 64, 96 or 128; K % 64 == 0); y [M][N] = RN_bf16(epilogue(y_pre +
+// (r = 32, 64, 96 or 128; K % 128 == 0); y [M][N] = RN_bf16(epilogue(y_pre +
 // t L2^T)) from l2 [N][r] (N % 32 == 0; y may be y_pre).
 hipError_t launch_lowrank_down(const void* x, int64_t M, int64_t K, const void* l1t, int64_t r, void* t,
                                hipStream_t s);

@@ -34,119 +34,193 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 // One 32 x 32 MFMA tile: D[i][j] = sum_k A[i][k] B[j][k] over k < 16. Lane l
 // gives A row l % 32 and B row l % 32, k = 8 (l / 32) .. + 7 of each; its
 // result registers q hold D[8 (q / 4) + 4 (l / 32) + q % 4][l % 32].
+
+// ---- down projection: T = RN_bf16(x L1) ---------------------------------
 //
-// Down projection: A = L1^T rows (rank index), B = x rows (tokens), so a lane
-// ends with 16 rank values of one token. The contraction order is free, so
-// MFMA k-slot (h, e) of super-step k0 and step s (0..3) is element
-// k0 + 32 h + 8 s + e: each lane reads 64 contiguous bytes of its row per
-// super-step, 16 at a time. A workgroup (4 waves) owns 32 tokens; its waves
-// take contiguous quarters of K and fold their partial sums through LDS.
-constexpr int kLrWaves = 4;
+// A workgroup (4 waves) owns 64 rows of x and walks K in chunks of 128. Each
+// chunk of x (64 x 128 bf16, 16 KiB) and of L1^T (r x 128) is loaded with
+// row-contiguous 16-byte loads (whole 256-byte row runs per instruction) into
+// registers two chunks ahead, then through LDS to the matrix cores. Wave w takes k = 32 w .. 32 w + 31 of the chunk (two MFMA
+// steps) for every output tile (2 row tiles x r/32 rank tiles), with A = L1^T
+// rows and B = x rows, so a lane ends with 16 rank values of one row; the
+// four waves' partial sums are added through LDS at the end.
+constexpr int kDnRows = 64;
+constexpr int kDnKc = 128;
+constexpr int kDnPitch = kDnKc * 2 + 16;  // bytes per LDS row: 16-byte reads of 16 rows hit 16 bank groups
 
 template <int R>  // rank / 32
-__global__ __launch_bounds__(64 * kLrWaves) void lowrank_down_kernel(const uint16_t* __restrict__ x, int64_t M,
-                                                                     int64_t K, const uint16_t* __restrict__ l1t,
-                                                                     uint16_t* __restrict__ t) {
-  __shared__ float red[kLrWaves - 1][R][16][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__global__ __launch_bounds__(256) void lowrank_down_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                                          const uint16_t* __restrict__ l1t,
+                                                          uint16_t* __restrict__ t) {
+  constexpr int RANK = 32 * R;
+  constexpr int XB = kDnRows * kDnPitch, LB = RANK * kDnPitch;
+  constexpr int RED = 3 * 16 * 64 * 4;  // one output tile's partial sums of waves 1..3
+  __shared__ __attribute__((aligned(16))) uint8_t lds[(XB + LB) > RED ? (XB + LB) : RED];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 31, h = lane >> 5;
-  const int64_t row = (int64_t)blockIdx.x * 32 + r;
-  const bool row_ok = row < M;
-  const uint16_t* xr = x + (row_ok ? row : 0) * K + 32 * h;
-  const int64_t steps = K / 64;
-  const int64_t s_begin = steps * wave / kLrWaves, s_end = steps * (wave + 1) / kLrWaves;
-  v16f_t acc[R];
+  const int64_t row0 = (int64_t)blockIdx.x * kDnRows;
+  // loader mapping: 16-byte chunk c16 = tid % 16 of row tid / 16 (+ 16 i)
+  const int lc = tid & 15, lr = tid >> 4;
+  // two chunks in flight: register sets A and B alternate
+  uint4 xa[kDnRows / 16], la[RANK / 16], xb[kDnRows / 16], lb[RANK / 16];
+  auto load = [&](uint4 (&xr)[kDnRows / 16], uint4 (&lrg)[RANK / 16], int64_t k0) {
 #pragma unroll
-  for (int q = 0; q < R; ++q) acc[q] = v16f_t{};
-  for (int64_t st = s_begin; st < s_end; ++st) {
-    const int64_t k0 = st * 64;
-    uint4 xv[4];
+    for (int i = 0; i < kDnRows / 16; ++i) {
+      const int64_t row = row0 + lr + 16 * i;
+      xr[i] = row < M ? *reinterpret_cast<const uint4*>(x + row * K + k0 + 8 * lc) : make_uint4(0, 0, 0, 0);
+    }
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      xv[s] = row_ok ? reinterpret_cast<const uint4*>(xr + k0)[s] : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < RANK / 16; ++i)
+      lrg[i] = *reinterpret_cast<const uint4*>(l1t + (int64_t)(lr + 16 * i) * K + k0 + 8 * lc);
+  };
+  v16f_t acc[2][R];
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-      for (int q = 0; q < R; ++q) {
-        const uint4 lv = *reinterpret_cast<const uint4*>(l1t + (int64_t)(32 * q + r) * K + k0 + 32 * h + 8 * s);
-        acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lv), as_bf16x8(xv[s]), acc[q], 0, 0, 0);
+    for (int q = 0; q < R; ++q) acc[a][q] = v16f_t{};
+  // chunk k0 from (xr, lrg): into LDS, refill the registers with chunk k0 + 2 Kc, multiply
+  auto body = [&](uint4 (&xr)[kDnRows / 16], uint4 (&lrg)[RANK / 16], int64_t k0) {
+    __syncthreads();  // the previous chunk's reads are done
+#pragma unroll
+    for (int i = 0; i < kDnRows / 16; ++i)
+      *reinterpret_cast<uint4*>(lds + (lr + 16 * i) * kDnPitch + 16 * lc) = xr[i];
+#pragma unroll
+    for (int i = 0; i < RANK / 16; ++i)
+      *reinterpret_cast<uint4*>(lds + XB + (lr + 16 * i) * kDnPitch + 16 * lc) = lrg[i];
+    __syncthreads();
+    if (k0 + 2 * kDnKc < K) load(xr, lrg, k0 + 2 * kDnKc);
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int kb = (32 * wave + 16 * s + 8 * h) * 2;  // byte offset of the lane's 8 elements
+      uint4 bx[2], al[R];
+#pragma unroll
+      for (int a = 0; a < 2; ++a) bx[a] = *reinterpret_cast<const uint4*>(lds + (32 * a + r) * kDnPitch + kb);
+#pragma unroll
+      for (int q = 0; q < R; ++q) al[q] = *reinterpret_cast<const uint4*>(lds + XB + (32 * q + r) * kDnPitch + kb);
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int q = 0; q < R; ++q)
+          acc[a][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(al[q]), as_bf16x8(bx[a]), acc[a][q], 0, 0, 0);
+    }
+  };
+  load(xa, la, 0);
+  if (kDnKc < K) load(xb, lb, kDnKc);
+  for (int64_t k0 = 0; k0 < K; k0 += 2 * kDnKc) {
+    body(xa, la, k0);
+    if (k0 + kDnKc < K) body(xb, lb, k0 + kDnKc);
+  }
+  // fold the waves' partial sums tile by tile through LDS (every wave takes
+  // part in every barrier; wave 0 adds and stores)
+  float* red = reinterpret_cast<float*>(lds);
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    const int64_t row = row0 + 32 * a + r;
+#pragma unroll
+    for (int q = 0; q < R; ++q) {
+      __syncthreads();
+      if (wave > 0) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) red[((wave - 1) * 16 + i) * 64 + lane] = acc[a][q][i];
       }
-  }
-  if (wave > 0) {
+      __syncthreads();
+      if (wave != 0) continue;
 #pragma unroll
-    for (int q = 0; q < R; ++q)
+      for (int i = 0; i < 16; ++i)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) red[wave - 1][q][i][lane] = acc[q][i];
-  }
-  __syncthreads();
-  if (wave != 0 || !row_ok) return;
-  const int64_t rank = 32 * R;
+        for (int w = 0; w < 3; ++w) acc[a][q][i] += red[(w * 16 + i) * 64 + lane];
+      if (row < M) {
 #pragma unroll
-  for (int q = 0; q < R; ++q) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-#pragma unroll
-      for (int w = 0; w < kLrWaves - 1; ++w) acc[q][i] += red[w][q][i][lane];
-#pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {
-      const uint2 v = make_uint2(pack_bf16(acc[q][4 * t4], acc[q][4 * t4 + 1]),
-                                 pack_bf16(acc[q][4 * t4 + 2], acc[q][4 * t4 + 3]));
-      *reinterpret_cast<uint2*>(t + row * rank + 32 * q + 8 * t4 + 4 * h) = v;
+        for (int t4 = 0; t4 < 4; ++t4)
+          *reinterpret_cast<uint2*>(t + row * RANK + 32 * q + 8 * t4 + 4 * h) =
+              make_uint2(pack_bf16(acc[a][q][4 * t4], acc[a][q][4 * t4 + 1]),
+                         pack_bf16(acc[a][q][4 * t4 + 2], acc[a][q][4 * t4 + 3]));
+      }
     }
   }
 }
 
-// Up projection: A = L2 rows (output columns), B = T rows (tokens); a wave
-// owns 32 tokens x 128 columns (four 32 x 32 tiles), r / 16 MFMA steps per
-// tile. A lane ends with 16 columns of one token: 4 runs of 4 consecutive
-// columns, which it reads from y_pre and writes to y (8 bytes each), so y may
-// be y_pre itself. Rows past M are neither read nor written.
+// ---- up projection: y = RN_bf16(epilogue(y_pre + T L2^T)) ----------------
+//
+// A wave owns 32 rows x 128 columns, in two passes of 64 columns: two MFMA
+// tiles with A = L2 rows (columns of y) and B = T rows, r / 16 steps each.
+// The sums go through a per-wave LDS area as a row-major 32 x 64 fp32 block;
+// the lanes then read 8 consecutive columns each, 8 rows x 64 columns per
+// instruction, add y_pre (16-byte loads), apply the epilogue and store 16
+// bytes: whole 128-byte row runs per instruction. Every element is read and
+// written by one lane, so y may be y_pre. Rows past M are neither read nor
+// written.
+constexpr int kUpPitch = 64 * 4 + 16;  // bytes per LDS row of the 32 x 64 fp32 block
+
 template <int S, bool GELU>  // S = rank / 16
 __global__ __launch_bounds__(256) void lowrank_up_kernel(const uint16_t* __restrict__ y_pre,
                                                          const uint16_t* __restrict__ t,
                                                          const uint16_t* __restrict__ l2, int64_t M, int64_t N,
                                                          uint16_t* y) {
-  const int lane = threadIdx.x & 63;
-  const int64_t wave_id = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4][32 * kUpPitch];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t wave_id = (int64_t)blockIdx.x * 4 + wave;
   const int64_t strips = (N + 127) / 128;
   const int64_t row0 = wave_id / strips * 32, col0 = wave_id % strips * 128;
-  if (row0 >= M) return;  // whole waves only: no barrier follows
+  if (row0 >= M) return;  // whole waves only; the LDS area is the wave's own, no barrier follows
   const int r = lane & 31, h = lane >> 5;
-  const int64_t row = row0 + r;
-  const bool row_ok = row < M;
   constexpr int64_t rank = 16 * S;
+  uint8_t* blk = lds[wave];
+  const int64_t trow = row0 + r;
   uint4 tb[S];
 #pragma unroll
   for (int s = 0; s < S; ++s)
-    tb[s] = row_ok ? *reinterpret_cast<const uint4*>(t + row * rank + 16 * s + 8 * h) : make_uint4(0, 0, 0, 0);
-  for (int c = 0; c < 4; ++c) {
-    const int64_t n0 = col0 + 32 * c;
-    if (n0 >= N) break;
-    v16f_t acc = {};
+    tb[s] = trow < M ? *reinterpret_cast<const uint4*>(t + trow * rank + 16 * s + 8 * h) : make_uint4(0, 0, 0, 0);
+  const int lc = lane & 7;  // 8-column chunk of the pass
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int c = 0; c < 2; ++c) {
+      const int64_t n0 = col0 + 64 * pass + 32 * c;
+      v16f_t acc = {};
+      if (n0 < N) {
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-      const uint4 a = *reinterpret_cast<const uint4*>(l2 + (n0 + r) * rank + 16 * s + 8 * h);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(tb[s]), acc, 0, 0, 0);
+        for (int s = 0; s < S; ++s) {
+          const uint4 a = *reinterpret_cast<const uint4*>(l2 + (n0 + r) * rank + 16 * s + 8 * h);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(tb[s]), acc, 0, 0, 0);
+        }
+      }
+      // D[n][m] -> block[m = r][n = 32 c + 8 (q / 4) + 4 h + q % 4]
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4)
+        *reinterpret_cast<float4*>(blk + r * kUpPitch + (32 * c + 8 * t4 + 4 * h) * 4) =
+            make_float4(acc[4 * t4], acc[4 * t4 + 1], acc[4 * t4 + 2], acc[4 * t4 + 3]);
     }
-    if (!row_ok) continue;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {
-      const int64_t n = n0 + 8 * t4 + 4 * h;
-      const uint2 p = *reinterpret_cast<const uint2*>(y_pre + row * N + n);
-      float v[4] = {as_float(p.x << 16) + acc[4 * t4], as_float(p.x & 0xFFFF0000u) + acc[4 * t4 + 1],
-                    as_float(p.y << 16) + acc[4 * t4 + 2], as_float(p.y & 0xFFFF0000u) + acc[4 * t4 + 3]};
+    for (int it = 0; it < 4; ++it) {
+      const int rr = 8 * it + (lane >> 3);
+      const int64_t row = row0 + rr, n = col0 + 64 * pass + 8 * lc;
+      if (row >= M || n >= N) continue;
+      const float4 lo = *reinterpret_cast<const float4*>(blk + rr * kUpPitch + lc * 32);
+      const float4 hi = *reinterpret_cast<const float4*>(blk + rr * kUpPitch + lc * 32 + 16);
+      const uint4 p = *reinterpret_cast<const uint4*>(y_pre + row * N + n);
+      float v[8] = {as_float(p.x << 16) + lo.x, as_float(p.x & 0xFFFF0000u) + lo.y,
+                    as_float(p.y << 16) + lo.z, as_float(p.y & 0xFFFF0000u) + lo.w,
+                    as_float(p.z << 16) + hi.x, as_float(p.z & 0xFFFF0000u) + hi.y,
+                    as_float(p.w << 16) + hi.z, as_float(p.w & 0xFFFF0000u) + hi.w};
       if constexpr (GELU) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = gelu_tanh_dev(v[i]);
+        for (int i = 0; i < 8; ++i) v[i] = gelu_tanh_dev(v[i]);
       }
-      *reinterpret_cast<uint2*>(y + row * N + n) = make_uint2(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]));
+      *reinterpret_cast<uint4*>(y + row * N + n) =
+          make_uint4(pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3]), pack_bf16(v[4], v[5]), pack_bf16(v[6], v[7]));
     }
+    // the next pass overwrites the block: its writes stay behind these reads
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 
 hipError_t launch_lowrank_down(const void* x, int64_t M, int64_t K, const void* l1t, int64_t r, void* t,
                                hipStream_t s) {
-  const dim3 grid((unsigned)((M + 31) / 32)), block(64 * kLrWaves);
+  const dim3 grid((unsigned)((M + kDnRows - 1) / kDnRows)), block(256);
   const auto* xs = static_cast<const uint16_t*>(x);
   const auto* ls = static_cast<const uint16_t*>(l1t);
   auto* ts = static_cast<uint16_t*>(t);

@@ -256,7 +256,8 @@ def test_lowrank_validation():
     for r in (0, 16, 48, 160, -32):
         assert L.mxq_lowrank_down(FAKE, 64, 256, FAKE, r, FAKE, S) == mxq.ERR_SHAPE, r
         assert L.mxq_lowrank_up(FAKE, FAKE, FAKE, 64, 256, r, 0, FAKE, S) == mxq.ERR_SHAPE, r
-    assert L.mxq_lowrank_down(FAKE, 64, 96, FAKE, 32, FAKE, S) == mxq.ERR_SHAPE  # K % 64
+    assert L.mxq_lowrank_down(FAKE, 64, 96, FAKE, 32, FAKE, S) == mxq.ERR_SHAPE  # K % 128
+    assert L.mxq_lowrank_down(FAKE, 64, 192, FAKE, 32, FAKE, S) == mxq.ERR_SHAPE
     assert L.mxq_lowrank_up(FAKE, FAKE, FAKE, 64, 48, 32, 0, FAKE, S) == mxq.ERR_SHAPE  # N % 32
     assert L.mxq_lowrank_up(FAKE, FAKE, FAKE, 64, 256, 32, 2, FAKE, S) == mxq.ERR_MODE
     for pos in (0, 3, 5):

@@ -41,7 +41,8 @@ def _idx(a):
     return torch.from_numpy(np.asarray(a, np.int64)).to("cuda:0")
 
 
-@pytest.mark.parametrize("m,k,r", [(1, 64, 32), (37, 256, 64), (300, 5120, 128), (1000, 384, 96), (4097, 128, 32)])
+@pytest.mark.parametrize("m,k,r", [(1, 128, 32), (37, 256, 64), (300, 5120, 128), (1000, 384, 96), (4097, 128, 32),
+                                   (65, 13824, 32)])
 def test_lowrank_down_vs_oracle(m, k, r):
     say("lowrank down", m, k, r)
     g = np.random.default_rng(m + k + r)
