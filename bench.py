@@ -3,8 +3,10 @@
 A step is one forward pass of every quantized linear of the workload (the
 policy lookup, activation quantization and scaled GEMM of each linear, the
 FFN's GELU epilogue and the re-quantization of its hidden state), with all
-inputs and packed weights already resident in HBM. Weight packing is offline
-and is timed separately (reported, not part of the step).
+inputs and packed weights already resident in HBM. Linears that read the same
+tensor in the model (self-attention q, k, v; cross-attention k, v) share one
+quantization of it. Weight packing is offline and is timed separately
+(reported, not part of the step).
 
     python bench.py [--steps K] [--warmup W] [--workload a14b_stack|a14b_ffn|qkv|ti2v|tiny]
                     [--act-scale per_token|static] [--transform-on] [--svdquant-rank R] [--select]
@@ -75,6 +77,14 @@ def parse():
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+# Linears that read the same tensor in the model: self-attention q, k and v
+# take the same normalized hidden state, cross-attention k and v the same text
+# context. Their activation codes are computed once (by the first of them) and
+# feed each GEMM; every other linear quantizes its own input, also where the
+# synthetic data repeat a tensor.
+SHARED_INPUT = {"self_k": "self_q", "self_v": "self_q", "cross_v": "cross_k"}
 
 
 class Stack:
@@ -224,6 +234,7 @@ class Stack:
         for e in range(wl.n_experts):
             for b in range(wl.n_blocks):
                 mode = self.policy.mode(e, b)
+                codes_src = None  # the linear whose activation codes codes_buf holds
                 for li, lin in enumerate(wl.linears):
                     m = wl.m_of(lin)
                     if lin.m_role == "video":
@@ -246,6 +257,8 @@ class Stack:
                         (mode == 0 and mxq.gemm_mxfp4_out_supported(m, lin.n, lin.k))
                         or (static8 and mxq.gemm_fp8_static_out_supported(m, lin.n, lin.k)))
                     fed = lin.name == "ffn_down" and self.down_ready
+                    # transform_on factors belong to each linear: no sharing there
+                    shared = not tr and codes_src is not None and SHARED_INPUT.get(lin.name) == codes_src
                     if fed:
                         codes, scales = self._act_views(mode, m, lin.k, self.codes_buf2)
                     else:
@@ -253,7 +266,8 @@ class Stack:
                     if timed:
                         e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
                         e0.record()
-                    if not fed:
+                    if not fed and not shared:
+                        codes_src = lin.name
                         if tr:
                             mxq.quantize_mxfp4_hadamard(x, self.act_mult[(e, b, li)], codes, scales)
                         elif static8:
@@ -291,7 +305,7 @@ class Stack:
                         qbytes = m * lin.k * 2 + (m * lin.k // 2 + m * lin.k // 32 if mode == 0 else m * lin.k + 4 * m)
                         gbytes = ((m * lin.k // 2 + m * lin.k // 32) if mode == 0 else (m * lin.k + 4 * m)) \
                             + lin.n * lin.k // 2 + lin.n * lin.k // 32 + out_bytes
-                        if not fed:
+                        if not fed and not shared:
                             self.records.append(("quant", mode, 0, qbytes, e0, e1))
                         self.records.append(("gemm", mode, 2 * m * lin.n * lin.k, gbytes, e1, e2))
                         if lr is not None:
