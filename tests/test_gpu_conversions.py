@@ -26,7 +26,7 @@ def lib():
     import torch
 
     assert torch.cuda.is_available(), "GPU tests need a HIP device"
-    assert os.path.exists(LIB), f"{LIB} missing: run __graft_entry__.build()"
+    assert os.path.exists(LIB), f"{LIB} missing: run python -m mx_bit_quantized_amd._build"
     return ctypes.CDLL(LIB)
 
 
