@@ -20,7 +20,8 @@ quantize-dequantize emulation):
 * ``transform`` - the transform_on mode: block-diagonal 128-point Hadamard
                  rotation (fp32 butterflies) and SmoothQuant factors ahead of MXFP4.
 * ``lowrank``  - SVDQuant's 16-bit low-rank branch beside the quantized
-                 product: T = bf16(x L1), y = bf16(epilogue(y_pre + T L2)).
+                 product: T = bf16(x L1), y = bf16(epilogue(y_pre + T L2)),
+                 or with T L2 inside the product's sums (one rounding).
 * ``select``   - calibration-driven block selection: block-replay SQNR (OFF
                  = plain MXFP4, ON = transform) and the tiered rule ladder that
                  emits the policy artifact.
@@ -70,6 +71,7 @@ from .lowrank import (
     lowrank_down,
     lowrank_up,
     svdquant_linear,
+    svdquant_linear_fused,
 )
 from .select import (
     TIERS,

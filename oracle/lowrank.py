@@ -21,6 +21,15 @@ fix no arithmetic for the branch):
   whole pre-activation.
 * Layouts: L1 is given transposed, [r, K] (one rank vector per row, K
   contiguous), L2 as [N, r] (nn.Linear layout of the up projection).
+
+A second reading runs the branch's second half inside the quantized product:
+T L2 joins the quantized product's fp32 sums before the bias and the epilogue,
+and the output is rounded to bf16 once (``svdquant_linear_fused``):
+
+    y = RN_bf16( epilogue( Q(x) Q(R)^T + T L2 + bias ) )
+
+with T = RN_bf16(x L1) as before. It differs from the first only by the bf16
+rounding of y_pre that it leaves out.
 """
 
 import numpy as np
@@ -47,6 +56,23 @@ def lowrank_up(y_pre_bits, t_bits, l2_bits, epilogue=EPI_NONE):
     elif epilogue != EPI_NONE:
         raise ValueError(f"unknown epilogue {epilogue}")
     return f64_to_bf16_bits(v)
+
+
+def svdquant_linear_fused(mode, a_codes, a_scales, r_codes, r_scales, t_bits, l2_bits, bias=None,
+                          epilogue=EPI_NONE):
+    """float64 y [M, N] = epilogue(Q(x) Q(R)^T + T L2^T' + bias) before the output's bf16 rounding.
+
+    T [M, r] is the branch's first half in bf16 bits (``lowrank_down``), L2 [N, r]."""
+    t = bf16_bits_to_f64(np.asarray(t_bits, np.uint16))
+    l2 = bf16_bits_to_f64(np.asarray(l2_bits, np.uint16))
+    v = qdq_matmul(mode, a_codes, a_scales, r_codes, r_scales, None, EPI_NONE) + t @ l2.T
+    if bias is not None:
+        v = v + np.asarray(bias, dtype=np.float64)[None, :]
+    if epilogue == EPI_GELU_TANH:
+        v = gelu_tanh(v)
+    elif epilogue != EPI_NONE:
+        raise ValueError(f"unknown epilogue {epilogue}")
+    return v
 
 
 def svdquant_linear(mode, a_codes, a_scales, r_codes, r_scales, x_bits, l1t_bits, l2_bits, bias=None,

@@ -84,3 +84,64 @@ def test_zero_branch_is_the_plain_layer_rounded_once_more():
                                          np.zeros((64, 32), np.uint16))
     assert np.array_equal(y, y_pre)
     assert np.array_equal(y_pre, oracle.f64_to_bf16_bits(oracle.qdq_matmul(oracle.W4A4, ac, asc, wc, ws)))
+
+
+def test_fused_exact_dense_weight():
+    """Fused reading: W = L2 L1^T + R with R on the MXFP4 grid and x exact in MXFP4, small
+    integers throughout. The layer equals the dense product x W^T plus the bias exactly, whatever
+    the rounding of intermediate results."""
+    g = np.random.default_rng(6)
+    m, n, k, r = 8, 48, 64, 32
+    x = _bits(g.choice([-2.0, -1.0, 0.0, 1.0, 2.0, 0.5], (m, k)))
+    l1t = np.zeros((r, k), np.float32)
+    for j in range(r):
+        l1t[j, g.choice(k, 2, replace=False)] = g.choice([-1.0, 1.0], 2)
+    l1t = _bits(l1t)
+    l2 = _bits(g.integers(-1, 2, (n, r)))
+    res = _bits(g.choice([-1.0, 0.0, 0.5, 1.5, 3.0], (n, k)))  # E2M1 values with scale 1 per block
+    bias = g.integers(-4, 5, n).astype(np.float64)
+    rc, rs = oracle.mxfp4_quantize(res)
+    ac, asc = oracle.mxfp4_quantize(x)
+    assert np.array_equal(oracle.mxfp4_dequantize(rc, rs), oracle.bf16_bits_to_f64(res))
+    assert np.array_equal(oracle.mxfp4_dequantize(ac, asc), oracle.bf16_bits_to_f64(x))
+    t = oracle.lowrank_down(x, l1t)
+    y = oracle.svdquant_linear_fused(oracle.W4A4, ac, asc, rc, rs, t, l2, bias)
+    xf = oracle.bf16_bits_to_f64(x)
+    w = oracle.bf16_bits_to_f64(l2) @ oracle.bf16_bits_to_f64(l1t) + oracle.bf16_bits_to_f64(res)
+    want = np.zeros((m, n))
+    for i in range(m):                       # brute force, element by element
+        for c in range(n):
+            want[i, c] = sum(xf[i, q] * w[c, q] for q in range(k)) + bias[c]
+    assert np.array_equal(y, want)
+
+
+def test_fused_without_branch_is_the_qdq_product():
+    g = np.random.default_rng(7)
+    x = synth.activation_bf16(9, 24, 256, ("student_t",))
+    w = synth.weight_bf16(9, 64, 256)
+    wc, ws = oracle.mxfp4_quantize(w)
+    ac, asc = oracle.mxfp4_quantize(x)
+    b = g.standard_normal(64)
+    for epi in (oracle.EPI_NONE, oracle.EPI_GELU_TANH):
+        y = oracle.svdquant_linear_fused(oracle.W4A4, ac, asc, wc, ws, np.zeros((24, 32), np.uint16),
+                                         np.zeros((64, 32), np.uint16), b, epi)
+        assert np.array_equal(y, oracle.qdq_matmul(oracle.W4A4, ac, asc, wc, ws, b, epi))
+
+
+def test_fused_and_two_step_readings_agree_when_y_pre_is_exact_in_bf16():
+    """With the quantized product exact in bf16 the y_pre rounding of the two-step reading does
+    nothing, so the two readings give the same bf16 output; with GELU both apply it to the whole
+    sum."""
+    g = np.random.default_rng(8)
+    m, n, k, r = 16, 64, 128, 64
+    x = _bits(g.choice([-1.0, 0.0, 1.0, 2.0], (m, k)))
+    res = _bits(g.choice([-0.5, 0.0, 0.5, 1.0], (n, k)))
+    rc, rs = oracle.mxfp4_quantize(res)
+    ac, asc = oracle.mxfp4_quantize(x)
+    l1t = _bits(g.standard_normal((r, k)) * 0.05)
+    l2 = _bits(g.standard_normal((n, r)) * 0.05)
+    for epi in (oracle.EPI_NONE, oracle.EPI_GELU_TANH):
+        y2, y_pre, t = oracle.svdquant_linear(oracle.W4A4, ac, asc, rc, rs, x, l1t, l2, None, epi)
+        assert np.array_equal(oracle.bf16_bits_to_f64(y_pre), oracle.qdq_matmul(oracle.W4A4, ac, asc, rc, rs))
+        yf = oracle.f64_to_bf16_bits(oracle.svdquant_linear_fused(oracle.W4A4, ac, asc, rc, rs, t, l2, None, epi))
+        assert np.array_equal(yf, y2)
