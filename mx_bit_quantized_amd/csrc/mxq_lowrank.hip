@@ -59,19 +59,24 @@ __global__ __launch_bounds__(256) void lowrank_down_kernel(const uint16_t* __res
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 31, h = lane >> 5;
   const int64_t row0 = (int64_t)blockIdx.x * kDnRows;
-  // loader mapping: 16-byte chunk c16 = tid % 16 of row tid / 16 (+ 16 i)
+  // loader mapping: 16-byte chunk lc = tid % 16 of row lr = tid / 16 (+ 16 i)
   const int lc = tid & 15, lr = tid >> 4;
+  constexpr int XN = kDnRows / 16, LN = RANK / 16;  // 16-byte loads per thread and chunk
   // two chunks in flight: register sets A and B alternate
-  uint4 xa[kDnRows / 16], la[RANK / 16], xb[kDnRows / 16], lb[RANK / 16];
-  auto load = [&](uint4 (&xr)[kDnRows / 16], uint4 (&lrg)[RANK / 16], int64_t k0) {
+  uint4 xa[XN], la[LN], xb[XN], lb[LN];
+  auto load = [&](uint4 (&xr)[XN], uint4 (&lrg)[LN], int64_t k0) {
 #pragma unroll
-    for (int i = 0; i < kDnRows / 16; ++i) {
-      const int64_t row = row0 + lr + 16 * i;
-      xr[i] = row < M ? *reinterpret_cast<const uint4*>(x + row * K + k0 + 8 * lc) : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < XN; ++i) {
+      const int rr = lr + 16 * i;
+      const int64_t row = row0 + rr;
+      xr[i] = (rr < kDnRows && row < M) ? *reinterpret_cast<const uint4*>(x + row * K + k0 + 8 * lc)
+                                        : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < RANK / 16; ++i)
-      lrg[i] = *reinterpret_cast<const uint4*>(l1t + (int64_t)(lr + 16 * i) * K + k0 + 8 * lc);
+    for (int i = 0; i < LN; ++i) {
+      const int rr = lr + 16 * i;
+      lrg[i] = rr < RANK ? *reinterpret_cast<const uint4*>(l1t + (int64_t)rr * K + k0 + 8 * lc) : make_uint4(0, 0, 0, 0);
+    }
   };
   v16f_t acc[2][R];
 #pragma unroll
@@ -79,14 +84,14 @@ __global__ __launch_bounds__(256) void lowrank_down_kernel(const uint16_t* __res
 #pragma unroll
     for (int q = 0; q < R; ++q) acc[a][q] = v16f_t{};
   // chunk k0 from (xr, lrg): into LDS, refill the registers with chunk k0 + 2 Kc, multiply
-  auto body = [&](uint4 (&xr)[kDnRows / 16], uint4 (&lrg)[RANK / 16], int64_t k0) {
+  auto body = [&](uint4 (&xr)[XN], uint4 (&lrg)[LN], int64_t k0) {
     __syncthreads();  // the previous chunk's reads are done
 #pragma unroll
-    for (int i = 0; i < kDnRows / 16; ++i)
-      *reinterpret_cast<uint4*>(lds + (lr + 16 * i) * kDnPitch + 16 * lc) = xr[i];
+    for (int i = 0; i < XN; ++i)
+      if (lr + 16 * i < kDnRows) *reinterpret_cast<uint4*>(lds + (lr + 16 * i) * kDnPitch + 16 * lc) = xr[i];
 #pragma unroll
-    for (int i = 0; i < RANK / 16; ++i)
-      *reinterpret_cast<uint4*>(lds + XB + (lr + 16 * i) * kDnPitch + 16 * lc) = lrg[i];
+    for (int i = 0; i < LN; ++i)
+      if (lr + 16 * i < RANK) *reinterpret_cast<uint4*>(lds + XB + (lr + 16 * i) * kDnPitch + 16 * lc) = lrg[i];
     __syncthreads();
     if (k0 + 2 * kDnKc < K) load(xr, lrg, k0 + 2 * kDnKc);
 #pragma unroll
@@ -146,10 +151,11 @@ __global__ __launch_bounds__(256) void lowrank_down_kernel(const uint16_t* __res
 // tiles with A = L2 rows (columns of y) and B = T rows, r / 16 steps each.
 // The sums go through a per-wave LDS area as a row-major 32 x 64 fp32 block;
 // the lanes then read 8 consecutive columns each, 8 rows x 64 columns per
-// instruction, add y_pre (16-byte loads), apply the epilogue and store 16
-// bytes: whole 128-byte row runs per instruction. Every element is read and
-// written by one lane, so y may be y_pre. Rows past M are neither read nor
-// written.
+// instruction, add y_pre, apply the epilogue and store 16 bytes: whole
+// 128-byte row runs per instruction. The wave's y_pre loads (16 bytes each,
+// same lane-to-element map) are all issued before the MFMAs. Every element is
+// read and written by one lane, so y may be y_pre. Rows past M are neither
+// read nor written.
 constexpr int kUpPitch = 64 * 4 + 16;  // bytes per LDS row of the 32 x 64 fp32 block
 
 template <int S, bool GELU>  // S = rank / 16
@@ -167,11 +173,22 @@ __global__ __launch_bounds__(256) void lowrank_up_kernel(const uint16_t* __restr
   constexpr int64_t rank = 16 * S;
   uint8_t* blk = lds[wave];
   const int64_t trow = row0 + r;
+  const int lc = lane & 7;  // 8-column chunk of the pass
+  // both passes' y_pre loads go out first, so that they are in flight during the MFMAs
+  uint4 pre[2][4];
+#pragma unroll
+  for (int pass = 0; pass < 2; ++pass)
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int64_t row = row0 + 8 * it + (lane >> 3), n = col0 + 64 * pass + 8 * lc;
+      pre[pass][it] =
+          (row < M && n < N) ? *reinterpret_cast<const uint4*>(y_pre + row * N + n) : make_uint4(0, 0, 0, 0);
+    }
   uint4 tb[S];
 #pragma unroll
   for (int s = 0; s < S; ++s)
     tb[s] = trow < M ? *reinterpret_cast<const uint4*>(t + trow * rank + 16 * s + 8 * h) : make_uint4(0, 0, 0, 0);
-  const int lc = lane & 7;  // 8-column chunk of the pass
+#pragma unroll
   for (int pass = 0; pass < 2; ++pass) {
     for (int c = 0; c < 2; ++c) {
       const int64_t n0 = col0 + 64 * pass + 32 * c;
@@ -199,7 +216,7 @@ __global__ __launch_bounds__(256) void lowrank_up_kernel(const uint16_t* __restr
       if (row >= M || n >= N) continue;
       const float4 lo = *reinterpret_cast<const float4*>(blk + rr * kUpPitch + lc * 32);
       const float4 hi = *reinterpret_cast<const float4*>(blk + rr * kUpPitch + lc * 32 + 16);
-      const uint4 p = *reinterpret_cast<const uint4*>(y_pre + row * N + n);
+      const uint4 p = pre[pass][it];
       float v[8] = {as_float(p.x << 16) + lo.x, as_float(p.x & 0xFFFF0000u) + lo.y,
                     as_float(p.y << 16) + lo.z, as_float(p.y & 0xFFFF0000u) + lo.w,
                     as_float(p.z << 16) + hi.x, as_float(p.z & 0xFFFF0000u) + hi.y,
