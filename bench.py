@@ -23,7 +23,10 @@ transformed. Such a block's FFN runs up-projection -> bf16 h -> transformed
 quantizer -> down-projection (the fused MXFP4 epilogue does not rotate).
 
 --svdquant-rank R adds SVDQuant's rank-R bf16 branch to every W4A4 linear:
-GEMM on the residual (no epilogue) -> T = x L1 -> y = epilogue(y_pre + T L2).
+T = x L1, then the GEMM on the residual with T L2 in its fp32 sums and the
+epilogue (one kernel; shapes the pipelined GEMM does not take run the GEMM
+without epilogue, then y = epilogue(y_pre + T L2)). The FFN's first
+projection writes its bf16 hidden state, which the second one's branch reads.
 The factors are random bf16 of the right shapes (no trained weights to
 decompose); the branch's cost does not depend on their values.
 
@@ -253,6 +256,10 @@ class Stack:
                     static8 = mode == 1 and self.static
                     tr = mode == 0 and self.transform
                     lr = self.lowrank.get((e, b, li)) if mode == 0 else None
+                    # SVDQuant: the branch's second half runs inside the GEMM where the
+                    # pipelined kernel takes the shape; the FFN's second projection needs
+                    # the bf16 hidden state for its own branch, so the first one keeps it
+                    lr_fused = lr is not None and mxq.gemm_lowrank_supported(m, lin.n, lin.k)
                     fused_up = lin.name == "ffn_up" and not tr and lr is None and (
                         (mode == 0 and mxq.gemm_mxfp4_out_supported(m, lin.n, lin.k))
                         or (static8 and mxq.gemm_fp8_static_out_supported(m, lin.n, lin.k)))
@@ -276,7 +283,16 @@ class Stack:
                             mxq.quantize_act(mode, x, codes, scales)
                     if timed:
                         e1.record()
-                    if fused_up and mode == 0:
+                    if lr is not None:
+                        t = self.t_buf[: m * self.lr_rank].view(m, self.lr_rank)
+                        mxq.lowrank_down(x, lr[0], t)
+                    if timed:
+                        e1b = torch.cuda.Event(enable_timing=True)
+                        e1b.record()
+                    if lr_fused:
+                        mxq.gemm_lowrank(codes, scales, wc, wsc, t, lr[1], None, lin.epilogue, y=out)
+                        out_bytes = m * lin.n * 2 + (m + lin.n) * self.lr_rank * 2
+                    elif fused_up and mode == 0:
                         oc, osc = self._act_views(mode, m, lin.n, self.codes_buf2)
                         mxq.gemm_mxfp4_out(codes, scales, wc, wsc, None, lin.epilogue, oc, osc)
                         out_bytes = m * lin.n // 2 + m * lin.n // 32
@@ -294,9 +310,7 @@ class Stack:
                         out_bytes = m * lin.n * 2
                     if timed:
                         e2.record()
-                    if lr is not None:
-                        t = self.t_buf[: m * self.lr_rank].view(m, self.lr_rank)
-                        mxq.lowrank_down(x, lr[0], t)
+                    if lr is not None and not lr_fused:
                         mxq.lowrank_up(out, t, lr[1], lin.epilogue, y=out)
                     self.down_ready = fused_up
                     if timed:
@@ -307,11 +321,16 @@ class Stack:
                             + lin.n * lin.k // 2 + lin.n * lin.k // 32 + out_bytes
                         if not fed and not shared:
                             self.records.append(("quant", mode, 0, qbytes, e0, e1))
-                        self.records.append(("gemm", mode, 2 * m * lin.n * lin.k, gbytes, e1, e2))
+                        # the GEMM's flops are those of the quantized product (the branch's
+                        # 2 m n r bf16 flops inside the fused kernel are not counted)
+                        self.records.append(("gemm", mode, 2 * m * lin.n * lin.k, gbytes, e1b, e2))
                         if lr is not None:
                             rr = self.lr_rank
-                            self.records.append(("lowrank", mode, 2 * m * rr * (lin.k + lin.n),
-                                                 m * lin.k * 2 + 2 * m * lin.n * 2, e2, e5))
+                            self.records.append(("lowrank_down", mode, 2 * m * rr * lin.k,
+                                                 m * lin.k * 2 + m * rr * 2, e1, e1b))
+                            if not lr_fused:
+                                self.records.append(("lowrank_up", mode, 2 * m * rr * lin.n,
+                                                     2 * m * lin.n * 2, e2, e5))
 
 
 # the pipelined GEMM's symbol per mode, as the profile summaries write it
@@ -396,7 +415,8 @@ def cpu_baseline(wl, sample_rows, static=False, transform=False, lr_rank=0):
                 l1t = synth.f32_to_bf16_bits((g.standard_normal((lr_rank, lin.k)) * 0.02).astype(np.float32))
                 l2 = synth.f32_to_bf16_bits((g.standard_normal((lin.n, lr_rank)) * 0.02).astype(np.float32))
                 ac, asc = oracle.mxfp4_quantize(xs)
-                y = oracle.svdquant_linear(md, ac, asc, wq, wsc, xs, l1t, l2, None, lin.epilogue)[0]
+                t = oracle.lowrank_down(xs, l1t)
+                y = oracle.svdquant_linear_fused(md, ac, asc, wq, wsc, t, l2, None, lin.epilogue)
             elif md == 1 and static:
                 ac, asc = oracle.fp8_quantize_static(xs, amax)
                 y = oracle.qdq_matmul(md, ac, asc, wq, wsc, None, lin.epilogue)
@@ -588,9 +608,6 @@ def main():
         if kind == "gemm":
             d["tflops"] = round(a["flops"] / (a["ms"] * 1e-3) / 1e12, 1)
             d["frac_of_peak"] = round(d["tflops"] / PEAK_TFLOPS[mode], 4)
-        elif kind == "lowrank":
-            d["gbs"] = round(a["bytes"] / (a["ms"] * 1e-3) / 1e9, 1)
-            d["frac_of_hbm"] = round(d["gbs"] / PEAK_HBM_GBS, 4)
         else:
             d["gbs"] = round(a["bytes"] / (a["ms"] * 1e-3) / 1e9, 1)
             d["frac_of_hbm"] = round(d["gbs"] / PEAK_HBM_GBS, 4)

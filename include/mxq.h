@@ -268,6 +268,33 @@ int mxq_lowrank_up(const void* y_pre, const void* t, const void* l2, int64_t M, 
                    int epilogue, void* y, hipStream_t stream);
 
 /*
+ * SVDQuant's branch inside the W4A4 GEMM (same sections): the second half of
+ * the branch joins the quantized product's fp32 sums, and the output is
+ * rounded once,
+ *   y [M][N] = RN_bf16(epilogue( sum_k deqA[m][k] deqR[n][k]
+ *                                + sum_j t[m][j] l2[n][j] + bias[n] )),
+ * with deqR the packed residual weight. Unlike mxq_gemm + mxq_lowrank_up it
+ * does not round the quantized product to bf16 before the branch is added,
+ * and it reads and writes the output once. Run mxq_lowrank_down first.
+ *   a_codes/a_scales  device, from mxq_quantize_act(MXQ_W4A4, ...)
+ *   w_codes/w_scales  device, the residual from mxq_quantize_weight_mxfp4
+ *   bias              device bf16 [N], or null for none
+ *   t                 device bf16 [M][r] (mxq_lowrank_down's output)
+ *   l2                device bf16 [N][r]
+ *   r                 32, 64, 96 or 128
+ *   y_scales null:    y is device bf16 [M][N] (output)
+ *   y_scales given:   y and y_scales are the MXFP4 activation of a next W4A4
+ *                     layer, as mxq_gemm_mxfp4_out writes them (its shapes:
+ *                     N a multiple of 128), of the bf16 values above
+ * Only for the shapes of the pipelined kernel (mxq_gemm_kernel_name(MXQ_W4A4,
+ * M, N, K) starts with "pipe_"): MXQ_ERR_SHAPE otherwise, and nothing is
+ * written (use mxq_gemm and mxq_lowrank_up). All pointers 16-byte aligned.
+ */
+int mxq_gemm_lowrank(const void* a_codes, const void* a_scales, const void* w_codes, const void* w_scales,
+                     const void* bias, const void* t, const void* l2, int64_t r, int epilogue, void* y,
+                     void* y_scales, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/*
  * Scaled GEMM on quantized operands (the native MXFP4 / W4A8 execution of
  * "Quantization formats", kernel note): y [M][N] bf16 =
  *   epilogue( sum_k deqA[m][k] deqW[n][k] + bias[n] ).

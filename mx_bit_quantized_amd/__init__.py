@@ -48,6 +48,8 @@ _SIGS = {
     "mxq_fp8_calibrate": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P]),
     "mxq_lowrank_down": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P]),
     "mxq_lowrank_up": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P, _P]),
+    "mxq_gemm_lowrank": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I64, ctypes.c_int, _P, _P, _I64, _I64, _I64,
+                                        _P]),
     "mxq_sqnr_accumulate": (ctypes.c_int, [_P, _P, _I64, _P, _P]),
     "mxq_replay_workspace_bytes": (ctypes.c_int, [_P, _I32, ctypes.POINTER(ctypes.c_size_t)]),
     "mxq_block_replay_sqnr": (ctypes.c_int, [_P, _I32, _P, ctypes.c_size_t, _P, _P, _P]),
@@ -506,6 +508,39 @@ def lowrank_down(x, l1t, t=None, stream=None):
                                  _dev_ptr(t, "t", torch.bfloat16), _stream_handle(stream))
     _check(st, "lowrank_down")
     return t
+
+
+def gemm_lowrank(a_codes, a_scales, w_codes, w_scales, t, l2, bias=None, epilogue=EPI_NONE, y=None, y_scales=None,
+                 mxfp4_out=False, stream=None):
+    """W4A4 GEMM with SVDQuant's branch t @ l2^T in its fp32 sums, rounded to bf16 once.
+
+    bf16 output y [M, N] by default; with ``mxfp4_out`` (or y_scales given) the output is the
+    next W4A4 layer's activation, (y_codes, y_scales), as gemm_mxfp4_out writes it."""
+    torch = _torch()
+    m = int(a_codes.shape[0])
+    n = int(w_codes.shape[0])
+    k = int(w_codes.shape[1]) * 2
+    r = int(t.shape[1])
+    if tuple(t.shape) != (m, r) or tuple(l2.shape) != (n, r):
+        raise ValueError(f"t must be [{m}, r] and l2 [{n}, r]; got {tuple(t.shape)} and {tuple(l2.shape)}")
+    mxfp4_out = mxfp4_out or y_scales is not None
+    if mxfp4_out and (y is None or y_scales is None):
+        y, y_scales = act_buffers(W4A4, m, n, w_codes.device)
+    elif y is None:
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=w_codes.device)
+    st = lib().mxq_gemm_lowrank(_dev_ptr(a_codes, "a_codes"), _dev_ptr(a_scales, "a_scales"),
+                                 _dev_ptr(w_codes, "w_codes", torch.uint8), _dev_ptr(w_scales, "w_scales", torch.uint8),
+                                 _dev_ptr(bias, "bias", torch.bfloat16), _dev_ptr(t, "t", torch.bfloat16),
+                                 _dev_ptr(l2, "l2", torch.bfloat16), r, int(epilogue),
+                                 _dev_ptr(y, "y", torch.uint8 if mxfp4_out else torch.bfloat16),
+                                 _dev_ptr(y_scales, "y_scales", torch.uint8), m, n, k, _stream_handle(stream))
+    _check(st, "gemm_lowrank")
+    return (y, y_scales) if mxfp4_out else y
+
+
+def gemm_lowrank_supported(M, N, K, mxfp4_out=False):
+    """Whether gemm_lowrank takes (M, N, K): the pipelined kernel's shapes (N % 128 == 0 for MXFP4 output)."""
+    return gemm_kernel_name(W4A4, M, N, K).startswith("pipe_") and (not mxfp4_out or N % 128 == 0)
 
 
 def lowrank_up(y_pre, t, l2, epilogue=EPI_NONE, y=None, stream=None):

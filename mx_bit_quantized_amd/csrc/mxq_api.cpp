@@ -204,6 +204,29 @@ int mxq_lowrank_up(const void* y_pre, const void* t, const void* l2, int64_t M, 
   return hip_status(mxq::launch_lowrank_up(y_pre, t, l2, M, N, r, epilogue, y, stream));
 }
 
+int mxq_gemm_lowrank(const void* a_codes, const void* a_scales, const void* w_codes, const void* w_scales,
+                     const void* bias, const void* t, const void* l2, int64_t r, int epilogue, void* y,
+                     void* y_scales, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  if (epilogue != MXQ_EPI_NONE && epilogue != MXQ_EPI_GELU_TANH) return MXQ_ERR_MODE;
+  int st = check_mk(M, K, K);
+  if (st != MXQ_OK) return st;
+  if (N < 0 || N >= kMaxDim || !lowrank_rank_ok(r)) return MXQ_ERR_SHAPE;
+  if (M == 0 || N == 0) return MXQ_OK;
+  if (!mxq::gemm_lowrank_supported(M, N, K, y_scales != nullptr)) return MXQ_ERR_SHAPE;
+  if (a_codes == nullptr || a_scales == nullptr || w_codes == nullptr || w_scales == nullptr || t == nullptr ||
+      l2 == nullptr || y == nullptr)
+    return MXQ_ERR_NULL;
+  if (!aligned16(a_codes) || !aligned16(a_scales) || !aligned16(w_codes) || !aligned16(w_scales) ||
+      !aligned16(t) || !aligned16(l2) || !aligned16(y) || (y_scales != nullptr && !aligned16(y_scales)) ||
+      (bias != nullptr && !aligned16(bias)))
+    return MXQ_ERR_ALIGN;
+  if (log_enabled())
+    fprintf(stderr, "[mxq] gemm w4a4 + rank-%lld branch%s M=%lld N=%lld K=%lld epi=%d\n", (long long)r,
+            y_scales != nullptr ? " -> mxfp4" : "", (long long)M, (long long)N, (long long)K, epilogue);
+  return hip_status(mxq::launch_gemm_lowrank(a_codes, a_scales, w_codes, w_scales, bias, t, l2, r, epilogue, y,
+                                             y_scales, M, N, K, stream));
+}
+
 int mxq_sqnr_accumulate(const void* y, const void* y_ref, int64_t n, double* sums, hipStream_t stream) {
   if (n < 0) return MXQ_ERR_SHAPE;
   if (n == 0) return MXQ_OK;

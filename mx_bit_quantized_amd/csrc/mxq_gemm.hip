@@ -385,6 +385,7 @@ struct StageScales {
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t v2u __attribute__((ext_vector_type(2)));
 
 // Static FP8 output (W4A8 GEMM writing the next W4A8 layer's activations):
@@ -460,13 +461,26 @@ __device__ __forceinline__ void buf_store16(const i32x4& rs, uint32_t voff, cons
 //         bytes) and group-major scales [N/128][M][4] (y_scales); N % 128 == 0.
 //   W4A8: static FP8 with the scale out_amax / 448: codes [M][N] (y) and the
 //         scale in every row of y_scales (float [M]).
-template <int MODE, int KT, int NB, bool GELU, bool BIAS, bool QOUT>
+//
+// LRB (W4A4 only): SVDQuant's low-rank branch joins the sums. After a tile's
+// K/128 code stages come r/32 more stages, one 32-wide rank panel each, with
+// L2 [N][r] in the W role and T [M][r] in the X role: a 32-element bf16 panel
+// row is 64 bytes, the size of a 128-element MXFP4 panel row, so the copies,
+// the LDS layout and the fragment reads are those of a code stage, and only
+// the MFMA changes (v_mfma_f32_32x32x16_bf16 into the same accumulators; its
+// lane g supplies elements 8 g .. 8 g + 7 of a 16-element step, so the two
+// steps of the stage read chunks {0, 2} and {1, 3} of the row, as both
+// operands do). The stage's scale copies go out of range: they write zeros
+// and read nothing, and keep the copy count of every stage the same.
+template <int MODE, int KT, int NB, bool GELU, bool BIAS, bool QOUT, bool LRB>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_pipe_kernel(
     const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws,
     const uint8_t* __restrict__ aq, const void* __restrict__ asc,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, uint8_t* __restrict__ y_scales,
-    const float* __restrict__ out_amax, int M, int N, int K, int tiles_m, int tiles_n) {
+    const float* __restrict__ out_amax, int M, int N, int K, int tiles_m, int tiles_n,
+    const uint16_t* __restrict__ lr_t, const uint16_t* __restrict__ lr_l2, int lr_rank) {
   using C = PipeCfg<MODE, KT, NB>;
+  static_assert(!LRB || (MODE == 0 && KT == 128), "the branch stages take the shape of a W4A4 code stage");
   // ring of NB stage slots, then two tile-parameter blocks: bias slice (512
   // bytes), a sink for the unused waves' copies (512), token scales (1024, FP8)
   constexpr int P_BIAS = 0, P_SINK = 512, P_TOK = 1024;
@@ -489,7 +503,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int KB = K >> 5;
   const uint32_t w_row = (uint32_t)K >> 1;
   const uint32_t x_row = MODE == 0 ? ((uint32_t)K >> 1) : (uint32_t)K;
-  const int n_stages = K / KT;
+  const int nq = K / KT;                                   // code stages of a tile
+  const int n_stages = nq + (LRB ? (lr_rank >> 5) : 0);   // + the branch's rank panels
 
   // This workgroup's tiles: first, first + stride, ... (count of them).
   const int total = tiles_m * tiles_n;
@@ -509,7 +524,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
   first = __builtin_amdgcn_readfirstlane(first);
   count = __builtin_amdgcn_readfirstlane(count);
-  const int total_stages = count * n_stages;
 
   // MXFP4 codes are K-panel-major with 128-element panels, one panel per
   // stage: stage s of a tile is the tile's 256 consecutive rows of panel s, one
@@ -531,6 +545,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     unswz<C::X_RB>((wave * C::X_INSTR + q) * 64 + lane, row, c);
     vx[q] = (uint32_t)row * (MODE == 0 ? (uint32_t)C::X_RB : x_row) + (uint32_t)c * 16;
   }
+  // branch stages: rank panel p of row `row` is at byte row * 2 r + 64 p
+  const uint32_t lr_pitch = LRB ? (uint32_t)lr_rank * 2u : 0u;
+  uint32_t vwl[LRB ? C::W_INSTR : 1], vxl[LRB ? C::X_INSTR : 1];
+  if constexpr (LRB) {
+#pragma unroll
+    for (int q = 0; q < C::W_INSTR; ++q) vwl[q] = vw[q] / C::W_RB * lr_pitch + vw[q] % C::W_RB;
+#pragma unroll
+    for (int q = 0; q < C::X_INSTR; ++q) vxl[q] = vx[q] / C::X_RB * lr_pitch + vx[q] % C::X_RB;
+  }
   const uint32_t w_panel = (uint32_t)N * C::W_RB;  // bytes of one code panel
   const uint32_t x_stage = MODE == 0 ? (uint32_t)M * C::X_RB : (uint32_t)C::X_RB;
   // Scales (group-major, 128-element groups): the tile's 256 dwords of group
@@ -547,6 +570,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const i32x4 rx = make_rsrc(aq, x_row * (uint32_t)M);
   const i32x4 rws = make_rsrc(ws, (uint32_t)KB * (uint32_t)N);
   const i32x4 rxs = make_rsrc(asc, MODE == 0 ? (uint32_t)KB * (uint32_t)M : 0u);
+  const i32x4 rl2 = make_rsrc(lr_l2, lr_pitch * (uint32_t)N);
+  const i32x4 rlt = make_rsrc(lr_t, lr_pitch * (uint32_t)M);
 
   // ---- copy cursor: the stage (tile cp_k, stage cp_s) whose copies come
   // next, with the byte offsets of its tile in the W, X and scale operands.
@@ -577,19 +602,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const bool live = cp_k < count;
     constexpr uint32_t oob = 0x80000000u;
     const uint32_t base = lds_ring + (uint32_t)slot * C::STAGE;
+    // a branch stage (LRB): its rank panel, and its source rows 2 r bytes apart
+    const bool br = LRB && cp_s >= nq;
+    const uint32_t lr_off = LRB ? (uint32_t)(cp_s - nq) * 64u : 0u;
     if (q < C::W_INSTR) {
       const uint32_t so = live ? cp_nb * (uint32_t)C::W_RB + (uint32_t)cp_s * w_panel : oob;
-      lds_dma16(rw, base + C::W_OFF + (wave * C::W_INSTR + q) * 1024, vw[q] + so);
+      if constexpr (LRB) {
+        const uint32_t sl = live ? cp_nb * lr_pitch + lr_off : oob;
+        lds_dma16(br ? rl2 : rw, base + C::W_OFF + (wave * C::W_INSTR + q) * 1024, br ? vwl[q] + sl : vw[q] + so);
+      } else {
+        lds_dma16(rw, base + C::W_OFF + (wave * C::W_INSTR + q) * 1024, vw[q] + so);
+      }
     } else if (q < C::W_INSTR + C::X_INSTR) {
       const int qx = q - C::W_INSTR;
       const uint32_t so =
           live ? cp_mb * (MODE == 0 ? (uint32_t)C::X_RB : x_row) + (uint32_t)cp_s * x_stage : oob;
-      lds_dma16(rx, base + C::X_OFF + (wave * C::X_INSTR + qx) * 1024, vx[qx] + so);
+      if constexpr (LRB) {
+        const uint32_t sl = live ? cp_mb * lr_pitch + lr_off : oob;
+        lds_dma16(br ? rlt : rx, base + C::X_OFF + (wave * C::X_INSTR + qx) * 1024, br ? vxl[qx] + sl : vx[qx] + so);
+      } else {
+        lds_dma16(rx, base + C::X_OFF + (wave * C::X_INSTR + qx) * 1024, vx[qx] + so);
+      }
     } else if (q == C::W_INSTR + C::X_INSTR) {
-      const uint32_t so = live ? cp_nb * 4u + (uint32_t)(cp_s * KT / 128) * ws_group : oob;
+      const uint32_t so = live && !br ? cp_nb * 4u + (uint32_t)(cp_s * KT / 128) * ws_group : oob;
       lds_dma4(rws, base + C::WS_OFF + wave * 256, vs + so);
     } else {
-      const uint32_t so = live ? cp_mb * 4u + (uint32_t)(cp_s * KT / 128) * xs_group : oob;
+      const uint32_t so = live && !br ? cp_mb * 4u + (uint32_t)(cp_s * KT / 128) * xs_group : oob;
       lds_dma4(rxs, base + C::XS_OFF + wave * 256, vs + so);
     }
   };
@@ -733,6 +771,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   };
   auto mfma_step = [&](const StepData<MODE>& f, const StageScales& sc, auto kk_tag, auto&& between) {
     mfma_step_x(f, sc, kk_tag, std::false_type{}, std::false_type{}, std::false_type{}, [](int) {}, between);
+  };
+  // the 16 MFMAs of one step of a branch stage: bf16 operands, no scales
+  auto mfma_step_bf = [&](const StepData<MODE>& f, auto&& between) {
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+      const int i = s >> 2, j = s & 3;
+      if constexpr (MODE == 0)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f.a[i]),
+                                                            __builtin_bit_cast(bf16x8, f.b[j]), acc[i][j], 0, 0, 0);
+      between(s);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   // ---- epilogue of one tile, staged through the slot of its last stage.
@@ -949,8 +999,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     static_assert(kLastCopySlot > 16, "epilogue stores end in slot 16");
 
     int slot = 0;  // ring slot of the stage being computed
-    auto run_stage = [&](int tile_k, int s_in, auto first_tag) {
+    auto run_stage = [&](int tile_k, int s_in, auto first_tag, auto br_tag) {
       constexpr bool FIRST = decltype(first_tag)::value;
+      constexpr bool BR = decltype(br_tag)::value;
       if (tile_k > 0 || s_in > 0) {
         // the stage after the first one may leave all of the first stage's
         // operations outstanding; the one after that, those issued after its
@@ -977,7 +1028,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         read_item(next, 0, next_half, kStageOrder[MODE][k], cur, cur_sc);
         if (kCopyAt[16 + k] >= 0) issue_one(kCopyAt[16 + k], slot_refill);
       };
-      if constexpr (!FIRST) {
+      if constexpr (!FIRST && BR) {
+        mfma_step_bf(cur, between0);
+        mfma_step_bf(nxt, between1);
+      } else if constexpr (!FIRST) {
         mfma_step(cur, cur_sc, std::integral_constant<int, 0>{}, between0);
         const StageScales sc1 = cur_sc;
         mfma_step(nxt, sc1, std::integral_constant<int, 1>{}, between1);
@@ -1147,9 +1201,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // at the end of an iteration, so no path leaves between a first stage's
     // MFMAs and the stages that use their sums
     for (int tile_k = 0; tile_k <= count; ++tile_k) {
-      run_stage(tile_k, 0, std::true_type{});
+      run_stage(tile_k, 0, std::true_type{}, std::false_type{});
       const int s_end = tile_k < count ? n_stages : 1;
-      for (int s_in = 1; s_in < s_end; ++s_in) run_stage(tile_k, s_in, std::false_type{});
+      if constexpr (LRB) {
+        // the code stages, then the branch stages (the last of the tile)
+        const int q_end = tile_k < count ? nq : 1;
+        for (int s_in = 1; s_in < q_end; ++s_in) run_stage(tile_k, s_in, std::false_type{}, std::false_type{});
+        for (int s_in = q_end; s_in < s_end; ++s_in) run_stage(tile_k, s_in, std::false_type{}, std::true_type{});
+      } else {
+        for (int s_in = 1; s_in < s_end; ++s_in) run_stage(tile_k, s_in, std::false_type{}, std::false_type{});
+      }
     }
   } else {
   int slot = 0;          // ring slot of the stage being computed
@@ -1215,10 +1276,11 @@ static int device_cu_count() {
   return cus;
 }
 
-template <int MODE, int KT, int NB, bool QOUT = false>
+template <int MODE, int KT, int NB, bool QOUT = false, bool LRB = false>
 static hipError_t launch_pipe(const void* aq, const void* as, const void* wq, const void* ws, const void* bias,
                               int epi, void* y, int64_t M, int64_t N, int64_t K, hipStream_t s,
-                              void* y_scales = nullptr, const float* out_amax = nullptr) {
+                              void* y_scales = nullptr, const float* out_amax = nullptr,
+                              const void* lr_t = nullptr, const void* lr_l2 = nullptr, int lr_rank = 0) {
   static const int cus = device_cu_count();
   const int tiles_m = (int)((M + 255) / 256);
   const int tiles_n = (int)((N + 255) / 256);
@@ -1227,11 +1289,12 @@ static hipError_t launch_pipe(const void* aq, const void* as, const void* wq, co
   // GELU and bias are kernel parameters, so that each kernel carries only
   // the epilogue work it does
   auto go = [&](auto gelu_tag, auto bias_tag) {
-    hipLaunchKernelGGL((gemm_pipe_kernel<MODE, KT, NB, decltype(gelu_tag)::value, decltype(bias_tag)::value, QOUT>),
-                       dim3(grid), dim3(256), 0, s, static_cast<const uint8_t*>(wq),
-                       static_cast<const uint8_t*>(ws), static_cast<const uint8_t*>(aq), as,
-                       static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y),
-                       static_cast<uint8_t*>(y_scales), out_amax, (int)M, (int)N, (int)K, tiles_m, tiles_n);
+    hipLaunchKernelGGL(
+        (gemm_pipe_kernel<MODE, KT, NB, decltype(gelu_tag)::value, decltype(bias_tag)::value, QOUT, LRB>),
+        dim3(grid), dim3(256), 0, s, static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws),
+        static_cast<const uint8_t*>(aq), as, static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y),
+        static_cast<uint8_t*>(y_scales), out_amax, (int)M, (int)N, (int)K, tiles_m, tiles_n,
+        static_cast<const uint16_t*>(lr_t), static_cast<const uint16_t*>(lr_l2), lr_rank);
   };
   if (epi == 1) {
     if (bias != nullptr) go(std::true_type{}, std::true_type{});
@@ -1304,6 +1367,23 @@ hipError_t launch_gemm_fp8_static_out(const void* a_codes, const void* a_scales,
                                       hipStream_t s) {
   return launch_pipe<1, kPipeKT[1], kPipeNB[1], true>(a_codes, a_scales, w_codes, w_scales, bias, epilogue, y_codes,
                                                       M, N, K, s, y_scales, out_amax);
+}
+
+// The branch rides on the pipelined W4A4 kernel (its shapes only); with
+// y_scales the output is MXFP4 as for launch_gemm_mxfp4_out (N % 128 == 0).
+bool gemm_lowrank_supported(int64_t M, int64_t N, int64_t K, bool mxfp4_out) {
+  return use_lds(0, M, N, K) && (!mxfp4_out || N % 128 == 0);
+}
+
+hipError_t launch_gemm_lowrank(const void* a_codes, const void* a_scales, const void* w_codes,
+                               const void* w_scales, const void* bias, const void* t, const void* l2, int64_t r,
+                               int epilogue, void* y, void* y_scales, int64_t M, int64_t N, int64_t K,
+                               hipStream_t s) {
+  if (y_scales != nullptr)
+    return launch_pipe<0, kPipeKT[0], kPipeNB[0], true, true>(a_codes, a_scales, w_codes, w_scales, bias, epilogue,
+                                                              y, M, N, K, s, y_scales, nullptr, t, l2, (int)r);
+  return launch_pipe<0, kPipeKT[0], kPipeNB[0], false, true>(a_codes, a_scales, w_codes, w_scales, bias, epilogue, y,
+                                                             M, N, K, s, nullptr, nullptr, t, l2, (int)r);
 }
 
 const char* gemm_variant_name(int mode, int64_t M, int64_t N, int64_t K) {

@@ -66,6 +66,15 @@ hipError_t launch_gemm_fp8_static_out(const void* a_codes, const void* a_scales,
                                       void* y_codes, void* y_scales, int64_t M, int64_t N, int64_t K,
                                       hipStream_t s);
 
+// W4A4 GEMM with SVDQuant's branch t [M][r] l2[N][r]^T in its fp32 sums,
+// bf16 output (y_scales null) or MXFP4 output as launch_gemm_mxfp4_out; only
+// where gemm_lowrank_supported holds.
+bool gemm_lowrank_supported(int64_t M, int64_t N, int64_t K, bool mxfp4_out);
+hipError_t launch_gemm_lowrank(const void* a_codes, const void* a_scales, const void* w_codes,
+                               const void* w_scales, const void* bias, const void* t, const void* l2, int64_t r,
+                               int epilogue, void* y, void* y_scales, int64_t M, int64_t N, int64_t K,
+                               hipStream_t s);
+
 // Name of the GEMM kernel variant launch_gemm picks for a shape (for logs).
 const char* gemm_variant_name(int mode, int64_t M, int64_t N, int64_t K);
 

@@ -25,7 +25,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = mxq.lib()
     names = declared_functions()
-    assert len(names) == 25, names
+    assert len(names) == 26, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(mxq._SIGS)
@@ -274,6 +274,38 @@ def test_lowrank_validation():
         assert L.mxq_lowrank_up(*args) == mxq.ERR_ALIGN, pos
     assert L.mxq_lowrank_down(None, 0, 256, None, 32, None, S) == mxq.OK
     assert L.mxq_lowrank_up(None, None, None, 0, 256, 32, 0, None, S) == mxq.OK
+
+
+def test_gemm_lowrank_validation():
+    """Host-side checks of the GEMM with the branch in its sums; every case is refused before any
+    launch (the valid argument list itself is never passed)."""
+    L = mxq.lib()
+    S = None
+    # a0 as1 w2 ws3 bias4 t5 l2_6 r7 epi8 y9 ys10 M11 N12 K13 stream
+    ok = [FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, 32, 0, FAKE, None, 512, 1024, 1024, S]
+
+    def call(**chg):
+        args = list(ok)
+        for pos, v in chg.items():
+            args[int(pos[1:])] = v
+        return L.mxq_gemm_lowrank(*args)
+
+    assert call(p8=2) == mxq.ERR_MODE
+    for r in (0, 16, 48, 160, -32):
+        assert call(p7=r) == mxq.ERR_SHAPE, r
+    assert call(p13=100) == mxq.ERR_SHAPE
+    # shapes the pipelined kernel does not take; N % 128 for the MXFP4 output
+    for m, n, k in [(255, 1024, 1024), (512, 1024, 384), (512, 1004, 1024)]:
+        assert call(p11=m, p12=n, p13=k) == mxq.ERR_SHAPE, (m, n, k)
+        assert call(p11=m, p12=n, p13=k, p10=FAKE) == mxq.ERR_SHAPE, (m, n, k)
+    assert call(p12=1088, p10=FAKE) == mxq.ERR_SHAPE
+    for pos in (0, 1, 2, 3, 5, 6, 9):
+        assert call(**{f"p{pos}": None}) == mxq.ERR_NULL, pos
+        assert call(**{f"p{pos}": None, "p10": FAKE}) == mxq.ERR_NULL, pos
+    for pos in (0, 1, 2, 3, 4, 5, 6, 9):
+        assert call(**{f"p{pos}": FAKE_ODD}) == mxq.ERR_ALIGN, pos
+    assert call(p10=FAKE_ODD) == mxq.ERR_ALIGN
+    assert call(p11=0, p0=None, p5=None, p9=None) == mxq.OK
 
 
 def test_static_fp8_validation():

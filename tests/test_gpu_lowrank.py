@@ -15,7 +15,7 @@ import torch
 import mx_bit_quantized_amd as mxq
 import oracle
 import synth
-from gpu_util import assert_output_close, dev_bf16, host_bits, sample_rows
+from gpu_util import assert_output_close, code_rows, dev_bf16, host_bits, host_u8, sample_rows
 
 pytestmark = pytest.mark.gpu
 
@@ -157,3 +157,129 @@ def test_svdquant_a14b_ffn_up_full_size():
     y_got = host_bits(y.index_select(0, _idx(rows)).index_select(1, _idx(cols)))
     rep = assert_output_close(y_got, oracle.bf16_bits_to_f64(y_ref), what)
     say(f"{what}: worst/bound {rep['worst_ratio']:.3f}")
+
+
+# ---- the branch inside the W4A4 GEMM (mxq_gemm_lowrank) ----------------------
+# N = 640 / 1288: last 256-column tile partly outside N (1288 is no multiple of
+# 128 or 256); M = 300 / 513 / 2250: ragged last row tile; 2250 x 7424: more
+# tiles than CUs; K = 512: the fewest code stages the W4A4 ring takes (4).
+FUSED_LR_CASES = [(256, 256, 512, 32, 0, False), (300, 640, 640, 64, 1, True), (600, 1288, 896, 96, 1, False),
+                  (513, 512, 512, 128, 0, True), (2250, 7424, 512, 32, 1, False)]
+
+
+def _fused_operands(m, n, k, r, seed, bias):
+    g = np.random.default_rng(seed)
+    x = synth.activation_bf16(seed, m, k, ("student_t",))
+    res = synth.weight_bf16(seed + 1, n, k)
+    l1t = _bits(g.standard_normal((r, k)) * 0.02)
+    l2 = _bits(g.standard_normal((n, r)) * 0.05)
+    b = _bits(g.standard_normal(n) * 0.1) if bias else None
+    return x, res, l1t, l2, b
+
+
+def _fused_gpu(x, res, l1t, l2, b, epi, mxfp4_out=False):
+    xd = dev_bf16(x)
+    rc, rs = mxq.quantize_weight_mxfp4(dev_bf16(res))
+    ac, asc = mxq.quantize_act(mxq.W4A4, xd)
+    t = mxq.lowrank_down(xd, dev_bf16(l1t))
+    bd = dev_bf16(b) if b is not None else None
+    y = mxq.gemm_lowrank(ac, asc, rc, rs, t, dev_bf16(l2), bd, epi, mxfp4_out=mxfp4_out)
+    torch.cuda.synchronize()
+    return y
+
+
+def _fused_oracle(x, res, l1t, l2, b, epi):
+    orc, ors = oracle.mxfp4_quantize(res)
+    oac, oas = oracle.mxfp4_quantize(x)
+    t = oracle.lowrank_down(x, l1t)
+    b64 = oracle.bf16_bits_to_f64(b) if b is not None else None
+    return oracle.svdquant_linear_fused(oracle.W4A4, oac, oas, orc, ors, t, l2, b64, epi)
+
+
+@pytest.mark.parametrize("m,n,k,r,epi,bias", FUSED_LR_CASES)
+def test_gemm_lowrank_vs_oracle(m, n, k, r, epi, bias):
+    what = f"gemm+branch [{m}x{n}x{k}] r={r} epi={epi} bias={bias}"
+    say(what)
+    assert mxq.gemm_lowrank_supported(m, n, k)
+    ops = _fused_operands(m, n, k, r, 1000 + m + n + r, bias)
+    y = _fused_gpu(*ops, epi)
+    rep = assert_output_close(host_bits(y), _fused_oracle(*ops, epi), what)
+    say(f"{what}: worst/bound {rep['worst_ratio']:.3f}")
+
+
+@pytest.mark.parametrize("m,n,k,r", [(256, 512, 512, 64), (300, 264, 640, 32), (520, 1032, 512, 128)])
+def test_gemm_lowrank_exact_sums(m, n, k, r):
+    """Operands whose every sum is exact in fp32 (MXFP4-exact activations and residual, small
+    integer branch factors): the GPU's bf16 output equals the oracle's rounding bit for bit, so a
+    misplaced branch element, rank panel or row shows up as a wrong bit."""
+    say("gemm+branch exact", m, n, k, r)
+    g = np.random.default_rng(m + n + r)
+    x = _bits(g.choice([-2.0, -1.0, -0.5, 0.0, 0.5, 1.0, 2.0, 3.0], (m, k)))
+    res = _bits(g.choice([-1.5, -0.5, 0.0, 0.5, 1.0, 2.0], (n, k)))
+    l1t = _bits(g.integers(-1, 2, (r, k)) * (g.random((r, k)) < 0.05))
+    l2 = _bits(g.integers(-2, 3, (n, r)))
+    b = _bits(g.integers(-8, 9, n))
+    for epi in (mxq.EPI_NONE,):
+        y = _fused_gpu(x, res, l1t, l2, b, epi)
+        want = oracle.f64_to_bf16_bits(_fused_oracle(x, res, l1t, l2, b, epi))
+        got = host_bits(y)
+        bad = np.argwhere(got != want)
+        assert bad.size == 0, f"{len(bad)} outputs differ, first {bad[:5].tolist()}"
+
+
+@pytest.mark.parametrize("m,n,k,r,epi,bias", [(300, 640, 640, 64, 1, True), (2250, 7424, 512, 32, 1, False),
+                                              (256, 512, 512, 128, 0, False)])
+def test_gemm_lowrank_mxfp4_out(m, n, k, r, epi, bias):
+    """MXFP4 output: byte for byte the library's quantizer applied to the bf16 output of the same
+    call, and the oracle's codes wherever the bf16 values agree with the oracle's on a whole block."""
+    say("gemm+branch -> mxfp4", m, n, k, r, epi, bias)
+    ops = _fused_operands(m, n, k, r, 2000 + m + r, bias)
+    y = _fused_gpu(*ops, epi)
+    fc, fs = _fused_gpu(*ops, epi, mxfp4_out=True)
+    rc, rs = mxq.quantize_act(mxq.W4A4, y)
+    torch.cuda.synchronize()
+    assert torch.equal(fc, rc) and torch.equal(fs, rs)
+    h_ref = oracle.f64_to_bf16_bits(_fused_oracle(*ops, epi))
+    want_c, want_s = oracle.quantize_act(mxq.W4A4, h_ref)
+    got_c = code_rows(fc, m, n, 4)
+    got_s = host_u8(fs).transpose(1, 0, 2).reshape(m, -1)[:, : n // 32]
+    agree = (host_bits(y) == h_ref).reshape(m, n // 32, 32).all(axis=2)
+    assert agree.mean() > 0.9, f"only {agree.mean():.3f} of the blocks agree in bf16"
+    ok = (got_c.reshape(m, n // 32, 16) == want_c.reshape(m, n // 32, 16)).all(axis=2) & (got_s == want_s)
+    bad = np.argwhere(agree & ~ok)
+    assert bad.size == 0, f"{len(bad)} blocks differ from the oracle, first {bad[:5].tolist()}"
+
+
+def test_gemm_lowrank_a14b_ffn_up_full_size():
+    """A14B FFN first projection at 720p (75600 x 13824 x 5120, GELU) with the rank-32 branch in
+    the GEMM: sampled rows and columns against the oracle; the MXFP4 output against the library's
+    quantizer on the bf16 output, whole buffers."""
+    wl = synth.workload(5)
+    up = next(l for l in wl.linears if l.name == "ffn_up")
+    m, n, k, r = wl.m_video, up.n, up.k, 32
+    what = f"gemm+branch a14b ffn up [{m}x{n}x{k}] r={r}"
+    say(what)
+    g = np.random.default_rng(56)
+    x = synth.activation_bf16(5, m, k, wl.outliers, tensor_id=synth.T_X_VIDEO)
+    res = synth.weight_bf16(5, n, k, 0, 0, 8)
+    l1t = _bits(g.standard_normal((r, k)) * 0.02)
+    l2 = _bits(g.standard_normal((n, r)) * 0.02)
+    xd = dev_bf16(x)
+    rc, rs = mxq.quantize_weight_mxfp4(dev_bf16(res))
+    ac, asc = mxq.quantize_act(mxq.W4A4, xd)
+    t = mxq.lowrank_down(xd, dev_bf16(l1t))
+    del xd
+    l2d = dev_bf16(l2)
+    y = mxq.gemm_lowrank(ac, asc, rc, rs, t, l2d, None, up.epilogue)
+    torch.cuda.synchronize()
+    rows = sample_rows(m, 16, 63)
+    cols = sample_rows(n, 256, 64)
+    y_got = host_bits(y.index_select(0, _idx(rows)).index_select(1, _idx(cols)))
+    y_ref = _fused_oracle(x[rows], res[cols], l1t, l2[cols], None, up.epilogue)
+    rep = assert_output_close(y_got, y_ref, what)
+    say(f"{what}: worst/bound {rep['worst_ratio']:.3f}")
+    qc, qs = mxq.quantize_act(mxq.W4A4, y)
+    del y
+    fc, fs = mxq.gemm_lowrank(ac, asc, rc, rs, t, l2d, None, up.epilogue, mxfp4_out=True)
+    torch.cuda.synchronize()
+    assert torch.equal(fc, qc) and torch.equal(fs, qs)
