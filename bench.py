@@ -10,6 +10,7 @@ quantization of it. Weight packing is offline and is timed separately
 
     python bench.py [--steps K] [--warmup W] [--workload a14b_stack|a14b_ffn|qkv|ti2v|tiny]
                     [--act-scale per_token|static] [--transform-on] [--svdquant-rank R] [--select]
+                    [--token-shards S]
 
 --act-scale static runs the W4A8 linears on static (per-tensor) FP8
 activations: each input's amax is calibrated once, untimed, on the same
@@ -33,8 +34,13 @@ decompose); the branch's cost does not depend on their values.
 --select replaces the step by the calibration-driven block selection over the
 A14B model (see run_select).
 
+--token-shards S times one GPU's share of the workload split S ways along the
+video tokens (ceil(M / S) rows; text rows and all weights whole on every GPU),
+the exchange-free split of this path. The line reports that one GPU's rate.
+
 Prints one JSON line. Per-launch kernel durations come from HIP events
-recorded on the launch stream around every kernel inside the timed steps.
+recorded on the launch stream around every kernel of the last timed step (the
+other timed steps run without them: the events cost 1.4% of a full-size step).
 """
 
 import argparse
@@ -71,6 +77,9 @@ def parse():
     ap.add_argument("--select", action="store_true",
                     help="instead of the step: calibration-driven block selection over the A14B model (one 480p "
                          "calibration sample), timing the library's block replay")
+    ap.add_argument("--token-shards", type=int, default=1,
+                    help="time one GPU's share of the workload split over this many GPUs along the video tokens "
+                         "(M / S rows each; text rows and weights whole on every GPU)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-rows", type=int, default=512)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -572,6 +581,11 @@ def main():
         run_select(args, torch, mxq)
         return
     wl = synth.workload(WORKLOADS[args.workload])
+    shards = max(1, args.token_shards)
+    if shards > 1:
+        # token sharding needs no exchange: MX blocks and per-token scales are row-local
+        import dataclasses
+        wl = dataclasses.replace(wl, name=f"{wl.name}_tokenshard{shards}", m_video=-(-wl.m_video // shards))
     static = args.act_scale == "static"
     transform = args.transform_on
     if transform and args.svdquant_rank:
@@ -583,8 +597,10 @@ def main():
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
-    for _ in range(args.steps):
-        stack.step(timed=True)
+    # per-kernel events on the last timed step only: recording them around every
+    # launch slows a step by 1.4% at full size (11% at an 8-way token shard)
+    for i in range(args.steps):
+        stack.step(timed=i == args.steps - 1)
     end.record()
     torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
@@ -603,8 +619,8 @@ def main():
     kernels = {}
     for (kind, mode), a in agg.items():
         name = f"{kind}_{'w4a4' if mode == 0 else 'w4a8'}"
-        d = {"launches_per_step": a["launches"] // args.steps, "avg_us": round(1e3 * a["ms"] / a["launches"], 2),
-             "share_of_step": round(a["ms"] / total_ms, 4)}
+        d = {"launches_per_step": a["launches"], "avg_us": round(1e3 * a["ms"] / a["launches"], 2),
+             "share_of_step": round(a["ms"] / ms_per_step, 4)}
         if kind == "gemm":
             d["tflops"] = round(a["flops"] / (a["ms"] * 1e-3) / 1e12, 1)
             d["frac_of_peak"] = round(d["tflops"] / PEAK_TFLOPS[mode], 4)
@@ -616,7 +632,8 @@ def main():
     a = agg[dom]
     achieved = a["flops"] / (a["ms"] * 1e-3) / 1e12
     tag = [k for k, v in WORKLOADS.items() if v == wl.config_id][0] + ("_static" if static else "") + \
-        ("_transform" if transform else "") + (f"_svdquant{args.svdquant_rank}" if args.svdquant_rank else "")
+        ("_transform" if transform else "") + (f"_svdquant{args.svdquant_rank}" if args.svdquant_rank else "") + \
+        (f"_tokenshard{shards}" if shards > 1 else "")
     roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_TFLOPS[dom[1]], "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_TFLOPS[dom[1]], 4),
                 "traffic": profiled_traffic(tag, dom[1]),
@@ -633,7 +650,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 3),
         "higher_is_better": True,
-        "scaling": "weak",
+        "scaling": "weak" if shards == 1 else "strong",
         "vs_baseline": None,
         "dtype": "+".join(x for x, md in (("mxfp4xmxfp4", 0), ("fp8e4m3xmxfp4", 1)) if md in modes) + "->fp32acc->bf16",
         "data": "synthetic (seeded activations with Student-t outlier channels; N(0,0.02) weights, RTN MXFP4"
@@ -646,7 +663,8 @@ def main():
                    "w4a8_activations": "fp8_static_per_tensor" if static else "fp8_per_token",
                    "w4a4_transform": "hadamard128+smoothquant" if transform else
                    (f"svdquant_rank{args.svdquant_rank}" if args.svdquant_rank else "none"),
-                   "linears_per_block": len(wl.linears), "tflop_per_step": round(wl.total_flops() / 1e12, 2)},
+                   "linears_per_block": len(wl.linears), "tflop_per_step": round(wl.total_flops() / 1e12, 2),
+                   **({"token_shards": shards} if shards > 1 else {})},
         "roofline": roofline,
         "kernels": kernels,
         "weight_pack_gbs": round(stack.pack_gbs, 1),
