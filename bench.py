@@ -24,7 +24,8 @@ transformed. Such a block's FFN runs up-projection -> bf16 h -> transformed
 quantizer -> down-projection (the fused MXFP4 epilogue does not rotate).
 
 --svdquant-rank R adds SVDQuant's rank-R bf16 branch to every W4A4 linear:
-T = x L1, then the GEMM on the residual with T L2 in its fp32 sums and the
+T = x L1 (in the quantizer's pass over x where the linear quantizes its own
+input), then the GEMM on the residual with T L2 in its fp32 sums and the
 epilogue (one kernel; shapes the pipelined GEMM does not take run the GEMM
 without epilogue, then y = epilogue(y_pre + T L2)). The FFN's first
 projection writes its bf16 hidden state, which the second one's branch reads.
@@ -282,7 +283,14 @@ class Stack:
                     if timed:
                         e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
                         e0.record()
-                    if not fed and not shared:
+                    # a branch linear that quantizes its own input takes T in the same pass over x
+                    quant_lr = lr is not None and not fed and not shared
+                    if lr is not None:
+                        t = self.t_buf[: m * self.lr_rank].view(m, self.lr_rank)
+                    if quant_lr:
+                        codes_src = lin.name
+                        mxq.quantize_act_lowrank(x, lr[0], codes, scales, t)
+                    elif not fed and not shared:
                         codes_src = lin.name
                         if tr:
                             mxq.quantize_mxfp4_hadamard(x, self.act_mult[(e, b, li)], codes, scales)
@@ -292,8 +300,7 @@ class Stack:
                             mxq.quantize_act(mode, x, codes, scales)
                     if timed:
                         e1.record()
-                    if lr is not None:
-                        t = self.t_buf[: m * self.lr_rank].view(m, self.lr_rank)
+                    if lr is not None and not quant_lr:
                         mxq.lowrank_down(x, lr[0], t)
                     if timed:
                         e1b = torch.cuda.Event(enable_timing=True)
@@ -328,12 +335,15 @@ class Stack:
                         qbytes = m * lin.k * 2 + (m * lin.k // 2 + m * lin.k // 32 if mode == 0 else m * lin.k + 4 * m)
                         gbytes = ((m * lin.k // 2 + m * lin.k // 32) if mode == 0 else (m * lin.k + 4 * m)) \
                             + lin.n * lin.k // 2 + lin.n * lin.k // 32 + out_bytes
-                        if not fed and not shared:
+                        if quant_lr:
+                            self.records.append(("quant_lowrank", mode, 2 * m * self.lr_rank * lin.k,
+                                                 qbytes + m * self.lr_rank * 2, e0, e1))
+                        elif not fed and not shared:
                             self.records.append(("quant", mode, 0, qbytes, e0, e1))
                         # the GEMM's flops are those of the quantized product (the branch's
                         # 2 m n r bf16 flops inside the fused kernel are not counted)
                         self.records.append(("gemm", mode, 2 * m * lin.n * lin.k, gbytes, e1b, e2))
-                        if lr is not None:
+                        if lr is not None and not quant_lr:
                             rr = self.lr_rank
                             self.records.append(("lowrank_down", mode, 2 * m * rr * lin.k,
                                                  m * lin.k * 2 + m * rr * 2, e1, e1b))

@@ -264,6 +264,16 @@ int mxq_policy_select(const double* sums_off, const double* sums_on, int32_t n_e
  * All pointers 16-byte aligned.
  */
 int mxq_lowrank_down(const void* x, int64_t M, int64_t K, const void* l1t, int64_t r, void* t, hipStream_t stream);
+/*
+ * mxq_quantize_act_lowrank: mxq_quantize_act(MXQ_W4A4, x, M, K, ldx = K, codes,
+ *   scales) and mxq_lowrank_down(x, M, K, l1t, r, t) in one pass over x: the
+ *   same codes and scales byte for byte, the same t. For a linear whose
+ *   activation and branch both come from x (the quantizer and the branch's
+ *   first half each read it whole). Arguments as for those two calls; K a
+ *   multiple of 128; codes M * K/2 bytes, scales [K/128][M][4].
+ */
+int mxq_quantize_act_lowrank(const void* x, int64_t M, int64_t K, const void* l1t, int64_t r, void* codes,
+                             void* scales, void* t, hipStream_t stream);
 int mxq_lowrank_up(const void* y_pre, const void* t, const void* l2, int64_t M, int64_t N, int64_t r,
                    int epilogue, void* y, hipStream_t stream);
 

@@ -48,6 +48,7 @@ _SIGS = {
     "mxq_fp8_calibrate": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P]),
     "mxq_lowrank_down": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P]),
     "mxq_lowrank_up": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _I64, ctypes.c_int, _P, _P]),
+    "mxq_quantize_act_lowrank": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P, _P, _P]),
     "mxq_gemm_lowrank": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I64, ctypes.c_int, _P, _P, _I64, _I64, _I64,
                                         _P]),
     "mxq_sqnr_accumulate": (ctypes.c_int, [_P, _P, _I64, _P, _P]),
@@ -541,6 +542,29 @@ def gemm_lowrank(a_codes, a_scales, w_codes, w_scales, t, l2, bias=None, epilogu
 def gemm_lowrank_supported(M, N, K, mxfp4_out=False):
     """Whether gemm_lowrank takes (M, N, K): the pipelined kernel's shapes (N % 128 == 0 for MXFP4 output)."""
     return gemm_kernel_name(W4A4, M, N, K).startswith("pipe_") and (not mxfp4_out or N % 128 == 0)
+
+
+def quantize_act_lowrank(x, l1t, codes=None, scales=None, t=None, stream=None):
+    """W4A4 activation codes/scales of x and the branch's t = bf16(x @ L1) in one pass over x.
+
+    Same bytes as quantize_act(W4A4, x) and the same t as lowrank_down(x, l1t). Returns
+    (codes, scales, t)."""
+    torch = _torch()
+    m, k = _rows_k(x, "x")
+    r = int(l1t.shape[0])
+    if tuple(l1t.shape) != (r, k):
+        raise ValueError(f"l1t must be [r, {k}], got {tuple(l1t.shape)}")
+    if codes is None or scales is None:
+        codes, scales = act_buffers(W4A4, m, k, x.device)
+    if t is None:
+        t = torch.empty((m, r), dtype=torch.bfloat16, device=x.device)
+    if tuple(t.shape) != (m, r):
+        raise ValueError(f"t must be [{m}, {r}], got {tuple(t.shape)}")
+    st = lib().mxq_quantize_act_lowrank(_dev_ptr(x, "x", torch.bfloat16), m, k, _dev_ptr(l1t, "l1t", torch.bfloat16), r,
+                                         _dev_ptr(codes, "codes", torch.uint8), _dev_ptr(scales, "scales", torch.uint8),
+                                         _dev_ptr(t, "t", torch.bfloat16), _stream_handle(stream))
+    _check(st, "quantize_act_lowrank")
+    return codes, scales, t
 
 
 def lowrank_up(y_pre, t, l2, epilogue=EPI_NONE, y=None, stream=None):

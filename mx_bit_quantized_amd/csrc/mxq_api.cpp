@@ -191,7 +191,19 @@ int mxq_lowrank_down(const void* x, int64_t M, int64_t K, const void* l1t, int64
   if (M == 0) return MXQ_OK;
   if (x == nullptr || l1t == nullptr || t == nullptr) return MXQ_ERR_NULL;
   if (!aligned16(x) || !aligned16(l1t) || !aligned16(t)) return MXQ_ERR_ALIGN;
-  return hip_status(mxq::launch_lowrank_down(x, M, K, l1t, r, t, stream));
+  return hip_status(mxq::launch_lowrank_down(x, M, K, l1t, r, t, nullptr, nullptr, stream));
+}
+
+int mxq_quantize_act_lowrank(const void* x, int64_t M, int64_t K, const void* l1t, int64_t r, void* codes,
+                             void* scales, void* t, hipStream_t stream) {
+  int st = check_mk(M, K, K);
+  if (st != MXQ_OK) return st;
+  if (K % 128 != 0 || !lowrank_rank_ok(r)) return MXQ_ERR_SHAPE;
+  if (M == 0) return MXQ_OK;
+  if (x == nullptr || l1t == nullptr || codes == nullptr || scales == nullptr || t == nullptr) return MXQ_ERR_NULL;
+  if (!aligned16(x) || !aligned16(l1t) || !aligned16(codes) || !aligned16(scales) || !aligned16(t))
+    return MXQ_ERR_ALIGN;
+  return hip_status(mxq::launch_lowrank_down(x, M, K, l1t, r, t, codes, scales, stream));
 }
 
 int mxq_lowrank_up(const void* y_pre, const void* t, const void* l2, int64_t M, int64_t N, int64_t r,

@@ -25,8 +25,10 @@ hipError_t launch_smoothquant_factors(const float* act_amax, const float* w_amax
 // SVDQuant's low-rank branch: t [M][r] = RN_bf16(x L1) from l1t [r][K]
 // (r = 32, 64, 96 or 128; K % 128 == 0); y [M][N] = RN_bf16(epilogue(y_pre +
 // t L2^T)) from l2 [N][r] (N % 32 == 0; y may be y_pre).
+// t = RN_bf16(x l1t^T); with codes non-null also the W4A4 activation of x
+// (codes in 128-element panels, scales [K/128][M][4]) in the same pass.
 hipError_t launch_lowrank_down(const void* x, int64_t M, int64_t K, const void* l1t, int64_t r, void* t,
-                               hipStream_t s);
+                               void* codes, void* scales, hipStream_t s);
 hipError_t launch_lowrank_up(const void* y_pre, const void* t, const void* l2, int64_t M, int64_t N, int64_t r,
                              int epilogue, void* y, hipStream_t s);
 

@@ -48,10 +48,18 @@ constexpr int kDnRows = 64;
 constexpr int kDnKc = 128;
 constexpr int kDnPitch = kDnKc * 2 + 16;  // bytes per LDS row: 16-byte reads of 16 rows hit 16 bank groups
 
-template <int R>  // rank / 32
+//
+// QUANT: the same pass also writes the W4A4 activation of x (the MXFP4
+// quantizer's codes and scales, byte for byte): once a chunk is in LDS and its
+// MFMAs are issued, thread u quantizes block u % 4 of chunk row u / 4 (32
+// elements: block amax, scale byte, 16 code bytes by the scaled conversion).
+// The chunk is one code panel: each wave stores 16 rows x 64 bytes of codes,
+// 1 KiB of consecutive memory, and the rows' scale dwords.
+template <int R, bool QUANT>  // rank / 32; with the activation quantizer
 __global__ __launch_bounds__(256) void lowrank_down_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                                           const uint16_t* __restrict__ l1t,
-                                                          uint16_t* __restrict__ t) {
+                                                          uint16_t* __restrict__ t, uint8_t* __restrict__ codes,
+                                                          uint32_t* __restrict__ scales) {
   constexpr int RANK = 32 * R;
   constexpr int XB = kDnRows * kDnPitch, LB = RANK * kDnPitch;
   constexpr int RED = 3 * 16 * 64 * 4;  // one output tile's partial sums of waves 1..3
@@ -107,6 +115,25 @@ __global__ __launch_bounds__(256) void lowrank_down_kernel(const uint16_t* __res
 #pragma unroll
         for (int q = 0; q < R; ++q)
           acc[a][q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(al[q]), as_bf16x8(bx[a]), acc[a][q], 0, 0, 0);
+    }
+    if constexpr (QUANT) {
+      const int qr = tid >> 2, qb = tid & 3;
+      const uint8_t* src = lds + qr * kDnPitch + qb * 64;
+      uint4 c[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) c[i] = *reinterpret_cast<const uint4*>(src + 16 * i);
+      const uint32_t am = umax(umax(chunk_amax(c[0]), chunk_amax(c[1])), umax(chunk_amax(c[2]), chunk_amax(c[3])));
+      const uint32_t sb = mx_scale_byte(am);
+      const uint4 cw = make_uint4(pack8_fp4(c[0], sb), pack8_fp4(c[1], sb), pack8_fp4(c[2], sb), pack8_fp4(c[3], sb));
+      // the row's four scale bytes, from the quad's lanes (row = lane / 4)
+      const uint32_t s1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)sb, 0x39, 0xF, 0xF, false);  // lane + 1
+      const uint32_t s2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)sb, 0x4E, 0xF, 0xF, false);  // lane + 2
+      const uint32_t s3 = (uint32_t)__builtin_amdgcn_mov_dpp((int)sb, 0x93, 0xF, 0xF, false);  // lane + 3
+      const int64_t row = row0 + qr, p = k0 >> 7;
+      if (row < M) {
+        *reinterpret_cast<uint4*>(codes + p * 64 * M + row * 64 + qb * 16) = cw;
+        if (qb == 0) scales[p * M + row] = sb | (s1 << 8) | (s2 << 16) | (s3 << 24);
+      }
     }
   };
   load(xa, la, 0);
@@ -236,17 +263,27 @@ __global__ __launch_bounds__(256) void lowrank_up_kernel(const uint16_t* __restr
 }
 
 hipError_t launch_lowrank_down(const void* x, int64_t M, int64_t K, const void* l1t, int64_t r, void* t,
-                               hipStream_t s) {
+                               void* codes, void* scales, hipStream_t s) {
   const dim3 grid((unsigned)((M + kDnRows - 1) / kDnRows)), block(256);
   const auto* xs = static_cast<const uint16_t*>(x);
   const auto* ls = static_cast<const uint16_t*>(l1t);
   auto* ts = static_cast<uint16_t*>(t);
-  switch (r / 32) {
-    case 1: hipLaunchKernelGGL(lowrank_down_kernel<1>, grid, block, 0, s, xs, M, K, ls, ts); break;
-    case 2: hipLaunchKernelGGL(lowrank_down_kernel<2>, grid, block, 0, s, xs, M, K, ls, ts); break;
-    case 3: hipLaunchKernelGGL(lowrank_down_kernel<3>, grid, block, 0, s, xs, M, K, ls, ts); break;
-    default: hipLaunchKernelGGL(lowrank_down_kernel<4>, grid, block, 0, s, xs, M, K, ls, ts); break;
-  }
+  auto* cs = static_cast<uint8_t*>(codes);
+  auto* ss = static_cast<uint32_t*>(scales);
+  auto go = [&](auto r_tag, auto q_tag) {
+    hipLaunchKernelGGL((lowrank_down_kernel<decltype(r_tag)::value, decltype(q_tag)::value>), grid, block, 0, s, xs,
+                       M, K, ls, ts, cs, ss);
+  };
+  auto by_rank = [&](auto q_tag) {
+    switch (r / 32) {
+      case 1: go(std::integral_constant<int, 1>{}, q_tag); break;
+      case 2: go(std::integral_constant<int, 2>{}, q_tag); break;
+      case 3: go(std::integral_constant<int, 3>{}, q_tag); break;
+      default: go(std::integral_constant<int, 4>{}, q_tag); break;
+    }
+  };
+  if (codes != nullptr) by_rank(std::true_type{});
+  else by_rank(std::false_type{});
   return hipGetLastError();
 }
 

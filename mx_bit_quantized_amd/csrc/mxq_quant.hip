@@ -12,6 +12,7 @@
 #include <type_traits>
 
 #include "mxq_convert.h"
+#include "mxq_device.h"
 #include "mxq_internal.h"
 
 namespace mxq {
@@ -35,32 +36,6 @@ namespace mxq {
 // wave) are issued before the first conversion. The
 // block amax is a max over the magnitude bit patterns (sign cleared), exact
 // for finite bf16, with no float compare and no denormal flush.
-
-__device__ __forceinline__ uint32_t chunk_amax(const uint4 c) {
-  uint32_t m0 = umax(c.x & 0x7FFFu, (c.x >> 16) & 0x7FFFu);
-  uint32_t m1 = umax(c.y & 0x7FFFu, (c.y >> 16) & 0x7FFFu);
-  uint32_t m2 = umax(c.z & 0x7FFFu, (c.z >> 16) & 0x7FFFu);
-  uint32_t m3 = umax(c.w & 0x7FFFu, (c.w >> 16) & 0x7FFFu);
-  return umax(umax(m0, m1), umax(m2, m3));
-}
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-// 8 bf16 -> 8 E2M1 codes (element 2t in the low nibble of byte t) of a block
-// with scale byte sb, with gfx950's scaled conversion: it divides by the
-// power of two whose exponent field is sb and rounds to nearest even,
-// saturating at 6, keeping the sign (also of zeros). For every finite bf16
-// and every scale byte of a block that can hold it this equals
-// e2m1_code_bf16 (an exhaustive GPU test checks it).
-__device__ __forceinline__ uint32_t pack8_fp4(const uint4 c, uint32_t sb) {
-  const float scale = as_float(sb << 23);
-  uint32_t out = 0;
-  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, __builtin_bit_cast(bf16x2_t, c.x), scale, 0);
-  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, __builtin_bit_cast(bf16x2_t, c.y), scale, 1);
-  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, __builtin_bit_cast(bf16x2_t, c.z), scale, 2);
-  out = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(out, __builtin_bit_cast(bf16x2_t, c.w), scale, 3);
-  return out;
-}
 
 constexpr int kQuantWaves = 4;  // waves per workgroup
 constexpr int kMxRows = 16;     // rows per wave unit

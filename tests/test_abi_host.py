@@ -25,7 +25,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = mxq.lib()
     names = declared_functions()
-    assert len(names) == 26, names
+    assert len(names) == 27, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(mxq._SIGS)
@@ -274,6 +274,29 @@ def test_lowrank_validation():
         assert L.mxq_lowrank_up(*args) == mxq.ERR_ALIGN, pos
     assert L.mxq_lowrank_down(None, 0, 256, None, 32, None, S) == mxq.OK
     assert L.mxq_lowrank_up(None, None, None, 0, 256, 32, 0, None, S) == mxq.OK
+
+
+def test_quantize_act_lowrank_validation():
+    """Host-side checks of the quantizer fused with the branch's first half (nothing is enqueued)."""
+    L = mxq.lib()
+    S = None
+    # x0 M1 K2 l1t3 r4 codes5 scales6 t7 stream
+    ok = [FAKE, 64, 256, FAKE, 32, FAKE, FAKE, FAKE, S]
+    for r in (0, 16, 48, 160, -32):
+        args = list(ok)
+        args[4] = r
+        assert L.mxq_quantize_act_lowrank(*args) == mxq.ERR_SHAPE, r
+    for k in (96, 192, 100):
+        args = list(ok)
+        args[2] = k
+        assert L.mxq_quantize_act_lowrank(*args) == mxq.ERR_SHAPE, k
+    for pos in (0, 3, 5, 6, 7):
+        args = list(ok)
+        args[pos] = None
+        assert L.mxq_quantize_act_lowrank(*args) == mxq.ERR_NULL, pos
+        args[pos] = FAKE_ODD
+        assert L.mxq_quantize_act_lowrank(*args) == mxq.ERR_ALIGN, pos
+    assert L.mxq_quantize_act_lowrank(None, 0, 256, None, 32, None, None, None, S) == mxq.OK
 
 
 def test_gemm_lowrank_validation():

@@ -283,3 +283,46 @@ def test_gemm_lowrank_a14b_ffn_up_full_size():
     fc, fs = mxq.gemm_lowrank(ac, asc, rc, rs, t, l2d, None, up.epilogue, mxfp4_out=True)
     torch.cuda.synchronize()
     assert torch.equal(fc, qc) and torch.equal(fs, qs)
+
+
+# ---- the activation quantizer fused with the branch's first half -------------
+@pytest.mark.parametrize("m,k,r", [(1, 128, 32), (37, 256, 64), (300, 5120, 128), (1000, 384, 96), (4097, 640, 32),
+                                   (65, 13824, 32)])
+def test_quantize_act_lowrank_matches_both_calls_and_oracle(m, k, r):
+    """Codes and scales byte for byte those of the W4A4 quantizer and of the oracle's MXFP4 rule;
+    t bit for bit that of the down kernel alone, and within the tolerance of the oracle."""
+    say("quantize+down", m, k, r)
+    g = np.random.default_rng(3 * m + k + r)
+    x = synth.activation_bf16(900 + m, m, k, ("student_t",))
+    l1t = _bits(g.standard_normal((r, k)) * 0.05)
+    xd, ld = dev_bf16(x), dev_bf16(l1t)
+    qc, qs, t = mxq.quantize_act_lowrank(xd, ld)
+    rc, rs = mxq.quantize_act(mxq.W4A4, xd)
+    t_alone = mxq.lowrank_down(xd, ld)
+    torch.cuda.synchronize()
+    assert torch.equal(qc, rc) and torch.equal(qs, rs)
+    assert torch.equal(t, t_alone)
+    want_c, want_s = oracle.mxfp4_quantize(x)
+    assert np.array_equal(code_rows(qc, m, k, 4), want_c)
+    assert np.array_equal(host_u8(qs).transpose(1, 0, 2).reshape(m, -1)[:, : k // 32], want_s)
+    assert_output_close(host_bits(t), oracle.bf16_bits_to_f64(oracle.lowrank_down(x, l1t)), f"t [{m}x{k}] r={r}")
+
+
+def test_quantize_act_lowrank_edge_blocks():
+    """Zero rows, blocks at the largest bf16 exponents and subnormal-only blocks: the fused
+    quantizer takes the same scale bytes and codes as the oracle."""
+    say("quantize+down edge blocks")
+    m, k = 70, 256
+    g = np.random.default_rng(4)
+    x = synth.activation_bf16(44, m, k, ("student_t",)).copy()
+    x[0] = 0
+    x[1, :32] = 0x7F7F                      # bf16 max in a whole block
+    x[2, 32:64] = 0x0001                    # smallest subnormal
+    x[3, 64:96] = (g.integers(1, 0x7F, 32) | 0x8000).astype(np.uint16)  # negative subnormals
+    x[69, 96:128] = 0x8000                  # negative zeros
+    l1t = _bits(g.standard_normal((32, k)) * 0.05)
+    qc, qs, _ = mxq.quantize_act_lowrank(dev_bf16(x), dev_bf16(l1t))
+    torch.cuda.synchronize()
+    want_c, want_s = oracle.mxfp4_quantize(x)
+    assert np.array_equal(code_rows(qc, m, k, 4), want_c)
+    assert np.array_equal(host_u8(qs).transpose(1, 0, 2).reshape(m, -1)[:, : k // 32], want_s)
