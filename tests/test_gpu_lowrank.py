@@ -326,3 +326,31 @@ def test_quantize_act_lowrank_edge_blocks():
     want_c, want_s = oracle.mxfp4_quantize(x)
     assert np.array_equal(code_rows(qc, m, k, 4), want_c)
     assert np.array_equal(host_u8(qs).transpose(1, 0, 2).reshape(m, -1)[:, : k // 32], want_s)
+
+
+def test_quantize_act_lowrank_a14b_full_size():
+    """The A14B video activation at 720p (75600 x 5120) with a rank-32 branch, as the bench runs it:
+    whole code and scale buffers against the quantizer, t against the down kernel, sampled rows of
+    both against the oracle."""
+    wl = synth.workload(5)
+    m, k, r = wl.m_video, wl.dim, 32
+    what = f"quantize+down a14b [{m}x{k}] r={r}"
+    say(what)
+    g = np.random.default_rng(57)
+    x = synth.activation_bf16(5, m, k, wl.outliers, tensor_id=synth.T_X_VIDEO)
+    l1t = _bits(g.standard_normal((r, k)) * 0.02)
+    xd, ld = dev_bf16(x), dev_bf16(l1t)
+    qc, qs, t = mxq.quantize_act_lowrank(xd, ld)
+    rc, rs = mxq.quantize_act(mxq.W4A4, xd)
+    t_alone = mxq.lowrank_down(xd, ld)
+    torch.cuda.synchronize()
+    assert torch.equal(qc, rc) and torch.equal(qs, rs)
+    assert torch.equal(t, t_alone)
+    rows = sample_rows(m, 24, 65)
+    want_c, want_s = oracle.mxfp4_quantize(x[rows])
+    assert np.array_equal(code_rows(qc, m, k, 4, rows), want_c)
+    got_s = host_u8(qs).transpose(1, 0, 2)[rows].reshape(len(rows), -1)
+    assert np.array_equal(got_s, want_s)
+    rep = assert_output_close(host_bits(t.index_select(0, _idx(rows))),
+                              oracle.bf16_bits_to_f64(oracle.lowrank_down(x[rows], l1t)), what)
+    say(f"{what}: worst/bound {rep['worst_ratio']:.3f}")
