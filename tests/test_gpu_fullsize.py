@@ -227,3 +227,34 @@ def test_config5_attention_linears_full_size(mode, name):
 @pytest.mark.parametrize("mode", [mxq.W4A4, mxq.W4A8])
 def test_config5_ffn_full_size(mode):
     _ffn_case(5, mode, 520 + mode)
+
+
+# The pipelined kernel addresses its output with 32-bit buffer offsets and takes
+# shapes whose bf16 output stays below 2^31 - 256 bytes; one row more and the
+# direct kernel (64-bit addresses) takes the shape. M = 131071 puts the last
+# 256-row tile one row short of full and the output 16 KiB under the bound;
+# M = 131072 gives exactly 2^31 bytes of output.
+@pytest.mark.parametrize("mode", [mxq.W4A4, mxq.W4A8])
+@pytest.mark.parametrize("m,kernel", [(131071, "pipe_"), (131072, "direct_")])
+def test_gemm_at_the_output_size_bound(mode, m, kernel):
+    n, k = 8192, 512
+    what = f"output bound mode={mode} [{m}x{n}x{k}] {kernel}"
+    say(what)
+    assert mxq.gemm_kernel_name(mode, m, n, k).startswith(kernel)
+    g = torch.Generator(device="cuda:0").manual_seed(m + mode)
+    x = torch.randn((m, k), generator=g, device="cuda:0").to(torch.bfloat16)
+    w = synth.weight_bf16(31, n, k)
+    wc, ws = mxq.quantize_weight_mxfp4(_to_dev(w))
+    codes, scales = mxq.quantize_act(mode, x)
+    y = mxq.gemm(mode, codes, scales, wc, ws, None, mxq.EPI_NONE)
+    torch.cuda.synchronize()
+    rows = sample_rows(m, N_ROWS, 70 + mode)
+    cols = sample_rows(n, N_COLS, 71 + mode)
+    x_rows = host_bits(x.index_select(0, _idx(rows)))
+    oac, oas = oracle.quantize_act(mode, x_rows)
+    _check_act(mode, codes, scales, rows, oac, oas, what)
+    owc, ows = oracle.mxfp4_quantize(w[cols])
+    y_ref = oracle.qdq_matmul(mode, oac, oas, owc, ows, None, mxq.EPI_NONE)
+    y_got = host_bits(y.index_select(0, _idx(rows)).index_select(1, _idx(cols)))
+    rep = assert_output_close(y_got, y_ref, what)
+    say(f"{what}: worst/bound {rep['worst_ratio']:.3f}")
