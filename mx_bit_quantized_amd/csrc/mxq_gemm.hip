@@ -486,12 +486,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int P_BIAS = 0, P_SINK = 512, P_TOK = 1024;
   constexpr int PARAM_BYTES = MODE == 1 ? 2048 : 1024;
   constexpr int PARAM_OFF = NB * C::STAGE;
-  // W4A4 stages its results through a small area of its own (the epilogue
-  // runs while the ring is busy, see below): 32 rows x 144 bytes per wave
-  constexpr int EV_PITCH = 144;
+  // The epilogue runs inside the next tile's first stage while the ring is
+  // busy (see below), so it stages its results through a small area of its
+  // own, per wave: W4A4 32 rows x 144 bytes (a 64-column tile pair), W4A8 32
+  // rows x 72 bytes (one 32-column MFMA tile; the larger W4A8 ring leaves 9
+  // KiB). W4A8 with static FP8 output runs its epilogue after the tile instead.
+  constexpr bool OVERLAP = MODE == 0 || !QOUT;
+  constexpr int EV_PITCH = MODE == 0 ? 144 : 72;
   constexpr int EV_BYTES = 32 * EV_PITCH;
   constexpr int EV_OFF = PARAM_OFF + 2 * PARAM_BYTES;
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[EV_OFF + (MODE == 0 ? 4 * EV_BYTES : 0)];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[EV_OFF + (OVERLAP ? 4 * EV_BYTES : 0)];
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -760,9 +764,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                                                                       kFmtFp4, kFmtFp4, SEL, (int)sc.ws[i], SEL,
                                                                       (int)sc.xs[j]);
         else
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, op_fp8(f.b[2 * j], f.b[2 * j + 1]), acc[i][j],
-                                                                      kFmtFp4, kFmtFp8, SEL, (int)sc.ws[i], SEL,
-                                                                      (int)kUnitScales);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, op_fp8(f.b[2 * j], f.b[2 * j + 1]),
+                                                                      ZERO ? v16f{} : acc[i][j], kFmtFp4, kFmtFp8,
+                                                                      SEL, (int)sc.ws[i], SEL, (int)kUnitScales);
         if constexpr (PIN) asm volatile("" ::"a"(acc[i][j]));
         between(s);
         __builtin_amdgcn_sched_barrier(0);
@@ -931,8 +935,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
   for (int k = 0; k < STAGE_ITEMS; ++k) read_item(ring, 0, 0, kStageOrder[MODE][k], cur, cur_sc);
 
-  if constexpr (MODE == 0) {
-    // ---- W4A4: the epilogue of tile t-1 runs inside the first stage of
+  if constexpr (OVERLAP) {
+    // ---- The epilogue of tile t-1 runs inside the first stage of
     // tile t. Before MFMA (i, j) of that stage's first step (which starts the
     // new sums from zero) the lane reads accumulator tile (i, j) of tile t-1
     // out of its registers, adds the bias, applies GELU and packs bf16 pairs;
@@ -944,6 +948,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // working while the vector unit does this. Tile 0's first stage has no
     // previous tile (its stores are dropped), and one extra stage after the
     // last tile, computing on zeros, carries the last tile's epilogue.
+    // W4A8 (bf16 output) does the same per MFMA tile: the per-token scale of
+    // the lane's row, bias and GELU, then the tile's 32 rows x 64 bytes go
+    // through the staging area and leave as 2 stores of 16 rows x 64 bytes
+    // one MFMA slot later.
     uint8_t* ev_region = ring + EV_OFF + wave * EV_BYTES;
     // bias of the lane's 16 columns of MFMA tile row group i, in accumulator
     // order (q = 4 t + c: column 32 i + 8 t + 4 g + c)
@@ -957,16 +965,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         b[4 * t2 + 3] = as_float(bb.y & 0xFFFF0000u);
       }
     };
-    // accumulator tile (i, j) of the finished tile (+ bias) -> 8 bf16 pairs:
-    // pair h of run t holds columns 8 t + 4 g + 2 h, + 1
-    auto ev_tile = [&](int i, int j, const v16f& b, uint32_t (&pk)[4][2]) {
+    // accumulator tile (i, j) of the finished tile (x the row's token scale
+    // for W4A8, + bias) -> 8 bf16 pairs: pair h of run t holds columns
+    // 8 t + 4 g + 2 h, + 1
+    auto ev_tile = [&](int i, int j, const v16f& b, float sm, uint32_t (&pk)[4][2]) {
 #pragma unroll
       for (int t2 = 0; t2 < 4; ++t2)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           float v0 = acc_read(acc[i][j][4 * t2 + 2 * h]);
           float v1 = acc_read(acc[i][j][4 * t2 + 2 * h + 1]);
-          if constexpr (BIAS) {
+          if constexpr (MODE == 1) {
+            v0 = BIAS ? __builtin_fmaf(v0, sm, b[4 * t2 + 2 * h]) : v0 * sm;
+            v1 = BIAS ? __builtin_fmaf(v1, sm, b[4 * t2 + 2 * h + 1]) : v1 * sm;
+          } else if constexpr (BIAS) {
             v0 += b[4 * t2 + 2 * h];
             v1 += b[4 * t2 + 2 * h + 1];
           }
@@ -991,12 +1003,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       for (int it = 0; it < 4; ++it)
         rd[it] = *reinterpret_cast<const uint4*>(ev_region + (8 * it + (lane >> 3)) * EV_PITCH + (lane & 7) * 16);
     };
+    // W4A8: one tile's 32 rows x 64 bytes; lane l reads 16 bytes of row
+    // 16 st + l / 4 at byte 16 (l % 4), as two 8-byte reads (the 72-byte
+    // pitch keeps 8-byte alignment and spreads the rows over the banks)
+    auto ev8_write = [&](const uint32_t (&p)[4][2]) {
+#pragma unroll
+      for (int t2 = 0; t2 < 4; ++t2)
+        *reinterpret_cast<uint2*>(ev_region + r * EV_PITCH + 16 * t2 + 8 * g) = make_uint2(p[t2][0], p[t2][1]);
+    };
+    auto ev8_read = [&](uint4 (&rd)[2]) {
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const uint8_t* src = ev_region + (16 * st + (lane >> 2)) * EV_PITCH + (lane & 3) * 16;
+        const uint2 lo = *reinterpret_cast<const uint2*>(src);
+        const uint2 hi = *reinterpret_cast<const uint2*>(src + 8);
+        rd[st] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
+    };
 
-    constexpr int D_SLACK1 = EPI_OPS;        // a wait that every op of the first stage may outlast
-    constexpr int D_SLACK2 = EPI_PARAM_OPS;  // ops of the first stage issued after its last copy
-    // every epilogue store of the first stage comes before its last copy
+    constexpr int D_SLACK1 = EPI_OPS;  // a wait that every op of the first stage may outlast
+    // The stage after the next may leave outstanding the ops of the first
+    // stage issued after its last copy: W4A4 issues every epilogue store
+    // before its last copy (slot > 16), W4A8 issues its 13 copies in slots
+    // 0..12 and the stores of tile t (2 each) after slot t + 1, tile 15's in
+    // the second step, so tiles 11..15 come after the last copy.
     constexpr int kLastCopySlot = COPY_SPAN * (C::PER_WAVE - 1) / C::PER_WAVE;
-    static_assert(kLastCopySlot > 16, "epilogue stores end in slot 16");
+    static_assert(MODE == 1 || kLastCopySlot > 16, "W4A4 epilogue stores end in slot 16");
+    static_assert(MODE == 0 || (kLastCopySlot >= 1 && kLastCopySlot <= 16), "W4A8 copies within the first step");
+    constexpr int D_SLACK2 = MODE == 0 ? EPI_PARAM_OPS : 2 * (17 - kLastCopySlot) + EPI_PARAM_OPS;
 
     int slot = 0;  // ring slot of the stage being computed
     auto run_stage = [&](int tile_k, int s_in, auto first_tag, auto br_tag) {
@@ -1084,7 +1118,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           auto beforeq = [&](int sl) {
             const int i = sl & 3, j = sl >> 2;
             uint32_t pk[4][2];
-            ev_tile(i, j, bq[i], pk);
+            ev_tile(i, j, bq[i], 1.0f, pk);
             typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
             u16x2 m2 = {0, 0};
 #pragma unroll
@@ -1137,6 +1171,55 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                         between1(k);
                         if (k == 0) group_store(3);
                       });
+        } else if constexpr (MODE == 1) {
+          // W4A8, bf16 output: tile k = 4 i + j (i outer) through the staging
+          // area after MFMA slot k, its two stores after slot k + 1 (tile 15's
+          // after the second step's first MFMA). Rows past M fall past the end
+          // of the output (dropped by the range check); columns past N (or no
+          // tile at all) get the offset's top bit.
+          const int ev_m0 = ptm * 256 + wm * 128 + (lane >> 2);  // + 32 j + 16 st
+          const int ev_n0 = ptn * 256 + wn * 128 + (lane & 3) * 8;  // + 32 i
+          const uint8_t* prm = ring + PARAM_OFF + ((tile_k - 1) & 1) * PARAM_BYTES;
+          float sm[4];  // token scales of the lane's rows, one per row group j
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sm[j] = *reinterpret_cast<const float*>(prm + P_TOK + (wm * 128 + 32 * j + r) * 4);
+          v16f c_cur, c_nxt;
+          if constexpr (BIAS) ev_bias(prm, 0, c_cur);
+          uint32_t pk[4][2];
+          uint4 rd[2];
+          auto tile_store = [&](int k) {
+            const int i = k >> 2, j = k & 3;
+            const uint32_t bad = ev_live && ev_n0 + 32 * i < N ? 0u : 0x80000000u;
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+              const uint32_t off = ((uint32_t)(ev_m0 + 32 * j + 16 * st) * (uint32_t)N + (uint32_t)(ev_n0 + 32 * i)) * 2u;
+              buf_store16(ry, off | bad, rd[st]);
+            }
+          };
+          auto before8 = [&](int k) {
+            const int i = k >> 2, j = k & 3;
+            if (BIAS && j == 0 && i > 0) c_cur = c_nxt;
+            ev_tile(i, j, c_cur, sm[j], pk);
+          };
+          auto after8 = [&](int k) {
+            const int i = k >> 2, j = k & 3;
+            between0(k);
+            if (k > 0) tile_store(k - 1);
+            ev8_write(pk);
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            ev8_read(rd);
+            // the next tile's writes stay behind these reads
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            if (BIAS && j == 1 && i < 3) ev_bias(prm, i + 1, c_nxt);
+          };
+          mfma_step_x(cur, cur_sc, std::integral_constant<int, 0>{}, std::true_type{}, std::true_type{},
+                      std::false_type{}, before8, after8);
+          const StageScales sc1 = cur_sc;
+          mfma_step_x(nxt, sc1, std::integral_constant<int, 1>{}, std::false_type{}, std::true_type{},
+                      std::false_type{}, [](int) {}, [&](int k) {
+                        between1(k);
+                        if (k == 0) tile_store(15);
+                      });
         } else {
           // byte offset of the lane's first store (+ 32 j rows + 8 it rows + 64 h
           // columns); rows past M fall past the end of the output, which the
@@ -1162,7 +1245,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           auto before0 = [&](int k) {
             const int i = k >> 2, j = k & 3;
             if (BIAS && j == 0 && i > 0) c_cur = c_nxt;
-            ev_tile(i, j, c_cur, evd[i][j]);
+            ev_tile(i, j, c_cur, 1.0f, evd[i][j]);
           };
           auto after0 = [&](int k) {
             const int i = k >> 2, j = k & 3;
