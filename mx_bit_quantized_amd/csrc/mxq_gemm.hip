@@ -250,14 +250,16 @@ __global__ __launch_bounds__(256) void gemm_direct_kernel(
 // MFMAs run it already reads the first fragments of stage G+1 from LDS, so the
 // matrix pipe keeps working across the barrier.
 //
-// Epilogue: after a tile's last stage its slot is free until the next stage's
-// copies; the waves stage their fp32 results there (16 rows at a time) and
-// send them out with range-checked buffer stores. The stores stay in flight
-// while the next tile computes: vmcnt counts loads and stores in issue order,
-// so for the NB-2 stages after an epilogue each wait allows that epilogue's
-// memory operations to remain outstanding. Bias and per-token scales reach LDS
-// by the same copy mechanism (issued one tile ahead), so the kernel issues no
-// load whose wait the compiler would place.
+// Epilogue: a tile's results leave during the next tile's first stage, whose
+// first MFMA on each accumulator tile starts from zero: just before it the
+// lane reads that accumulator tile out, and the values go through a small
+// per-wave staging area to range-checked buffer stores (details at the
+// stage loop below). The stores stay in flight while the next stages run:
+// vmcnt counts loads and stores in issue order, so the wait of the stage
+// after next allows the first stage's operations issued after its last copy
+// to remain outstanding. Bias and per-token scales reach LDS by the same copy
+// mechanism (issued one tile ahead), so the kernel issues no load whose wait
+// the compiler would place.
 //
 // LDS rows hold one stage of one operand row (32, 64 or 128 bytes); their
 // 16-byte chunks are XOR-permuted per row (swz) so that the 16 lanes of a
@@ -489,13 +491,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // The epilogue runs inside the next tile's first stage while the ring is
   // busy (see below), so it stages its results through a small area of its
   // own, per wave: W4A4 32 rows x 144 bytes (a 64-column tile pair), W4A8 32
-  // rows x 72 bytes (one 32-column MFMA tile; the larger W4A8 ring leaves 9
-  // KiB). W4A8 with static FP8 output runs its epilogue after the tile instead.
-  constexpr bool OVERLAP = MODE == 0 || !QOUT;
+  // rows x 72 bytes (one 32-column MFMA tile in bf16, or a tile pair of
+  // static FP8 codes; the larger W4A8 ring leaves 9 KiB).
   constexpr int EV_PITCH = MODE == 0 ? 144 : 72;
   constexpr int EV_BYTES = 32 * EV_PITCH;
   constexpr int EV_OFF = PARAM_OFF + 2 * PARAM_BYTES;
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[EV_OFF + (OVERLAP ? 4 * EV_BYTES : 0)];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[EV_OFF + 4 * EV_BYTES];
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -789,130 +790,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
   };
 
-  // ---- epilogue of one tile, staged through the slot of its last stage.
-  // Accumulator q of lane (r, g) in a 32x32 tile holds n = 8 (q / 4) + 4 g +
-  // (q % 4), m = r. Pass p = 2 j + h takes row group j (32 token rows) and
-  // column half h (MFMA tiles i = 2h, 2h+1: 64 columns): every lane writes its
-  // accumulators to LDS straight from the accumulator registers (rows of 64
-  // fp32, 272-byte pitch: conflict-free 16-byte writes and reads), then reads
-  // them back 8 lanes per row, 8 consecutive columns per lane, applies scale,
-  // bias and GELU, converts to bf16 and stores 16 bytes: each store writes 8
-  // rows x 128 contiguous bytes, whole cache lines. A pass issues all of its
-  // LDS reads before the first use, so the wave waits for LDS once per pass.
-  // The bias slice in LDS holds zeros when there is no bias, so the add needs
-  // no branch. Exactly EPI_STORES stores per wave, whatever the shape: rows
-  // past M and columns past N get an offset the range check drops.
-  constexpr int EP = 272;
-  // W4A4 with QOUT: per 32-row group two 1 KiB code stores and one scale
-  // store; W4A8 with QOUT: the 32 code stores and one store of row scales
-  constexpr int EPI_STORES = MODE == 0 ? (QOUT ? 12 : 32) : (QOUT ? 33 : 32);
+  // Epilogue stores per wave and tile (W4A4: 32 bf16 stores, or with QOUT per
+  // 32-row group two 1 KiB code stores and one scale store; W4A8: 32 bf16
+  // stores, or with QOUT 2 per tile pair and one store of row scales), the
+  // same whatever the shape: rows past M and columns past N get an offset
+  // the range check drops.
+  constexpr int EPI_STORES = MODE == 0 ? (QOUT ? 12 : 32) : (QOUT ? 17 : 32);
   constexpr int EPI_OPS = EPI_STORES + EPI_PARAM_OPS;
-  static_assert(4 * 32 * EP <= C::STAGE, "epilogue staging fits in one ring slot");
   const i32x4 ry = make_rsrc(y, (uint32_t)M * (uint32_t)N * (MODE == 1 && QOUT ? 1u : 2u));
   Fp8Out fo{};
   if constexpr (MODE == 1 && QOUT) fo = fp8_out_setup(*out_amax);
-  const int lrow = lane >> 3;        // row within a group of 8 (read phase)
-  const int lcol = (lane & 7) * 8;   // first of the lane's 8 columns (read phase)
-  auto write_pass = [&](uint8_t* wbase, auto p_tag) {
-    constexpr int J = decltype(p_tag)::value >> 1, H = decltype(p_tag)::value & 1;
-#pragma unroll
-    for (int i2 = 0; i2 < 2; ++i2)
-#pragma unroll
-      for (int qq = 0; qq < 4; ++qq)
-        *reinterpret_cast<float4*>(wbase + (32 * i2 + 8 * qq) * 4) =
-            make_float4(acc[2 * H + i2][J][4 * qq], acc[2 * H + i2][J][4 * qq + 1], acc[2 * H + i2][J][4 * qq + 2],
-                        acc[2 * H + i2][J][4 * qq + 3]);
-  };
-  auto epilogue = [&](int k, int slot) {
-    int tm, tn;
-    tile_of(first + k * stride, tiles_m, tiles_n, tm, tn);
-    const int m_base = tm * 256, n_base = tn * 256;
-    // every wave is done with this slot's operands
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    const int region_off = slot * C::STAGE + wave * (32 * EP);
-    uint8_t* region = ring + region_off;
-    uint8_t* wbase = region + r * EP + 16 * g;
-    const uint8_t* rbase = region + lrow * EP + lcol * 4;
-    const uint8_t* params = ring + PARAM_OFF + (k & 1) * PARAM_BYTES;
-    auto pass = [&](auto p_tag) {
-      constexpr int p = decltype(p_tag)::value;
-      constexpr int J = p >> 1, H = p & 1;
-      write_pass(wbase, p_tag);
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-      const int row_grp = wm * 128 + 32 * J;
-      const int ncol = wn * 128 + 64 * H + lcol;  // column within the tile
-      const int n = n_base + ncol;
-      const uint4 braw = *reinterpret_cast<const uint4*>(params + P_BIAS + ncol * 2);
-      float4 lo[4], hi[4];
-      float sm[4];
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        lo[it] = *reinterpret_cast<const float4*>(rbase + 8 * it * EP);
-        hi[it] = *reinterpret_cast<const float4*>(rbase + 8 * it * EP + 16);
-        if constexpr (MODE == 1) sm[it] = *reinterpret_cast<const float*>(params + P_TOK + (row_grp + 8 * it + lrow) * 4);
-      }
-      // the next pass overwrites the region: its writes stay behind these reads
-      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-      const uint32_t bw[4] = {braw.x, braw.y, braw.z, braw.w};
-      float b[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) b[u] = as_float((u & 1) ? (bw[u >> 1] & 0xFFFF0000u) : (bw[u >> 1] << 16));
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const int m = m_base + row_grp + 8 * it + lrow;
-        float v[8] = {lo[it].x, lo[it].y, lo[it].z, lo[it].w, hi[it].x, hi[it].y, hi[it].z, hi[it].w};
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          if constexpr (MODE == 1) v[u] = BIAS ? __builtin_fmaf(v[u], sm[it], b[u]) : v[u] * sm[it];
-          else if constexpr (BIAS) v[u] += b[u];
-          if constexpr (GELU) v[u] = gelu_tanh_dev(v[u]);
-        }
-        uint4 h;
-        h.x = pack_bf16x2(v[0], v[1]);
-        h.y = pack_bf16x2(v[2], v[3]);
-        h.z = pack_bf16x2(v[4], v[5]);
-        h.w = pack_bf16x2(v[6], v[7]);
-        const bool in = m < M && n < N;
-        if constexpr (MODE == 1 && QOUT) {
-          // the bf16 values as the next layer would read them, then their
-          // static FP8 codes: 8 bytes of row m
-          const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
-          uint32_t cw[2];
-#pragma unroll
-          for (int c2 = 0; c2 < 2; ++c2) {
-            const float q0 = fp8_out_quotient(as_float(hw[2 * c2] << 16), fo);
-            const float q1 = fp8_out_quotient(as_float(hw[2 * c2] & 0xFFFF0000u), fo);
-            const float q2 = fp8_out_quotient(as_float(hw[2 * c2 + 1] << 16), fo);
-            const float q3 = fp8_out_quotient(as_float(hw[2 * c2 + 1] & 0xFFFF0000u), fo);
-            uint32_t o = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
-            o = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, (int)o, true);
-            cw[c2] = o;
-          }
-          buf_store8(ry, in ? (uint32_t)m * (uint32_t)N + (uint32_t)n : 0x80000000u, cw[0], cw[1]);
-        } else {
-          buf_store16(ry, in ? ((uint32_t)m * (uint32_t)N + (uint32_t)n) * 2u : 0x80000000u, h);
-        }
-      }
-    };
-    // the accumulator indices are static: one copy of the pass per (j, h)
-    [&]<int... Q>(std::integer_sequence<int, Q...>) {
-      (pass(std::integral_constant<int, Q>{}), ...);
-    }(std::make_integer_sequence<int, 8>{});
-    if constexpr (MODE == 1 && QOUT) {
-      // the row scales: thread t writes that of the tile's row t, from the
-      // tiles of the first column only (one store per wave either way)
-      const int m = m_base + t;
-      const i32x4 rs = make_rsrc(y_scales, (uint32_t)M * 4u);
-      buf_store4(rs, tn == 0 && m < M ? (uint32_t)m * 4u : 0x80000000u, as_uint(fo.s));
-    }
-    // parameters of the next tile (its block was last read two tiles ago)
-    issue_params(k + 1);
-    // the copy cursor is in tile k+1 by now (it runs fewer than n_stages
-    // stages ahead); the tile it moves to next is k+2
-    tile_base(cp_k + 1, nx_nb, nx_mb);
-  };
 
   constexpr int D = NB - 1;  // copies run D stages ahead of the stage computed
   constexpr int WAIT_BASE = (D - 2) * C::PER_WAVE;
@@ -935,7 +822,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
   for (int k = 0; k < STAGE_ITEMS; ++k) read_item(ring, 0, 0, kStageOrder[MODE][k], cur, cur_sc);
 
-  if constexpr (OVERLAP) {
+  {
     // ---- The epilogue of tile t-1 runs inside the first stage of
     // tile t. Before MFMA (i, j) of that stage's first step (which starts the
     // new sums from zero) the lane reads accumulator tile (i, j) of tile t-1
@@ -1030,7 +917,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     constexpr int kLastCopySlot = COPY_SPAN * (C::PER_WAVE - 1) / C::PER_WAVE;
     static_assert(MODE == 1 || kLastCopySlot > 16, "W4A4 epilogue stores end in slot 16");
     static_assert(MODE == 0 || (kLastCopySlot >= 1 && kLastCopySlot <= 16), "W4A8 copies within the first step");
-    constexpr int D_SLACK2 = MODE == 0 ? EPI_PARAM_OPS : 2 * (17 - kLastCopySlot) + EPI_PARAM_OPS;
+    // (W4A8 static FP8 output: tile pairs complete at slots 4 + j and 12 + j
+    // and are stored one slot later, so 4 pairs after slot 12.)
+    constexpr int D_SLACK2 = MODE == 0 ? EPI_PARAM_OPS
+                             : QOUT    ? 2 * 4 + EPI_PARAM_OPS
+                                       : 2 * (17 - kLastCopySlot) + EPI_PARAM_OPS;
+    static_assert(MODE == 0 || !QOUT || kLastCopySlot == 12, "W4A8 static-FP8 store schedule");
 
     int slot = 0;  // ring slot of the stage being computed
     auto run_stage = [&](int tile_k, int s_in, auto first_tag, auto br_tag) {
@@ -1076,7 +968,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const bool ev_live = tile_k > 0;
         int ptm = 0, ptn = 0;
         if (ev_live) tile_of(first + (tile_k - 1) * stride, tiles_m, tiles_n, ptm, ptn);
-        if constexpr (QOUT) {
+        if constexpr (MODE == 0 && QOUT) {
           // MXFP4 output. The wave's 128 columns are one code panel of the
           // output (64 bytes per row, rows contiguous) and one scale dword per
           // row. The first step runs j-outer: before MFMA (i, j) the lane turns
@@ -1170,6 +1062,84 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                       std::false_type{}, [](int) {}, [&](int k) {
                         between1(k);
                         if (k == 0) group_store(3);
+                      });
+        } else if constexpr (MODE == 1 && QOUT) {
+          // W4A8 with static FP8 output: each tile's bf16 values (token scale,
+          // bias, GELU) become the static quantizer's codes, 4 bytes per run of
+          // 4 columns. Tile (2h, j)'s codes wait in registers for tile
+          // (2h + 1, j) (4 slots later, i outer); the pair's 32 rows x 64
+          // bytes go through the staging area and leave as two stores of 16
+          // rows x 64 bytes one slot later. The row scales (out_amax / 448)
+          // leave in one store per wave, from the tiles of the first column.
+          const int ev_m0 = ptm * 256 + wm * 128 + (lane >> 2);  // + 32 j + 16 st
+          const int ev_n0 = ptn * 256 + wn * 128 + (lane & 3) * 16;  // + 64 h
+          const uint8_t* prm = ring + PARAM_OFF + ((tile_k - 1) & 1) * PARAM_BYTES;
+          float sm[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sm[j] = *reinterpret_cast<const float*>(prm + P_TOK + (wm * 128 + 32 * j + r) * 4);
+          v16f c_cur, c_nxt;
+          if constexpr (BIAS) ev_bias(prm, 0, c_cur);
+          uint32_t q_even[4][4];  // codes of tile (2h, j), per j, per run
+          uint32_t q_cur[4];
+          uint4 rd[2];
+          auto pair_store = [&](int h, int j) {
+            const uint32_t bad = ev_live && ev_n0 + 64 * h < N ? 0u : 0x80000000u;
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+              const uint32_t off = (uint32_t)(ev_m0 + 32 * j + 16 * st) * (uint32_t)N + (uint32_t)(ev_n0 + 64 * h);
+              buf_store16(ry, off | bad, rd[st]);
+            }
+          };
+          auto before8 = [&](int k) {
+            const int i = k >> 2, j = k & 3;
+            if (BIAS && j == 0 && i > 0) c_cur = c_nxt;
+            uint32_t pk[4][2];
+            ev_tile(i, j, c_cur, sm[j], pk);
+#pragma unroll
+            for (int t2 = 0; t2 < 4; ++t2) {
+              const float q0 = fp8_out_quotient(as_float(pk[t2][0] << 16), fo);
+              const float q1 = fp8_out_quotient(as_float(pk[t2][0] & 0xFFFF0000u), fo);
+              const float q2 = fp8_out_quotient(as_float(pk[t2][1] << 16), fo);
+              const float q3 = fp8_out_quotient(as_float(pk[t2][1] & 0xFFFF0000u), fo);
+              uint32_t o = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q0, q1, 0, false);
+              q_cur[t2] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q2, q3, (int)o, true);
+            }
+          };
+          auto after8 = [&](int k) {
+            const int i = k >> 2, j = k & 3;
+            between0(k);
+            if (k == 0) {
+              const int m = ptm * 256 + t;
+              const i32x4 rs = make_rsrc(y_scales, (uint32_t)M * 4u);
+              buf_store4(rs, ev_live && ptn == 0 && m < M ? (uint32_t)m * 4u : 0x80000000u, as_uint(fo.s));
+            }
+            // the pair completed in the previous slot
+            if (k >= 5 && k <= 8) pair_store(0, k - 5);
+            if (k >= 13) pair_store(1, k - 13);
+            if ((i & 1) == 0) {
+#pragma unroll
+              for (int t2 = 0; t2 < 4; ++t2) q_even[j][t2] = q_cur[t2];
+            } else {
+              // staging row r: bytes 8 t + 4 g of tile 2h, 32 + 8 t + 4 g of tile 2h + 1
+#pragma unroll
+              for (int t2 = 0; t2 < 4; ++t2) {
+                *reinterpret_cast<uint32_t*>(ev_region + r * EV_PITCH + 8 * t2 + 4 * g) = q_even[j][t2];
+                *reinterpret_cast<uint32_t*>(ev_region + r * EV_PITCH + 32 + 8 * t2 + 4 * g) = q_cur[t2];
+              }
+              __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+              ev8_read(rd);
+              // the next pair's writes stay behind these reads
+              __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            }
+            if (BIAS && j == 1 && i < 3) ev_bias(prm, i + 1, c_nxt);
+          };
+          mfma_step_x(cur, cur_sc, std::integral_constant<int, 0>{}, std::true_type{}, std::true_type{},
+                      std::false_type{}, before8, after8);
+          const StageScales sc1 = cur_sc;
+          mfma_step_x(nxt, sc1, std::integral_constant<int, 1>{}, std::false_type{}, std::true_type{},
+                      std::false_type{}, [](int) {}, [&](int k) {
+                        between1(k);
+                        if (k == 0) pair_store(1, 3);
                       });
         } else if constexpr (MODE == 1) {
           // W4A8, bf16 output: tile k = 4 i + j (i outer) through the staging
@@ -1294,55 +1264,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       } else {
         for (int s_in = 1; s_in < s_end; ++s_in) run_stage(tile_k, s_in, std::false_type{}, std::false_type{});
       }
-    }
-  } else {
-  int slot = 0;          // ring slot of the stage being computed
-    int since_epi = D;     // stages since the last epilogue, minus one (D: none pending)
-    for (int tile_k = 0; tile_k < count; ++tile_k) {
-  #pragma unroll
-      for (int i = 0; i < 4; ++i)
-  #pragma unroll
-        for (int j = 0; j < 4; ++j)
-  #pragma unroll
-          for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
-      for (int s_in = 0; s_in < n_stages; ++s_in) {
-        if (tile_k > 0 || s_in > 0) {
-          if (since_epi < D - 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(WAIT_BASE + EPI_OPS));
-          else __builtin_amdgcn_s_waitcnt(waitcnt_vm(WAIT_BASE));
-          __builtin_amdgcn_s_barrier();
-          __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-        }
-        const int G = tile_k * n_stages + s_in;
-        const int slot_next = slot + 1 == NB ? 0 : slot + 1;
-        const int slot_refill = slot == 0 ? NB - 1 : slot - 1;  // (G + D) mod NB
-        const uint8_t* here = ring + slot * C::STAGE;
-        const uint8_t* next = ring + slot_next * C::STAGE;
-        const int next_half = (G + 1) & 1;
-        StepData<MODE> nxt;
-        StageScales nxt_sc;
-        // step 0: MFMAs on `cur`; between them the reads of step 1's fragments
-        // (early, they are needed next) and the first copies of stage G+D
-        mfma_step(cur, cur_sc, std::integral_constant<int, 0>{}, [&](int k) {
-          if (k < DATA_ITEMS) read_item(here, 1, 0, kStepOrder[MODE][k], nxt, nxt_sc);
-          if (kCopyAt[k] >= 0) issue_one(kCopyAt[k], slot_refill);
-        });
-        // step 1: MFMAs on `nxt`; between them the reads of stage G+1's step-0
-        // fragments and scales, in the order the next stage consumes them, and
-        // the rest of the copies
-        const StageScales sc1 = cur_sc;
-        mfma_step(nxt, sc1, std::integral_constant<int, 1>{}, [&](int k) {
-          read_item(next, 0, next_half, kStageOrder[MODE][k], cur, cur_sc);
-          if (kCopyAt[16 + k] >= 0) issue_one(kCopyAt[16 + k], slot_refill);
-        });
-        advance_cursor();
-        __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  
-        ++since_epi;
-        if (s_in + 1 < n_stages) slot = slot_next;
-      }
-      epilogue(tile_k, slot);
-      since_epi = 0;
-      slot = slot + 1 == NB ? 0 : slot + 1;
     }
   }
   // no copy or store may still be in flight when the workgroup retires
