@@ -125,6 +125,19 @@ def test_gemm_pipelined_kernel_matches_oracle(mode, m, n, k):
     assert_output_close(y, y_ref, f"gemm pipe mode={mode} {m}x{n}x{k}")
 
 
+# The fewest stages the pipelined kernel takes: as many as its ring holds (W4A4
+# four stages of 128 elements, W4A8 three), so the copy ring wraps inside
+# every tile and the waits of the first stages overlap the previous tile's.
+@pytest.mark.parametrize("mode,m,n,k", [(mxq.W4A4, 700, 2048, 512), (mxq.W4A8, 256, 512, 384),
+                                        (mxq.W4A8, 700, 2048, 384), (mxq.W4A8, 4352, 4096, 384)])
+def test_gemm_pipelined_at_the_fewest_stages(mode, m, n, k):
+    say("gemm pipe fewest stages", mode, m, n, k)
+    assert mxq.gemm_kernel_name(mode, m, n, k).startswith("pipe_")
+    assert not mxq.gemm_kernel_name(mode, m, n, k - 128).startswith("pipe_")
+    y, y_ref = _gemm_case(mode, m, n, k, seed=7 * m + n + k)
+    assert_output_close(y, y_ref, f"gemm pipe fewest stages mode={mode} {m}x{n}x{k}")
+
+
 # Each combination of bias and GELU is a kernel of its own (the one without
 # either is covered above).
 @pytest.mark.parametrize("mode", [mxq.W4A4, mxq.W4A8])
