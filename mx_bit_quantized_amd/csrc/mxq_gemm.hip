@@ -646,7 +646,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     cp_nb = (nx_nb & take) | (cp_nb & ~take);
     cp_mb = (nx_mb & take) | (cp_mb & ~take);
   };
-  // Tile parameters of tile k into parameter block k & 1: the bias slice
+  // Tile parameters of tile k into parameter block k & 1 (issued in stage 1
+  // of tile k - 1, read in the first stage of tile k + 1): the bias slice
   // (waves 0, 1: 256 bytes each; waves 2, 3 copy nothing into the sink) and,
   // for FP8 activations, the 256 token scales (256 bytes per wave). Always
   // EPI_PARAM_OPS copies per wave; no bias reads as zeros.
@@ -908,9 +909,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       }
     };
 
-    constexpr int D_SLACK1 = EPI_OPS;  // a wait that every op of the first stage may outlast
+    // The next tile's parameters are copied at the start of stage 1 (below),
+    // so the first stage issues copies and stores only.
+    constexpr int D_SLACK1 = EPI_STORES;  // a wait that every op of the first stage may outlast
     // The stage after the next may leave outstanding the ops of the first
-    // stage issued after its last copy: W4A4 issues every epilogue store
+    // stage issued after its last copy, and those of stage 1 (its parameter
+    // copies come before its stage copies): W4A4 issues every epilogue store
     // before its last copy (slot > 16), W4A8 issues its 13 copies in slots
     // 0..12 and the stores of tile t (2 each) after slot t + 1, tile 15's in
     // the second step, so tiles 11..15 come after the last copy.
@@ -919,9 +923,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     static_assert(MODE == 0 || (kLastCopySlot >= 1 && kLastCopySlot <= 16), "W4A8 copies within the first step");
     // (W4A8 static FP8 output: tile pairs complete at slots 4 + j and 12 + j
     // and are stored one slot later, so 4 pairs after slot 12.)
-    constexpr int D_SLACK2 = MODE == 0 ? EPI_PARAM_OPS
-                             : QOUT    ? 2 * 4 + EPI_PARAM_OPS
-                                       : 2 * (17 - kLastCopySlot) + EPI_PARAM_OPS;
+    constexpr int D_SLACK2 = MODE == 0 ? EPI_PARAM_OPS  // stage 1 (D = 3): parameters + a stage of copies
+                             : QOUT    ? 2 * 4          // D = 2: stage 0's late stores only
+                                       : 2 * (17 - kLastCopySlot);
     static_assert(MODE == 0 || !QOUT || kLastCopySlot == 12, "W4A8 static-FP8 store schedule");
 
     int slot = 0;  // ring slot of the stage being computed
@@ -937,6 +941,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         else __builtin_amdgcn_s_waitcnt(waitcnt_vm(WAIT_BASE));
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      }
+      // The parameters of tile k + 1 go into the block that the epilogue of
+      // tile k - 1 read during the first stage; the barrier that opens stage 1
+      // is the first point at which every wave has finished those reads (the
+      // block is next read in the first stage of tile k + 2).
+      if constexpr (!FIRST) {
+        if (s_in == 1) issue_params(tile_k + 1);
       }
       const int G = tile_k * n_stages + s_in;
       const int slot_next = slot + 1 == NB ? 0 : slot + 1;
@@ -1240,9 +1251,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                         if (k == 0) unit_store(3, 1);
                       });
         }
-        // parameters of the next tile go into the block just read: wait for those reads
-        __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-        issue_params(tile_k + 1);
       }
       advance_cursor();
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
