@@ -87,8 +87,9 @@ enum {
                             ld < K, or a size beyond the supported range    */
   MXQ_ERR_ALIGN = 3,     /* device pointer not 16-byte aligned, or ld not a
                             multiple of 8                                   */
-  MXQ_ERR_MODE = 4,      /* mode/epilogue not supported: only W4A4 and W4A8
-                            are quantized-linear modes (no silent fallback) */
+  MXQ_ERR_MODE = 4,      /* mode/epilogue not supported: W4A4 and W4A8 are
+                            the quantized-linear modes (transform_on also a
+                            policy entry); no silent fallback               */
   MXQ_ERR_WORKSPACE = 5, /* workspace missing or too small                  */
   MXQ_ERR_HIP = 6,       /* a HIP launch or runtime call failed             */
   MXQ_ERR_RANGE = 7      /* policy index (expert, block) out of range       */
@@ -366,6 +367,32 @@ int mxq_gemm_fp8_static_out(const void* a_codes, const void* a_scales,
                             int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 /*
+ * Conversion between the library's MXFP4 layouts (code panels, group-major
+ * scales; see "Data formats" above) and the canonical row-major layout of the
+ * OCP MXFP4 format ("Quantization formats": OCP MXFP4, the page's reference
+ * [7]): codes [rows][K/2] bytes with element 2t of a row in the low nibble of
+ * byte t, and E8M0 scales [rows][K/32] bytes, one per 32 consecutive
+ * elements of a row. The bytes themselves are unchanged; only their places
+ * move.
+ *   mxq_mxfp4_to_canonical: codes (M * K/2 bytes in code panels) and scales
+ *     ([ceil(K/128)][rows][4]) -> codes_rm [rows][K/2], scales_rm [rows][K/32].
+ *     Use it to hand the output of mxq_quantize_weight_mxfp4,
+ *     mxq_quantize_act(MXQ_W4A4, ...) or mxq_gemm_mxfp4_out to code that
+ *     expects the OCP layout.
+ *   mxq_mxfp4_from_canonical: the inverse; the padding bytes of the last
+ *     scale group (blocks past K/32) are written as zero. Use it to feed
+ *     MXFP4 weights or activations held in the OCP layout to mxq_gemm.
+ * All four buffers are device memory owned by the caller, 16-byte aligned,
+ * and must not overlap; K is a positive multiple of 32 (MXQ_ERR_SHAPE
+ * otherwise). rows == 0 enqueues nothing. Errors are detected before anything
+ * is enqueued, so nothing is written on an error.
+ */
+int mxq_mxfp4_to_canonical(const void* codes, const void* scales, int64_t rows, int64_t K, void* codes_rm,
+                           void* scales_rm, hipStream_t stream);
+int mxq_mxfp4_from_canonical(const void* codes_rm, const void* scales_rm, int64_t rows, int64_t K, void* codes,
+                             void* scales, hipStream_t stream);
+
+/*
  * Name of the kernel that mxq_gemm runs for (mode, M, N, K), as a static
  * string: "pipe_..." for the LDS-pipelined persistent kernel (M, N >= 256,
  * N a multiple of 8, K a multiple of 128 with at least one ring of stages),
@@ -376,9 +403,15 @@ const char* mxq_gemm_kernel_name(int mode, int64_t M, int64_t N, int64_t K);
 
 /*
  * Per-expert, per-block policy table ("Practical workflow", step 6).
- *   modes   host, uint8 [n_experts][n_blocks]; each entry MXQ_W4A4 or
- *           MXQ_W4A8 (anything else: MXQ_ERR_MODE). Copied; the caller may
- *           free it after the call.
+ *   modes   host, uint8 [n_experts][n_blocks]; each entry MXQ_W4A4, MXQ_W4A8
+ *           or MXQ_POLICY_TRANSFORM_ON (run by mxq_qlinear_transform);
+ *           anything else, MXQ_POLICY_BF16 included, is MXQ_ERR_MODE (with
+ *           MXQ_LOG set, the first offending (expert, block) is printed).
+ *           A table written by mxq_policy_select may hold MXQ_POLICY_BF16
+ *           entries: those blocks stay in bf16 outside this library, and the
+ *           caller replaces their entries (by any quantized mode, never
+ *           read for them) before creating the policy. Copied; the caller
+ *           may free it after the call.
  *   policy  host, receives an opaque handle owned by the caller, released
  *           with mxq_policy_destroy.
  */

@@ -11,6 +11,7 @@ Names mirror the C ABI without its ``mxq_`` prefix:
     quantize_act(mode, x)                         -> (codes, scales)
     gemm(mode, a_codes, a_scales, w_codes, w_scales, bias=None, epilogue=EPI_NONE)
     gemm_kernel_name(mode, M, N, K)
+    mxfp4_to_canonical(codes, scales, rows, K) / mxfp4_from_canonical(codes_rm, scales_rm)
     Policy(table) / policy_create / policy_destroy / policy_mode
     qlinear_workspace_bytes(mode, M, K)
     qlinear(policy, expert, block, x, w_codes, w_scales, bias=None, epilogue=EPI_NONE)
@@ -64,6 +65,8 @@ _SIGS = {
     "mxq_gemm_fp8_static_out": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int, _P, _P, _P, _I64, _I64, _I64,
                                                 _P]),
     "mxq_gemm_kernel_name": (ctypes.c_char_p, [ctypes.c_int, _I64, _I64, _I64]),
+    "mxq_mxfp4_to_canonical": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P, _P]),
+    "mxq_mxfp4_from_canonical": (ctypes.c_int, [_P, _P, _I64, _I64, _P, _P, _P]),
     "mxq_policy_create": (ctypes.c_int, [_P, _I32, _I32, ctypes.POINTER(_P)]),
     "mxq_policy_destroy": (ctypes.c_int, [_P]),
     "mxq_policy_mode": (ctypes.c_int, [_P, _I32, _I32, ctypes.POINTER(ctypes.c_int)]),
@@ -338,6 +341,39 @@ def gemm_fp8_static_out_supported(M, N, K):
 def gemm_kernel_name(mode, M, N, K):
     """Name of the kernel gemm() runs for this mode and shape (host query)."""
     return lib().mxq_gemm_kernel_name(int(mode), int(M), int(N), int(K)).decode()
+
+
+# ------------------------------------------------------------- layouts ----
+
+def mxfp4_to_canonical(codes, scales, rows, K, codes_rm=None, scales_rm=None, stream=None):
+    """Library MXFP4 layout -> canonical OCP row-major: (codes_rm uint8 [rows, K/2], scales_rm uint8 [rows, K/32])."""
+    torch = _torch()
+    if codes_rm is None:
+        codes_rm = torch.empty((rows, K // 2), dtype=torch.uint8, device=codes.device)
+    if scales_rm is None:
+        scales_rm = torch.empty((rows, K // 32), dtype=torch.uint8, device=codes.device)
+    st = lib().mxq_mxfp4_to_canonical(_dev_ptr(codes, "codes", torch.uint8), _dev_ptr(scales, "scales", torch.uint8),
+                                       int(rows), int(K), _dev_ptr(codes_rm, "codes_rm", torch.uint8),
+                                       _dev_ptr(scales_rm, "scales_rm", torch.uint8), _stream_handle(stream))
+    _check(st, "mxfp4_to_canonical")
+    return codes_rm, scales_rm
+
+
+def mxfp4_from_canonical(codes_rm, scales_rm, codes=None, scales=None, stream=None):
+    """Canonical OCP row-major MXFP4 ([rows, K/2], [rows, K/32]) -> library layout (codes, scales)."""
+    torch = _torch()
+    rows, half = _rows_k(codes_rm, "codes_rm")
+    k = 2 * half
+    if codes is None:
+        codes = torch.empty((rows, half), dtype=torch.uint8, device=codes_rm.device)
+    if scales is None:
+        scales = torch.empty(mx_scale_shape(rows, k), dtype=torch.uint8, device=codes_rm.device)
+    st = lib().mxq_mxfp4_from_canonical(_dev_ptr(codes_rm, "codes_rm", torch.uint8),
+                                         _dev_ptr(scales_rm, "scales_rm", torch.uint8), rows, k,
+                                         _dev_ptr(codes, "codes", torch.uint8), _dev_ptr(scales, "scales", torch.uint8),
+                                         _stream_handle(stream))
+    _check(st, "mxfp4_from_canonical")
+    return codes, scales
 
 
 # -------------------------------------------------------------- policy ----

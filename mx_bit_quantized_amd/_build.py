@@ -22,7 +22,8 @@ CONVCHECK_LIB = os.path.join(ROOT, "tests", "hip", "libmxq_convcheck.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-DEVICE_SOURCES = ["mxq_api.cpp", "mxq_quant.hip", "mxq_gemm.hip", "mxq_select.hip", "mxq_lowrank.hip"]
+DEVICE_SOURCES = ["mxq_api.cpp", "mxq_quant.hip", "mxq_gemm.hip", "mxq_select.hip", "mxq_lowrank.hip",
+                  "mxq_layout.hip"]
 
 COMMON_FLAGS = [
     "-O3",

@@ -120,7 +120,7 @@ const char* mxq_status_string(int status) {
   }
 }
 
-int mxq_version(void) { return 10000; }
+int mxq_version(void) { return 10100; }
 
 int mxq_quantize_weight_mxfp4(const void* w, int64_t N, int64_t K, int64_t ldw,
                               void* codes, void* scales, hipStream_t stream) {
@@ -424,6 +424,32 @@ int mxq_gemm_fp8_static_out(const void* a_codes, const void* a_scales, const voi
                                                     y_codes, y_scales, M, N, K, stream));
 }
 
+static int mxfp4_layout_call(bool to_canonical, const void* src_codes, const void* src_scales, int64_t rows,
+                             int64_t K, void* dst_codes, void* dst_scales, hipStream_t stream) {
+  int st = check_mk(rows, K, K);
+  if (st != MXQ_OK) return st;
+  if (rows == 0) return MXQ_OK;
+  if (src_codes == nullptr || src_scales == nullptr || dst_codes == nullptr || dst_scales == nullptr)
+    return MXQ_ERR_NULL;
+  if (!aligned16(src_codes) || !aligned16(src_scales) || !aligned16(dst_codes) || !aligned16(dst_scales))
+    return MXQ_ERR_ALIGN;
+  if (log_enabled())
+    fprintf(stderr, "[mxq] mxfp4 layout %s rows=%lld K=%lld\n", to_canonical ? "-> canonical" : "<- canonical",
+            (long long)rows, (long long)K);
+  return hip_status(mxq::launch_mxfp4_layout(to_canonical, src_codes, src_scales, rows, K, dst_codes, dst_scales,
+                                             stream));
+}
+
+int mxq_mxfp4_to_canonical(const void* codes, const void* scales, int64_t rows, int64_t K, void* codes_rm,
+                           void* scales_rm, hipStream_t stream) {
+  return mxfp4_layout_call(true, codes, scales, rows, K, codes_rm, scales_rm, stream);
+}
+
+int mxq_mxfp4_from_canonical(const void* codes_rm, const void* scales_rm, int64_t rows, int64_t K, void* codes,
+                             void* scales, hipStream_t stream) {
+  return mxfp4_layout_call(false, codes_rm, scales_rm, rows, K, codes, scales, stream);
+}
+
 const char* mxq_gemm_kernel_name(int mode, int64_t M, int64_t N, int64_t K) {
   if (mode != MXQ_W4A4 && mode != MXQ_W4A8) return "invalid";
   return mxq::gemm_variant_name(mode, M, N, K);
@@ -436,7 +462,12 @@ int mxq_policy_create(const uint8_t* modes, int32_t n_experts, int32_t n_blocks,
   if (modes == nullptr) return MXQ_ERR_NULL;
   const size_t n = (size_t)n_experts * (size_t)n_blocks;
   for (size_t i = 0; i < n; ++i)
-    if (modes[i] != MXQ_W4A4 && modes[i] != MXQ_W4A8 && modes[i] != MXQ_POLICY_TRANSFORM_ON) return MXQ_ERR_MODE;
+    if (modes[i] != MXQ_W4A4 && modes[i] != MXQ_W4A8 && modes[i] != MXQ_POLICY_TRANSFORM_ON) {
+      if (log_enabled())
+        fprintf(stderr, "[mxq] policy_create: expert %lld block %lld has mode %d (not W4A4, W4A8 or transform_on)\n",
+                (long long)(i / (size_t)n_blocks), (long long)(i % (size_t)n_blocks), (int)modes[i]);
+      return MXQ_ERR_MODE;
+    }
   Policy* p = new (std::nothrow) Policy;
   if (p == nullptr) return MXQ_ERR_HIP;
   p->n_experts = n_experts;

@@ -23,6 +23,7 @@
 // over K is the same set of products as in natural order.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 #include <array>
 
@@ -273,10 +274,13 @@ __global__ __launch_bounds__(256) void gemm_direct_kernel(
 // L2 (groups of 4 measured 1-2.5% faster than 8 on random data, 16 and 32
 // slower).
 
-template <int MODE, int KT_, int NB_>
+template <int MODE, int KT_, int NB_, int WAVES_>
 struct PipeCfg {
   static constexpr int KT = KT_;                      // K elements per stage
   static constexpr int NB = NB_;                      // ring depth
+  static constexpr int WAVES = WAVES_;                // waves per workgroup (one or two per SIMD)
+  static constexpr int TM = WAVES == 8 ? 2 : 4;       // 32-row MFMA tiles of X per wave (W: always 4)
+  static constexpr int NT = 4 * TM;                   // MFMAs per step and wave
   static constexpr int BPL = KT / 64;                 // blocks per lane slot per stage
   static constexpr int W_RB = KT / 2;                 // FP4 row bytes per stage
   static constexpr int X_RB = MODE == 0 ? KT / 2 : KT;  // FP4 / FP8 row bytes per stage
@@ -285,14 +289,15 @@ struct PipeCfg {
   static constexpr int WS_OFF = X_OFF + 256 * X_RB;   // 256 scale dwords (one group)
   static constexpr int XS_OFF = WS_OFF + 1024;
   static constexpr int STAGE = XS_OFF + (MODE == 0 ? 1024 : 0);
-  static constexpr int W_INSTR = 256 * W_RB / 1024 / 4;   // 1 KiB copies per wave per stage
-  static constexpr int X_INSTR = 256 * X_RB / 1024 / 4;
-  static constexpr int S_INSTR = MODE == 0 ? 2 : 1;       // 256 B scale copies per wave
+  static constexpr int W_INSTR = 256 * W_RB / 1024 / WAVES;   // 1 KiB copies per wave per stage
+  static constexpr int X_INSTR = 256 * X_RB / 1024 / WAVES;
+  static constexpr int S_INSTR = (MODE == 0 ? 8 : 4) / WAVES;  // 256 B scale copies per wave
   static constexpr int PER_WAVE = W_INSTR + X_INSTR + S_INSTR;
   static_assert(KT == 64 || KT == 128, "stage of one or two blocks per lane slot");
   static_assert(NB >= 3 && NB <= 8, "ring depth");
   static_assert(NB * STAGE <= 160 * 1024, "LDS");
   static_assert(KT == 128 || NB % 2 == 0, "half-group stages alternate scale bytes");
+  static_assert(WAVES == 4 || (WAVES == 8 && MODE == 0), "two waves per SIMD: W4A4");
 };
 
 // LDS placement of 16-byte chunk c of `row` in a tile with rows of RB bytes:
@@ -371,17 +376,18 @@ __device__ __forceinline__ void lds_dma4(const i32x4& rs, uint32_t lds, uint32_t
                :: "s"(lds), "v"(voff), "s"(rs) : "memory", "m0");
 }
 
-// Operand fragments of one MFMA step (4 W row groups, 4 X row groups) and the
-// scale registers of a stage (one 16-bit pair per row group for KT = 128,
+// Operand fragments of one MFMA step (4 W row groups, TM X row groups) and
+// the scale registers of a stage (one 16-bit pair per row group for KT = 128,
 // one byte for KT = 64).
-template <int MODE>
+template <int MODE, int TM>
 struct StepData {
   uint4 a[4];
-  uint4 b[MODE == 0 ? 4 : 8];
+  uint4 b[MODE == 0 ? TM : 2 * TM];
 };
+template <int TM>
 struct StageScales {
   uint32_t ws[4];
-  uint32_t xs[4];
+  uint32_t xs[TM];
 };
 
 typedef float v4f __attribute__((ext_vector_type(4)));
@@ -474,15 +480,17 @@ __device__ __forceinline__ void buf_store16(const i32x4& rs, uint32_t voff, cons
 // steps of the stage read chunks {0, 2} and {1, 3} of the row, as both
 // operands do). The stage's scale copies go out of range: they write zeros
 // and read nothing, and keep the copy count of every stage the same.
-template <int MODE, int KT, int NB, bool GELU, bool BIAS, bool QOUT, bool LRB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_pipe_kernel(
+template <int MODE, int KT, int NB, bool GELU, bool BIAS, bool QOUT, bool LRB, int WAVES>
+__global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(WAVES / 4, WAVES / 4))) void
+gemm_pipe_kernel(
     const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws,
     const uint8_t* __restrict__ aq, const void* __restrict__ asc,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, uint8_t* __restrict__ y_scales,
     const float* __restrict__ out_amax, int M, int N, int K, int tiles_m, int tiles_n,
     const uint16_t* __restrict__ lr_t, const uint16_t* __restrict__ lr_l2, int lr_rank) {
-  using C = PipeCfg<MODE, KT, NB>;
-  static_assert(!LRB || (MODE == 0 && KT == 128), "the branch stages take the shape of a W4A4 code stage");
+  using C = PipeCfg<MODE, KT, NB, WAVES>;
+  constexpr int TM = C::TM, NT = C::NT;
+  static_assert(!LRB || (MODE == 0 && KT == 128 && WAVES == 4), "the branch stages take the shape of a W4A4 code stage");
   // ring of NB stage slots, then two tile-parameter blocks: bias slice (512
   // bytes), a sink for the unused waves' copies (512), token scales (1024, FP8)
   constexpr int P_BIAS = 0, P_SINK = 512, P_TOK = 1024;
@@ -490,13 +498,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int PARAM_OFF = NB * C::STAGE;
   // The epilogue runs inside the next tile's first stage while the ring is
   // busy (see below), so it stages its results through a small area of its
-  // own, per wave: W4A4 32 rows x 144 bytes (a 64-column tile pair), W4A8 32
-  // rows x 72 bytes (one 32-column MFMA tile in bf16, or a tile pair of
-  // static FP8 codes; the larger W4A8 ring leaves 9 KiB).
-  constexpr int EV_PITCH = MODE == 0 ? 144 : 72;
-  constexpr int EV_BYTES = 32 * EV_PITCH;
+  // own, per wave: W4A4 with four waves 32 rows x 144 bytes (a 64-column tile
+  // pair); W4A8, and W4A4 with eight waves, 32 rows x 72 bytes (one 32-column
+  // MFMA tile in bf16, or a tile pair of static FP8 codes: the larger W4A8
+  // ring leaves 9 KiB, eight staging areas 18 KiB); MXFP4 output 32 rows x 80
+  // bytes (one code panel of 32 rows).
+  constexpr int EV_PITCH = MODE == 0 && WAVES == 4 ? 144 : 72;
+  constexpr int EV_BYTES = 32 * (MODE == 0 && QOUT && EV_PITCH < 80 ? 80 : EV_PITCH);
   constexpr int EV_OFF = PARAM_OFF + 2 * PARAM_BYTES;
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[EV_OFF + 4 * EV_BYTES];
+  static_assert(EV_OFF + WAVES * EV_BYTES <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[EV_OFF + WAVES * EV_BYTES];
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -563,12 +574,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const uint32_t x_stage = MODE == 0 ? (uint32_t)M * C::X_RB : (uint32_t)C::X_RB;
   // Scales (group-major, 128-element groups): the tile's 256 dwords of group
   // gi are contiguous at byte (gi * rows + base) * 4; wave w copies dwords
-  // 64 w .. 64 w + 63. A 64-element stage uses half of its group's bytes.
-  // Past the last row the dwords belong to other rows (or read as zero at the
-  // end of the buffer) and only feed outputs that are never stored.
-  const uint32_t vs = (uint32_t)(wave * 64 + lane) * 4u;
+  // 64 w .. 64 w + 63 of both operands (four waves), or of the W scales
+  // (waves 0-3 of eight) or X scales (waves 4-7, dwords 64 (w - 4) ..). A
+  // 64-element stage uses half of its group's bytes. Past the last row the
+  // dwords belong to other rows (or read as zero at the end of the buffer) and
+  // only feed outputs that are never stored.
+  const uint32_t vs = (uint32_t)((wave & 3) * 64 + lane) * 4u;
   const uint32_t ws_group = (uint32_t)N * 4u;
   const uint32_t xs_group = (uint32_t)M * 4u;
+  // eight waves: the operand whose scales this wave copies, fixed per wave
+  // (chosen here with masks, so that the copy in the MFMA sequence is one
+  // select on `live` like the others: a select of these inside the sequence
+  // became a branch, which splits the interleaved block)
+  const uint32_t sc_w = 0u - (uint32_t)(wave < 4);  // all ones: W scales
+  const uint32_t sc_group = (ws_group & sc_w) | (xs_group & ~sc_w);
+  const uint32_t sc_lds = (uint32_t)(wave < 4 ? C::WS_OFF : C::XS_OFF) + (uint32_t)(wave & 3) * 256u;
 
   // Whole-operand buffer resources: rows past M or N fall outside them.
   const i32x4 rw = make_rsrc(wq, w_row * (uint32_t)N);
@@ -577,6 +597,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const i32x4 rxs = make_rsrc(asc, MODE == 0 ? (uint32_t)KB * (uint32_t)M : 0u);
   const i32x4 rl2 = make_rsrc(lr_l2, lr_pitch * (uint32_t)N);
   const i32x4 rlt = make_rsrc(lr_t, lr_pitch * (uint32_t)M);
+  const i32x4 rsc = wave < 4 ? rws : rxs;  // eight waves: this wave's scale operand
 
   // ---- copy cursor: the stage (tile cp_k, stage cp_s) whose copies come
   // next, with the byte offsets of its tile in the W, X and scale operands.
@@ -628,6 +649,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       } else {
         lds_dma16(rx, base + C::X_OFF + (wave * C::X_INSTR + qx) * 1024, vx[qx] + so);
       }
+    } else if (WAVES == 8) {
+      // the offset is below 2^31, so or-ing in the top bit puts it out of range
+      // (a select of the computed offset here compiles to a branch)
+      const uint32_t row0 = (cp_nb & sc_w) | (cp_mb & ~sc_w);
+      const uint32_t so = (row0 * 4u + (uint32_t)cp_s * sc_group) | (live ? 0u : oob);
+      lds_dma4(rsc, base + sc_lds, vs + so);
     } else if (q == C::W_INSTR + C::X_INSTR) {
       const uint32_t so = live && !br ? cp_nb * 4u + (uint32_t)(cp_s * KT / 128) * ws_group : oob;
       lds_dma4(rws, base + C::WS_OFF + wave * 256, vs + so);
@@ -648,7 +675,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   };
   // Tile parameters of tile k into parameter block k & 1 (issued in stage 1
   // of tile k - 1, read in the first stage of tile k + 1): the bias slice
-  // (waves 0, 1: 256 bytes each; waves 2, 3 copy nothing into the sink) and,
+  // (waves 0, 1: 256 bytes each; the others copy nothing into the sink) and,
   // for FP8 activations, the 256 token scales (256 bytes per wave). Always
   // EPI_PARAM_OPS copies per wave; no bias reads as zeros.
   constexpr int EPI_PARAM_OPS = MODE == 1 ? 2 : 1;
@@ -659,7 +686,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const uint32_t pb = lds_ring + PARAM_OFF + (uint32_t)(k & 1) * PARAM_BYTES;
     const uint32_t nb = (uint32_t)tn * 256u, mb = (uint32_t)tm * 256u;
     const i32x4 rb = make_rsrc(bias + nb, bias != nullptr ? ((uint32_t)N - nb) * 2u : 0u);
-    lds_dma4(rb, pb + (wave < 2 ? P_BIAS + wave * 256 : P_SINK + (wave - 2) * 256),
+    lds_dma4(rb, pb + (wave < 2 ? P_BIAS + wave * 256 : P_SINK + ((wave - 2) & 1) * 256),
              live && wave < 2 ? (uint32_t)(wave * 256 + lane * 4) : 0x80000000u);
     if constexpr (MODE == 1) {
       const i32x4 rt = make_rsrc(static_cast<const uint8_t*>(asc) + mb * 4u, ((uint32_t)M - mb) * 4u);
@@ -667,39 +694,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
   };
 
-  v16f acc[4][4];
+  v16f acc[4][TM];
 
-  const int wrow0 = wn * 128 + r;  // + 32 i
-  const int xrow0 = wm * 128 + r;  // + 32 j
+  const int wrow0 = wn * 128 + r;       // + 32 i
+  const int xrow0 = wm * 32 * TM + r;   // + 32 j
 
   // LDS reads are issued one item at a time between MFMAs, in the order the
   // MFMAs consume them: an item is kind * 16 + index with kinds W fragment
   // (a[i]), X fragment (b[j]; for FP8 b[2j] / b[2j+1] are the two halves of
   // row group j), W scale (ws[i]) and X scale (xs[j]).
   constexpr int KA = 0, KBX = 16, KWS = 32, KXS = 48;
-  constexpr int DATA_ITEMS = MODE == 0 ? 8 : 12;   // fragments of one step
-  constexpr int STAGE_ITEMS = 16;                   // step-0 fragments + scales of a stage
-  constexpr int kStepOrder[2][12] = {
+  // four waves: W4A4, W4A8; eight waves: W4A4 (two X row groups per wave)
+  constexpr int OI = WAVES == 8 ? 2 : MODE;
+  constexpr int DATA_ITEMS = OI == 0 ? 8 : OI == 1 ? 12 : 6;   // fragments of one step
+  constexpr int STAGE_ITEMS = OI == 2 ? 12 : 16;               // step-0 fragments + scales of a stage
+  constexpr int kStepOrder[3][12] = {
       {KA + 0, KBX + 0, KBX + 1, KBX + 2, KBX + 3, KA + 1, KA + 2, KA + 3, -1, -1, -1, -1},
-      {KA + 0, KBX + 0, KBX + 1, KBX + 2, KBX + 3, KBX + 4, KBX + 5, KBX + 6, KBX + 7, KA + 1, KA + 2, KA + 3}};
-  constexpr int kStageOrder[2][16] = {
+      {KA + 0, KBX + 0, KBX + 1, KBX + 2, KBX + 3, KBX + 4, KBX + 5, KBX + 6, KBX + 7, KA + 1, KA + 2, KA + 3},
+      {KA + 0, KBX + 0, KBX + 1, KA + 1, KA + 2, KA + 3, -1, -1, -1, -1, -1, -1}};
+  constexpr int kStageOrder[3][16] = {
       {KA + 0, KBX + 0, KWS + 0, KXS + 0, KBX + 1, KXS + 1, KBX + 2, KXS + 2, KBX + 3, KXS + 3, KA + 1, KWS + 1,
        KA + 2, KWS + 2, KA + 3, KWS + 3},
       {KA + 0, KBX + 0, KBX + 1, KWS + 0, KBX + 2, KBX + 3, KBX + 4, KBX + 5, KBX + 6, KBX + 7, KA + 1, KWS + 1,
-       KA + 2, KWS + 2, KA + 3, KWS + 3}};
+       KA + 2, KWS + 2, KA + 3, KWS + 3},
+      {KA + 0, KBX + 0, KWS + 0, KXS + 0, KBX + 1, KXS + 1, KA + 1, KWS + 1, KA + 2, KWS + 2, KA + 3, KWS + 3,
+       -1, -1, -1, -1}};
   // Copy q of a stage goes after MFMA slot floor(SPAN q / PER_WAVE). With
-  // copies three or more stages ahead they spread over all 32 slots (a burst
-  // would fill the vector memory queue and stall the wave that also feeds the
-  // matrix pipe); two stages ahead, a copy issued late in its stage would be
-  // waited for almost at once, so they go out first.
-  constexpr int COPY_SPAN = NB - 1 >= 3 ? 32 : C::PER_WAVE;
+  // copies three or more stages ahead they spread over all 2 NT slots of the
+  // stage (a burst would fill the vector memory queue and stall the wave that
+  // also feeds the matrix pipe); two stages ahead, a copy issued late in its
+  // stage would be waited for almost at once, so they go out first.
+  constexpr int COPY_SPAN = NB - 1 >= 3 ? 2 * NT : C::PER_WAVE;
   constexpr auto kCopyAt = [] {
-    std::array<int, 32> at{};
-    for (int t = 0; t < 32; ++t) at[t] = -1;
+    std::array<int, 2 * NT> at{};
+    for (int t = 0; t < 2 * NT; ++t) at[t] = -1;
     for (int q = 0; q < C::PER_WAVE; ++q) at[(COPY_SPAN * q) / C::PER_WAVE] = q;
     return at;
   }();
-  static_assert(C::PER_WAVE <= 32, "one copy per MFMA slot at most");
+  static_assert(C::PER_WAVE <= 2 * NT, "one copy per MFMA slot at most");
   // Per-lane parts of the fragment offsets in a stage slot. Rows 32 apart
   // differ only in bits the chunk permutation does not use, so the offset of
   // row group idx is the lane part plus the constant 32 idx RB, which the
@@ -718,7 +750,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
   // scale dwords: row group idx adds 128 bytes; the lane's 16-bit pair is at + 2 g
   const uint32_t lofs_ws = C::WS_OFF + wrow0 * 4 + 2 * g, lofs_xs = C::XS_OFF + xrow0 * 4 + 2 * g;
-  auto read_item = [&](const uint8_t* base, int kk, int half, int code, StepData<MODE>& f, StageScales& sc) {
+  auto read_item = [&](const uint8_t* base, int kk, int half, int code, StepData<MODE, TM>& f,
+                       StageScales<TM>& sc) {
     const int kind = code & ~15, idx = code & 15;
     if (kind == KA) {
       f.a[idx] = *reinterpret_cast<const uint4*>(base + lofs_a[kk] + 32 * idx * C::W_RB);
@@ -738,8 +771,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
   };
 
-  // The 16 MFMAs of one step; after MFMA number k (0..15) `between(k)` may
-  // issue one deferred operation, and the order is pinned by a scheduling
+  // The NT MFMAs of one step; after MFMA number k (0 .. NT-1) `between(k)`
+  // may issue deferred operations, and the order is pinned by a scheduling
   // barrier so that the reads stay spread between the MFMAs.
   // `before(k)` runs before MFMA k; with `zero_tag` true the step starts the
   // tile's sums (accumulator input 0, an inline constant).
@@ -748,16 +781,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // step, the MFMA cannot be moved away from the work interleaved with it.
   // `order_tag` true takes the MFMAs j-outer (slot s = 4 j + i), so that a
   // 32-row group of the output is complete every 4 slots.
-  auto mfma_step_x = [&](const StepData<MODE>& f, const StageScales& sc, auto kk_tag, auto zero_tag, auto pin_tag,
-                         auto order_tag, auto&& before, auto&& between) {
+  auto mfma_step_x = [&](const StepData<MODE, TM>& f, const StageScales<TM>& sc, auto kk_tag, auto zero_tag,
+                         auto pin_tag, auto order_tag, auto&& before, auto&& between) {
     constexpr int KK = decltype(kk_tag)::value;
     constexpr bool ZERO = decltype(zero_tag)::value;
     constexpr bool PIN = decltype(pin_tag)::value;
     constexpr bool JOUT = decltype(order_tag)::value;
     constexpr int SEL = KT == 128 ? KK : 0;
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-      const int i = JOUT ? (s & 3) : (s >> 2), j = JOUT ? (s >> 2) : (s & 3);
+    for (int s = 0; s < NT; ++s) {
+      const int i = JOUT ? (s & 3) : (s / TM), j = JOUT ? (s >> 2) : (s % TM);
       {
         before(s);
         const v8i a = op_fp4(f.a[i]);
@@ -769,17 +802,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, op_fp8(f.b[2 * j], f.b[2 * j + 1]),
                                                                       ZERO ? v16f{} : acc[i][j], kFmtFp4, kFmtFp8,
                                                                       SEL, (int)sc.ws[i], SEL, (int)kUnitScales);
-        if constexpr (PIN) asm volatile("" ::"a"(acc[i][j]));
+        if constexpr (PIN && WAVES == 4) asm volatile("" ::"a"(acc[i][j]));
+        // (one element suffices to keep the MFMA in place; a whole 16-float
+        // vector is no valid operand of the host's "v" constraint)
+        if constexpr (PIN && WAVES == 8) asm volatile("" ::"v"(acc[i][j][0]));
         between(s);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
-  auto mfma_step = [&](const StepData<MODE>& f, const StageScales& sc, auto kk_tag, auto&& between) {
+  auto mfma_step = [&](const StepData<MODE, TM>& f, const StageScales<TM>& sc, auto kk_tag, auto&& between) {
     mfma_step_x(f, sc, kk_tag, std::false_type{}, std::false_type{}, std::false_type{}, [](int) {}, between);
   };
   // the 16 MFMAs of one step of a branch stage: bf16 operands, no scales
-  auto mfma_step_bf = [&](const StepData<MODE>& f, auto&& between) {
+  auto mfma_step_bf = [&](const StepData<MODE, TM>& f, auto&& between) {
 #pragma unroll
     for (int s = 0; s < 16; ++s) {
       const int i = s >> 2, j = s & 3;
@@ -791,12 +827,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
   };
 
-  // Epilogue stores per wave and tile (W4A4: 32 bf16 stores, or with QOUT per
-  // 32-row group two 1 KiB code stores and one scale store; W4A8: 32 bf16
-  // stores, or with QOUT 2 per tile pair and one store of row scales), the
-  // same whatever the shape: rows past M and columns past N get an offset
-  // the range check drops.
-  constexpr int EPI_STORES = MODE == 0 ? (QOUT ? 12 : 32) : (QOUT ? 17 : 32);
+  // Epilogue stores per wave and tile (W4A4: 32 bf16 stores with four waves,
+  // 2 per MFMA tile with eight, or with QOUT per 32-row group two 1 KiB code
+  // stores and one scale store; W4A8: 32 bf16 stores, or with QOUT 2 per tile
+  // pair and one store of row scales), the same whatever the shape: rows past
+  // M and columns past N get an offset the range check drops.
+  constexpr int EPI_STORES = MODE == 0 ? (QOUT ? 3 * TM : WAVES == 4 ? 32 : 2 * NT) : (QOUT ? 17 : 32);
   constexpr int EPI_OPS = EPI_STORES + EPI_PARAM_OPS;
   const i32x4 ry = make_rsrc(y, (uint32_t)M * (uint32_t)N * (MODE == 1 && QOUT ? 1u : 2u));
   Fp8Out fo{};
@@ -818,10 +854,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(WAIT_BASE));
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-  StepData<MODE> cur;
-  StageScales cur_sc;
+  StepData<MODE, TM> cur;
+  StageScales<TM> cur_sc;
 #pragma unroll
-  for (int k = 0; k < STAGE_ITEMS; ++k) read_item(ring, 0, 0, kStageOrder[MODE][k], cur, cur_sc);
+  for (int k = 0; k < STAGE_ITEMS; ++k) read_item(ring, 0, 0, kStageOrder[OI][k], cur, cur_sc);
 
   {
     // ---- The epilogue of tile t-1 runs inside the first stage of
@@ -861,8 +897,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       for (int t2 = 0; t2 < 4; ++t2)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          float v0 = acc_read(acc[i][j][4 * t2 + 2 * h]);
-          float v1 = acc_read(acc[i][j][4 * t2 + 2 * h + 1]);
+          // four waves hold the sums in accumulator registers, eight in VGPRs
+          float v0, v1;
+          if constexpr (WAVES == 4) {
+            v0 = acc_read(acc[i][j][4 * t2 + 2 * h]);
+            v1 = acc_read(acc[i][j][4 * t2 + 2 * h + 1]);
+          } else {
+            v0 = acc[i][j][4 * t2 + 2 * h];
+            v1 = acc[i][j][4 * t2 + 2 * h + 1];
+          }
           if constexpr (MODE == 1) {
             v0 = BIAS ? __builtin_fmaf(v0, sm, b[4 * t2 + 2 * h]) : v0 * sm;
             v1 = BIAS ? __builtin_fmaf(v1, sm, b[4 * t2 + 2 * h + 1]) : v1 * sm;
@@ -919,7 +962,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     // 0..12 and the stores of tile t (2 each) after slot t + 1, tile 15's in
     // the second step, so tiles 11..15 come after the last copy.
     constexpr int kLastCopySlot = COPY_SPAN * (C::PER_WAVE - 1) / C::PER_WAVE;
-    static_assert(MODE == 1 || kLastCopySlot > 16, "W4A4 epilogue stores end in slot 16");
+    static_assert(MODE == 1 || kLastCopySlot > NT, "W4A4 epilogue stores end in slot NT");
     static_assert(MODE == 0 || (kLastCopySlot >= 1 && kLastCopySlot <= 16), "W4A8 copies within the first step");
     // (W4A8 static FP8 output: tile pairs complete at slots 4 + j and 12 + j
     // and are stored one slot later, so 4 pairs after slot 12.)
@@ -955,22 +998,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       const uint8_t* here = ring + slot * C::STAGE;
       const uint8_t* next = ring + slot_next * C::STAGE;
       const int next_half = (G + 1) & 1;
-      StepData<MODE> nxt;
-      StageScales nxt_sc;
+      StepData<MODE, TM> nxt;
+      StageScales<TM> nxt_sc;
       auto between0 = [&](int k) {
-        if (k < DATA_ITEMS) read_item(here, 1, 0, kStepOrder[MODE][k], nxt, nxt_sc);
+        if (k < DATA_ITEMS) read_item(here, 1, 0, kStepOrder[OI][k], nxt, nxt_sc);
         if (kCopyAt[k] >= 0) issue_one(kCopyAt[k], slot_refill);
       };
+      // the next stage's STAGE_ITEMS reads spread over the NT slots of step 1
       auto between1 = [&](int k) {
-        read_item(next, 0, next_half, kStageOrder[MODE][k], cur, cur_sc);
-        if (kCopyAt[16 + k] >= 0) issue_one(kCopyAt[16 + k], slot_refill);
+#pragma unroll
+        for (int it = k * STAGE_ITEMS / NT; it < (k + 1) * STAGE_ITEMS / NT; ++it)
+          read_item(next, 0, next_half, kStageOrder[OI][it], cur, cur_sc);
+        if (kCopyAt[NT + k] >= 0) issue_one(kCopyAt[NT + k], slot_refill);
       };
       if constexpr (!FIRST && BR) {
         mfma_step_bf(cur, between0);
         mfma_step_bf(nxt, between1);
       } else if constexpr (!FIRST) {
         mfma_step(cur, cur_sc, std::integral_constant<int, 0>{}, between0);
-        const StageScales sc1 = cur_sc;
+        const StageScales<TM> sc1 = cur_sc;
         mfma_step(nxt, sc1, std::integral_constant<int, 1>{}, between1);
       } else {
         // the cursor is in this tile (stage D): the tile it moves to next is
@@ -996,12 +1042,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           const int n_q = ptn * 256 + wn * 128;
           const uint32_t q_bad = ev_live && n_q < N ? 0u : 0x80000000u;
           const uint32_t q_pan = (uint32_t)(n_q >> 7);
-          const int m_q = ptm * 256 + wm * 128;
+          const int m_q = ptm * 256 + wm * 32 * TM;
           const i32x4 rq = make_rsrc(y, (uint32_t)M * (uint32_t)N / 2u);
           const i32x4 rsq = make_rsrc(y_scales, (uint32_t)(N >> 7) * (uint32_t)M * 4u);
           const uint8_t* prm = ring + PARAM_OFF + ((tile_k - 1) & 1) * PARAM_BYTES;
-          v16f bq[4];
-          if constexpr (BIAS) {
+          // bias of the four column tiles: held for the stage with four waves,
+          // read per tile with eight (whose 256 registers have no room for them)
+          v16f bq[WAVES == 4 ? 4 : 1];
+          if constexpr (BIAS && WAVES == 4) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) ev_bias(prm, i, bq[i]);
           }
@@ -1021,7 +1069,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           auto beforeq = [&](int sl) {
             const int i = sl & 3, j = sl >> 2;
             uint32_t pk[4][2];
-            ev_tile(i, j, bq[i], 1.0f, pk);
+            if constexpr (WAVES == 4) {
+              ev_tile(i, j, bq[i], 1.0f, pk);
+            } else {
+              if constexpr (BIAS) ev_bias(prm, i, bq[0]);
+              ev_tile(i, j, bq[0], 1.0f, pk);
+            }
             typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
             u16x2 m2 = {0, 0};
 #pragma unroll
@@ -1068,11 +1121,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           };
           mfma_step_x(cur, cur_sc, std::integral_constant<int, 0>{}, std::true_type{}, std::true_type{},
                       std::true_type{}, beforeq, afterq);
-          const StageScales sc1 = cur_sc;
+          const StageScales<TM> sc1 = cur_sc;
           mfma_step_x(nxt, sc1, std::integral_constant<int, 1>{}, std::false_type{}, std::true_type{},
                       std::false_type{}, [](int) {}, [&](int k) {
                         between1(k);
-                        if (k == 0) group_store(3);
+                        if (k == 0) group_store(TM - 1);
                       });
         } else if constexpr (MODE == 1 && QOUT) {
           // W4A8 with static FP8 output: each tile's bf16 values (token scale,
@@ -1146,7 +1199,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           };
           mfma_step_x(cur, cur_sc, std::integral_constant<int, 0>{}, std::true_type{}, std::true_type{},
                       std::false_type{}, before8, after8);
-          const StageScales sc1 = cur_sc;
+          const StageScales<TM> sc1 = cur_sc;
           mfma_step_x(nxt, sc1, std::integral_constant<int, 1>{}, std::false_type{}, std::true_type{},
                       std::false_type{}, [](int) {}, [&](int k) {
                         between1(k);
@@ -1195,11 +1248,58 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           };
           mfma_step_x(cur, cur_sc, std::integral_constant<int, 0>{}, std::true_type{}, std::true_type{},
                       std::false_type{}, before8, after8);
-          const StageScales sc1 = cur_sc;
+          const StageScales<TM> sc1 = cur_sc;
           mfma_step_x(nxt, sc1, std::integral_constant<int, 1>{}, std::false_type{}, std::true_type{},
                       std::false_type{}, [](int) {}, [&](int k) {
                         between1(k);
                         if (k == 0) tile_store(15);
+                      });
+        } else if constexpr (WAVES == 8) {
+          // W4A4, bf16 output, eight waves: tile k = 2 i + j (i outer) through
+          // the staging area after MFMA slot k, its two stores of 16 rows x 64
+          // bytes after slot k + 1 (tile 7's after the second step's first
+          // MFMA), as in the W4A8 epilogue without the token scale. Rows past M
+          // fall past the end of the output (dropped by the range check);
+          // columns past N (or no tile at all) get the offset's top bit.
+          const int ev_m0 = ptm * 256 + wm * 32 * TM + (lane >> 2);  // + 32 j + 16 st
+          const int ev_n0 = ptn * 256 + wn * 128 + (lane & 3) * 8;   // + 32 i
+          const uint8_t* prm = ring + PARAM_OFF + ((tile_k - 1) & 1) * PARAM_BYTES;
+          v16f c_cur, c_nxt;
+          if constexpr (BIAS) ev_bias(prm, 0, c_cur);
+          uint32_t pk[4][2];
+          uint4 rd[2];
+          auto tile_store = [&](int k) {
+            const int i = k / TM, j = k % TM;
+            const uint32_t bad = ev_live && ev_n0 + 32 * i < N ? 0u : 0x80000000u;
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+              const uint32_t off = ((uint32_t)(ev_m0 + 32 * j + 16 * st) * (uint32_t)N + (uint32_t)(ev_n0 + 32 * i)) * 2u;
+              buf_store16(ry, off | bad, rd[st]);
+            }
+          };
+          auto before8 = [&](int k) {
+            const int i = k / TM, j = k % TM;
+            if (BIAS && j == 0 && i > 0) c_cur = c_nxt;
+            ev_tile(i, j, c_cur, 1.0f, pk);
+          };
+          auto after8 = [&](int k) {
+            const int i = k / TM, j = k % TM;
+            between0(k);
+            if (k > 0) tile_store(k - 1);
+            ev8_write(pk);
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            ev8_read(rd);
+            // the next tile's writes stay behind these reads
+            __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+            if (BIAS && j == 0 && i < 3) ev_bias(prm, i + 1, c_nxt);
+          };
+          mfma_step_x(cur, cur_sc, std::integral_constant<int, 0>{}, std::true_type{}, std::true_type{},
+                      std::false_type{}, before8, after8);
+          const StageScales<TM> sc1 = cur_sc;
+          mfma_step_x(nxt, sc1, std::integral_constant<int, 1>{}, std::false_type{}, std::true_type{},
+                      std::false_type{}, [](int) {}, [&](int k) {
+                        between1(k);
+                        if (k == 0) tile_store(NT - 1);
                       });
         } else {
           // byte offset of the lane's first store (+ 32 j rows + 8 it rows + 64 h
@@ -1244,7 +1344,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           };
           mfma_step_x(cur, cur_sc, std::integral_constant<int, 0>{}, std::true_type{}, std::true_type{},
                       std::false_type{}, before0, after0);
-          const StageScales sc1 = cur_sc;
+          const StageScales<TM> sc1 = cur_sc;
           mfma_step_x(nxt, sc1, std::integral_constant<int, 1>{}, std::false_type{}, std::true_type{},
                       std::false_type{}, [](int) {}, [&](int k) {
                         between1(k);
@@ -1288,7 +1388,7 @@ static int device_cu_count() {
   return cus;
 }
 
-template <int MODE, int KT, int NB, bool QOUT = false, bool LRB = false>
+template <int MODE, int KT, int NB, int WAVES, bool QOUT = false, bool LRB = false>
 static hipError_t launch_pipe(const void* aq, const void* as, const void* wq, const void* ws, const void* bias,
                               int epi, void* y, int64_t M, int64_t N, int64_t K, hipStream_t s,
                               void* y_scales = nullptr, const float* out_amax = nullptr,
@@ -1302,8 +1402,8 @@ static hipError_t launch_pipe(const void* aq, const void* as, const void* wq, co
   // the epilogue work it does
   auto go = [&](auto gelu_tag, auto bias_tag) {
     hipLaunchKernelGGL(
-        (gemm_pipe_kernel<MODE, KT, NB, decltype(gelu_tag)::value, decltype(bias_tag)::value, QOUT, LRB>),
-        dim3(grid), dim3(256), 0, s, static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws),
+        (gemm_pipe_kernel<MODE, KT, NB, decltype(gelu_tag)::value, decltype(bias_tag)::value, QOUT, LRB, WAVES>),
+        dim3(grid), dim3(64 * WAVES), 0, s, static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws),
         static_cast<const uint8_t*>(aq), as, static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y),
         static_cast<uint8_t*>(y_scales), out_amax, (int)M, (int)N, (int)K, tiles_m, tiles_n,
         static_cast<const uint16_t*>(lr_t), static_cast<const uint16_t*>(lr_l2), lr_rank);
@@ -1331,9 +1431,29 @@ static hipError_t launch_direct(const void* aq, const void* as, const void* wq, 
 }
 
 // Stage shape of the pipelined kernel per mode: K elements per stage and LDS
-// ring depth (both chosen from measurements on MI355X).
+// ring depth (chosen from measurements on MI355X). W4A4 runs one wave per SIMD
+// (four per workgroup, 128 x 128 outputs each) or two (eight, 128 x 64 each:
+// one wave's copies, LDS reads, barrier wait and epilogue overlap the other's
+// MFMAs); W4A8, whose ring leaves no room for eight staging areas, and the
+// SVDQuant branch stages run one wave per SIMD.
 constexpr int kPipeKT[2] = {128, 128};
 constexpr int kPipeNB[2] = {4, 3};
+
+// W4A4 wave count per launch. Under sustained load the board holds its power
+// cap (1400 W measured on random data) by lowering the clock, and there the
+// eight-wave kernel, busier but with 1.5x the LDS reads per MFMA, runs no
+// faster than the four-wave one (A14B stack step 1003.6 / 1004.5 ms). Short
+// launches finish at a higher clock, where the eight-wave kernel's shorter
+// epilogue stage (6.0k against 8.1k cycles) and better overlap pay: 3-4% on
+// the TI2V-5B linears, 8% on the 512-token text GEMMs, measured interleaved.
+// MXQ_W4A4_WAVES=4 or 8 fixes the choice (read at every call, so tests can
+// run either kernel on any shape).
+constexpr double kEightWaveMaxFlops = 2e12;
+static bool w4a4_eight_waves(int64_t M, int64_t N, int64_t K) {
+  const char* v = getenv("MXQ_W4A4_WAVES");
+  if (v != nullptr && (v[0] == '4' || v[0] == '8') && v[1] == '\0') return v[0] == '8';
+  return 2.0 * (double)M * (double)N * (double)K < kEightWaveMaxFlops;
+}
 
 // The pipelined kernel needs whole stages along K, at least NB of them (one
 // tile's epilogue is over before the next one starts), and N in multiples of 8
@@ -1351,10 +1471,14 @@ hipError_t launch_gemm(int mode, const void* a_codes, const void* a_scales,
                        int epilogue, void* y, int64_t M, int64_t N, int64_t K,
                        hipStream_t s) {
   if (use_lds(mode, M, N, K)) {
+    if (mode == 0 && w4a4_eight_waves(M, N, K))
+      return launch_pipe<0, kPipeKT[0], kPipeNB[0], 8>(a_codes, a_scales, w_codes, w_scales, bias, epilogue, y, M, N,
+                                                       K, s);
     if (mode == 0)
-      return launch_pipe<0, kPipeKT[0], kPipeNB[0]>(a_codes, a_scales, w_codes, w_scales, bias, epilogue, y, M, N,
-                                                    K, s);
-    return launch_pipe<1, kPipeKT[1], kPipeNB[1]>(a_codes, a_scales, w_codes, w_scales, bias, epilogue, y, M, N, K, s);
+      return launch_pipe<0, kPipeKT[0], kPipeNB[0], 4>(a_codes, a_scales, w_codes, w_scales, bias, epilogue, y, M, N,
+                                                       K, s);
+    return launch_pipe<1, kPipeKT[1], kPipeNB[1], 4>(a_codes, a_scales, w_codes, w_scales, bias, epilogue, y, M, N,
+                                                     K, s);
   }
   if (mode == 0)
     return launch_direct<0, 2, 2>(a_codes, a_scales, w_codes, w_scales, bias, epilogue, y, M, N, K, s);
@@ -1366,8 +1490,11 @@ bool gemm_mxfp4_out_supported(int64_t M, int64_t N, int64_t K) { return use_lds(
 hipError_t launch_gemm_mxfp4_out(const void* a_codes, const void* a_scales, const void* w_codes,
                                  const void* w_scales, const void* bias, int epilogue, void* y_codes,
                                  void* y_scales, int64_t M, int64_t N, int64_t K, hipStream_t s) {
-  return launch_pipe<0, kPipeKT[0], kPipeNB[0], true>(a_codes, a_scales, w_codes, w_scales, bias, epilogue, y_codes,
-                                                      M, N, K, s, y_scales);
+  if (w4a4_eight_waves(M, N, K))
+    return launch_pipe<0, kPipeKT[0], kPipeNB[0], 8, true>(a_codes, a_scales, w_codes, w_scales, bias, epilogue,
+                                                           y_codes, M, N, K, s, y_scales);
+  return launch_pipe<0, kPipeKT[0], kPipeNB[0], 4, true>(a_codes, a_scales, w_codes, w_scales, bias, epilogue,
+                                                         y_codes, M, N, K, s, y_scales);
 }
 
 // N is the next layer's K: a multiple of 32
@@ -1377,8 +1504,8 @@ hipError_t launch_gemm_fp8_static_out(const void* a_codes, const void* a_scales,
                                       const void* w_scales, const void* bias, int epilogue, const float* out_amax,
                                       void* y_codes, void* y_scales, int64_t M, int64_t N, int64_t K,
                                       hipStream_t s) {
-  return launch_pipe<1, kPipeKT[1], kPipeNB[1], true>(a_codes, a_scales, w_codes, w_scales, bias, epilogue, y_codes,
-                                                      M, N, K, s, y_scales, out_amax);
+  return launch_pipe<1, kPipeKT[1], kPipeNB[1], 4, true>(a_codes, a_scales, w_codes, w_scales, bias, epilogue,
+                                                         y_codes, M, N, K, s, y_scales, out_amax);
 }
 
 // The branch rides on the pipelined W4A4 kernel (its shapes only); with
@@ -1392,15 +1519,17 @@ hipError_t launch_gemm_lowrank(const void* a_codes, const void* a_scales, const 
                                int epilogue, void* y, void* y_scales, int64_t M, int64_t N, int64_t K,
                                hipStream_t s) {
   if (y_scales != nullptr)
-    return launch_pipe<0, kPipeKT[0], kPipeNB[0], true, true>(a_codes, a_scales, w_codes, w_scales, bias, epilogue,
-                                                              y, M, N, K, s, y_scales, nullptr, t, l2, (int)r);
-  return launch_pipe<0, kPipeKT[0], kPipeNB[0], false, true>(a_codes, a_scales, w_codes, w_scales, bias, epilogue, y,
-                                                             M, N, K, s, nullptr, nullptr, t, l2, (int)r);
+    return launch_pipe<0, kPipeKT[0], kPipeNB[0], 4, true, true>(a_codes, a_scales, w_codes, w_scales, bias,
+                                                                 epilogue, y, M, N, K, s, y_scales, nullptr, t, l2,
+                                                                 (int)r);
+  return launch_pipe<0, kPipeKT[0], kPipeNB[0], 4, false, true>(a_codes, a_scales, w_codes, w_scales, bias, epilogue,
+                                                                y, M, N, K, s, nullptr, nullptr, t, l2, (int)r);
 }
 
 const char* gemm_variant_name(int mode, int64_t M, int64_t N, int64_t K) {
   if (use_lds(mode, M, N, K))
-    return mode == 0 ? "pipe_w4a4_wg256x256_wave128x128" : "pipe_w4a8_wg256x256_wave128x128";
+    return mode == 0 ? (w4a4_eight_waves(M, N, K) ? "pipe_w4a4_wg256x256_wave128x64" : "pipe_w4a4_wg256x256_wave128x128")
+                     : "pipe_w4a8_wg256x256_wave128x128";
   return mode == 0 ? "direct_w4a4_wg128x128_wave64x64" : "direct_w4a8_wg128x128_wave64x64";
 }
 

@@ -77,6 +77,11 @@ hipError_t launch_gemm_lowrank(const void* a_codes, const void* a_scales, const 
                                int epilogue, void* y, void* y_scales, int64_t M, int64_t N, int64_t K,
                                hipStream_t s);
 
+// MXFP4 codes and scales between the library layout (code panels, group-major
+// scales) and the canonical row-major one ([rows][K/2], [rows][K/32]).
+hipError_t launch_mxfp4_layout(bool to_canonical, const void* src_codes, const void* src_scales, int64_t rows,
+                               int64_t K, void* dst_codes, void* dst_scales, hipStream_t s);
+
 // Name of the GEMM kernel variant launch_gemm picks for a shape (for logs).
 const char* gemm_variant_name(int mode, int64_t M, int64_t N, int64_t K);
 

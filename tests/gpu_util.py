@@ -1,6 +1,9 @@
 """Helpers for the GPU parity tests: host<->device transfer of bf16 bit
 arrays, and oracle comparisons on full or sampled rows."""
 
+import contextlib
+import os
+
 import numpy as np
 import torch
 
@@ -85,3 +88,22 @@ def assert_output_close(y_bits, y_ref, what):
     assert rep["finite"], f"{what}: non-finite output"
     assert rep["worst_ratio"] <= 1.0, f"{what}: tolerance exceeded {rep}"
     return rep
+
+
+# The pipelined W4A4 GEMM has a four-wave and an eight-wave kernel; the
+# library picks one by the launch's size, and MXQ_W4A4_WAVES (read at every
+# call) fixes the choice so that either one can be tested on any shape.
+W4A4_WAVE_KERNEL = {4: "pipe_w4a4_wg256x256_wave128x128", 8: "pipe_w4a4_wg256x256_wave128x64"}
+
+
+@contextlib.contextmanager
+def w4a4_waves(waves):
+    old = os.environ.get("MXQ_W4A4_WAVES")
+    os.environ["MXQ_W4A4_WAVES"] = str(waves)
+    try:
+        yield
+    finally:
+        if old is None:
+            os.environ.pop("MXQ_W4A4_WAVES", None)
+        else:
+            os.environ["MXQ_W4A4_WAVES"] = old

@@ -25,14 +25,14 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = mxq.lib()
     names = declared_functions()
-    assert len(names) == 27, names
+    assert len(names) == 29, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(mxq._SIGS)
 
 
 def test_status_strings_and_version():
-    assert mxq.version() == 10000
+    assert mxq.version() == 10100
     for st in range(8):
         assert mxq.status_string(st)
     assert mxq.status_string(99) == "unknown status"
@@ -55,6 +55,24 @@ def test_quantize_act_rejects_modes_shapes_nulls_alignment():
     assert L.mxq_quantize_act(mxq.W4A8, FAKE, 4, 64, 68, FAKE, FAKE, S) == mxq.ERR_ALIGN  # ld % 8
     # empty problems enqueue nothing and accept null pointers
     assert L.mxq_quantize_act(mxq.W4A4, None, 0, 64, 64, None, None, S) == mxq.OK
+
+
+def test_mxfp4_layout_validation():
+    L = mxq.lib()
+    S = None
+    for fn in (L.mxq_mxfp4_to_canonical, L.mxq_mxfp4_from_canonical):
+        for k in (0, 16, 48, -32):
+            assert fn(FAKE, FAKE, 4, k, FAKE, FAKE, S) == mxq.ERR_SHAPE
+        assert fn(FAKE, FAKE, -1, 64, FAKE, FAKE, S) == mxq.ERR_SHAPE
+        assert fn(FAKE, FAKE, 1 << 31, 64, FAKE, FAKE, S) == mxq.ERR_SHAPE
+        for i in range(4):
+            args = [FAKE] * 4
+            args[i] = None
+            assert fn(args[0], args[1], 4, 64, args[2], args[3], S) == mxq.ERR_NULL
+            args[i] = FAKE_ODD
+            assert fn(args[0], args[1], 4, 64, args[2], args[3], S) == mxq.ERR_ALIGN
+        # no rows: nothing enqueued, null pointers accepted
+        assert fn(None, None, 0, 64, None, None, S) == mxq.OK
 
 
 def test_weight_pack_and_gemm_validation():

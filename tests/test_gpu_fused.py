@@ -22,7 +22,7 @@ import torch
 import mx_bit_quantized_amd as mxq
 import oracle
 import synth
-from gpu_util import code_rows, dev_bf16, host_bits, host_u8
+from gpu_util import W4A4_WAVE_KERNEL, code_rows, dev_bf16, host_bits, host_u8, w4a4_waves
 
 pytestmark = pytest.mark.gpu
 
@@ -65,25 +65,30 @@ def _both_paths(m, n, k, seed, epilogue, bias):
 FUSED_SHAPES = [(256, 512, 512), (300, 640, 640), (600, 1280, 896), (2250, 7424, 512), (4352, 4096, 640)]
 
 
+@pytest.mark.parametrize("waves", [4, 8])
 @pytest.mark.parametrize("m,n,k", FUSED_SHAPES)
 @pytest.mark.parametrize("epilogue,bias", [(mxq.EPI_GELU_TANH, False), (mxq.EPI_NONE, False),
                                            (mxq.EPI_GELU_TANH, True), (mxq.EPI_NONE, True)])
-def test_fused_equals_gemm_then_quantize(m, n, k, epilogue, bias):
-    say("fused vs two-step", m, n, k, epilogue, bias)
-    assert mxq.gemm_kernel_name(mxq.W4A4, m, n, k).startswith("pipe_")
-    _, _, _, (rc, rs), (fc, fs) = _both_paths(m, n, k, 31 + m + n, epilogue, bias)
+def test_fused_equals_gemm_then_quantize(waves, m, n, k, epilogue, bias):
+    say("fused vs two-step", waves, m, n, k, epilogue, bias)
+    with w4a4_waves(waves):
+        assert mxq.gemm_kernel_name(mxq.W4A4, m, n, k) == W4A4_WAVE_KERNEL[waves]
+        _, _, _, (rc, rs), (fc, fs) = _both_paths(m, n, k, 31 + m + n, epilogue, bias)
     assert fc.shape == rc.shape and fs.shape == rs.shape
     bad_c = int((fc != rc).sum())
     bad_s = int((fs != rs).sum())
     assert bad_c == 0 and bad_s == 0, f"{bad_c} code bytes and {bad_s} scale bytes differ"
 
 
+@pytest.mark.parametrize("waves", [4, 8])
 @pytest.mark.parametrize("m,n,k,epilogue,bias", [(300, 640, 640, mxq.EPI_GELU_TANH, False),
                                                  (600, 1280, 896, mxq.EPI_GELU_TANH, True),
                                                  (256, 512, 512, mxq.EPI_NONE, False)])
-def test_fused_matches_oracle_where_bf16_agrees(m, n, k, epilogue, bias):
-    say("fused vs oracle", m, n, k, epilogue, bias)
-    (x, w, b), _, y, _, (fc, fs) = _both_paths(m, n, k, 77 + m, epilogue, bias)
+def test_fused_matches_oracle_where_bf16_agrees(waves, m, n, k, epilogue, bias):
+    say("fused vs oracle", waves, m, n, k, epilogue, bias)
+    with w4a4_waves(waves):
+        assert mxq.gemm_kernel_name(mxq.W4A4, m, n, k) == W4A4_WAVE_KERNEL[waves]
+        (x, w, b), _, y, _, (fc, fs) = _both_paths(m, n, k, 77 + m, epilogue, bias)
     oac, oas = oracle.quantize_act(mxq.W4A4, x)
     owc, ows = oracle.mxfp4_quantize(w)
     b64 = oracle.bf16_bits_to_f64(b) if bias else None

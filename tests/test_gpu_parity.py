@@ -14,8 +14,18 @@ import torch
 import mx_bit_quantized_amd as mxq
 import oracle
 import synth
-from gpu_util import (assert_codes_equal, assert_output_close, code_rows, dev_bf16, group_major_scales, host_bits,
-                      host_f32, host_u8, sample_rows)
+from gpu_util import (W4A4_WAVE_KERNEL, assert_codes_equal, assert_output_close, code_rows, dev_bf16,
+                      group_major_scales, host_bits, host_f32, host_u8, sample_rows, w4a4_waves)
+
+# (mode, waves): the pipelined W4A4 GEMM with one and with two waves per SIMD, W4A8
+PIPE_KINDS = [(mxq.W4A4, 4), (mxq.W4A4, 8), (mxq.W4A8, 4)]
+
+
+def _pipe_kernel_check(mode, waves, m, n, k):
+    name = mxq.gemm_kernel_name(mode, m, n, k)
+    assert name.startswith("pipe_"), name
+    if mode == mxq.W4A4:
+        assert name == W4A4_WAVE_KERNEL[waves], name
 
 pytestmark = pytest.mark.gpu
 
@@ -116,39 +126,62 @@ PIPE_SHAPES = [(256, 256, 512), (300, 264, 640), (600, 512, 512), (257, 768, 102
                (1000, 1280, 896), (2250, 7424, 512), (4352, 4096, 640)]
 
 
-@pytest.mark.parametrize("mode", [mxq.W4A4, mxq.W4A8])
+@pytest.mark.parametrize("mode,waves", PIPE_KINDS)
 @pytest.mark.parametrize("m,n,k", PIPE_SHAPES)
-def test_gemm_pipelined_kernel_matches_oracle(mode, m, n, k):
-    say("gemm pipe", mode, m, n, k)
-    assert mxq.gemm_kernel_name(mode, m, n, k).startswith("pipe_")
-    y, y_ref = _gemm_case(mode, m, n, k, seed=m + 3 * n + k)
-    assert_output_close(y, y_ref, f"gemm pipe mode={mode} {m}x{n}x{k}")
+def test_gemm_pipelined_kernel_matches_oracle(mode, waves, m, n, k):
+    say("gemm pipe", mode, waves, m, n, k)
+    with w4a4_waves(waves):
+        _pipe_kernel_check(mode, waves, m, n, k)
+        y, y_ref = _gemm_case(mode, m, n, k, seed=m + 3 * n + k)
+    assert_output_close(y, y_ref, f"gemm pipe mode={mode} waves={waves} {m}x{n}x{k}")
 
 
 # The fewest stages the pipelined kernel takes: as many as its ring holds (W4A4
 # four stages of 128 elements, W4A8 three), so the copy ring wraps inside
 # every tile and the waits of the first stages overlap the previous tile's.
-@pytest.mark.parametrize("mode,m,n,k", [(mxq.W4A4, 700, 2048, 512), (mxq.W4A8, 256, 512, 384),
-                                        (mxq.W4A8, 700, 2048, 384), (mxq.W4A8, 4352, 4096, 384)])
-def test_gemm_pipelined_at_the_fewest_stages(mode, m, n, k):
-    say("gemm pipe fewest stages", mode, m, n, k)
-    assert mxq.gemm_kernel_name(mode, m, n, k).startswith("pipe_")
-    assert not mxq.gemm_kernel_name(mode, m, n, k - 128).startswith("pipe_")
-    y, y_ref = _gemm_case(mode, m, n, k, seed=7 * m + n + k)
-    assert_output_close(y, y_ref, f"gemm pipe fewest stages mode={mode} {m}x{n}x{k}")
+@pytest.mark.parametrize("mode,waves,m,n,k", [(mxq.W4A4, 4, 700, 2048, 512), (mxq.W4A4, 8, 700, 2048, 512),
+                                              (mxq.W4A4, 8, 4352, 4096, 512), (mxq.W4A8, 4, 256, 512, 384),
+                                              (mxq.W4A8, 4, 700, 2048, 384), (mxq.W4A8, 4, 4352, 4096, 384)])
+def test_gemm_pipelined_at_the_fewest_stages(mode, waves, m, n, k):
+    say("gemm pipe fewest stages", mode, waves, m, n, k)
+    with w4a4_waves(waves):
+        _pipe_kernel_check(mode, waves, m, n, k)
+        assert not mxq.gemm_kernel_name(mode, m, n, k - 128).startswith("pipe_")
+        y, y_ref = _gemm_case(mode, m, n, k, seed=7 * m + n + k)
+    assert_output_close(y, y_ref, f"gemm pipe fewest stages mode={mode} waves={waves} {m}x{n}x{k}")
 
 
 # Each combination of bias and GELU is a kernel of its own (the one without
 # either is covered above).
-@pytest.mark.parametrize("mode", [mxq.W4A4, mxq.W4A8])
+@pytest.mark.parametrize("mode,waves", PIPE_KINDS)
 @pytest.mark.parametrize("m,n,k", [(300, 512, 640), (4352, 4096, 640)])
 @pytest.mark.parametrize("epilogue,bias", [(mxq.EPI_GELU_TANH, True), (mxq.EPI_NONE, True),
                                            (mxq.EPI_GELU_TANH, False)])
-def test_gemm_pipelined_bias_and_gelu(mode, m, n, k, epilogue, bias):
-    say("gemm pipe epilogue", mode, m, n, k, epilogue, bias)
-    assert mxq.gemm_kernel_name(mode, m, n, k).startswith("pipe_")
-    y, y_ref = _gemm_case(mode, m, n, k, seed=8, epilogue=epilogue, bias=bias)
-    assert_output_close(y, y_ref, f"pipe epilogue={epilogue} bias={bias} {m}x{n}x{k}")
+def test_gemm_pipelined_bias_and_gelu(mode, waves, m, n, k, epilogue, bias):
+    say("gemm pipe epilogue", mode, waves, m, n, k, epilogue, bias)
+    with w4a4_waves(waves):
+        _pipe_kernel_check(mode, waves, m, n, k)
+        y, y_ref = _gemm_case(mode, m, n, k, seed=8, epilogue=epilogue, bias=bias)
+    assert_output_close(y, y_ref, f"pipe epilogue={epilogue} bias={bias} waves={waves} {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m,n,k", [(300, 512, 640), (2250, 7424, 512), (4352, 4096, 640)])
+def test_gemm_w4a4_four_and_eight_waves_bit_identical(m, n, k):
+    """Both W4A4 kernels take the same MFMAs in the same order over K: equal bits."""
+    say("gemm 4 vs 8 waves", m, n, k)
+    x = dev_bf16(_edge_activation(m, k, 5 * m))
+    wc, ws = mxq.quantize_weight_mxfp4(dev_bf16(synth.weight_bf16(9, n, k)))
+    ac, asc = mxq.quantize_act(mxq.W4A4, x)
+    b = dev_bf16(_bits(np.random.default_rng(m).standard_normal(n) * 0.1))
+    outs = {}
+    for waves in (4, 8):
+        with w4a4_waves(waves):
+            _pipe_kernel_check(mxq.W4A4, waves, m, n, k)
+            outs[waves] = (mxq.gemm(mxq.W4A4, ac, asc, wc, ws, b, mxq.EPI_GELU_TANH),
+                           mxq.gemm_mxfp4_out(ac, asc, wc, ws, b, mxq.EPI_GELU_TANH))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[4][0], outs[8][0])
+    assert torch.equal(outs[4][1][0], outs[8][1][0]) and torch.equal(outs[4][1][1], outs[8][1][1])
 
 
 @pytest.mark.parametrize("mode", [mxq.W4A4, mxq.W4A8])
