@@ -92,7 +92,9 @@ enum {
                             policy entry); no silent fallback               */
   MXQ_ERR_WORKSPACE = 5, /* workspace missing or too small                  */
   MXQ_ERR_HIP = 6,       /* a HIP launch or runtime call failed             */
-  MXQ_ERR_RANGE = 7      /* policy index (expert, block) out of range       */
+  MXQ_ERR_RANGE = 7,     /* policy index (expert, block) out of range       */
+  MXQ_ERR_SCRATCH = 8    /* problem too large for the allocation-free
+                            scratch area (mxq_qlinear_noalloc)              */
 };
 
 /* Precision modes: values of the policy table (the page's policy artifact,
@@ -440,6 +442,31 @@ int mxq_qlinear(const void* policy, int32_t expert, int32_t block,
                 const void* w_codes, const void* w_scales, int64_t N,
                 const void* bias, int epilogue, void* y,
                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * mxq_qlinear without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc. The activation codes and scales go to a scratch area of
+ * MXQ_NOALLOC_SCRATCH_BYTES that the library holds on every device it runs on
+ * until the process ends (a static device array; nothing is allocated). The
+ * first call on a device looks up that device's address of the array (a host
+ * call with no stream work): make one call there before capturing a graph; a
+ * call with M == 0 does only that.
+ *   Limits: mxq_qlinear_workspace_bytes(mode, M, K) <= MXQ_NOALLOC_SCRATCH_BYTES
+ *   (64 MiB: e.g. M * K <= 126 M elements for W4A4, 67 M for W4A8), else
+ *   MXQ_ERR_SCRATCH and nothing is written.
+ *   Concurrency: every call on a device uses that device's one scratch area,
+ *   so calls that overlap on one device (other streams, other threads) race;
+ *   calls ordered on one stream do not. The area keeps the last call's
+ *   activation codes (each call overwrites what it reads).
+ * Otherwise exactly mxq_qlinear (same arguments without the workspace, same
+ * validation, same kernels and results).
+ */
+#define MXQ_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+int mxq_qlinear_noalloc(const void* policy, int32_t expert, int32_t block,
+                        const void* x, int64_t M, int64_t K,
+                        const void* w_codes, const void* w_scales, int64_t N,
+                        const void* bias, int epilogue, void* y, hipStream_t stream);
 
 /*
  * mxq_qlinear for tables that hold MXQ_POLICY_TRANSFORM_ON blocks. A

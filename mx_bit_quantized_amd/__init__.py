@@ -15,6 +15,7 @@ Names mirror the C ABI without its ``mxq_`` prefix:
     Policy(table) / policy_create / policy_destroy / policy_mode
     qlinear_workspace_bytes(mode, M, K)
     qlinear(policy, expert, block, x, w_codes, w_scales, bias=None, epilogue=EPI_NONE)
+    qlinear_noalloc(policy, expert, block, x, w_codes, w_scales, y, bias=None, epilogue=EPI_NONE)
 """
 
 import ctypes
@@ -26,7 +27,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmxq.so")
 
 # status codes, modes and epilogues (include/mxq.h)
-OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_MODE, ERR_WORKSPACE, ERR_HIP, ERR_RANGE = range(8)
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_MODE, ERR_WORKSPACE, ERR_HIP, ERR_RANGE, ERR_SCRATCH = range(9)
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MXQ_NOALLOC_SCRATCH_BYTES
 W4A4, W4A8, POLICY_BF16, POLICY_TRANSFORM_ON = 0, 1, 2, 3
 TIER_LOW, TIER_MID, TIER_HIGH = 0, 1, 2
 EPI_NONE, EPI_GELU_TANH = 0, 1
@@ -75,6 +77,7 @@ _SIGS = {
                                    _P, ctypes.c_size_t, _P]),
     "mxq_qlinear_transform": (ctypes.c_int, [_P, _I32, _I32, _P, _I64, _I64, _P, _P, _I64, _P, ctypes.c_int, _P,
                                              _P, _P, ctypes.c_size_t, _P]),
+    "mxq_qlinear_noalloc": (ctypes.c_int, [_P, _I32, _I32, _P, _I64, _I64, _P, _P, _I64, _P, ctypes.c_int, _P, _P]),
 }
 
 
@@ -446,6 +449,23 @@ def qlinear(policy, expert, block, x, w_codes, w_scales, bias=None, epilogue=EPI
                             _dev_ptr(y, "y", torch.bfloat16), _dev_ptr(workspace, "workspace", torch.uint8),
                             int(workspace.numel()), _stream_handle(stream))
     _check(st, "qlinear")
+    return y
+
+
+def qlinear_noalloc(policy, expert, block, x, w_codes, w_scales, y, bias=None, epilogue=EPI_NONE, stream=None):
+    """qlinear into a caller-provided y with the library's fixed scratch area instead of a workspace.
+
+    Allocates nothing (y must be given); calls that overlap on one device race on the scratch area."""
+    torch = _torch()
+    handle = policy.handle if isinstance(policy, Policy) else policy
+    m, k = _rows_k(x, "x")
+    n = int(w_codes.shape[0])
+    st = lib().mxq_qlinear_noalloc(handle, int(expert), int(block), _dev_ptr(x, "x", torch.bfloat16), m, k,
+                                    _dev_ptr(w_codes, "w_codes", torch.uint8),
+                                    _dev_ptr(w_scales, "w_scales", torch.uint8), n,
+                                    _dev_ptr(bias, "bias", torch.bfloat16), int(epilogue),
+                                    _dev_ptr(y, "y", torch.bfloat16), _stream_handle(stream))
+    _check(st, "qlinear_noalloc")
     return y
 
 

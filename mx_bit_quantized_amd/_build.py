@@ -23,7 +23,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 DEVICE_SOURCES = ["mxq_api.cpp", "mxq_quant.hip", "mxq_gemm.hip", "mxq_select.hip", "mxq_lowrank.hip",
-                  "mxq_layout.hip"]
+                  "mxq_layout.hip", "mxq_noalloc.hip"]
 
 COMMON_FLAGS = [
     "-O3",

@@ -116,6 +116,7 @@ const char* mxq_status_string(int status) {
     case MXQ_ERR_WORKSPACE: return "workspace missing or too small";
     case MXQ_ERR_HIP: return "HIP launch or runtime error";
     case MXQ_ERR_RANGE: return "policy index out of range";
+    case MXQ_ERR_SCRATCH: return "problem too large for the allocation-free scratch area (64 MiB)";
     default: return "unknown status";
   }
 }

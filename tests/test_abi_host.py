@@ -25,7 +25,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = mxq.lib()
     names = declared_functions()
-    assert len(names) == 29, names
+    assert len(names) == 30, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(mxq._SIGS)
@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     assert mxq.version() == 10100
-    for st in range(8):
+    for st in range(9):
         assert mxq.status_string(st)
     assert mxq.status_string(99) == "unknown status"
 
@@ -73,6 +73,25 @@ def test_mxfp4_layout_validation():
             assert fn(args[0], args[1], 4, 64, args[2], args[3], S) == mxq.ERR_ALIGN
         # no rows: nothing enqueued, null pointers accepted
         assert fn(None, None, 0, 64, None, None, S) == mxq.OK
+
+
+def test_qlinear_noalloc_validation():
+    """Checks that come before the scratch area is touched (no GPU needed)."""
+    L = mxq.lib()
+    assert L.mxq_qlinear_noalloc(None, 0, 0, FAKE, 4, 64, FAKE, FAKE, 64, None, 0, FAKE, None) == mxq.ERR_NULL
+    for mode, m in ((mxq.W4A4, 1 << 20), (mxq.W4A8, 100000)):
+        p = mxq.Policy([[mode]])
+        assert mxq.qlinear_workspace_bytes(mode, m, 5120) > mxq.NOALLOC_SCRATCH_BYTES
+        assert L.mxq_qlinear_noalloc(p.handle, 0, 0, FAKE, m, 5120, FAKE, FAKE, 64, None, 0, FAKE,
+                                     None) == mxq.ERR_SCRATCH
+        assert L.mxq_qlinear_noalloc(p.handle, 0, 1, FAKE, 4, 64, FAKE, FAKE, 64, None, 0, FAKE,
+                                     None) == mxq.ERR_RANGE
+        assert L.mxq_qlinear_noalloc(p.handle, 0, 0, FAKE, 4, 48, FAKE, FAKE, 64, None, 0, FAKE,
+                                     None) == mxq.ERR_SHAPE
+        p.close()
+    p = mxq.Policy([[mxq.POLICY_TRANSFORM_ON]])
+    assert L.mxq_qlinear_noalloc(p.handle, 0, 0, FAKE, 4, 128, FAKE, FAKE, 64, None, 0, FAKE, None) == mxq.ERR_MODE
+    p.close()
 
 
 def test_weight_pack_and_gemm_validation():
