@@ -82,14 +82,131 @@ def parse():
                     help="time one GPU's share of the workload split over this many GPUs along the video tokens "
                          "(M / S rows each; text rows and weights whole on every GPU)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peak-probe", action="store_true", help="leave out roofline.measured_peak")
     ap.add_argument("--cpu-sample-rows", type=int, default=512)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (calibrates HBM byte counters) and exit")
+    ap.add_argument("--peak", action="store_true",
+                    help="only measure the roofline denominators: the register-only scaled-MFMA rate (FP4xFP4, "
+                         "FP4xFP8) on random operands and a device copy, with clock and socket power, and exit")
+    ap.add_argument("--peak-seconds", type=float, default=1.0,
+                    help="seconds per MFMA probe (the default bench line runs them for this long too)")
     return ap.parse_args()
 
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+class PowerSampler:
+    """Socket power and gfx clock, sampled with amd-smi in a thread while a region runs.
+
+    The board holds a power cap by lowering the clock, so these say whether a
+    measured rate was capped. Reports medians (None where amd-smi is absent)."""
+
+    def __init__(self, period=0.5):
+        import threading
+        self.period, self.samples, self._stop = period, [], threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        import subprocess
+        while not self._stop.is_set():
+            try:
+                r = subprocess.run(["amd-smi", "metric", "-p", "-c", "--json"], capture_output=True, text=True,
+                                   timeout=10)
+                d = json.loads(r.stdout)
+                d = d[0] if isinstance(d, list) else d
+                d = d["gpu_data"][0] if "gpu_data" in d else d
+                val = lambda v: v.get("value") if isinstance(v, dict) else v
+                pw = val(d.get("power", {}).get("socket_power"))
+                ck = val((d.get("clock", {}).get("gfx_0") or {}).get("clk"))
+                if isinstance(pw, (int, float)) and isinstance(ck, (int, float)):
+                    self.samples.append((float(pw), float(ck)))
+            except Exception:
+                pass
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return {"socket_w": None, "gfx_mhz": None, "samples": 0}
+        # the first sample can predate the load
+        body = self.samples[1:] if len(self.samples) > 2 else self.samples
+        return {"socket_w": float(np.median([p for p, _ in body])), "gfx_mhz": float(np.median([c for _, c in body])),
+                "samples": len(body)}
+
+
+def measure_peaks(torch, seconds):
+    """Roofline denominators measured on this GPU (mxq_probe.hip).
+
+    mfma: the register-only scaled MFMA of the GEMMs on random operands, one
+    wave per SIMD on every CU, FP4 x FP4 (W4A4) and FP4 x FP8 (W4A8), each run
+    for about `seconds`, with the shader clock of the run and the board's
+    socket power; copy: a device copy of 2 GiB (read + write bytes)."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "mx_bit_quantized_amd", "libmxq_probe.so"))
+    lib.mxq_probe_mfma_words.restype = ctypes.c_size_t
+    lib.mxq_probe_mfma_words.argtypes = [ctypes.c_int]
+    lib.mxq_probe_mfma.restype = ctypes.c_int
+    lib.mxq_probe_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_void_p, ctypes.c_void_p]
+    lib.mxq_probe_copy.restype = ctypes.c_int
+    lib.mxq_probe_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p]
+    dev = "cuda:0"
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    grid = cus  # one 4-wave workgroup per CU: one wave per SIMD
+    words = lib.mxq_probe_mfma_words(grid)
+    g = torch.Generator(device=dev).manual_seed(77)
+    rnd = torch.randint(-2 ** 31, 2 ** 31 - 1, (words * 4,), dtype=torch.int32, device=dev, generator=g)
+    out = torch.empty((grid * 256,), dtype=torch.float32, device=dev)
+    clk = torch.zeros((1,), dtype=torch.int64, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())
+    res = {}
+    for name, fp8, flops_per_mfma in (("fp4xfp4", 0, 2 * 32 * 32 * 64), ("fp4xfp8", 1, 2 * 32 * 32 * 64)):
+        def run(iters):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            assert lib.mxq_probe_mfma(fp8, grid, iters, P(rnd), P(out), P(clk), stream) == 0
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e-3
+        t = run(256)
+        iters = max(256, int(256 * seconds / 4 / max(t, 1e-6)))  # about seconds / 4 per launch
+        run(iters)  # warm the clock and power state
+        with PowerSampler() as ps:
+            ts, cycles = [], []
+            for _ in range(4):
+                ts.append(run(iters))
+                cycles.append(int(clk.item()))
+        flops = grid * 4 * iters * 128 * flops_per_mfma
+        best = min(ts)
+        res[name] = {"tflops": round(flops / best / 1e12, 1), "clock_ghz": round(cycles[ts.index(best)] / best / 1e9, 3),
+                     **ps.summary()}
+    del rnd, out
+    n = (2 << 30) // 16
+    src = torch.ones((n * 4,), dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        assert lib.mxq_probe_copy(P(src), P(dst), n, cus * 8, stream) == 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        assert lib.mxq_probe_copy(P(src), P(dst), n, cus * 8, stream) == 0
+    e1.record()
+    torch.cuda.synchronize()
+    res["copy_gbs"] = round(5 * 2 * n * 16 / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
+    del src, dst
+    torch.cuda.empty_cache()
+    return res
 
 
 # Linears that read the same tensor in the model: self-attention q, k and v
@@ -447,7 +564,8 @@ def cpu_baseline(wl, sample_rows, static=False, transform=False, lr_rank=0):
                 break
         if secs > 10:
             break
-    return {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    return {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "host_cpus": os.cpu_count(), "kind": "oracle",
             "sample": f"{rows} token rows through the first W4A4 and first W4A8 block's video-token linears "
                       f"(quantize{' (W4A8: static FP8)' if static else ''}"
                       f"{' (W4A4: transform_on)' if transform else ''}"
@@ -587,6 +705,13 @@ def main():
         print(json.dumps({"copy_probe_bytes": n}), flush=True)
         return
     mxq.lib()
+    if args.peak:
+        pk = measure_peaks(torch, args.peak_seconds)
+        print(json.dumps({"metric": "roofline denominators measured on this GPU", "n_gpus": 1,
+                          "mfma_fp4xfp4_tflops": pk["fp4xfp4"]["tflops"], "mfma_fp4xfp8_tflops": pk["fp4xfp8"]["tflops"],
+                          "spec_peak_tflops": {"fp4xfp4": PEAK_TFLOPS[0], "fp4xfp8": PEAK_TFLOPS[1]},
+                          "hbm_copy_gbs": pk["copy_gbs"], "spec_hbm_gbs": PEAK_HBM_GBS, "detail": pk}), flush=True)
+        return
     if args.select:
         run_select(args, torch, mxq)
         return
@@ -606,13 +731,14 @@ def main():
         stack.step(timed=False)
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    # per-kernel events on the last timed step only: recording them around every
-    # launch slows a step by 1.4% at full size (11% at an 8-way token shard)
-    for i in range(args.steps):
-        stack.step(timed=i == args.steps - 1)
-    end.record()
-    torch.cuda.synchronize()
+    with PowerSampler() as power:
+        start.record()
+        # per-kernel events on the last timed step only: recording them around every
+        # launch slows a step by 1.4% at full size (11% at an 8-way token shard)
+        for i in range(args.steps):
+            stack.step(timed=i == args.steps - 1)
+        end.record()
+        torch.cuda.synchronize()
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
     tflops = wl.total_flops() / (ms_per_step * 1e-3) / 1e12
@@ -650,6 +776,16 @@ def main():
                 "kernel": KERNEL_SYMBOL[dom[1]],
                 "avg_launch_us": round(1e3 * a["ms"] / a["launches"], 1),
                 "flop_per_launch": a["flops"] // a["launches"]}
+    if not args.no_peak_probe:
+        # the same instruction with nothing else running, on random operands, at
+        # the clock the board's power cap allows (spec peak assumes 2.4 GHz)
+        pk = measure_peaks(torch, args.peak_seconds)
+        mp = pk["fp4xfp4" if dom[1] == 0 else "fp4xfp8"]
+        roofline["measured_peak"] = {"value": mp["tflops"], "unit": "TFLOP/s", "clock_ghz": mp["clock_ghz"],
+                                     "socket_w": mp["socket_w"],
+                                     "kind": "register-only scaled MFMA, random operands, one wave per SIMD on every CU"}
+        roofline["frac_of_measured_peak"] = round(achieved / mp["tflops"], 4)
+        roofline["hbm_copy_gbs"] = pk["copy_gbs"]
     modes = set(int(v) for v in stack.policy_table.flat)
     out = {
         "metric": METRIC,
@@ -676,8 +812,12 @@ def main():
                    "linears_per_block": len(wl.linears), "tflop_per_step": round(wl.total_flops() / 1e12, 2),
                    **({"token_shards": shards} if shards > 1 else {})},
         "roofline": roofline,
+        "power": power.summary(),
         "kernels": kernels,
         "weight_pack_gbs": round(stack.pack_gbs, 1),
+        # high-water mark of device memory over the run (every buffer is a torch
+        # allocation: the library allocates none)
+        "peak_device_gib": round(torch.cuda.max_memory_allocated() / 2 ** 30, 2),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_sample_rows, static, transform, args.svdquant_rank)

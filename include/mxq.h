@@ -67,6 +67,16 @@
  *     must stay below 2^31 elements per dimension and 2^31 rows.
  *   - Functions are thread-safe; calls that share output buffers must be
  *     ordered by the caller.
+ *   - Inputs are assumed finite. With the environment variable
+ *     MXQ_CHECK_FINITE set (not "0"), the entry points that read bf16
+ *     activations or weights scan them before enqueueing anything and return
+ *     MXQ_ERR_NONFINITE, writing nothing, when one holds an infinity or NaN;
+ *     those that write bf16 outputs (mxq_gemm, mxq_lowrank_up,
+ *     mxq_gemm_lowrank, and the quantized linears through them) scan the
+ *     output afterwards and return MXQ_ERR_NONFINITE when it overflowed. Each
+ *     scan synchronizes the stream: a debugging aid, the fail-closed guard
+ *     the "Wan q8 performance investigation" page asks for after all-black
+ *     outputs, not a mode for graph capture.
  */
 #ifndef MXQ_H
 #define MXQ_H
@@ -93,8 +103,10 @@ enum {
   MXQ_ERR_WORKSPACE = 5, /* workspace missing or too small                  */
   MXQ_ERR_HIP = 6,       /* a HIP launch or runtime call failed             */
   MXQ_ERR_RANGE = 7,     /* policy index (expert, block) out of range       */
-  MXQ_ERR_SCRATCH = 8    /* problem too large for the allocation-free
+  MXQ_ERR_SCRATCH = 8,   /* problem too large for the allocation-free
                             scratch area (mxq_qlinear_noalloc)              */
+  MXQ_ERR_NONFINITE = 9  /* MXQ_CHECK_FINITE: an input or output holds an
+                            infinity or NaN                                 */
 };
 
 /* Precision modes: values of the policy table (the page's policy artifact,

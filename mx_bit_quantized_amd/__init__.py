@@ -27,7 +27,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmxq.so")
 
 # status codes, modes and epilogues (include/mxq.h)
-OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_MODE, ERR_WORKSPACE, ERR_HIP, ERR_RANGE, ERR_SCRATCH = range(9)
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_MODE, ERR_WORKSPACE, ERR_HIP, ERR_RANGE, ERR_SCRATCH, ERR_NONFINITE = range(10)
 NOALLOC_SCRATCH_BYTES = 64 << 20  # MXQ_NOALLOC_SCRATCH_BYTES
 W4A4, W4A8, POLICY_BF16, POLICY_TRANSFORM_ON = 0, 1, 2, 3
 TIER_LOW, TIER_MID, TIER_HIGH = 0, 1, 2

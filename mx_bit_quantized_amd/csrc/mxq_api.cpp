@@ -48,6 +48,24 @@ int check_mk(int64_t rows, int64_t K, int64_t ld) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MXQ_OK : MXQ_ERR_HIP; }
 
+// MXQ_CHECK_FINITE: scan a bf16 [rows][ld] input (or output) for infinities and
+// NaNs; MXQ_OK when the guard is off.
+int finite_guard(const char* what, const void* x, int64_t rows, int64_t cols, int64_t ld, hipStream_t stream) {
+  if (!mxq::check_finite_enabled()) return MXQ_OK;
+  bool bad = false;
+  if (mxq::scan_nonfinite_bf16(x, rows, cols, ld, stream, &bad) != 0) return MXQ_ERR_HIP;
+  if (!bad) return MXQ_OK;
+  if (log_enabled()) fprintf(stderr, "[mxq] non-finite value in %s [%lld x %lld]\n", what, (long long)rows,
+                             (long long)cols);
+  return MXQ_ERR_NONFINITE;
+}
+
+// a launch's status, then the guard on its bf16 output
+int output_guard(hipError_t e, const char* what, const void* y, int64_t rows, int64_t cols, hipStream_t stream) {
+  if (e != hipSuccess) return MXQ_ERR_HIP;
+  return finite_guard(what, y, rows, cols, cols, stream);
+}
+
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Workspace layout of mxq_qlinear: codes first, scales at a 256-byte boundary.
@@ -117,6 +135,7 @@ const char* mxq_status_string(int status) {
     case MXQ_ERR_HIP: return "HIP launch or runtime error";
     case MXQ_ERR_RANGE: return "policy index out of range";
     case MXQ_ERR_SCRATCH: return "problem too large for the allocation-free scratch area (64 MiB)";
+    case MXQ_ERR_NONFINITE: return "non-finite value (infinity or NaN) in an input or output (MXQ_CHECK_FINITE)";
     default: return "unknown status";
   }
 }
@@ -131,7 +150,8 @@ int mxq_quantize_weight_mxfp4(const void* w, int64_t N, int64_t K, int64_t ldw,
   if (w == nullptr || codes == nullptr || scales == nullptr) return MXQ_ERR_NULL;
   if (!aligned16(w) || !aligned16(codes) || !aligned16(scales) || ldw % 8 != 0) return MXQ_ERR_ALIGN;
   if (log_enabled()) fprintf(stderr, "[mxq] quantize_weight_mxfp4 N=%lld K=%lld\n", (long long)N, (long long)K);
-  return hip_status(mxq::launch_mxfp4_quant(w, N, K, ldw, codes, scales, stream));
+  if ((st = finite_guard("weight", w, N, K, ldw, stream)) != MXQ_OK) return st;
+  return hip_status(mxq::launch_mxfp4_quant(w, N, K, ldw, codes, scales, stream, true));
 }
 
 int mxq_quantize_act(int mode, const void* x, int64_t M, int64_t K, int64_t ldx,
@@ -145,6 +165,7 @@ int mxq_quantize_act(int mode, const void* x, int64_t M, int64_t K, int64_t ldx,
   if (log_enabled())
     fprintf(stderr, "[mxq] quantize_act %s M=%lld K=%lld\n", mode == MXQ_W4A4 ? "mxfp4" : "fp8_per_token",
             (long long)M, (long long)K);
+  if ((st = finite_guard("activation", x, M, K, ldx, stream)) != MXQ_OK) return st;
   if (mode == MXQ_W4A4) return hip_status(mxq::launch_mxfp4_quant(x, M, K, ldx, codes, scales, stream));
   return hip_status(mxq::launch_fp8_quant(x, M, K, ldx, codes, scales, stream));
 }
@@ -157,6 +178,7 @@ int mxq_hadamard_channel_amax(const void* x, int64_t M, int64_t K, int64_t ldx, 
   if (x == nullptr || amax == nullptr) return MXQ_ERR_NULL;
   if (!aligned16(x) || ldx % 8 != 0 || (reinterpret_cast<uintptr_t>(amax) & 3u) != 0) return MXQ_ERR_ALIGN;
   if (log_enabled()) fprintf(stderr, "[mxq] hadamard_channel_amax M=%lld K=%lld\n", (long long)M, (long long)K);
+  if ((st = finite_guard("calibration input", x, M, K, ldx, stream)) != MXQ_OK) return st;
   return hip_status(mxq::launch_hadamard_amax(x, M, K, ldx, amax, stream));
 }
 
@@ -180,6 +202,7 @@ int mxq_quantize_mxfp4_hadamard(const void* x, int64_t M, int64_t K, int64_t ldx
   if (!aligned16(x) || !aligned16(mult) || !aligned16(codes) || !aligned16(scales) || ldx % 8 != 0)
     return MXQ_ERR_ALIGN;
   if (log_enabled()) fprintf(stderr, "[mxq] quantize_mxfp4_hadamard M=%lld K=%lld\n", (long long)M, (long long)K);
+  if ((st = finite_guard("activation", x, M, K, ldx, stream)) != MXQ_OK) return st;
   return hip_status(mxq::launch_mxfp4_hadamard_quant(x, M, K, ldx, mult, codes, scales, stream));
 }
 
@@ -192,6 +215,7 @@ int mxq_lowrank_down(const void* x, int64_t M, int64_t K, const void* l1t, int64
   if (M == 0) return MXQ_OK;
   if (x == nullptr || l1t == nullptr || t == nullptr) return MXQ_ERR_NULL;
   if (!aligned16(x) || !aligned16(l1t) || !aligned16(t)) return MXQ_ERR_ALIGN;
+  if ((st = finite_guard("activation", x, M, K, K, stream)) != MXQ_OK) return st;
   return hip_status(mxq::launch_lowrank_down(x, M, K, l1t, r, t, nullptr, nullptr, stream));
 }
 
@@ -204,6 +228,7 @@ int mxq_quantize_act_lowrank(const void* x, int64_t M, int64_t K, const void* l1
   if (x == nullptr || l1t == nullptr || codes == nullptr || scales == nullptr || t == nullptr) return MXQ_ERR_NULL;
   if (!aligned16(x) || !aligned16(l1t) || !aligned16(codes) || !aligned16(scales) || !aligned16(t))
     return MXQ_ERR_ALIGN;
+  if ((st = finite_guard("activation", x, M, K, K, stream)) != MXQ_OK) return st;
   return hip_status(mxq::launch_lowrank_down(x, M, K, l1t, r, t, codes, scales, stream));
 }
 
@@ -214,7 +239,7 @@ int mxq_lowrank_up(const void* y_pre, const void* t, const void* l2, int64_t M, 
   if (M == 0 || N == 0) return MXQ_OK;
   if (y_pre == nullptr || t == nullptr || l2 == nullptr || y == nullptr) return MXQ_ERR_NULL;
   if (!aligned16(y_pre) || !aligned16(t) || !aligned16(l2) || !aligned16(y)) return MXQ_ERR_ALIGN;
-  return hip_status(mxq::launch_lowrank_up(y_pre, t, l2, M, N, r, epilogue, y, stream));
+  return output_guard(mxq::launch_lowrank_up(y_pre, t, l2, M, N, r, epilogue, y, stream), "output", y, M, N, stream);
 }
 
 int mxq_gemm_lowrank(const void* a_codes, const void* a_scales, const void* w_codes, const void* w_scales,
@@ -236,8 +261,10 @@ int mxq_gemm_lowrank(const void* a_codes, const void* a_scales, const void* w_co
   if (log_enabled())
     fprintf(stderr, "[mxq] gemm w4a4 + rank-%lld branch%s M=%lld N=%lld K=%lld epi=%d\n", (long long)r,
             y_scales != nullptr ? " -> mxfp4" : "", (long long)M, (long long)N, (long long)K, epilogue);
-  return hip_status(mxq::launch_gemm_lowrank(a_codes, a_scales, w_codes, w_scales, bias, t, l2, r, epilogue, y,
-                                             y_scales, M, N, K, stream));
+  const hipError_t e = mxq::launch_gemm_lowrank(a_codes, a_scales, w_codes, w_scales, bias, t, l2, r, epilogue, y,
+                                                y_scales, M, N, K, stream);
+  if (y_scales != nullptr) return hip_status(e);  // MXFP4 output: always finite
+  return output_guard(e, "output", y, M, N, stream);
 }
 
 int mxq_sqnr_accumulate(const void* y, const void* y_ref, int64_t n, double* sums, hipStream_t stream) {
@@ -342,6 +369,7 @@ int mxq_fp8_calibrate(const void* x, int64_t M, int64_t K, int64_t ldx, float* a
   if (x == nullptr || amax == nullptr) return MXQ_ERR_NULL;
   if (!aligned16(x) || ldx % 8 != 0 || (reinterpret_cast<uintptr_t>(amax) & 3u) != 0) return MXQ_ERR_ALIGN;
   if (log_enabled()) fprintf(stderr, "[mxq] fp8_calibrate M=%lld K=%lld\n", (long long)M, (long long)K);
+  if ((st = finite_guard("calibration input", x, M, K, ldx, stream)) != MXQ_OK) return st;
   return hip_status(mxq::launch_fp8_amax(x, M, K, ldx, amax, stream));
 }
 
@@ -355,6 +383,7 @@ int mxq_quantize_act_fp8_static(const void* x, int64_t M, int64_t K, int64_t ldx
       (reinterpret_cast<uintptr_t>(amax) & 3u) != 0)
     return MXQ_ERR_ALIGN;
   if (log_enabled()) fprintf(stderr, "[mxq] quantize_act fp8_static M=%lld K=%lld\n", (long long)M, (long long)K);
+  if ((st = finite_guard("activation", x, M, K, ldx, stream)) != MXQ_OK) return st;
   return hip_status(mxq::launch_fp8_static_quant(x, M, K, ldx, amax, codes, scales, stream));
 }
 
@@ -376,7 +405,8 @@ int mxq_gemm(int mode, const void* a_codes, const void* a_scales,
   if (log_enabled())
     fprintf(stderr, "[mxq] gemm %s M=%lld N=%lld K=%lld epi=%d kernel=%s\n", mode == MXQ_W4A4 ? "w4a4" : "w4a8",
             (long long)M, (long long)N, (long long)K, epilogue, mxq::gemm_variant_name(mode, M, N, K));
-  return hip_status(mxq::launch_gemm(mode, a_codes, a_scales, w_codes, w_scales, bias, epilogue, y, M, N, K, stream));
+  return output_guard(mxq::launch_gemm(mode, a_codes, a_scales, w_codes, w_scales, bias, epilogue, y, M, N, K, stream),
+                      "output", y, M, N, stream);
 }
 
 int mxq_gemm_mxfp4_out(const void* a_codes, const void* a_scales, const void* w_codes, const void* w_scales,

@@ -7,8 +7,10 @@
 
 namespace mxq {
 
+// MXFP4 quantizer; `weight` selects the kernel instance that offline weight
+// packing runs under (same code, its own symbol in profiles).
 hipError_t launch_mxfp4_quant(const void* x, int64_t rows, int64_t K, int64_t ld,
-                              void* codes, void* scales, hipStream_t s);
+                              void* codes, void* scales, hipStream_t s, bool weight = false);
 
 hipError_t launch_fp8_quant(const void* x, int64_t rows, int64_t K, int64_t ld,
                             void* codes, void* scales, hipStream_t s);
@@ -81,6 +83,13 @@ hipError_t launch_gemm_lowrank(const void* a_codes, const void* a_scales, const 
 // scales) and the canonical row-major one ([rows][K/2], [rows][K/32]).
 hipError_t launch_mxfp4_layout(bool to_canonical, const void* src_codes, const void* src_scales, int64_t rows,
                                int64_t K, void* dst_codes, void* dst_scales, hipStream_t s);
+
+// The optional non-finite guard: whether MXQ_CHECK_FINITE is set, and a scan
+// of a bf16 [rows][ld] matrix's first cols columns (synchronizes the stream;
+// *found tells whether a value is infinite or NaN; returns nonzero on a HIP
+// error).
+bool check_finite_enabled();
+int scan_nonfinite_bf16(const void* x, int64_t rows, int64_t cols, int64_t ld, hipStream_t s, bool* found);
 
 // Name of the GEMM kernel variant launch_gemm picks for a shape (for logs).
 const char* gemm_variant_name(int mode, int64_t M, int64_t N, int64_t K);

@@ -48,6 +48,10 @@ __device__ __forceinline__ uint32_t quad_max(uint32_t v) {
   return v;
 }
 
+// WEIGHT only names the instance: the offline weight pack and the activation
+// quantizer run the same code, and separate symbols keep their launches apart
+// in profiles.
+template <bool WEIGHT>
 __global__ __launch_bounds__(64 * kQuantWaves) void mxfp4_quant_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t K, int64_t ld,
     uint8_t* __restrict__ codes, uint32_t* __restrict__ scales) {
@@ -536,14 +540,19 @@ static int grid_for_rows(int64_t rows) {
 }
 
 hipError_t launch_mxfp4_quant(const void* x, int64_t rows, int64_t K, int64_t ld,
-                              void* codes, void* scales, hipStream_t s) {
+                              void* codes, void* scales, hipStream_t s, bool weight) {
   const int64_t pchunks = ((K + 127) / 128 + kMxPanels - 1) / kMxPanels;
   const int64_t units = (rows + kMxRows - 1) / kMxRows * pchunks;
   int64_t blocks = (units + kQuantWaves - 1) / kQuantWaves;
   if (blocks > (1 << 16)) blocks = 1 << 16;  // units loop beyond
-  hipLaunchKernelGGL(mxfp4_quant_kernel, dim3((unsigned)blocks), dim3(64 * kQuantWaves), 0, s,
-                     static_cast<const uint16_t*>(x), rows, K, ld, static_cast<uint8_t*>(codes),
-                     static_cast<uint32_t*>(scales));
+  if (weight)
+    hipLaunchKernelGGL(mxfp4_quant_kernel<true>, dim3((unsigned)blocks), dim3(64 * kQuantWaves), 0, s,
+                       static_cast<const uint16_t*>(x), rows, K, ld, static_cast<uint8_t*>(codes),
+                       static_cast<uint32_t*>(scales));
+  else
+    hipLaunchKernelGGL(mxfp4_quant_kernel<false>, dim3((unsigned)blocks), dim3(64 * kQuantWaves), 0, s,
+                       static_cast<const uint16_t*>(x), rows, K, ld, static_cast<uint8_t*>(codes),
+                       static_cast<uint32_t*>(scales));
   return hipGetLastError();
 }
 

@@ -11,6 +11,11 @@ GOLDEN = os.path.join(ROOT, "tests", "golden")
 
 
 def pytest_configure(config):
+    # a different build of the library (the host-sanitized one) for host tests
+    alt = os.environ.get("MXQ_TEST_LIB")
+    if alt:
+        import mx_bit_quantized_amd as mxq
+        mxq.LIB_PATH = alt
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: long-running CPU test")
 

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings_and_version():
     assert mxq.version() == 10100
-    for st in range(9):
+    for st in range(10):
         assert mxq.status_string(st)
     assert mxq.status_string(99) == "unknown status"
 
