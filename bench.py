@@ -89,6 +89,9 @@ def parse():
     ap.add_argument("--peak", action="store_true",
                     help="only measure the roofline denominators: the register-only scaled-MFMA rate (FP4xFP4, "
                          "FP4xFP8) on random operands and a device copy, with clock and socket power, and exit")
+    ap.add_argument("--gemm-power", action="store_true",
+                    help="only run the A14B W4A4 GEMM (75600 x 5120 x 5120) back to back with both wave counts, on "
+                         "random and on constant data, sampling socket power and clock, and exit")
     ap.add_argument("--peak-seconds", type=float, default=1.0,
                     help="seconds per MFMA probe (the default bench line runs them for this long too)")
     return ap.parse_args()
@@ -142,6 +145,55 @@ class PowerSampler:
         body = self.samples[1:] if len(self.samples) > 2 else self.samples
         return {"socket_w": float(np.median([p for p, _ in body])), "gfx_mhz": float(np.median([c for _, c in body])),
                 "samples": len(body)}
+
+
+def gemm_power(torch, mxq, seconds=4.0):
+    """The A14B W4A4 GEMM run back to back for `seconds` per case, with socket power and clock.
+
+    Cases: the four- and eight-wave kernels (MXQ_W4A4_WAVES) on random
+    activations and weights (the synthetic distribution) and on constant ones.
+    Shows whether the kernel's rate is set by its schedule or by the board's
+    power cap: a capped kernel holds the cap and drops its clock."""
+    dev = "cuda:0"
+    m, n, k = 75600, 5120, 5120
+    out = []
+    for data in ("random", "constant"):
+        if data == "random":
+            g = torch.Generator(device=dev).manual_seed(3)
+            x = torch.randn((m, k), generator=g, device=dev).to(torch.bfloat16)
+            w = (torch.randn((n, k), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+        else:
+            x = torch.full((m, k), 1.5, device=dev).to(torch.bfloat16)
+            w = torch.full((n, k), 0.03, device=dev).to(torch.bfloat16)
+        wc, ws = mxq.quantize_weight_mxfp4(w)
+        ac, asc = mxq.quantize_act(mxq.W4A4, x)
+        del x, w
+        y = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+        for waves in (4, 8):
+            os.environ["MXQ_W4A4_WAVES"] = str(waves)
+            for _ in range(5):
+                mxq.gemm(mxq.W4A4, ac, asc, wc, ws, y=y)
+            torch.cuda.synchronize()
+            launches = 0
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with PowerSampler() as ps:
+                t0 = time.time()
+                e0.record()
+                while time.time() - t0 < seconds:
+                    for _ in range(10):
+                        mxq.gemm(mxq.W4A4, ac, asc, wc, ws, y=y)
+                    launches += 10
+                    torch.cuda.synchronize()
+                e1.record()
+                torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / launches
+            out.append({"data": data, "kernel": mxq.gemm_kernel_name(mxq.W4A4, m, n, k), "avg_us": round(us, 1),
+                        "tflops": round(2 * m * n * k / us / 1e6, 1), **ps.summary()})
+            log(json.dumps(out[-1]))
+        os.environ.pop("MXQ_W4A4_WAVES", None)
+        del ac, asc, wc, ws, y
+        torch.cuda.empty_cache()
+    return out
 
 
 def measure_peaks(torch, seconds):
@@ -711,6 +763,10 @@ def main():
                           "mfma_fp4xfp4_tflops": pk["fp4xfp4"]["tflops"], "mfma_fp4xfp8_tflops": pk["fp4xfp8"]["tflops"],
                           "spec_peak_tflops": {"fp4xfp4": PEAK_TFLOPS[0], "fp4xfp8": PEAK_TFLOPS[1]},
                           "hbm_copy_gbs": pk["copy_gbs"], "spec_hbm_gbs": PEAK_HBM_GBS, "detail": pk}), flush=True)
+        return
+    if args.gemm_power:
+        print(json.dumps({"metric": "A14B W4A4 GEMM 75600x5120x5120 under sustained load: rate, socket power, clock",
+                          "n_gpus": 1, "cases": gemm_power(torch, mxq)}), flush=True)
         return
     if args.select:
         run_select(args, torch, mxq)
