@@ -20,8 +20,10 @@ hidden state's static FP8 codes itself. The default is the per-token scale.
 --transform-on runs every W4A4 block as transform_on: block Hadamard rotation
 plus SmoothQuant ahead of MXFP4. The factors are calibrated once, untimed, on
 the same synthetic inputs and on each weight, and the weights are packed
-transformed. Such a block's FFN runs up-projection -> bf16 h -> transformed
-quantizer -> down-projection (the fused MXFP4 epilogue does not rotate).
+transformed. Such a block's FFN first projection rotates, rescales and
+quantizes the hidden state for the second one in its epilogue
+(mxq_gemm_mxfp4_hadamard_out), as the plain W4A4 FFN does without the
+transform.
 
 --svdquant-rank R adds SVDQuant's rank-R bf16 branch to every W4A4 linear:
 T = x L1 (in the quantizer's pass over x where the linear quantizes its own
@@ -269,6 +271,11 @@ def measure_peaks(torch, seconds):
 SHARED_INPUT = {"self_k": "self_q", "self_v": "self_q", "cross_v": "cross_k"}
 
 
+def input_group(name):
+    """The first linear reading the same input as `name` (itself if none)."""
+    return SHARED_INPUT.get(name, name)
+
+
 class Stack:
     """Packed weights, inputs and buffers of one workload on the device."""
 
@@ -281,6 +288,7 @@ class Stack:
         t0 = time.time()
         self.policy_table = wl.policy()
         self.policy = mxq.Policy(self.policy_table)
+        self.li_down = next((i for i, l in enumerate(wl.linears) if l.name == "ffn_down"), None)
         to_dev = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
         self.x_video = to_dev(synth.activation_bf16(wl.config_id, wl.m_video, wl.dim, wl.outliers,
                                                     tensor_id=synth.T_X_VIDEO))
@@ -300,10 +308,26 @@ class Stack:
         # transform_on: rotated per-channel maxima of the shared inputs, and each
         # linear's activation factors
         self.act_mult = {}
+        # Linears that read one input share its factors, as SmoothQuant folds the
+        # activation factor into the op that produces that input: lambda comes
+        # from the input's maxima and the largest of their weights' maxima (so
+        # q, k, v, and cross k, v, keep sharing one quantized input).
+        self.aw_group = {}
         if transform:
             self.ax_role = {"video": mxq.hadamard_channel_amax(self.x_video)}
             if self.x_text is not None:
                 self.ax_role["text"] = mxq.hadamard_channel_amax(self.x_text)
+            grouped = {input_group(n) for n in SHARED_INPUT}
+            for e in range(wl.n_experts):
+                for b in range(wl.n_blocks):
+                    if self.policy.mode(e, b) != 0:
+                        continue
+                    for li, lin in enumerate(wl.linears):
+                        g = input_group(lin.name)
+                        if g in grouped:
+                            w = synth.weight_bf16_device(wl.config_id, lin.n, lin.k, e, b, li)
+                            self.aw_group[(e, b, g)] = mxq.hadamard_channel_amax(w, self.aw_group.get((e, b, g)))
+                            del w
         # packed weights: drawn on the device per linear, packed, bf16 copy freed
         self.weights = {}
         pack_bytes, pack_ms = 0, 0.0
@@ -318,7 +342,9 @@ class Stack:
                     if tr:
                         # calibration (untimed): the input's and the weight's rotated
                         # maxima give the factors; the weight is packed transformed
-                        aw = mxq.hadamard_channel_amax(w)
+                        aw = self.aw_group.get((e, b, input_group(lin.name)))
+                        if aw is None:
+                            aw = mxq.hadamard_channel_amax(w)
                         ax = ax_h if lin.m_role == "ffn_hidden" else self.ax_role[lin.m_role]
                         am, wm = mxq.smoothquant_factors(ax, aw)
                         self.act_mult[(e, b, li)] = am
@@ -430,8 +456,9 @@ class Stack:
                     # FFN: the first projection quantizes its GELU output for
                     # the second one in its epilogue (same codes as quantizing
                     # its bf16 output), the second one reads them as they are.
-                    # W4A4: MXFP4; W4A8: only with static scales (a per-token
-                    # scale needs the row's amax first)
+                    # W4A4: MXFP4 (transform_on: rotated and rescaled by the
+                    # second projection's factors first); W4A8: only with static
+                    # scales (a per-token scale needs the row's amax first)
                     static8 = mode == 1 and self.static
                     tr = mode == 0 and self.transform
                     lr = self.lowrank.get((e, b, li)) if mode == 0 else None
@@ -439,12 +466,12 @@ class Stack:
                     # pipelined kernel takes the shape; the FFN's second projection needs
                     # the bf16 hidden state for its own branch, so the first one keeps it
                     lr_fused = lr is not None and mxq.gemm_lowrank_supported(m, lin.n, lin.k)
-                    fused_up = lin.name == "ffn_up" and not tr and lr is None and (
+                    fused_up = lin.name == "ffn_up" and lr is None and (
                         (mode == 0 and mxq.gemm_mxfp4_out_supported(m, lin.n, lin.k))
                         or (static8 and mxq.gemm_fp8_static_out_supported(m, lin.n, lin.k)))
                     fed = lin.name == "ffn_down" and self.down_ready
-                    # transform_on factors belong to each linear: no sharing there
-                    shared = not tr and codes_src is not None and SHARED_INPUT.get(lin.name) == codes_src
+                    # (transform_on: the linears of one input share its factors too)
+                    shared = codes_src is not None and SHARED_INPUT.get(lin.name) == codes_src
                     if fed:
                         codes, scales = self._act_views(mode, m, lin.k, self.codes_buf2)
                     else:
@@ -477,6 +504,12 @@ class Stack:
                     if lr_fused:
                         mxq.gemm_lowrank(codes, scales, wc, wsc, t, lr[1], None, lin.epilogue, y=out)
                         out_bytes = m * lin.n * 2 + (m + lin.n) * self.lr_rank * 2
+                    elif fused_up and tr:
+                        # the second projection's rotation and factors, in the epilogue
+                        oc, osc = self._act_views(mode, m, lin.n, self.codes_buf2)
+                        mxq.gemm_mxfp4_hadamard_out(codes, scales, wc, wsc, self.act_mult[(e, b, self.li_down)],
+                                                    None, lin.epilogue, oc, osc)
+                        out_bytes = m * lin.n // 2 + m * lin.n // 32
                     elif fused_up and mode == 0:
                         oc, osc = self._act_views(mode, m, lin.n, self.codes_buf2)
                         mxq.gemm_mxfp4_out(codes, scales, wc, wsc, None, lin.epilogue, oc, osc)
@@ -580,6 +613,14 @@ def cpu_baseline(wl, sample_rows, static=False, transform=False, lr_rank=0):
     flops, secs = 0, 0.0
     rows = min(sample_rows, wl.m_video)
     x = synth.activation_bf16(wl.config_id, rows, wl.dim, wl.outliers, tensor_id=synth.T_X_VIDEO)
+    aw_group = {}  # transform_on: joint weight maxima of the linears that read one input (as on the GPU)
+    if transform and mode_block[0] is not None:
+        grouped = {input_group(n) for n in SHARED_INPUT}
+        for li, lin in enumerate(wl.linears):
+            g = input_group(lin.name)
+            if g in grouped:
+                aw = oracle.hadamard_channel_amax([synth.weight_bf16(wl.config_id, lin.n, lin.k, 0, mode_block[0], li)])
+                aw_group[g] = aw if g not in aw_group else np.maximum(aw_group[g], aw)
     for md, b in mode_block.items():
         if b is None:
             continue
@@ -589,8 +630,9 @@ def cpu_baseline(wl, sample_rows, static=False, transform=False, lr_rank=0):
             w = synth.weight_bf16(wl.config_id, lin.n, lin.k, 0, b, li)
             xs = x[:, : lin.k]
             if md == 0 and transform:
+                aw = aw_group.get(input_group(lin.name))
                 am, wm = oracle.smoothquant_factors(oracle.hadamard_channel_amax([xs]),
-                                                    oracle.hadamard_channel_amax([w]))
+                                                    oracle.hadamard_channel_amax([w]) if aw is None else aw)
                 wq, wsc = oracle.mxfp4_quantize_hadamard(w, wm)  # offline on both sides; not timed
             else:
                 wq, wsc = oracle.mxfp4_quantize(w)  # offline on both sides; not timed

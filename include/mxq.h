@@ -357,6 +357,28 @@ int mxq_gemm_mxfp4_out(const void* a_codes, const void* a_scales,
                        int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 /*
+ * The same for a next layer that runs transform_on (sections "Mixed-Precision
+ * selection" and "Calibration-driven block selection": fixed Hadamard
+ * rotation and SmoothQuant in front of the MXFP4 W4A4 linear): the FFN of a
+ * transform_on block quantizes its hidden state with the second projection's
+ * rotation and factors. The result is exactly that of mxq_gemm(MXQ_W4A4, ...)
+ * into a bf16 [M][N] buffer followed by mxq_quantize_mxfp4_hadamard(that
+ * buffer, mult): the same bf16 values, rotated and rescaled in the same fp32
+ * order, quantized by the same rule; the hidden state never goes to memory.
+ *   mult              device float32 [N], 16-byte aligned: the second
+ *                     projection's act_mult (mxq_smoothquant_factors over
+ *                     its K = N)
+ *   other arguments   as for mxq_gemm_mxfp4_out
+ * Same shapes as mxq_gemm_mxfp4_out (N a multiple of 128, the transform's
+ * panel width): MXQ_ERR_SHAPE otherwise, and nothing is written. Finite
+ * values whose transform stays finite only.
+ */
+int mxq_gemm_mxfp4_hadamard_out(const void* a_codes, const void* a_scales,
+                                const void* w_codes, const void* w_scales, const void* bias,
+                                int epilogue, const float* mult, void* y_codes, void* y_scales,
+                                int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+/*
  * W4A8 GEMM whose output is the static FP8 activation of a next W4A8 layer:
  * the FFN of a W4A8 block takes the first projection (with tanh-GELU),
  * quantizes the hidden state with its calibrated static scale (the FP8 E4M3

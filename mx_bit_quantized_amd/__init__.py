@@ -64,6 +64,8 @@ _SIGS = {
     "mxq_quantize_act_fp8_static": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "mxq_gemm": (ctypes.c_int, [ctypes.c_int, _P, _P, _P, _P, _P, ctypes.c_int, _P, _I64, _I64, _I64, _P]),
     "mxq_gemm_mxfp4_out": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int, _P, _P, _I64, _I64, _I64, _P]),
+    "mxq_gemm_mxfp4_hadamard_out": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int, _P, _P, _P, _I64, _I64,
+                                                    _I64, _P]),
     "mxq_gemm_fp8_static_out": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int, _P, _P, _P, _I64, _I64, _I64,
                                                 _P]),
     "mxq_gemm_kernel_name": (ctypes.c_char_p, [ctypes.c_int, _I64, _I64, _I64]),
@@ -304,6 +306,31 @@ def gemm_mxfp4_out(a_codes, a_scales, w_codes, w_scales, bias=None, epilogue=EPI
                                    _dev_ptr(y_codes, "y_codes", torch.uint8),
                                    _dev_ptr(y_scales, "y_scales", torch.uint8), m, n, k, _stream_handle(stream))
     _check(st, "gemm_mxfp4_out")
+    return y_codes, y_scales
+
+
+def gemm_mxfp4_hadamard_out(a_codes, a_scales, w_codes, w_scales, mult, bias=None, epilogue=EPI_NONE,
+                            y_codes=None, y_scales=None, stream=None):
+    """W4A4 GEMM whose output is quantized straight to the transform_on activation of a next layer.
+
+    Returns (y_codes, y_scales), equal to quantize_mxfp4_hadamard(gemm(W4A4, ...), mult); mult is
+    the next layer's act_mult (float32 [N]). Same shapes as gemm_mxfp4_out.
+    """
+    torch = _torch()
+    m = int(a_codes.shape[0])
+    n = int(w_codes.shape[0])
+    k = int(w_codes.shape[1]) * 2
+    if y_codes is None or y_scales is None:
+        y_codes, y_scales = act_buffers(W4A4, m, n, w_codes.device)
+    st = lib().mxq_gemm_mxfp4_hadamard_out(_dev_ptr(a_codes, "a_codes"), _dev_ptr(a_scales, "a_scales"),
+                                            _dev_ptr(w_codes, "w_codes", torch.uint8),
+                                            _dev_ptr(w_scales, "w_scales", torch.uint8),
+                                            _dev_ptr(bias, "bias", torch.bfloat16), int(epilogue),
+                                            _dev_ptr(mult, "mult", torch.float32),
+                                            _dev_ptr(y_codes, "y_codes", torch.uint8),
+                                            _dev_ptr(y_scales, "y_scales", torch.uint8), m, n, k,
+                                            _stream_handle(stream))
+    _check(st, "gemm_mxfp4_hadamard_out")
     return y_codes, y_scales
 
 

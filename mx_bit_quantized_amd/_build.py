@@ -47,6 +47,14 @@ DEVICE_FLAGS = [
 ]
 
 
+# Per-source extra flags. The GEMM's MFMA sequence is a fully unrolled loop
+# whose slot index must be a constant (it selects accumulator registers); the
+# transformed-output epilogue makes the unrolled body larger than clang's
+# default size limit for an unroll pragma, past which the loop would stay
+# rolled and the accumulators would live in memory.
+SOURCE_FLAGS = {"mxq_gemm.hip": ["-mllvm", "-pragma-unroll-threshold=1000000"]}
+
+
 def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -66,7 +74,8 @@ def _compile_and_link(flags, sources, out_path, verbose):
     compile_flags = [f for f in flags if f not in ("-shared",) and not f.startswith("-Wl,")]
     with tempfile.TemporaryDirectory(prefix="mxq_build_") as tmpdir:
         objs = [os.path.join(tmpdir, os.path.basename(src) + ".o") for src in sources]
-        jobs = [[HIPCC] + compile_flags + ["-c", src, "-o", obj] for src, obj in zip(sources, objs)]
+        jobs = [[HIPCC] + compile_flags + SOURCE_FLAGS.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
+                for src, obj in zip(sources, objs)]
         with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1, 16)) as pool:
             list(pool.map(lambda c: _run(c, verbose), jobs))
         tmp = out_path + ".tmp"

@@ -469,6 +469,13 @@ __device__ __forceinline__ void buf_store16(const i32x4& rs, uint32_t voff, cons
 //         bytes) and group-major scales [N/128][M][4] (y_scales); N % 128 == 0.
 //   W4A8: static FP8 with the scale out_amax / 448: codes [M][N] (y) and the
 //         scale in every row of y_scales (float [M]).
+// QOUT = 1 writes these; QOUT = 2 (W4A4, four waves) writes the MXFP4 codes
+// of the transform_on activation instead: each row's 128 values of a code
+// panel, as bf16, go through the unnormalized 128-point Walsh-Hadamard
+// butterflies (h = 1, 2, 4, ..., 64 in that order, fp32, each a + b and
+// a - b of the elements h apart), one fp32 multiply by the channel factor
+// out_mult[n] (RN(t * mult + 0)) and rounding to bf16 before the MXFP4 rule,
+// the arithmetic of the stand-alone transformed quantizer step for step.
 //
 // LRB (W4A4 only): SVDQuant's low-rank branch joins the sums. After a tile's
 // K/128 code stages come r/32 more stages, one 32-wide rank panel each, with
@@ -480,21 +487,24 @@ __device__ __forceinline__ void buf_store16(const i32x4& rs, uint32_t voff, cons
 // steps of the stage read chunks {0, 2} and {1, 3} of the row, as both
 // operands do). The stage's scale copies go out of range: they write zeros
 // and read nothing, and keep the copy count of every stage the same.
-template <int MODE, int KT, int NB, bool GELU, bool BIAS, bool QOUT, bool LRB, int WAVES>
+template <int MODE, int KT, int NB, bool GELU, bool BIAS, int QOUT, bool LRB, int WAVES>
 __global__ __launch_bounds__(64 * WAVES) __attribute__((amdgpu_waves_per_eu(WAVES / 4, WAVES / 4))) void
 gemm_pipe_kernel(
     const uint8_t* __restrict__ wq, const uint8_t* __restrict__ ws,
     const uint8_t* __restrict__ aq, const void* __restrict__ asc,
     const uint16_t* __restrict__ bias, uint16_t* __restrict__ y, uint8_t* __restrict__ y_scales,
     const float* __restrict__ out_amax, int M, int N, int K, int tiles_m, int tiles_n,
-    const uint16_t* __restrict__ lr_t, const uint16_t* __restrict__ lr_l2, int lr_rank) {
+    const uint16_t* __restrict__ lr_t, const uint16_t* __restrict__ lr_l2, int lr_rank,
+    const float* __restrict__ out_mult) {
   using C = PipeCfg<MODE, KT, NB, WAVES>;
   constexpr int TM = C::TM, NT = C::NT;
   static_assert(!LRB || (MODE == 0 && KT == 128 && WAVES == 4), "the branch stages take the shape of a W4A4 code stage");
+  static_assert(QOUT < 2 || (MODE == 0 && WAVES == 4 && !LRB), "transformed output: W4A4, four waves");
   // ring of NB stage slots, then two tile-parameter blocks: bias slice (512
   // bytes), a sink for the unused waves' copies (512), token scales (1024, FP8)
-  constexpr int P_BIAS = 0, P_SINK = 512, P_TOK = 1024;
-  constexpr int PARAM_BYTES = MODE == 1 ? 2048 : 1024;
+  // or channel factors (1024, transformed MXFP4 output)
+  constexpr int P_BIAS = 0, P_SINK = 512, P_TOK = 1024, P_MULT = 1024;
+  constexpr int PARAM_BYTES = MODE == 1 || QOUT == 2 ? 2048 : 1024;
   constexpr int PARAM_OFF = NB * C::STAGE;
   // The epilogue runs inside the next tile's first stage while the ring is
   // busy (see below), so it stages its results through a small area of its
@@ -676,9 +686,10 @@ gemm_pipe_kernel(
   // Tile parameters of tile k into parameter block k & 1 (issued in stage 1
   // of tile k - 1, read in the first stage of tile k + 1): the bias slice
   // (waves 0, 1: 256 bytes each; the others copy nothing into the sink) and,
-  // for FP8 activations, the 256 token scales (256 bytes per wave). Always
+  // for FP8 activations, the 256 token scales, for the transformed MXFP4
+  // output the 256 channel factors (256 bytes per wave). Always
   // EPI_PARAM_OPS copies per wave; no bias reads as zeros.
-  constexpr int EPI_PARAM_OPS = MODE == 1 ? 2 : 1;
+  constexpr int EPI_PARAM_OPS = MODE == 1 || QOUT == 2 ? 2 : 1;
   auto issue_params = [&](int k) {
     const bool live = k < count;
     int tm = 0, tn = 0;
@@ -691,6 +702,10 @@ gemm_pipe_kernel(
     if constexpr (MODE == 1) {
       const i32x4 rt = make_rsrc(static_cast<const uint8_t*>(asc) + mb * 4u, ((uint32_t)M - mb) * 4u);
       lds_dma4(rt, pb + P_TOK + wave * 256, live ? (uint32_t)(wave * 256 + lane * 4) : 0x80000000u);
+    }
+    if constexpr (QOUT == 2) {
+      const i32x4 rm = make_rsrc(out_mult + nb, ((uint32_t)N - nb) * 4u);
+      lds_dma4(rm, pb + P_MULT + wave * 256, live ? (uint32_t)(wave * 256 + lane * 4) : 0x80000000u);
     }
   };
 
@@ -1048,8 +1063,10 @@ gemm_pipe_kernel(
           const uint8_t* prm = ring + PARAM_OFF + ((tile_k - 1) & 1) * PARAM_BYTES;
           // bias of the four column tiles: held for the stage with four waves,
           // read per tile with eight (whose 256 registers have no room for them)
-          v16f bq[WAVES == 4 ? 4 : 1];
-          if constexpr (BIAS && WAVES == 4) {
+          // and with the transform (whose 64 rotated values take that room)
+          constexpr bool BQ4 = WAVES == 4 && QOUT == 1;
+          v16f bq[BQ4 ? 4 : 1];
+          if constexpr (BIAS && BQ4) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) ev_bias(prm, i, bq[i]);
           }
@@ -1066,15 +1083,9 @@ gemm_pipe_kernel(
             const uint32_t soff = (q_pan * (uint32_t)M + (uint32_t)srow) * 4u;
             buf_store4(rsq, g == 0 && srow < M ? (soff | q_bad) : 0x80000000u, sbs_done);
           };
-          auto beforeq = [&](int sl) {
-            const int i = sl & 3, j = sl >> 2;
-            uint32_t pk[4][2];
-            if constexpr (WAVES == 4) {
-              ev_tile(i, j, bq[i], 1.0f, pk);
-            } else {
-              if constexpr (BIAS) ev_bias(prm, i, bq[0]);
-              ev_tile(i, j, bq[0], 1.0f, pk);
-            }
+          // E8M0 scale byte of a 32-column block from the lane's 8 bf16 pairs
+          // and its partner's (lane +- 32)
+          auto block_scale = [&](const uint32_t (&pk)[4][2]) {
             typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
             u16x2 m2 = {0, 0};
 #pragma unroll
@@ -1085,7 +1096,142 @@ gemm_pipe_kernel(
             uint32_t am = umax((uint32_t)m2.x, (uint32_t)m2.y);
             const auto sw = __builtin_amdgcn_permlane32_swap(am, am, false, false);
             am = umax(am, g ? (uint32_t)sw[0] : (uint32_t)sw[1]);
-            const uint32_t sb = mx_scale_byte(am);
+            return mx_scale_byte(am);
+          };
+          // Transformed output: tile i's values of the lane's row after the
+          // butterflies h = 1 .. 16 (and later 32, 64), hv[i][4 t + c]:
+          // c = 0, 1 column 32 i + 8 t + 2 g + c, c = 2, 3 column
+          // 32 i + 8 t + 4 + 2 g + c - 2 of the code panel.
+          float hv[4][16];
+          auto bfly = [](float& a, float& b) {
+            const float x0 = a, x1 = b;
+            a = x0 + x1;
+            b = x0 - x1;
+          };
+          // tile ii of the row group: factors, bf16, MXFP4 codes into staging.
+          // (These two must be inlined: their tile index has to be a constant
+          // where it indexes the accumulators and hv, or both go to memory.)
+          auto quant_rotated = [&](int ii) __attribute__((always_inline)) {
+            uint32_t pk[4][2];  // [t][0]: columns 8 t + 2 g, + 1; [t][1]: + 4
+#pragma unroll
+            for (int t2 = 0; t2 < 4; ++t2)
+#pragma unroll
+              for (int h = 0; h < 2; ++h) {
+                const float2 m = *reinterpret_cast<const float2*>(
+                    prm + P_MULT + (wn * 128 + 32 * ii + 8 * t2 + 4 * h + 2 * g) * 4);
+                // RN(t * mult + 0): an exact zero becomes +0, as in the
+                // stand-alone quantizer
+                pk[t2][h] = pack_bf16x2(__builtin_fmaf(hv[ii][4 * t2 + 2 * h], m.x, 0.0f),
+                                        __builtin_fmaf(hv[ii][4 * t2 + 2 * h + 1], m.y, 0.0f));
+              }
+            const uint32_t sb = block_scale(pk);
+            const float scq = as_float(sb << 23);
+            // byte 4 t + 2 h + g of the row's 16 code bytes per pair: code
+            // dword e0 holds runs t = 0, 1, e1 runs 2, 3 (bytes of one parity)
+            uint32_t e0 = 0, e1 = 0;
+            e0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(e0, __builtin_bit_cast(bf16x2, pk[0][0]), scq, 0);
+            e0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(e0, __builtin_bit_cast(bf16x2, pk[0][1]), scq, 1);
+            e0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(e0, __builtin_bit_cast(bf16x2, pk[1][0]), scq, 2);
+            e0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(e0, __builtin_bit_cast(bf16x2, pk[1][1]), scq, 3);
+            e1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(e1, __builtin_bit_cast(bf16x2, pk[2][0]), scq, 0);
+            e1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(e1, __builtin_bit_cast(bf16x2, pk[2][1]), scq, 1);
+            e1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(e1, __builtin_bit_cast(bf16x2, pk[3][0]), scq, 2);
+            e1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(e1, __builtin_bit_cast(bf16x2, pk[3][1]), scq, 3);
+            // after the swap the lower lane holds the even and odd bytes 0 .. 7,
+            // the upper lane bytes 8 .. 15; interleaving them gives each lane 8
+            // contiguous bytes
+            const auto pq = __builtin_amdgcn_permlane32_swap(e0, e1, false, false);
+            const uint32_t wlo = __builtin_amdgcn_perm((uint32_t)pq[1], (uint32_t)pq[0], 0x05010400u);
+            const uint32_t whi = __builtin_amdgcn_perm((uint32_t)pq[1], (uint32_t)pq[0], 0x07030602u);
+            *reinterpret_cast<uint2*>(ev_region + r * QP + 16 * ii + 8 * g) = make_uint2(wlo, whi);
+            sbs |= sb << (8 * ii);
+          };
+          auto beforeh = [&](int sl) __attribute__((always_inline)) {
+            const int i = sl & 3, j = sl >> 2;
+            // accumulator tile (i, j) -> bias, GELU, bf16 (as ev_tile, with the
+            // bias read per run of 4 columns: the rotated values leave no room
+            // for a whole tile's)
+            uint32_t pk[4][2];
+#pragma unroll
+            for (int t2 = 0; t2 < 4; ++t2) {
+              uint2 bb = make_uint2(0u, 0u);
+              if constexpr (BIAS)
+                bb = *reinterpret_cast<const uint2*>(prm + P_BIAS + (wn * 128 + 32 * i + 8 * t2 + 4 * g) * 2);
+#pragma unroll
+              for (int h = 0; h < 2; ++h) {
+                float v0 = acc_read(acc[i][j][4 * t2 + 2 * h]);
+                float v1 = acc_read(acc[i][j][4 * t2 + 2 * h + 1]);
+                if constexpr (BIAS) {
+                  const uint32_t b2 = h ? bb.y : bb.x;
+                  v0 += as_float(b2 << 16);
+                  v1 += as_float(b2 & 0xFFFF0000u);
+                }
+                if constexpr (GELU) {
+                  v0 = gelu_tanh_dev(v0);
+                  v1 = gelu_tanh_dev(v1);
+                }
+                pk[t2][h] = pack_bf16x2(v0, v1);
+              }
+            }
+            // the bf16 values of columns 8 t + 4 g + c, exactly, in fp32
+            float f[4][4];
+#pragma unroll
+            for (int t2 = 0; t2 < 4; ++t2) {
+              f[t2][0] = as_float(pk[t2][0] << 16);
+              f[t2][1] = as_float(pk[t2][0] & 0xFFFF0000u);
+              f[t2][2] = as_float(pk[t2][1] << 16);
+              f[t2][3] = as_float(pk[t2][1] & 0xFFFF0000u);
+              bfly(f[t2][0], f[t2][1]);  // h = 1
+              bfly(f[t2][2], f[t2][3]);
+              bfly(f[t2][0], f[t2][2]);  // h = 2
+              bfly(f[t2][1], f[t2][3]);
+            }
+            // h = 4 pairs the lane with its partner: one swap of columns c and
+            // c + 2 gives the lower lane both halves' column c and the upper
+            // lane both halves' column c + 2, the g = 0 element first
+#pragma unroll
+            for (int t2 = 0; t2 < 4; ++t2)
+#pragma unroll
+              for (int c = 0; c < 2; ++c) {
+                const auto sw = __builtin_amdgcn_permlane32_swap(as_uint(f[t2][c]), as_uint(f[t2][c + 2]), false, false);
+                const float lo = as_float((uint32_t)sw[0]), hi = as_float((uint32_t)sw[1]);
+                hv[i][4 * t2 + c] = lo + hi;
+                hv[i][4 * t2 + 2 + c] = lo - hi;
+              }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              bfly(hv[i][e], hv[i][4 + e]);  // h = 8
+              bfly(hv[i][8 + e], hv[i][12 + e]);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              bfly(hv[i][e], hv[i][8 + e]);  // h = 16
+              bfly(hv[i][4 + e], hv[i][12 + e]);
+            }
+            if (i & 1) {
+#pragma unroll
+              for (int e = 0; e < 16; ++e) bfly(hv[i - 1][e], hv[i][e]);  // h = 32
+            }
+            if (i == 3) {
+#pragma unroll
+              for (int e = 0; e < 16; ++e) {
+                bfly(hv[0][e], hv[2][e]);  // h = 64
+                bfly(hv[1][e], hv[3][e]);
+              }
+#pragma unroll
+              for (int ii = 0; ii < 4; ++ii) quant_rotated(ii);
+            }
+          };
+          auto beforeq = [&](int sl) {
+            const int i = sl & 3, j = sl >> 2;
+            uint32_t pk[4][2];
+            if constexpr (WAVES == 4) {
+              ev_tile(i, j, bq[i], 1.0f, pk);
+            } else {
+              if constexpr (BIAS) ev_bias(prm, i, bq[0]);
+              ev_tile(i, j, bq[0], 1.0f, pk);
+            }
+            const uint32_t sb = block_scale(pk);
             const float scq = as_float(sb << 23);
             uint32_t e0 = 0, e1 = 0;
             e0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(e0, __builtin_bit_cast(bf16x2, pk[0][0]), scq, 0);
@@ -1120,7 +1266,10 @@ gemm_pipe_kernel(
             }
           };
           mfma_step_x(cur, cur_sc, std::integral_constant<int, 0>{}, std::true_type{}, std::true_type{},
-                      std::true_type{}, beforeq, afterq);
+                      std::true_type{}, [&](int sl) {
+                        if constexpr (QOUT == 2) beforeh(sl);
+                        else beforeq(sl);
+                      }, afterq);
           const StageScales<TM> sc1 = cur_sc;
           mfma_step_x(nxt, sc1, std::integral_constant<int, 1>{}, std::false_type{}, std::true_type{},
                       std::false_type{}, [](int) {}, [&](int k) {
@@ -1388,11 +1537,12 @@ static int device_cu_count() {
   return cus;
 }
 
-template <int MODE, int KT, int NB, int WAVES, bool QOUT = false, bool LRB = false>
+template <int MODE, int KT, int NB, int WAVES, int QOUT = 0, bool LRB = false>
 static hipError_t launch_pipe(const void* aq, const void* as, const void* wq, const void* ws, const void* bias,
                               int epi, void* y, int64_t M, int64_t N, int64_t K, hipStream_t s,
                               void* y_scales = nullptr, const float* out_amax = nullptr,
-                              const void* lr_t = nullptr, const void* lr_l2 = nullptr, int lr_rank = 0) {
+                              const void* lr_t = nullptr, const void* lr_l2 = nullptr, int lr_rank = 0,
+                              const float* out_mult = nullptr) {
   static const int cus = device_cu_count();
   const int tiles_m = (int)((M + 255) / 256);
   const int tiles_n = (int)((N + 255) / 256);
@@ -1406,7 +1556,7 @@ static hipError_t launch_pipe(const void* aq, const void* as, const void* wq, co
         dim3(grid), dim3(64 * WAVES), 0, s, static_cast<const uint8_t*>(wq), static_cast<const uint8_t*>(ws),
         static_cast<const uint8_t*>(aq), as, static_cast<const uint16_t*>(bias), static_cast<uint16_t*>(y),
         static_cast<uint8_t*>(y_scales), out_amax, (int)M, (int)N, (int)K, tiles_m, tiles_n,
-        static_cast<const uint16_t*>(lr_t), static_cast<const uint16_t*>(lr_l2), lr_rank);
+        static_cast<const uint16_t*>(lr_t), static_cast<const uint16_t*>(lr_l2), lr_rank, out_mult);
   };
   if (epi == 1) {
     if (bias != nullptr) go(std::true_type{}, std::true_type{});
@@ -1491,10 +1641,22 @@ hipError_t launch_gemm_mxfp4_out(const void* a_codes, const void* a_scales, cons
                                  const void* w_scales, const void* bias, int epilogue, void* y_codes,
                                  void* y_scales, int64_t M, int64_t N, int64_t K, hipStream_t s) {
   if (w4a4_eight_waves(M, N, K))
-    return launch_pipe<0, kPipeKT[0], kPipeNB[0], 8, true>(a_codes, a_scales, w_codes, w_scales, bias, epilogue,
-                                                           y_codes, M, N, K, s, y_scales);
-  return launch_pipe<0, kPipeKT[0], kPipeNB[0], 4, true>(a_codes, a_scales, w_codes, w_scales, bias, epilogue,
-                                                         y_codes, M, N, K, s, y_scales);
+    return launch_pipe<0, kPipeKT[0], kPipeNB[0], 8, 1>(a_codes, a_scales, w_codes, w_scales, bias, epilogue,
+                                                        y_codes, M, N, K, s, y_scales);
+  return launch_pipe<0, kPipeKT[0], kPipeNB[0], 4, 1>(a_codes, a_scales, w_codes, w_scales, bias, epilogue,
+                                                      y_codes, M, N, K, s, y_scales);
+}
+
+// The transformed output runs on the four-wave kernel at every size (its
+// rotated row group needs the registers that the eight-wave kernel's second
+// wave takes).
+hipError_t launch_gemm_mxfp4_hadamard_out(const void* a_codes, const void* a_scales, const void* w_codes,
+                                          const void* w_scales, const void* bias, int epilogue, const float* mult,
+                                          void* y_codes, void* y_scales, int64_t M, int64_t N, int64_t K,
+                                          hipStream_t s) {
+  return launch_pipe<0, kPipeKT[0], kPipeNB[0], 4, 2>(a_codes, a_scales, w_codes, w_scales, bias, epilogue,
+                                                      y_codes, M, N, K, s, y_scales, nullptr, nullptr, nullptr, 0,
+                                                      mult);
 }
 
 // N is the next layer's K: a multiple of 32
@@ -1504,8 +1666,8 @@ hipError_t launch_gemm_fp8_static_out(const void* a_codes, const void* a_scales,
                                       const void* w_scales, const void* bias, int epilogue, const float* out_amax,
                                       void* y_codes, void* y_scales, int64_t M, int64_t N, int64_t K,
                                       hipStream_t s) {
-  return launch_pipe<1, kPipeKT[1], kPipeNB[1], 4, true>(a_codes, a_scales, w_codes, w_scales, bias, epilogue,
-                                                         y_codes, M, N, K, s, y_scales, out_amax);
+  return launch_pipe<1, kPipeKT[1], kPipeNB[1], 4, 1>(a_codes, a_scales, w_codes, w_scales, bias, epilogue,
+                                                      y_codes, M, N, K, s, y_scales, out_amax);
 }
 
 // The branch rides on the pipelined W4A4 kernel (its shapes only); with
@@ -1519,11 +1681,11 @@ hipError_t launch_gemm_lowrank(const void* a_codes, const void* a_scales, const 
                                int epilogue, void* y, void* y_scales, int64_t M, int64_t N, int64_t K,
                                hipStream_t s) {
   if (y_scales != nullptr)
-    return launch_pipe<0, kPipeKT[0], kPipeNB[0], 4, true, true>(a_codes, a_scales, w_codes, w_scales, bias,
-                                                                 epilogue, y, M, N, K, s, y_scales, nullptr, t, l2,
-                                                                 (int)r);
-  return launch_pipe<0, kPipeKT[0], kPipeNB[0], 4, false, true>(a_codes, a_scales, w_codes, w_scales, bias, epilogue,
-                                                                y, M, N, K, s, nullptr, nullptr, t, l2, (int)r);
+    return launch_pipe<0, kPipeKT[0], kPipeNB[0], 4, 1, true>(a_codes, a_scales, w_codes, w_scales, bias,
+                                                              epilogue, y, M, N, K, s, y_scales, nullptr, t, l2,
+                                                              (int)r);
+  return launch_pipe<0, kPipeKT[0], kPipeNB[0], 4, 0, true>(a_codes, a_scales, w_codes, w_scales, bias, epilogue,
+                                                             y, M, N, K, s, nullptr, nullptr, t, l2, (int)r);
 }
 
 const char* gemm_variant_name(int mode, int64_t M, int64_t N, int64_t K) {

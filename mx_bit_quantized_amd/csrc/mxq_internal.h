@@ -61,6 +61,14 @@ hipError_t launch_gemm_mxfp4_out(const void* a_codes, const void* a_scales, cons
                                  const void* w_scales, const void* bias, int epilogue, void* y_codes,
                                  void* y_scales, int64_t M, int64_t N, int64_t K, hipStream_t s);
 
+// The same with the transform_on rotation of the output before MXFP4: the
+// codes and scales of launch_mxfp4_hadamard_quant(bf16 output, mult), mult
+// device float [N].
+hipError_t launch_gemm_mxfp4_hadamard_out(const void* a_codes, const void* a_scales, const void* w_codes,
+                                          const void* w_scales, const void* bias, int epilogue, const float* mult,
+                                          void* y_codes, void* y_scales, int64_t M, int64_t N, int64_t K,
+                                          hipStream_t s);
+
 // W4A8 GEMM whose bf16 output goes straight into static FP8 with the scale
 // out_amax / 448 (device fp32): codes [M][N], the scale in every row of
 // y_scales (float [M]); only where gemm_fp8_static_out_supported holds.
