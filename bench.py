@@ -92,8 +92,9 @@ def parse():
                     help="only measure the roofline denominators: the register-only scaled-MFMA rate (FP4xFP4, "
                          "FP4xFP8) on random operands and a device copy, with clock and socket power, and exit")
     ap.add_argument("--gemm-power", action="store_true",
-                    help="only run the A14B W4A4 GEMM (75600 x 5120 x 5120) back to back with both wave counts, on "
-                         "random and on constant data, sampling socket power and clock, and exit")
+                    help="only run the A14B W4A4 GEMM (75600 x 5120 x 5120, both wave counts) and the A14B W4A8 "
+                         "FFN GEMMs (up with GELU, down) back to back, on random and on constant data, sampling "
+                         "socket power and clock, and exit")
     ap.add_argument("--peak-seconds", type=float, default=1.0,
                     help="seconds per MFMA probe (the default bench line runs them for this long too)")
     return ap.parse_args()
@@ -150,10 +151,12 @@ class PowerSampler:
 
 
 def gemm_power(torch, mxq, seconds=4.0):
-    """The A14B W4A4 GEMM run back to back for `seconds` per case, with socket power and clock.
+    """The A14B W4A4 GEMM, then the A14B W4A8 FFN GEMMs, each run back to back
+    for `seconds` per case, with socket power and clock.
 
-    Cases: the four- and eight-wave kernels (MXQ_W4A4_WAVES) on random
-    activations and weights (the synthetic distribution) and on constant ones.
+    Cases: the four- and eight-wave W4A4 kernels (MXQ_W4A4_WAVES) and the W4A8
+    FFN up (GELU) and down projections, on random activations and weights (the
+    synthetic distribution) and on constant ones.
     Shows whether the kernel's rate is set by its schedule or by the board's
     power cap: a capped kernel holds the cap and drops its clock."""
     dev = "cuda:0"
@@ -195,6 +198,42 @@ def gemm_power(torch, mxq, seconds=4.0):
         os.environ.pop("MXQ_W4A4_WAVES", None)
         del ac, asc, wc, ws, y
         torch.cuda.empty_cache()
+    # W4A8: the A14B FFN's two projections (per-token FP8 activations), same protocol
+    for name, (m8, n8, k8, epi) in (("ffn_up_gelu", (75600, 13824, 5120, mxq.EPI_GELU_TANH)),
+                                    ("ffn_down", (75600, 5120, 13824, mxq.EPI_NONE))):
+        for data in ("random", "constant"):
+            if data == "random":
+                g = torch.Generator(device=dev).manual_seed(5)
+                x = torch.randn((m8, k8), generator=g, device=dev).to(torch.bfloat16)
+                w = (torch.randn((n8, k8), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+            else:
+                x = torch.full((m8, k8), 1.5, device=dev).to(torch.bfloat16)
+                w = torch.full((n8, k8), 0.03, device=dev).to(torch.bfloat16)
+            wc, ws = mxq.quantize_weight_mxfp4(w)
+            ac, asc = mxq.quantize_act(mxq.W4A8, x)
+            del x, w
+            y = torch.empty((m8, n8), dtype=torch.bfloat16, device=dev)
+            for _ in range(3):
+                mxq.gemm(mxq.W4A8, ac, asc, wc, ws, None, epi, y)
+            torch.cuda.synchronize()
+            launches = 0
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with PowerSampler() as ps:
+                t0 = time.time()
+                e0.record()
+                while time.time() - t0 < seconds:
+                    for _ in range(4):
+                        mxq.gemm(mxq.W4A8, ac, asc, wc, ws, None, epi, y)
+                    launches += 4
+                    torch.cuda.synchronize()
+                e1.record()
+                torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / launches
+            out.append({"data": data, "linear": name, "kernel": mxq.gemm_kernel_name(mxq.W4A8, m8, n8, k8),
+                        "avg_us": round(us, 1), "tflops": round(2 * m8 * n8 * k8 / us / 1e6, 1), **ps.summary()})
+            log(json.dumps(out[-1]))
+            del ac, asc, wc, ws, y
+            torch.cuda.empty_cache()
     return out
 
 
@@ -807,7 +846,8 @@ def main():
                           "hbm_copy_gbs": pk["copy_gbs"], "spec_hbm_gbs": PEAK_HBM_GBS, "detail": pk}), flush=True)
         return
     if args.gemm_power:
-        print(json.dumps({"metric": "A14B W4A4 GEMM 75600x5120x5120 under sustained load: rate, socket power, clock",
+        print(json.dumps({"metric": "A14B W4A4 GEMM 75600x5120x5120 and W4A8 FFN GEMMs under sustained load: "
+                                    "rate, socket power, clock",
                           "n_gpus": 1, "cases": gemm_power(torch, mxq)}), flush=True)
         return
     if args.select:
