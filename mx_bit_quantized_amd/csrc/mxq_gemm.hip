@@ -795,7 +795,12 @@ gemm_pipe_kernel(
   // statement right after it: ordered with the other asm statements of the
   // step, the MFMA cannot be moved away from the work interleaved with it.
   // `order_tag` true takes the MFMAs j-outer (slot s = 4 j + i), so that a
-  // 32-row group of the output is complete every 4 slots.
+  // 32-row group of the output is complete every 4 slots. Otherwise they run
+  // i-outer, and in the steps that do not start the sums every other row runs
+  // backwards (a snake): consecutive MFMAs then always share one operand, so
+  // fewer operand bits switch (0.25-0.3% faster on the A14B shapes under the
+  // power cap, measured interleaved; same sums). The first step keeps the
+  // plain order, which the bf16 epilogues walk.
   auto mfma_step_x = [&](const StepData<MODE, TM>& f, const StageScales<TM>& sc, auto kk_tag, auto zero_tag,
                          auto pin_tag, auto order_tag, auto&& before, auto&& between) {
     constexpr int KK = decltype(kk_tag)::value;
@@ -805,7 +810,8 @@ gemm_pipe_kernel(
     constexpr int SEL = KT == 128 ? KK : 0;
 #pragma unroll
     for (int s = 0; s < NT; ++s) {
-      const int i = JOUT ? (s & 3) : (s / TM), j = JOUT ? (s >> 2) : (s % TM);
+      const int i = JOUT ? (s & 3) : (s / TM);
+      const int j = JOUT ? (s >> 2) : (!ZERO && (i & 1)) ? TM - 1 - s % TM : s % TM;
       {
         before(s);
         const v8i a = op_fp4(f.a[i]);
