@@ -5,12 +5,14 @@ policy lookup, activation quantization and scaled GEMM of each linear, the
 FFN's GELU epilogue and the re-quantization of its hidden state), with all
 inputs and packed weights already resident in HBM. Linears that read the same
 tensor in the model (self-attention q, k, v; cross-attention k, v) share one
-quantization of it. Weight packing is offline and is timed separately
-(reported, not part of the step).
+quantization of it and run as one GEMM over their weights stacked along N, the
+usual fused projection (--separate-qkv runs one GEMM each on the shared
+codes; the outputs are the same column for column). Weight packing is offline
+and is timed separately (reported, not part of the step).
 
     python bench.py [--steps K] [--warmup W] [--workload a14b_stack|a14b_ffn|qkv|ti2v|tiny]
                     [--act-scale per_token|static] [--transform-on] [--svdquant-rank R] [--select]
-                    [--token-shards S]
+                    [--token-shards S] [--separate-qkv]
 
 --act-scale static runs the W4A8 linears on static (per-tensor) FP8
 activations: each input's amax is calibrated once, untimed, on the same
@@ -95,6 +97,9 @@ def parse():
                     help="only run the A14B W4A4 GEMM (75600 x 5120 x 5120, both wave counts) and the A14B W4A8 "
                          "FFN GEMMs (up with GELU, down) back to back, on random and on constant data, sampling "
                          "socket power and clock, and exit")
+    ap.add_argument("--separate-qkv", action="store_true",
+                    help="run q, k, v (and cross-attention k, v) as separate GEMMs on their shared quantized input "
+                         "instead of one GEMM over the stacked weights")
     ap.add_argument("--peak-seconds", type=float, default=1.0,
                     help="seconds per MFMA probe (the default bench line runs them for this long too)")
     return ap.parse_args()
@@ -315,11 +320,45 @@ def input_group(name):
     return SHARED_INPUT.get(name, name)
 
 
+def exec_linears(linears, fuse, fits=lambda lin: True):
+    """The GEMMs of one block, as (Linear, [indices into `linears`]).
+
+    With `fuse`, the linears that read one input (SHARED_INPUT: q, k, v;
+    cross-attention k, v) run as one GEMM over their weights stacked along N,
+    the usual fused projection: every output column is computed as by its own
+    GEMM (same codes, same K order), and one launch replaces three or two.
+    A stacked GEMM for which `fits` is false stays split into its linears."""
+    out = []
+    lead = {}
+    for li, lin in enumerate(linears):
+        g = input_group(lin.name)
+        if fuse and g != lin.name and g in lead:
+            i = lead[g]
+            l0, parts = out[i]
+            out[i] = (synth.Linear(l0.name + "+" + lin.name, l0.m_role, l0.k, l0.n + lin.n, l0.epilogue), parts + [li])
+        else:
+            lead[lin.name] = len(out)
+            out.append((lin, [li]))
+    split = []
+    for lin, parts in out:
+        split += [(lin, parts)] if len(parts) == 1 or fits(lin) else [(linears[i], [i]) for i in parts]
+    return split
+
+
 class Stack:
     """Packed weights, inputs and buffers of one workload on the device."""
 
-    def __init__(self, wl, torch, mxq, static=False, transform=False, lr_rank=0):
+    def __init__(self, wl, torch, mxq, static=False, transform=False, lr_rank=0, fuse=True):
         self.wl, self.torch, self.mxq = wl, torch, mxq
+        # the GEMMs of a block: fused projections where the pipelined kernel takes
+        # the stacked shape in both modes (its 32-bit offsets bound the output
+        # below 2 GiB, so A14B's 720p q, k, v stay apart); SVDQuant's per-linear
+        # branches keep them apart too
+        pipelined = lambda lin: all(mxq.gemm_kernel_name(md, wl.m_of(lin), lin.n, lin.k).startswith("pipe_")
+                                    for md in (0, 1))
+        ex = exec_linears(wl.linears, fuse and not lr_rank, pipelined)
+        self.lins = [l for l, _ in ex]
+        self.parts = [p for _, p in ex]
         self.static = static
         self.transform = transform
         self.lr_rank = lr_rank
@@ -327,7 +366,7 @@ class Stack:
         t0 = time.time()
         self.policy_table = wl.policy()
         self.policy = mxq.Policy(self.policy_table)
-        self.li_down = next((i for i, l in enumerate(wl.linears) if l.name == "ffn_down"), None)
+        self.li_down = next((i for i, l in enumerate(self.lins) if l.name == "ffn_down"), None)
         to_dev = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).to(dev)
         self.x_video = to_dev(synth.activation_bf16(wl.config_id, wl.m_video, wl.dim, wl.outliers,
                                                     tensor_id=synth.T_X_VIDEO))
@@ -337,7 +376,7 @@ class Stack:
                                                        tensor_id=synth.T_X_TEXT))
         log(f"activations ready in {time.time() - t0:.1f}s")
         m_max = wl.m_video
-        n_max = max(l.n for l in wl.linears)
+        n_max = max(l.n for l in self.lins)
         self.y = torch.empty((m_max * n_max,), dtype=torch.bfloat16, device=dev)
         self.h = torch.empty((wl.m_video * max(wl.ffn, 1),), dtype=torch.bfloat16, device=dev)
         ws = max(mxq.qlinear_workspace_bytes(md, m_max, l.k) for md in (0, 1) for l in wl.linears)
@@ -361,10 +400,10 @@ class Stack:
                 for b in range(wl.n_blocks):
                     if self.policy.mode(e, b) != 0:
                         continue
-                    for li, lin in enumerate(wl.linears):
+                    for li, lin in enumerate(self.lins):
                         g = input_group(lin.name)
                         if g in grouped:
-                            w = synth.weight_bf16_device(wl.config_id, lin.n, lin.k, e, b, li)
+                            w = self._weight(e, b, li)
                             self.aw_group[(e, b, g)] = mxq.hadamard_channel_amax(w, self.aw_group.get((e, b, g)))
                             del w
         # packed weights: drawn on the device per linear, packed, bf16 copy freed
@@ -373,8 +412,8 @@ class Stack:
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         for e in range(wl.n_experts):
             for b in range(wl.n_blocks):
-                for li, lin in enumerate(wl.linears):
-                    w = synth.weight_bf16_device(wl.config_id, lin.n, lin.k, e, b, li)
+                for li, lin in enumerate(self.lins):
+                    w = self._weight(e, b, li)
                     codes = torch.empty((lin.n, lin.k // 2), dtype=torch.uint8, device=dev)
                     scales = torch.empty(mxq.mx_scale_shape(lin.n, lin.k), dtype=torch.uint8, device=dev)
                     tr = transform and self.policy.mode(e, b) == 0
@@ -417,7 +456,7 @@ class Stack:
                 for b in range(wl.n_blocks):
                     if self.policy.mode(e, b) != 0:
                         continue
-                    for li, lin in enumerate(wl.linears):
+                    for li, lin in enumerate(self.lins):
                         l1t = (torch.randn((lr_rank, lin.k), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
                         l2 = (torch.randn((lin.n, lr_rank), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
                         self.lowrank[(e, b, li)] = (l1t, l2)
@@ -426,6 +465,12 @@ class Stack:
         self.down_ready = False  # the FFN's second projection has its input codes in codes_buf2
         if static:
             self._calibrate()
+
+    def _weight(self, e, b, i):
+        """bf16 weight of GEMM i of block (e, b): its linears' synthetic weights stacked along N."""
+        wl = self.wl
+        ws = [synth.weight_bf16_device(wl.config_id, wl.linears[p].n, wl.linears[p].k, e, b, p) for p in self.parts[i]]
+        return ws[0] if len(ws) == 1 else self.torch.cat(ws, dim=0)
 
     def _calibrate(self):
         """Static FP8 scales (untimed): the amax of each W4A8 input tensor over the synthetic inputs.
@@ -443,7 +488,7 @@ class Stack:
             for b in range(wl.n_blocks):
                 if self.policy.mode(e, b) != 1:
                     continue
-                for li, lin in enumerate(wl.linears):
+                for li, lin in enumerate(self.lins):
                     if lin.name != "ffn_up":
                         continue
                     m = wl.m_of(lin)
@@ -482,7 +527,7 @@ class Stack:
             for b in range(wl.n_blocks):
                 mode = self.policy.mode(e, b)
                 codes_src = None  # the linear whose activation codes codes_buf holds
-                for li, lin in enumerate(wl.linears):
+                for li, lin in enumerate(self.lins):
                     m = wl.m_of(lin)
                     if lin.m_role == "video":
                         x = self.x_video
@@ -864,7 +909,7 @@ def main():
     if transform and args.svdquant_rank:
         print("--transform-on and --svdquant-rank are separate W4A4 transforms: pick one", file=sys.stderr)
         sys.exit(2)
-    stack = Stack(wl, torch, mxq, static, transform, args.svdquant_rank)
+    stack = Stack(wl, torch, mxq, static, transform, args.svdquant_rank, fuse=not args.separate_qkv)
     for _ in range(args.warmup):
         stack.step(timed=False)
     torch.cuda.synchronize()
@@ -947,7 +992,8 @@ def main():
                    "w4a8_activations": "fp8_static_per_tensor" if static else "fp8_per_token",
                    "w4a4_transform": "hadamard128+smoothquant" if transform else
                    (f"svdquant_rank{args.svdquant_rank}" if args.svdquant_rank else "none"),
-                   "linears_per_block": len(wl.linears), "tflop_per_step": round(wl.total_flops() / 1e12, 2),
+                   "linears_per_block": len(wl.linears), "gemms_per_block": len(stack.lins),
+                   "tflop_per_step": round(wl.total_flops() / 1e12, 2),
                    **({"token_shards": shards} if shards > 1 else {})},
         "roofline": roofline,
         "power": power.summary(),

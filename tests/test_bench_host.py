@@ -88,3 +88,33 @@ def test_more_than_one_gpu_is_refused_before_any_device_work():
     assert r.returncode == 2
     assert "one GPU only" in r.stderr
     assert r.stdout == ""
+
+
+def test_fused_projections_cover_every_linear_once_with_the_same_flops():
+    """exec_linears stacks only linears that read one input, keeps K, role and epilogue, and does not
+    change the work: each linear in exactly one GEMM, the GEMMs' FLOPs summing to the workload's."""
+    for cfg in (1, 2, 3, 4, 5):
+        wl = synth.workload(cfg)
+        for fuse in (False, True):
+            ex = bench.exec_linears(wl.linears, fuse)
+            parts = [p for _, p in ex]
+            assert sorted(i for p in parts for i in p) == list(range(len(wl.linears)))
+            flops = sum(2 * wl.m_of(lin) * lin.n * lin.k for lin, _ in ex)
+            assert flops * wl.n_experts * wl.n_blocks == wl.total_flops()
+            for lin, p in ex:
+                members = [wl.linears[i] for i in p]
+                assert lin.n == sum(m.n for m in members)
+                assert all((m.k, m.m_role, m.epilogue) == (lin.k, lin.m_role, lin.epilogue) for m in members)
+                assert len({bench.input_group(m.name) for m in members}) == 1
+            if not fuse:
+                assert all(len(p) == 1 for p in parts)
+    five = [lin.name for lin, _ in bench.exec_linears(synth.workload(5).linears, True)]
+    assert five == ["self_q+self_k+self_v", "self_o", "cross_q", "cross_k+cross_v", "cross_o", "ffn_up", "ffn_down"]
+
+
+def test_fused_projection_that_does_not_fit_stays_split():
+    wl = synth.workload(5)
+    ex = bench.exec_linears(wl.linears, True, fits=lambda lin: lin.n * wl.m_of(lin) * 2 < 2 ** 31)
+    names = [lin.name for lin, _ in ex]
+    assert names[:3] == ["self_q", "self_k", "self_v"] and "cross_k+cross_v" in names
+    assert sorted(i for _, p in ex for i in p) == list(range(len(wl.linears)))
