@@ -348,8 +348,9 @@ int mxq_gemm(int mode, const void* a_codes, const void* a_scales,
  *                     its K is N)
  *   y_scales          device uint8 [N/128][M][4] (output)
  * Only for the shapes of the pipelined kernel (mxq_gemm_kernel_name(MXQ_W4A4,
- * M, N, K) starts with "pipe_") with N a multiple of 128: MXQ_ERR_SHAPE
- * otherwise, and nothing is written (use mxq_gemm and mxq_quantize_act).
+ * M, N, K) starts with "pipe_") with N a multiple of 128 and M * N/2 below
+ * 2^31 - 256: MXQ_ERR_SHAPE otherwise, and nothing is written (use mxq_gemm
+ * and mxq_quantize_act).
  */
 int mxq_gemm_mxfp4_out(const void* a_codes, const void* a_scales,
                        const void* w_codes, const void* w_scales, const void* bias,
@@ -431,8 +432,10 @@ int mxq_mxfp4_from_canonical(const void* codes_rm, const void* scales_rm, int64_
 /*
  * Name of the kernel that mxq_gemm runs for (mode, M, N, K), as a static
  * string: "pipe_..." for the LDS-pipelined persistent kernel (M, N >= 256,
- * N a multiple of 8, K a multiple of 128 with at least one ring of stages),
- * "direct_..." for the register-tiled kernel, "invalid" for a mode that is
+ * N a multiple of 8, K a multiple of 128 with at least one ring of stages,
+ * the activation codes and the packed weight each below 2^31 bytes; the
+ * output may be larger), "direct_..." for the register-tiled kernel,
+ * "invalid" for a mode that is
  * not W4A4 or W4A8. Host only: enqueues nothing, never fails.
  */
 const char* mxq_gemm_kernel_name(int mode, int64_t M, int64_t N, int64_t K);

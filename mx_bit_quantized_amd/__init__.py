@@ -335,8 +335,9 @@ def gemm_mxfp4_hadamard_out(a_codes, a_scales, w_codes, w_scales, mult, bias=Non
 
 
 def gemm_mxfp4_out_supported(M, N, K):
-    """Whether gemm_mxfp4_out takes (M, N, K): the pipelined kernel's shapes with N % 128 == 0."""
-    return gemm_kernel_name(W4A4, M, N, K).startswith("pipe_") and N % 128 == 0
+    """Whether gemm_mxfp4_out takes (M, N, K): the pipelined kernel's shapes with N % 128 == 0 and
+    an MXFP4 output below 2 GiB."""
+    return gemm_kernel_name(W4A4, M, N, K).startswith("pipe_") and N % 128 == 0 and M * (N // 2) < 2 ** 31 - 256
 
 
 def gemm_fp8_static_out(a_codes, a_scales, w_codes, w_scales, out_amax, bias=None, epilogue=EPI_NONE,
@@ -623,8 +624,10 @@ def gemm_lowrank(a_codes, a_scales, w_codes, w_scales, t, l2, bias=None, epilogu
 
 
 def gemm_lowrank_supported(M, N, K, mxfp4_out=False):
-    """Whether gemm_lowrank takes (M, N, K): the pipelined kernel's shapes (N % 128 == 0 for MXFP4 output)."""
-    return gemm_kernel_name(W4A4, M, N, K).startswith("pipe_") and (not mxfp4_out or N % 128 == 0)
+    """Whether gemm_lowrank takes (M, N, K): the pipelined kernel's shapes (for MXFP4 output N % 128 == 0
+    and the output below 2 GiB)."""
+    return gemm_kernel_name(W4A4, M, N, K).startswith("pipe_") and (
+        not mxfp4_out or (N % 128 == 0 and M * (N // 2) < 2 ** 31 - 256))
 
 
 def quantize_act_lowrank(x, l1t, codes=None, scales=None, t=None, stream=None):

@@ -855,7 +855,16 @@ gemm_pipe_kernel(
   // M and columns past N get an offset the range check drops.
   constexpr int EPI_STORES = MODE == 0 ? (QOUT ? 3 * TM : WAVES == 4 ? 32 : 2 * NT) : (QOUT ? 17 : 32);
   constexpr int EPI_OPS = EPI_STORES + EPI_PARAM_OPS;
-  const i32x4 ry = make_rsrc(y, (uint32_t)M * (uint32_t)N * (MODE == 1 && QOUT ? 1u : 2u));
+  // Output resource of one tile's rows for the row-major outputs (bf16, or
+  // static FP8 codes): its base is the tile's first row, so the offsets stay
+  // far below 2^31 for outputs of any size, and rows past M fall past its end
+  // (dropped by the range check).
+  constexpr uint32_t Y_ELT = MODE == 1 && QOUT ? 1u : 2u;
+  auto tile_out = [&](int ptm) {
+    const int rows = min(256, M - ptm * 256);
+    return make_rsrc(reinterpret_cast<const uint8_t*>(y) + (size_t)ptm * 256u * (size_t)N * Y_ELT,
+                     (uint32_t)rows * (uint32_t)N * Y_ELT);
+  };
   Fp8Out fo{};
   if constexpr (MODE == 1 && QOUT) fo = fp8_out_setup(*out_amax);
 
@@ -1290,7 +1299,8 @@ gemm_pipe_kernel(
           // bytes go through the staging area and leave as two stores of 16
           // rows x 64 bytes one slot later. The row scales (out_amax / 448)
           // leave in one store per wave, from the tiles of the first column.
-          const int ev_m0 = ptm * 256 + wm * 128 + (lane >> 2);  // + 32 j + 16 st
+          const i32x4 ry = tile_out(ptm);
+          const int ev_m0 = wm * 128 + (lane >> 2);  // row in the tile, + 32 j + 16 st
           const int ev_n0 = ptn * 256 + wn * 128 + (lane & 3) * 16;  // + 64 h
           const uint8_t* prm = ring + PARAM_OFF + ((tile_k - 1) & 1) * PARAM_BYTES;
           float sm[4];
@@ -1366,7 +1376,8 @@ gemm_pipe_kernel(
           // after the second step's first MFMA). Rows past M fall past the end
           // of the output (dropped by the range check); columns past N (or no
           // tile at all) get the offset's top bit.
-          const int ev_m0 = ptm * 256 + wm * 128 + (lane >> 2);  // + 32 j + 16 st
+          const i32x4 ry = tile_out(ptm);
+          const int ev_m0 = wm * 128 + (lane >> 2);  // row in the tile, + 32 j + 16 st
           const int ev_n0 = ptn * 256 + wn * 128 + (lane & 3) * 8;  // + 32 i
           const uint8_t* prm = ring + PARAM_OFF + ((tile_k - 1) & 1) * PARAM_BYTES;
           float sm[4];  // token scales of the lane's rows, one per row group j
@@ -1416,7 +1427,8 @@ gemm_pipe_kernel(
           // MFMA), as in the W4A8 epilogue without the token scale. Rows past M
           // fall past the end of the output (dropped by the range check);
           // columns past N (or no tile at all) get the offset's top bit.
-          const int ev_m0 = ptm * 256 + wm * 32 * TM + (lane >> 2);  // + 32 j + 16 st
+          const i32x4 ry = tile_out(ptm);
+          const int ev_m0 = wm * 32 * TM + (lane >> 2);  // row in the tile, + 32 j + 16 st
           const int ev_n0 = ptn * 256 + wn * 128 + (lane & 3) * 8;   // + 32 i
           const uint8_t* prm = ring + PARAM_OFF + ((tile_k - 1) & 1) * PARAM_BYTES;
           v16f c_cur, c_nxt;
@@ -1457,11 +1469,13 @@ gemm_pipe_kernel(
                         if (k == 0) tile_store(NT - 1);
                       });
         } else {
-          // byte offset of the lane's first store (+ 32 j rows + 8 it rows + 64 h
-          // columns); rows past M fall past the end of the output, which the
-          // range check drops, and columns past N (or no tile at all) get the
-          // offset's top bit, past every output of fewer than 2^31 bytes
-          const int ev_m0 = ptm * 256 + wm * 128 + (lane >> 3);
+          // byte offset of the lane's first store in the tile's rows (+ 32 j
+          // rows + 8 it rows + 64 h columns); rows past M fall past the end of
+          // the tile's resource, which the range check drops, and columns past
+          // N (or no tile at all) get the offset's top bit, past every tile's
+          // rows (256 N 2 bytes < 2^31)
+          const i32x4 ry = tile_out(ptm);
+          const int ev_m0 = wm * 128 + (lane >> 3);
           const int ev_n0 = ptn * 256 + wn * 128 + (lane & 7) * 8;
           const uint32_t ev_off0 = ((uint32_t)ev_m0 * (uint32_t)N + (uint32_t)ev_n0) * 2u;
           const uint32_t ev_bad0 = ev_live && ev_n0 < N ? 0u : 0x80000000u;
@@ -1615,12 +1629,17 @@ static bool w4a4_eight_waves(int64_t M, int64_t N, int64_t K) {
 // tile's epilogue is over before the next one starts), and N in multiples of 8
 // (16-byte stores); every Wan2.2 linear qualifies. Everything else takes the
 // direct kernel. 32-bit buffer offsets, and the out-of-range offset 2^31 that
-// must exceed every size, bound every operand and the output below 2^31 bytes.
+// must exceed every size, bound every operand below 2^31 bytes; row-major
+// outputs are addressed per tile (256 rows: any M), the MXFP4 output as a whole.
 static bool use_lds(int mode, int64_t M, int64_t N, int64_t K) {
   const int64_t a_bytes = mode == 0 ? M * (K / 2) : M * K;
   return K % kPipeKT[mode] == 0 && K / kPipeKT[mode] >= kPipeNB[mode] && N % 8 == 0 && M >= 256 && N >= 256 &&
-         a_bytes < (int64_t(1) << 31) && N * (K / 2) < (int64_t(1) << 31) && M * N * 2 < (int64_t(1) << 31) - 256;
+         a_bytes < (int64_t(1) << 31) && N * (K / 2) < (int64_t(1) << 31) && 256 * N * 2 < (int64_t(1) << 31) &&
+         M < (int64_t(1) << 31) / 4;
 }
+
+// MXFP4 output (codes in panels over all M rows, scales [N/128][M][4]): below 2^31 bytes.
+static bool mxfp4_out_fits(int64_t M, int64_t N) { return M * (N / 2) < (int64_t(1) << 31) - 256; }
 
 hipError_t launch_gemm(int mode, const void* a_codes, const void* a_scales,
                        const void* w_codes, const void* w_scales, const void* bias,
@@ -1641,7 +1660,9 @@ hipError_t launch_gemm(int mode, const void* a_codes, const void* a_scales,
   return launch_direct<1, 2, 2>(a_codes, a_scales, w_codes, w_scales, bias, epilogue, y, M, N, K, s);
 }
 
-bool gemm_mxfp4_out_supported(int64_t M, int64_t N, int64_t K) { return use_lds(0, M, N, K) && N % 128 == 0; }
+bool gemm_mxfp4_out_supported(int64_t M, int64_t N, int64_t K) {
+  return use_lds(0, M, N, K) && N % 128 == 0 && mxfp4_out_fits(M, N);
+}
 
 hipError_t launch_gemm_mxfp4_out(const void* a_codes, const void* a_scales, const void* w_codes,
                                  const void* w_scales, const void* bias, int epilogue, void* y_codes,
@@ -1679,7 +1700,7 @@ hipError_t launch_gemm_fp8_static_out(const void* a_codes, const void* a_scales,
 // The branch rides on the pipelined W4A4 kernel (its shapes only); with
 // y_scales the output is MXFP4 as for launch_gemm_mxfp4_out (N % 128 == 0).
 bool gemm_lowrank_supported(int64_t M, int64_t N, int64_t K, bool mxfp4_out) {
-  return use_lds(0, M, N, K) && (!mxfp4_out || N % 128 == 0);
+  return use_lds(0, M, N, K) && (!mxfp4_out || (N % 128 == 0 && mxfp4_out_fits(M, N)));
 }
 
 hipError_t launch_gemm_lowrank(const void* a_codes, const void* a_scales, const void* w_codes,

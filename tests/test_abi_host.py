@@ -481,13 +481,20 @@ def test_python_binding_refuses_cpu_tensors():
 def test_gemm_kernel_selection():
     """The pipelined kernel takes the workload shapes; everything else the direct kernel."""
     pipe = [(0, 75600, 5120, 5120), (0, 75600, 13824, 5120), (1, 75600, 5120, 13824), (0, 32760, 15360, 5120),
-            (1, 11440, 3072, 14336), (0, 512, 5120, 5120), (0, 256, 256, 512), (1, 256, 256, 384)]
+            (1, 11440, 3072, 14336), (0, 512, 5120, 5120), (0, 256, 256, 512), (1, 256, 256, 384),
+            (0, 75600, 15360, 5120), (1, 111600, 13824, 5120)]   # outputs past 2 GiB (addressed per tile)
     direct = [(0, 255, 512, 512),     # M below one tile
               (0, 512, 260, 512),     # N not a multiple of 8
               (0, 512, 512, 384),     # fewer stages than the W4A4 ring
               (1, 512, 512, 256),     # fewer stages than the W4A8 ring
               (0, 512, 512, 544),     # K not a multiple of 128
-              (0, 75600, 15360, 5120)]  # output of 2^31 bytes or more
+              (1, 170000, 512, 13824),  # FP8 activation codes of 2^31 bytes or more
+              (0, 512, 300000, 16384)]  # packed weight of 2^31 bytes or more
+    # the MXFP4 output is addressed as a whole: below 2^31 bytes
+    assert mxq.gemm_mxfp4_out_supported(75600, 13824, 5120)
+    assert not mxq.gemm_mxfp4_out_supported(200000, 22528, 512)
+    assert mxq.lib().mxq_gemm_mxfp4_out(FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, FAKE, 200000, 22528, 512,
+                                        None) == mxq.ERR_SHAPE
     for mode, m, n, k in pipe:
         assert mxq.gemm_kernel_name(mode, m, n, k).startswith("pipe_"), (mode, m, n, k)
     for mode, m, n, k in direct:

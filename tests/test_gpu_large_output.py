@@ -1,0 +1,98 @@
+"""GPU tests of row-major GEMM outputs larger than 2 GiB.
+
+The pipelined kernel addresses a bf16 (or static FP8) output per tile of 256
+rows, so the output may exceed 2^31 bytes, as a stacked q+k+v projection at
+720p does (75600 x 15360 bf16, 2.3 GB). Two checks per case:
+
+* the stacked GEMM against separate GEMMs on column slices of the weight,
+  byte for byte (each output column is computed the same way whatever N is);
+* sampled rows (row 0, rows past 2^31 / (2 N) where the old 32-bit offsets
+  would have wrapped, and the ragged last tile) against the oracle, within the
+  output tolerance.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import mx_bit_quantized_amd as mxq
+import oracle
+import synth
+from gpu_util import W4A4_WAVE_KERNEL, assert_output_close, host_bits, w4a4_waves
+
+pytestmark = pytest.mark.gpu
+
+M, K = 75600, 512            # 720p tokens; a short K keeps the cases quick
+N_STACK, N_PART = 15360, 5120
+ROWS = [0, 1, 255, 69905, 70000, 75519, 75520, 75599]   # 2^31 / (2 * 15360) = 69905.07; last tile from 75520
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _device():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    mxq.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def operands():
+    g = torch.Generator(device="cuda:0").manual_seed(17)
+    x = (torch.randn((M, K), generator=g, device="cuda:0")).to(torch.bfloat16)
+    w = synth.weight_bf16(17, N_STACK, K)
+    return x, w
+
+
+def _x_rows(x):
+    return host_bits(x[ROWS])
+
+
+@pytest.mark.parametrize("mode,waves", [(mxq.W4A4, 4), (mxq.W4A4, 8), (mxq.W4A8, 4)])
+def test_bf16_output_past_2gib(operands, mode, waves):
+    x, w = operands
+    say("bf16 output > 2 GiB", mode, waves, M, N_STACK, K)
+    assert M * N_STACK * 2 > 2 ** 31
+    with w4a4_waves(waves):
+        assert mxq.gemm_kernel_name(mode, M, N_STACK, K) == (W4A4_WAVE_KERNEL[waves] if mode == mxq.W4A4
+                                                              else "pipe_w4a8_wg256x256_wave128x128")
+        wd = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+        wc, ws = mxq.quantize_weight_mxfp4(wd)
+        ac, asc = mxq.quantize_act(mode, x)
+        y = mxq.gemm(mode, ac, asc, wc, ws, None, mxq.EPI_GELU_TANH)
+        parts = []
+        for p in range(N_STACK // N_PART):
+            wpc, wps = mxq.quantize_weight_mxfp4(wd[p * N_PART:(p + 1) * N_PART])
+            parts.append(mxq.gemm(mode, ac, asc, wpc, wps, None, mxq.EPI_GELU_TANH))
+        torch.cuda.synchronize()
+    for p, yp in enumerate(parts):
+        assert torch.equal(y[:, p * N_PART:(p + 1) * N_PART], yp), f"column slice {p} differs from its own GEMM"
+    del parts
+    oac, oas = oracle.quantize_act(mode, _x_rows(x))
+    owc, ows = oracle.mxfp4_quantize(w)
+    y_ref = oracle.qdq_matmul(mode, oac, oas, owc, ows, None, mxq.EPI_GELU_TANH)
+    assert_output_close(host_bits(y[ROWS]), y_ref, f"rows {ROWS} of the {M}x{N_STACK} output")
+
+
+def test_static_fp8_output_past_2gib(operands):
+    x, _ = operands
+    n = 28672  # M * n bytes of codes = 2.17 GB
+    say("static FP8 output > 2 GiB", M, n, K)
+    assert M * n > 2 ** 31 and mxq.gemm_fp8_static_out_supported(M, n, K)
+    w = synth.weight_bf16_device(17, n, K, 0, 0, 1)
+    wc, ws = mxq.quantize_weight_mxfp4(w)
+    del w
+    ac, asc = mxq.quantize_act(mxq.W4A8, x)
+    y = mxq.gemm(mxq.W4A8, ac, asc, wc, ws, None, mxq.EPI_GELU_TANH)
+    amax = mxq.fp8_calibrate(y)
+    rc, rs = mxq.quantize_act_fp8_static(y, amax)
+    del y
+    fc, fs = mxq.gemm_fp8_static_out(ac, asc, wc, ws, amax, None, mxq.EPI_GELU_TANH)
+    torch.cuda.synchronize()
+    assert torch.equal(fc, rc) and torch.equal(fs, rs)
