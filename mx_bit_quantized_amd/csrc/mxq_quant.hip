@@ -27,19 +27,22 @@ namespace mxq {
 // E8M0 bytes of one row's blocks in one panel form one dword, and the dwords
 // of all rows for one panel are contiguous.
 //
-// Mapping: a wave unit is 16 consecutive rows times up to 4 panels, in steps
-// of 4 rows per panel. Lane l takes 8-element chunk l % 16 of row l / 16 of a
-// step: one load reads 4 rows x 256 B, four neighbouring lanes hold one
-// 32-element block (a quad-shuffle max gives its amax), and one store writes
-// the 4 rows' codes of the panel, 256 contiguous bytes; the 16 rows' codes of
-// a panel are 1 KiB of consecutive memory. All 16 loads of a unit (16 KiB per
-// wave) are issued before the first conversion. The
-// block amax is a max over the magnitude bit patterns (sign cleared), exact
-// for finite bf16, with no float compare and no denormal flush.
+// Mapping: a wave unit is 16 consecutive rows times up to 4 panels, one row
+// per step. Lane l takes 8-element chunk l % 16 of panel l / 16: one load
+// reads 1 KiB of one row (512 consecutive elements), four neighbouring lanes
+// hold one 32-element block (a quad-shuffle max gives its amax), and one store
+// writes the row's 64 code bytes of each of the 4 panels (consecutive rows of
+// a panel are adjacent, so the unit's 16 rows fill 1 KiB per panel). All 16
+// loads of a unit (16 KiB per wave) are issued before the first conversion.
+// (Four rows x 256 B per load, with 256 B code stores, ran as fast at
+// K = 5120 and 4-11% slower at K = 3072 and 13824, same bytes.) The block
+// amax is a max over the magnitude bit patterns (sign cleared), exact for
+// finite bf16, with no float compare and no denormal flush.
 
 constexpr int kQuantWaves = 4;  // waves per workgroup
 constexpr int kMxRows = 16;     // rows per wave unit
 constexpr int kMxPanels = 4;    // panels per wave unit (fewer in the last one)
+constexpr int64_t kStreamInputBytes = int64_t(256) << 20;  // the last-level (Infinity) cache
 
 // Max over the 4 lanes of a quad, by DPP quad permutations (lane ^ 1, lane ^ 2).
 __device__ __forceinline__ uint32_t quad_max(uint32_t v) {
@@ -50,56 +53,58 @@ __device__ __forceinline__ uint32_t quad_max(uint32_t v) {
 
 // WEIGHT only names the instance: the offline weight pack and the activation
 // quantizer run the same code, and separate symbols keep their launches apart
-// in profiles.
-template <bool WEIGHT>
+// in profiles. NT loads the input with the non-temporal hint: an input larger
+// than the 256 MiB Infinity Cache is not going to be found there by the next
+// pass, and streaming it keeps the codes the GEMM reads next (A14B 720p,
+// 774 MB: 212 -> 195 us); a smaller input is, and loses its reuse (TI2V-5B,
+// 70 MB: 16.5 -> 17.9 us), so the launch picks by size. Same bytes either way.
+template <bool WEIGHT, bool NT>
 __global__ __launch_bounds__(64 * kQuantWaves) void mxfp4_quant_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t K, int64_t ld,
     uint8_t* __restrict__ codes, uint32_t* __restrict__ scales) {
   const int lane = threadIdx.x & 63;
   const int64_t unit0 = (int64_t)blockIdx.x * kQuantWaves + (threadIdx.x >> 6);
   const int64_t n_waves = (int64_t)gridDim.x * kQuantWaves;
-  const int64_t chunks = K >> 3;            // 8-element chunks per row
+  const int64_t chunks = K >> 3;  // 8-element chunks per row
   const int n_panels = (int)((K + 127) >> 7);
   const int pchunks = (n_panels + kMxPanels - 1) / kMxPanels;
   const int64_t units = (rows + kMxRows - 1) / kMxRows * pchunks;
-  const int rs = lane >> 4, c = lane & 15;  // row within a step of 4, chunk within the panel
+  const int pp = lane >> 4, c = lane & 15;  // panel within the unit, chunk within the panel
   for (int64_t u = unit0; u < units; u += n_waves) {
     const int64_t row0 = u / pchunks * kMxRows;
-    const int p0 = (int)(u % pchunks) * kMxPanels;
-    // all loads of the unit first: step (pp, t) covers rows row0 + 4 t + 0..3 of panel p0 + pp
-    uint4 v[kMxPanels][4];
+    const int p = (int)(u % pchunks) * kMxPanels + pp;
+    const int64_t ch = 16 * (int64_t)p + c;
+    // chunks is a multiple of 4 and a panel's first chunk of 16, so a whole
+    // 4-lane block is in or out of range: the shuffles stay uniform per block
+    const bool ch_ok = ch < chunks;
+    uint4 v[kMxRows];
 #pragma unroll
-    for (int pp = 0; pp < kMxPanels; ++pp)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int64_t row = row0 + 4 * t + rs;
-        const int64_t ch = 16 * (int64_t)(p0 + pp) + c;
-        const bool ok = row < rows && ch < chunks;
-        v[pp][t] = ok ? reinterpret_cast<const uint4*>(x + row * ld)[ch] : make_uint4(0, 0, 0, 0);
+    for (int t = 0; t < kMxRows; ++t) {
+      const int64_t row = row0 + t;
+      if constexpr (NT) {
+        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+        u32x4 q = {0u, 0u, 0u, 0u};
+        if (row < rows && ch_ok) q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + row * ld) + ch);
+        v[t] = make_uint4(q.x, q.y, q.z, q.w);
+      } else {
+        v[t] = row < rows && ch_ok ? reinterpret_cast<const uint4*>(x + row * ld)[ch] : make_uint4(0, 0, 0, 0);
       }
+    }
+    const int64_t w = K - 128 * (int64_t)p < 128 ? K - 128 * (int64_t)p : 128;  // panel width
 #pragma unroll
-    for (int pp = 0; pp < kMxPanels; ++pp) {
-      const int p = p0 + pp;
-      const int64_t ch = 16 * (int64_t)p + c;
-      // chunks is a multiple of 4 and a panel's first chunk of 16, so a whole
-      // 4-lane block is in or out of range: the shuffles stay uniform per block
-      const bool ch_ok = ch < chunks;
-      const int64_t w = K - 128 * (int64_t)p < 128 ? K - 128 * (int64_t)p : 128;  // panel width
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int64_t row = row0 + 4 * t + rs;
-        const uint32_t amax = quad_max(chunk_amax(v[pp][t]));
-        const uint32_t sb = ch_ok ? mx_scale_byte(amax) : 0u;
-        const uint32_t packed = pack8_fp4(v[pp][t], sb);
-        // the row's 4 block scales (block leaders at lanes +0, +4, +8, +12)
-        const uint32_t s1 = (uint32_t)__shfl_down((int)sb, 4);
-        const uint32_t s2 = (uint32_t)__shfl_down((int)sb, 8);
-        const uint32_t s3 = (uint32_t)__shfl_down((int)sb, 12);
-        if (row < rows && p < n_panels) {
-          // 4 consecutive rows of the panel: 4 x (w / 2) contiguous bytes
-          if (ch_ok) *reinterpret_cast<uint32_t*>(codes + (int64_t)p * 64 * rows + row * (w >> 1) + 4 * c) = packed;
-          if (c == 0) scales[(int64_t)p * rows + row] = sb | (s1 << 8) | (s2 << 16) | (s3 << 24);
-        }
+    for (int t = 0; t < kMxRows; ++t) {
+      const int64_t row = row0 + t;
+      const uint32_t amax = quad_max(chunk_amax(v[t]));
+      const uint32_t sb = ch_ok ? mx_scale_byte(amax) : 0u;
+      const uint32_t packed = pack8_fp4(v[t], sb);
+      // the panel's 4 block scales (block leaders at lanes +0, +4, +8, +12 of
+      // the 16-lane row): DPP row shifts left by 4, 8, 12
+      const uint32_t s1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)sb, 0x104, 0xF, 0xF, true);
+      const uint32_t s2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)sb, 0x108, 0xF, 0xF, true);
+      const uint32_t s3 = (uint32_t)__builtin_amdgcn_mov_dpp((int)sb, 0x10C, 0xF, 0xF, true);
+      if (row < rows && p < n_panels) {
+        if (ch_ok) *reinterpret_cast<uint32_t*>(codes + (int64_t)p * 64 * rows + row * (w >> 1) + 4 * c) = packed;
+        if (c == 0) scales[(int64_t)p * rows + row] = sb | (s1 << 8) | (s2 << 16) | (s3 << 24);
       }
     }
   }
@@ -289,7 +294,8 @@ __device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
 // The MXFP4 quantizer's mapping and stores, on transformed rows: each step's
 // 16 lanes of a row panel transform their 128 elements together, apply the
 // channel factors as RN(t * mult + 0), round to bf16, and continue exactly as
-// the plain quantizer. K is a multiple of 128 (whole panels).
+// the plain quantizer. A lane keeps its panel for the whole unit, so it reads
+// its 8 channel factors once. K is a multiple of 128 (whole panels).
 __global__ __launch_bounds__(64 * kQuantWaves) void mxfp4_hadamard_quant_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t K, int64_t ld, const float* __restrict__ mult,
     uint8_t* __restrict__ codes, uint32_t* __restrict__ scales) {
@@ -299,62 +305,56 @@ __global__ __launch_bounds__(64 * kQuantWaves) void mxfp4_hadamard_quant_kernel(
   const int n_panels = (int)(K >> 7);
   const int pchunks = (n_panels + kMxPanels - 1) / kMxPanels;
   const int64_t units = (rows + kMxRows - 1) / kMxRows * pchunks;
-  const int rs = lane >> 4, c = lane & 15;
+  const int pp = lane >> 4, c = lane & 15;  // panel within the unit, chunk within the panel
   for (int64_t u = unit0; u < units; u += n_waves) {
     const int64_t row0 = u / pchunks * kMxRows;
-    const int p0 = (int)(u % pchunks) * kMxPanels;
-    uint4 v[kMxPanels][4];
+    const int p = (int)(u % pchunks) * kMxPanels + pp;
+    const bool p_ok = p < n_panels;
+    uint4 v[kMxRows];
 #pragma unroll
-    for (int pp = 0; pp < kMxPanels; ++pp)
+    for (int t = 0; t < kMxRows; ++t) {
+      const int64_t row = row0 + t;
+      v[t] = row < rows && p_ok ? reinterpret_cast<const uint4*>(x + row * ld)[16 * (int64_t)p + c]
+                                : make_uint4(0, 0, 0, 0);
+    }
+    // the factors with the lane's sign from the transform folded in
+    float m[8];
+    if (p_ok) {
+      const uint32_t neg = (uint32_t)(__builtin_popcount(c) & 1) << 31;
+      const float4 m0 = reinterpret_cast<const float4*>(mult + 128 * (int64_t)p + 8 * c)[0];
+      const float4 m1 = reinterpret_cast<const float4*>(mult + 128 * (int64_t)p + 8 * c)[1];
+      m[0] = m0.x; m[1] = m0.y; m[2] = m0.z; m[3] = m0.w;
+      m[4] = m1.x; m[5] = m1.y; m[6] = m1.z; m[7] = m1.w;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int64_t row = row0 + 4 * t + rs;
-        const bool ok = row < rows && p0 + pp < n_panels;
-        v[pp][t] = ok ? reinterpret_cast<const uint4*>(x + row * ld)[16 * (int64_t)(p0 + pp) + c]
-                      : make_uint4(0, 0, 0, 0);
-      }
+      for (int e = 0; e < 8; ++e) m[e] = as_float(as_uint(m[e]) ^ neg);
+    } else {
 #pragma unroll
-    for (int pp = 0; pp < kMxPanels; ++pp) {
-      const int p = p0 + pp;
-      float m[8];
-      if (p < n_panels) {
-        // the factors with the lane's sign from the transform folded in
-        const uint32_t neg = (uint32_t)(__builtin_popcount(c) & 1) << 31;
-        const float4 m0 = reinterpret_cast<const float4*>(mult + 128 * (int64_t)p + 8 * c)[0];
-        const float4 m1 = reinterpret_cast<const float4*>(mult + 128 * (int64_t)p + 8 * c)[1];
-        m[0] = m0.x; m[1] = m0.y; m[2] = m0.z; m[3] = m0.w;
-        m[4] = m1.x; m[5] = m1.y; m[6] = m1.z; m[7] = m1.w;
+      for (int e = 0; e < 8; ++e) m[e] = 0.0f;
+    }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) m[e] = as_float(as_uint(m[e]) ^ neg);
-      } else {
+    for (int t = 0; t < kMxRows; ++t) {
+      const int64_t row = row0 + t;
+      float f[8];
+      bf16x8_to_f32(v[t], f);
+      fwht128_lanes(f, c);
+      // RN(t * mult + 0): exact zeros become +0 (their sign is not known here)
+      float q[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) m[e] = 0.0f;
-      }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int64_t row = row0 + 4 * t + rs;
-        float f[8];
-        bf16x8_to_f32(v[pp][t], f);
-        fwht128_lanes(f, c);
-        // RN(t * mult + 0): exact zeros become +0 (their sign is not known here)
-        float q[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) q[e] = __builtin_fmaf(f[e], m[e], 0.0f);
-        uint4 tv;
-        tv.x = bf16x2_rne(q[0], q[1]);
-        tv.y = bf16x2_rne(q[2], q[3]);
-        tv.z = bf16x2_rne(q[4], q[5]);
-        tv.w = bf16x2_rne(q[6], q[7]);
-        const uint32_t amax = quad_max(chunk_amax(tv));
-        const uint32_t sb = mx_scale_byte(amax);
-        const uint32_t packed = pack8_fp4(tv, sb);
-        const uint32_t s1 = (uint32_t)__shfl_down((int)sb, 4);
-        const uint32_t s2 = (uint32_t)__shfl_down((int)sb, 8);
-        const uint32_t s3 = (uint32_t)__shfl_down((int)sb, 12);
-        if (row < rows && p < n_panels) {
-          *reinterpret_cast<uint32_t*>(codes + (int64_t)p * 64 * rows + row * 64 + 4 * c) = packed;
-          if (c == 0) scales[(int64_t)p * rows + row] = sb | (s1 << 8) | (s2 << 16) | (s3 << 24);
-        }
+      for (int e = 0; e < 8; ++e) q[e] = __builtin_fmaf(f[e], m[e], 0.0f);
+      uint4 tv;
+      tv.x = bf16x2_rne(q[0], q[1]);
+      tv.y = bf16x2_rne(q[2], q[3]);
+      tv.z = bf16x2_rne(q[4], q[5]);
+      tv.w = bf16x2_rne(q[6], q[7]);
+      const uint32_t amax = quad_max(chunk_amax(tv));
+      const uint32_t sb = mx_scale_byte(amax);
+      const uint32_t packed = pack8_fp4(tv, sb);
+      const uint32_t s1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)sb, 0x104, 0xF, 0xF, true);
+      const uint32_t s2 = (uint32_t)__builtin_amdgcn_mov_dpp((int)sb, 0x108, 0xF, 0xF, true);
+      const uint32_t s3 = (uint32_t)__builtin_amdgcn_mov_dpp((int)sb, 0x10C, 0xF, 0xF, true);
+      if (row < rows && p_ok) {
+        *reinterpret_cast<uint32_t*>(codes + (int64_t)p * 64 * rows + row * 64 + 4 * c) = packed;
+        if (c == 0) scales[(int64_t)p * rows + row] = sb | (s1 << 8) | (s2 << 16) | (s3 << 24);
       }
     }
   }
@@ -545,14 +545,17 @@ hipError_t launch_mxfp4_quant(const void* x, int64_t rows, int64_t K, int64_t ld
   const int64_t units = (rows + kMxRows - 1) / kMxRows * pchunks;
   int64_t blocks = (units + kQuantWaves - 1) / kQuantWaves;
   if (blocks > (1 << 16)) blocks = 1 << 16;  // units loop beyond
+  const auto* xs = static_cast<const uint16_t*>(x);
+  auto* cs = static_cast<uint8_t*>(codes);
+  auto* ss = static_cast<uint32_t*>(scales);
+  const dim3 grid((unsigned)blocks), block(64 * kQuantWaves);
+  const bool streamed = rows * ld * 2 > kStreamInputBytes;
   if (weight)
-    hipLaunchKernelGGL(mxfp4_quant_kernel<true>, dim3((unsigned)blocks), dim3(64 * kQuantWaves), 0, s,
-                       static_cast<const uint16_t*>(x), rows, K, ld, static_cast<uint8_t*>(codes),
-                       static_cast<uint32_t*>(scales));
+    hipLaunchKernelGGL((mxfp4_quant_kernel<true, false>), grid, block, 0, s, xs, rows, K, ld, cs, ss);
+  else if (streamed)
+    hipLaunchKernelGGL((mxfp4_quant_kernel<false, true>), grid, block, 0, s, xs, rows, K, ld, cs, ss);
   else
-    hipLaunchKernelGGL(mxfp4_quant_kernel<false>, dim3((unsigned)blocks), dim3(64 * kQuantWaves), 0, s,
-                       static_cast<const uint16_t*>(x), rows, K, ld, static_cast<uint8_t*>(codes),
-                       static_cast<uint32_t*>(scales));
+    hipLaunchKernelGGL((mxfp4_quant_kernel<false, false>), grid, block, 0, s, xs, rows, K, ld, cs, ss);
   return hipGetLastError();
 }
 
