@@ -44,6 +44,19 @@ constexpr int kMxRows = 16;     // rows per wave unit
 constexpr int kMxPanels = 4;    // panels per wave unit (fewer in the last one)
 constexpr int64_t kStreamInputBytes = int64_t(256) << 20;  // the last-level (Infinity) cache
 
+// 16-byte load of 8 bf16 input elements; with NT, with the non-temporal hint
+// (inputs larger than the last-level cache, read once: see mxfp4_quant_kernel).
+template <bool NT>
+__device__ __forceinline__ uint4 load_chunk(const uint4* p) {
+  if constexpr (NT) {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(q.x, q.y, q.z, q.w);
+  } else {
+    return *p;
+  }
+}
+
 // Max over the 4 lanes of a quad, by DPP quad permutations (lane ^ 1, lane ^ 2).
 __device__ __forceinline__ uint32_t quad_max(uint32_t v) {
   v = umax(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));
@@ -81,14 +94,8 @@ __global__ __launch_bounds__(64 * kQuantWaves) void mxfp4_quant_kernel(
 #pragma unroll
     for (int t = 0; t < kMxRows; ++t) {
       const int64_t row = row0 + t;
-      if constexpr (NT) {
-        typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-        u32x4 q = {0u, 0u, 0u, 0u};
-        if (row < rows && ch_ok) q = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + row * ld) + ch);
-        v[t] = make_uint4(q.x, q.y, q.z, q.w);
-      } else {
-        v[t] = row < rows && ch_ok ? reinterpret_cast<const uint4*>(x + row * ld)[ch] : make_uint4(0, 0, 0, 0);
-      }
+      v[t] = row < rows && ch_ok ? load_chunk<NT>(reinterpret_cast<const uint4*>(x + row * ld) + ch)
+                                 : make_uint4(0, 0, 0, 0);
     }
     const int64_t w = K - 128 * (int64_t)p < 128 ? K - 128 * (int64_t)p : 128;  // panel width
 #pragma unroll
@@ -565,7 +572,9 @@ hipError_t launch_fp8_quant(const void* x, int64_t rows, int64_t K, int64_t ld,
   auto* cs = static_cast<uint8_t*>(codes);
   auto* ss = static_cast<float*>(scales);
   const dim3 grid(grid_for_rows(rows)), block(64 * kQuantWaves);
-  // one read per row while the row fits the registers of a wave
+  // one read per row while the row fits the registers of a wave (the
+  // non-temporal input hint of the MXFP4 quantizer made the W4A8 GEMM that
+  // follows slower by as much as it saved here, so these loads keep the default)
   if (K <= 64 * 8 * 4)
     hipLaunchKernelGGL(fp8_quant_row_kernel<4>, grid, block, 0, s, xs, rows, K, ld, cs, ss);
   else if (K <= 64 * 8 * 12)
