@@ -44,6 +44,11 @@ def _bits(x):
     return synth.f32_to_bf16_bits(np.asarray(x, np.float32))
 
 
+def _bit(v):
+    """bf16 bit pattern of one float, as an int."""
+    return int(_bits([v])[0])
+
+
 def _rows_with_edges(m, k, seed):
     """Student-t outlier rows plus a zero row, a subnormal row, FP8 ties and a huge row."""
     g = np.random.default_rng(seed)
@@ -52,9 +57,9 @@ def _rows_with_edges(m, k, seed):
     x[2] = (g.integers(0, 0x80, k) | (g.integers(0, 2, k) << 15)).astype(np.uint16)
     # values whose quotient by s = 448 / 448 = 1 lands on E4M3 ties (row amax 448)
     x[3] = _bits(g.choice([1.0625, 2.125, 4.25, 17.0, 208.0, -0.0], k))
-    x[3, 0] = _bits(np.float32(448.0))
+    x[3, 0] = _bit(448.0)
     x[4] = _bits(g.standard_normal(k) * 1e30)
-    x[5, k - 1] = _bits(np.float32(-3e4))  # the row amax sits in the last element
+    x[5, k - 1] = _bit(-3e4)  # the row amax sits in the last element
     return x
 
 
@@ -103,7 +108,7 @@ def test_fp8_per_token_long_rows(k):
 def test_quantize_act_leading_dimension(mode, m, k, ld):
     say("quantize_act ld", mode, m, k, ld)
     x = _rows_with_edges(m, k, 700 + m)
-    for fill in (_bits(np.float32(3e38)), 0x8000):
+    for fill in (_bit(3e38), 0x8000):
         xp = _padded(x, ld, int(fill))
         codes, scales = _abi_quantize_act(mode, xp, m, k, ld)
         _check_act(mode, codes, scales, x, f"mode={mode} [{m}x{k}] ld={ld} fill={int(fill):#06x}")
@@ -114,7 +119,7 @@ def test_quantize_weight_leading_dimension(n, k, ldw):
     say("quantize_weight ld", n, k, ldw)
     w = synth.weight_bf16(7, n, k)
     w[0, :32] = 0
-    wp = _padded(w, ldw, int(_bits(np.float32(-2e38))))
+    wp = _padded(w, ldw, _bit(-2e38))
     wd = dev_bf16(wp)
     codes = torch.empty((n, k // 2), dtype=torch.uint8, device="cuda:0")
     scales = torch.empty(mxq.mx_scale_shape(n, k), dtype=torch.uint8, device="cuda:0")
