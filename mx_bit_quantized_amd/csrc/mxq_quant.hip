@@ -302,7 +302,10 @@ __device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
 // 16 lanes of a row panel transform their 128 elements together, apply the
 // channel factors as RN(t * mult + 0), round to bf16, and continue exactly as
 // the plain quantizer. A lane keeps its panel for the whole unit, so it reads
-// its 8 channel factors once. K is a multiple of 128 (whole panels).
+// its 8 channel factors once. K is a multiple of 128 (whole panels). NT: the
+// non-temporal input loads of the plain quantizer, for the same reason and
+// chosen by the same size rule.
+template <bool NT>
 __global__ __launch_bounds__(64 * kQuantWaves) void mxfp4_hadamard_quant_kernel(
     const uint16_t* __restrict__ x, int64_t rows, int64_t K, int64_t ld, const float* __restrict__ mult,
     uint8_t* __restrict__ codes, uint32_t* __restrict__ scales) {
@@ -321,7 +324,7 @@ __global__ __launch_bounds__(64 * kQuantWaves) void mxfp4_hadamard_quant_kernel(
 #pragma unroll
     for (int t = 0; t < kMxRows; ++t) {
       const int64_t row = row0 + t;
-      v[t] = row < rows && p_ok ? reinterpret_cast<const uint4*>(x + row * ld)[16 * (int64_t)p + c]
+      v[t] = row < rows && p_ok ? load_chunk<NT>(reinterpret_cast<const uint4*>(x + row * ld) + 16 * (int64_t)p + c)
                                 : make_uint4(0, 0, 0, 0);
     }
     // the factors with the lane's sign from the transform folded in
@@ -592,9 +595,14 @@ hipError_t launch_mxfp4_hadamard_quant(const void* x, int64_t rows, int64_t K, i
   const int64_t units = (rows + kMxRows - 1) / kMxRows * pchunks;
   int64_t blocks = (units + kQuantWaves - 1) / kQuantWaves;
   if (blocks > (1 << 16)) blocks = 1 << 16;  // units loop beyond
-  hipLaunchKernelGGL(mxfp4_hadamard_quant_kernel, dim3((unsigned)blocks), dim3(64 * kQuantWaves), 0, s,
-                     static_cast<const uint16_t*>(x), rows, K, ld, mult, static_cast<uint8_t*>(codes),
-                     static_cast<uint32_t*>(scales));
+  if (rows * ld * 2 > kStreamInputBytes)
+    hipLaunchKernelGGL(mxfp4_hadamard_quant_kernel<true>, dim3((unsigned)blocks), dim3(64 * kQuantWaves), 0, s,
+                       static_cast<const uint16_t*>(x), rows, K, ld, mult, static_cast<uint8_t*>(codes),
+                       static_cast<uint32_t*>(scales));
+  else
+    hipLaunchKernelGGL(mxfp4_hadamard_quant_kernel<false>, dim3((unsigned)blocks), dim3(64 * kQuantWaves), 0, s,
+                       static_cast<const uint16_t*>(x), rows, K, ld, mult, static_cast<uint8_t*>(codes),
+                       static_cast<uint32_t*>(scales));
   return hipGetLastError();
 }
 
