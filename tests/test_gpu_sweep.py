@@ -8,8 +8,9 @@ direct one), mode, epilogue, bias and the W4A4 wave count. Checks:
 * activation codes and scales equal the oracle's byte for byte;
 * the bf16 output is within the output tolerance of the oracle's QDQ result
   on every element (the shapes are small enough for the full product);
-* where the shape allows them, the fused MXFP4 and transformed-MXFP4 outputs
-  equal the plain GEMM followed by the matching quantizer, byte for byte.
+* where the shape allows them, the fused MXFP4, transformed-MXFP4 and static
+  FP8 outputs equal the plain GEMM followed by the matching quantizer (the
+  static scale calibrated on that GEMM's output), byte for byte.
 """
 
 import sys
@@ -46,9 +47,13 @@ def _draw(case):
     pipelined = case % 4 != 3  # every fourth case may take the direct kernel
     m = int(g.integers(256, 1800)) if pipelined else int(g.integers(1, 600))
     mode = int(g.integers(0, 2)) if pipelined else (case // 4) % 2
-    # half the pipelined W4A4 cases take N in whole 128-column panels, the
-    # shapes of the fused MXFP4 outputs
-    n = 128 * int(g.integers(2, 26)) if mode == 0 and pipelined and case % 2 == 0 else 8 * int(g.integers(32, 400))
+    # half the pipelined cases take N in whole 128-column panels (W4A4) or in
+    # multiples of 32 (W4A8), the shapes of the fused MXFP4 and static FP8
+    # outputs
+    if pipelined and case % 2 == 0:
+        n = 128 * int(g.integers(2, 26)) if mode == 0 else 32 * int(g.integers(8, 100))
+    else:
+        n = 8 * int(g.integers(32, 400))
     k = 128 * int(g.integers(4, 24)) if pipelined else 32 * int(g.integers(1, 80))
     if mode == mxq.W4A8 and pipelined:
         k = max(k, 384)  # the W4A8 ring holds three stages
@@ -101,6 +106,13 @@ def test_random_shape_matches_oracle(case):
         assert torch.equal(fc, rc) and torch.equal(fs, rs), f"case {case}: fused MXFP4 output differs"
         assert torch.equal(hc, tc) and torch.equal(hs, ts), f"case {case}: fused transformed output differs"
 
+    if mode == mxq.W4A8 and mxq.gemm_fp8_static_out_supported(m, n, k):
+        amax = mxq.fp8_calibrate(y)
+        rc, rs = mxq.quantize_act_fp8_static(y, amax)
+        fc, fs = mxq.gemm_fp8_static_out(ac, asc, wc, ws, amax, bd, epilogue)
+        torch.cuda.synchronize()
+        assert torch.equal(fc, rc) and torch.equal(fs, rs), f"case {case}: fused static FP8 output differs"
+
 
 def test_sweep_covers_both_kernels_modes_and_options():
     draws = [_draw(c) for c in range(N_CASES)]
@@ -109,3 +121,4 @@ def test_sweep_covers_both_kernels_modes_and_options():
     assert {d[3] for d in draws} == {0, 1} and {d[4] for d in draws} == {0, 1} and {d[5] for d in draws} == {False, True}
     assert any(d[0] % 256 for d in draws) and any(d[1] % 256 for d in draws)
     assert sum(1 for d in draws if d[3] == 0 and mxq.gemm_mxfp4_out_supported(d[0], d[1], d[2])) >= 3
+    assert sum(1 for d in draws if d[3] == 1 and mxq.gemm_fp8_static_out_supported(d[0], d[1], d[2])) >= 3
