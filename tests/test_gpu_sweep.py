@@ -10,7 +10,11 @@ direct one), mode, epilogue, bias and the W4A4 wave count. Checks:
   on every element (the shapes are small enough for the full product);
 * where the shape allows them, the fused MXFP4, transformed-MXFP4 and static
   FP8 outputs equal the plain GEMM followed by the matching quantizer (the
-  static scale calibrated on that GEMM's output), byte for byte.
+  static scale calibrated on that GEMM's output), byte for byte;
+* on the pipelined W4A4 shapes, the GEMM with SVDQuant's low-rank branch (a
+  seeded rank of 32 to 128) is within the output tolerance of the oracle on
+  every element, and its MXFP4 output equals the quantizer applied to its
+  bf16 output.
 """
 
 import sys
@@ -105,6 +109,24 @@ def test_random_shape_matches_oracle(case):
             torch.cuda.synchronize()
         assert torch.equal(fc, rc) and torch.equal(fs, rs), f"case {case}: fused MXFP4 output differs"
         assert torch.equal(hc, tc) and torch.equal(hs, ts), f"case {case}: fused transformed output differs"
+
+    if mode == mxq.W4A4 and mxq.gemm_lowrank_supported(m, n, k):
+        # SVDQuant's branch in the GEMM's sums: a seeded rank and factors
+        gr = np.random.default_rng(5000 + case)
+        r = int(gr.choice([32, 64, 96, 128]))
+        t = synth.f32_to_bf16_bits((gr.standard_normal((m, r)) * 0.5).astype(np.float32))
+        l2 = synth.f32_to_bf16_bits((gr.standard_normal((n, r)) * 0.05).astype(np.float32))
+        with w4a4_waves(waves):
+            yl = mxq.gemm_lowrank(ac, asc, wc, ws, dev_bf16(t), dev_bf16(l2), bd, epilogue)
+            torch.cuda.synchronize()
+        want = oracle.svdquant_linear_fused(mxq.W4A4, oac, oas, owc, ows, t, l2, b64, epilogue)
+        assert_output_close(host_bits(yl), want, f"case {case} gemm+branch r={r} [{m}x{n}x{k}]")
+        if mxq.gemm_lowrank_supported(m, n, k, mxfp4_out=True):
+            with w4a4_waves(waves):
+                lc, ls = mxq.gemm_lowrank(ac, asc, wc, ws, dev_bf16(t), dev_bf16(l2), bd, epilogue, mxfp4_out=True)
+                qc, qs = mxq.quantize_act(mxq.W4A4, yl)
+                torch.cuda.synchronize()
+            assert torch.equal(lc, qc) and torch.equal(ls, qs), f"case {case}: fused branch MXFP4 output differs"
 
     if mode == mxq.W4A8 and mxq.gemm_fp8_static_out_supported(m, n, k):
         amax = mxq.fp8_calibrate(y)
