@@ -30,7 +30,7 @@ from gpu_util import assert_codes_equal, assert_output_close, dev_bf16, host_bit
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 24
+N_CASES = 48
 
 
 @pytest.fixture(scope="module", autouse=True)
