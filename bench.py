@@ -351,9 +351,9 @@ class Stack:
     def __init__(self, wl, torch, mxq, static=False, transform=False, lr_rank=0, fuse=True):
         self.wl, self.torch, self.mxq = wl, torch, mxq
         # the GEMMs of a block: fused projections where the pipelined kernel takes
-        # the stacked shape in both modes (its 32-bit offsets bound the output
-        # below 2 GiB, so A14B's 720p q, k, v stay apart); SVDQuant's per-linear
-        # branches keep them apart too
+        # the stacked shape in both modes (every Wan2.2 shape here, A14B's 720p
+        # q+k+v with its 2.3 GB output included); SVDQuant's per-linear branches
+        # keep the projections apart
         pipelined = lambda lin: all(mxq.gemm_kernel_name(md, wl.m_of(lin), lin.n, lin.k).startswith("pipe_")
                                     for md in (0, 1))
         ex = exec_linears(wl.linears, fuse and not lr_rank, pipelined)
