@@ -33,8 +33,11 @@ input), then the GEMM on the residual with T L2 in its fp32 sums and the
 epilogue (one kernel; shapes the pipelined GEMM does not take run the GEMM
 without epilogue, then y = epilogue(y_pre + T L2)). The FFN's first
 projection writes its bf16 hidden state, which the second one's branch reads.
-The factors are random bf16 of the right shapes (no trained weights to
-decompose); the branch's cost does not depend on their values.
+A fused projection (q+k+v, cross-attention k+v) is one linear there too, with
+one branch whose L2 spans its stacked columns (--separate-qkv gives each of
+its linears a branch of its own). The factors are random bf16 of the right
+shapes (no trained weights to decompose); the branch's cost does not depend
+on their values.
 
 --select replaces the step by the calibration-driven block selection over the
 A14B model (see run_select).
@@ -352,11 +355,12 @@ class Stack:
         self.wl, self.torch, self.mxq = wl, torch, mxq
         # the GEMMs of a block: fused projections where the pipelined kernel takes
         # the stacked shape in both modes (every Wan2.2 shape here, A14B's 720p
-        # q+k+v with its 2.3 GB output included); SVDQuant's per-linear branches
-        # keep the projections apart
+        # q+k+v with its 2.3 GB output included). With SVDQuant a fused
+        # projection is one linear with one branch of the given rank, as any
+        # other linear (its factors are those of the stacked weight)
         pipelined = lambda lin: all(mxq.gemm_kernel_name(md, wl.m_of(lin), lin.n, lin.k).startswith("pipe_")
                                     for md in (0, 1))
-        ex = exec_linears(wl.linears, fuse and not lr_rank, pipelined)
+        ex = exec_linears(wl.linears, fuse, pipelined)
         self.lins = [l for l, _ in ex]
         self.parts = [p for _, p in ex]
         self.static = static

@@ -96,3 +96,27 @@ def test_static_fp8_output_past_2gib(operands):
     fc, fs = mxq.gemm_fp8_static_out(ac, asc, wc, ws, amax, None, mxq.EPI_GELU_TANH)
     torch.cuda.synchronize()
     assert torch.equal(fc, rc) and torch.equal(fs, rs)
+
+
+def test_lowrank_bf16_output_past_2gib(operands):
+    """The GEMM with SVDQuant's branch on the stacked shape: each output column is its slice's own
+    GEMM with the branch (the same codes, T and L2 row), byte for byte, past 2 GiB of output."""
+    x, w = operands
+    r = 32
+    say("gemm+branch bf16 output > 2 GiB", M, N_STACK, K, r)
+    assert mxq.gemm_lowrank_supported(M, N_STACK, K)
+    g = torch.Generator(device="cuda:0").manual_seed(23)
+    t = (torch.randn((M, r), generator=g, device="cuda:0") * 0.5).to(torch.bfloat16)
+    l2 = (torch.randn((N_STACK, r), generator=g, device="cuda:0") * 0.05).to(torch.bfloat16)
+    wd = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    wc, ws = mxq.quantize_weight_mxfp4(wd)
+    ac, asc = mxq.quantize_act(mxq.W4A4, x)
+    y = mxq.gemm_lowrank(ac, asc, wc, ws, t, l2, None, mxq.EPI_GELU_TANH)
+    torch.cuda.synchronize()
+    for p in range(N_STACK // N_PART):
+        wpc, wps = mxq.quantize_weight_mxfp4(wd[p * N_PART:(p + 1) * N_PART])
+        yp = mxq.gemm_lowrank(ac, asc, wpc, wps, t, l2[p * N_PART:(p + 1) * N_PART].contiguous(), None,
+                              mxq.EPI_GELU_TANH)
+        torch.cuda.synchronize()
+        assert torch.equal(y[:, p * N_PART:(p + 1) * N_PART], yp), f"column slice {p} differs from its own GEMM"
+        del yp
