@@ -9,6 +9,9 @@ rows, so the output may exceed 2^31 bytes, as a stacked q+k+v projection at
 * sampled rows (row 0, rows past 2^31 / (2 N) where the old 32-bit offsets
   would have wrapped, and the ragged last tile) against the oracle, within the
   output tolerance.
+
+The same column-slice check covers the GEMM with SVDQuant's branch on the
+stacked shape and the stacked cross-attention k+v on the 512 text tokens.
 """
 
 import sys
@@ -120,3 +123,30 @@ def test_lowrank_bf16_output_past_2gib(operands):
         torch.cuda.synchronize()
         assert torch.equal(y[:, p * N_PART:(p + 1) * N_PART], yp), f"column slice {p} differs from its own GEMM"
         del yp
+
+
+@pytest.mark.parametrize("waves", [4, 8])
+def test_stacked_text_projection_equals_slices(waves):
+    """Cross-attention k+v on the 512 text tokens as one GEMM (512 x 10240 x 5120, the eight-wave kernel
+    by default): each half equals its own GEMM byte for byte, as for the stacked video projections."""
+    m, n_part, k = 512, 5120, 5120
+    say("stacked text k+v", m, 2 * n_part, k, waves)
+    x = synth.activation_bf16(31, m, k, ("student_t",))
+    w = synth.weight_bf16(32, 2 * n_part, k)
+    with w4a4_waves(waves):
+        xd = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+        wd = torch.from_numpy(w.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+        ac, asc = mxq.quantize_act(mxq.W4A4, xd)
+        wc, ws = mxq.quantize_weight_mxfp4(wd)
+        y = mxq.gemm(mxq.W4A4, ac, asc, wc, ws, None, mxq.EPI_NONE)
+        parts = []
+        for p in range(2):
+            wpc, wps = mxq.quantize_weight_mxfp4(wd[p * n_part:(p + 1) * n_part])
+            parts.append(mxq.gemm(mxq.W4A4, ac, asc, wpc, wps, None, mxq.EPI_NONE))
+        torch.cuda.synchronize()
+    for p, yp in enumerate(parts):
+        assert torch.equal(y[:, p * n_part:(p + 1) * n_part], yp), f"half {p} differs from its own GEMM"
+    oac, oas = oracle.quantize_act(mxq.W4A4, x[:64])
+    owc, ows = oracle.mxfp4_quantize(w)
+    y_ref = oracle.qdq_matmul(mxq.W4A4, oac, oas, owc, ows, None, mxq.EPI_NONE)
+    assert_output_close(host_bits(y[:64]), y_ref, "first 64 rows of the stacked text projection")
